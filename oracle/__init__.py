@@ -1,0 +1,36 @@
+"""Plain fp64 CPU oracle for one decode step of certified sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or link
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP path;
+the two agree only through the written rules stated in the docstrings below.
+
+Sources, cited by page and section (no other citation style is used here):
+
+* [S]  "Certified Sparse Attention via Perturbed Retrieval", structured summary of
+  the paper: sections Theoretical Foundation; Methodology > Problem Setup;
+  Methodology > Algorithm Components items 1-4; Theorems 1-4.
+* [A]  "Certified Sparse Attention via Perturbed Retrieval", the authors'
+  abstract (GQA-shared 4-bit scan, fresh perturbations per step).
+
+Where the pages leave a step open, the reading taken is stated where it is used
+and listed in the design doc's register of readings.
+
+Pinned against something other than itself in ``tests/test_oracle_*.py``:
+dense attention (library softmax), pack (exact rational residual norms), score
+bounds (brute force over every key), hash (published SplitMix64 outputs, KS test),
+inclusion probability, HT unbiasedness and variance, nesting, the small-tau
+limit, the error identity behind beta, the KL roots (library root finder),
+certificate coverage and the empirical failure rate.  Parity unpinned: the
+specific constants of the certificate completion (per-level tail split, the
+centre, the G and Q tails) -- the pages print no numbers for them; they are
+pinned only by their coverage tests and by agreement with the HIP path.
+"""
+
+from .canon import LN2, RSQRT_D, PADF, csum128, logtau, first_level  # noqa: F401
+from .dense import dense_attention, exact_scores  # noqa: F401
+from .pack import pack_kv_4bit  # noqa: F401
+from .bounds import scan_bounds  # noqa: F401
+from .perturb import splitmix64_mix, hash_prefix, perturbations  # noqa: F401
+from .certify import kl, kl_upper_root, kl_lower_root, level_certificate, tails_per_level  # noqa: F401
+from .decode import certified_decode, certified_decode_layer, level_sums  # noqa: F401

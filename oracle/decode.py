@@ -1,0 +1,144 @@
+"""One certified decode step for one layer (test infrastructure only).
+
+Follows the method's steps in the pages' order:
+
+1. Window / pool split: the last ``window`` tokens R are read exactly, the rest is
+   the pool P ([S] Algorithm Components item 1).
+2. Deterministic score bounds from the 4-bit keys, shared by the GQA group
+   (``bounds.scan_bounds``; [S] item 4, [A]).
+3. Exact maximum over a small set: c_lo = max(c_R, max_P LB); C_max = {UB >= c_lo};
+   c* = max(c_R, max over C_max of s) ([S] item 4, "exact maximum").
+4. Perturbations E_i (``perturb``), and each pool key's earliest possible level
+   l^ub = first((UB + E) - c*) ("bucketed by earliest possible inclusion level",
+   [S] item 4).  Reading: buckets are taken relative to the exact c*.
+5. Exact 16-bit reads only for candidates (l^ub <= J): s_i, the heavy level
+   h = first(s - c*) and the entry level l = first((s + E) - c*) (so l <= h, and
+   l^ub <= l because UB >= s).
+6. Per level j (tau_j = exp(LOGTAU[j])): B_j = {h <= j} (w >= tau, always in),
+   A_j = P \\ B_j, S_j = {l <= j}, k = |S_j & A_j|,
+   D^ = D_R + D_B + tau k, N^ = N_R + N_B + tau sum_{S&A} v ([S] item 2); the
+   letters R, B, A, k are read so that [S] Theorem 1's Var D^ <= tau D_A holds.
+7. Certificate per level (``certify``) and the stop at the first level with
+   beta <= eps ([S] item 3); if none, the exact fallback ([S] Results > Certificate
+   Validity mentions heads falling back to exact attention): o exact, beta = 0,
+   stop level J + 1, keys read n.  With n <= window every key is in the window:
+   o exact, beta = 0, stop level 0, keys read n.
+
+keys_read counts exact 16-bit key reads: window + |C_max union {l^ub <= j*}|
+(reading of "keys read", [S] Summary and Table 1's caption).
+"""
+
+import numpy as np
+
+from .canon import LN2, csum128, first_level, logtau  # noqa: F401
+from .bounds import scan_bounds
+from .certify import MEASURE_VALUE, budget_L, level_certificate
+from .dense import dense_attention, exact_scores
+from .perturb import perturbations
+
+
+def level_sums(j, hl, ll, w, Vr, vsq, D_R, N_R, Q_R):
+    """Deterministic and sampled sums at level j over the rescored keys.
+
+    Heavy keys B_j = {h <= j} add (w, w v, w |v|^2); light sampled keys
+    S_j & A_j = {l <= j < h} add (1, v, |v|^2).  Keys never rescored have l > J and
+    contribute nothing at any level.
+    """
+    heavy = hl <= j
+    light = (ll <= j) & ~heavy
+    return {
+        "D_det": D_R + float(w[heavy].sum()),
+        "N_det": N_R + w[heavy] @ Vr[heavy],
+        "Q_det": Q_R + float(w[heavy] @ vsq[heavy]),
+        "k": int(light.sum()),
+        "Vs": Vr[light].sum(axis=0),
+        "Ps": float(vsq[light].sum()),
+        "n_heavy": int(heavy.sum()),
+        "n_sample": int((ll <= j).sum()),
+    }
+
+
+def _exact_result(q16, K16, V16, n, stop_level):
+    d = dense_attention(q16, K16, V16, n)
+    return {"o_hat": d["o"], "beta": 0.0, "stop_level": stop_level, "keys_read": n,
+            "values_read": n, "dense": d}
+
+
+def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64,
+                     seed=0x5EED, step=0, layer=0, measure=MEASURE_VALUE, with_dense=True):
+    """Certified decode for the G queries q16 [G][128] of KV head h.
+
+    K16, V16: fp16 [n_cap][128] of this KV head.  Returns a list (one entry per
+    query) of dicts with o_hat, beta, stop_level, keys_read and a trace.
+    """
+    G = q16.shape[0]
+    W = window
+    if n <= W:
+        return [_exact_result(q16[g], K16, V16, n, 0) for g in range(G)]
+    npool = n - W
+    LT = logtau(r, J)
+    TAU = np.exp(LT)
+    L = budget_L(J, delta, measure)
+    Vd_all = V16[:n].astype(np.float64)
+    vsq_all = csum128(Vd_all * Vd_all)
+    Vmax = float(packed["vnorm"][h, :npool].astype(np.float64).max())
+    bnd = scan_bounds(q16, packed, h, npool)
+    E = perturbations(seed, step, layer, h, np.arange(npool))
+    results = []
+    for g in range(G):
+        s_R = exact_scores(q16[g], K16[npool:n])
+        c_R = float(s_R.max())
+        UB, LB = bnd["UB"][g], bnd["LB"][g]
+        c_lo = max(c_R, float(LB.max()))
+        cmax_pos = np.nonzero(UB >= c_lo)[0]
+        s_cm = exact_scores(q16[g], K16[cmax_pos])
+        c_star = max(c_R, float(s_cm.max())) if cmax_pos.size else c_R
+        p = UB + E
+        lub = first_level(p - c_star, LT)
+        cand = np.nonzero(lub <= J)[0]
+        s_c = exact_scores(q16[g], K16[cand])
+        hl = first_level(s_c - c_star, LT)
+        ll = first_level((s_c + E[cand]) - c_star, LT)
+        w_c = np.exp(s_c - c_star)
+        Vc = Vd_all[cand]
+        vsq_c = vsq_all[cand]
+        w_R = np.exp(s_R - c_star)
+        D_R = float(w_R.sum())
+        N_R = w_R @ Vd_all[npool:n]
+        Q_R = float(w_R @ vsq_all[npool:n])
+        levels = []
+        stop = None
+        for j in range(J + 1):
+            st = level_sums(j, hl, ll, w_c, Vc, vsq_c, D_R, N_R, Q_R)
+            cert = level_certificate(D_det=st["D_det"], N_det=st["N_det"], Q_det=st["Q_det"],
+                                     k=st["k"], Vs=st["Vs"], Ps=st["Ps"],
+                                     tau=float(TAU[j]), L=L, Vmax=Vmax, measure=measure)
+            cert.update(st)
+            levels.append(cert)
+            if cert["beta"] <= eps:
+                stop = j
+                break
+        trace = {"c_R": c_R, "c_lo": c_lo, "c_star": c_star, "cmax_pos": cmax_pos,
+                 "lub": lub, "cand": cand, "s_c": s_c, "h": hl, "l": ll, "E": E, "UB": UB,
+                 "LB": LB, "levels": levels, "L": L, "Vmax": Vmax, "D_R": D_R}
+        if stop is None:
+            res = _exact_result(q16[g], K16, V16, n, J + 1)
+            res["trace"] = trace
+            results.append(res)
+            continue
+        read_set = np.union1d(cmax_pos, cand[lub[cand] <= stop])
+        res = {"o_hat": levels[stop]["o_hat"], "beta": float(levels[stop]["beta"]),
+               "stop_level": stop, "keys_read": int(W + read_set.size),
+               "values_read": int(W + int((ll <= stop).sum())), "trace": trace}
+        if with_dense:
+            res["dense"] = dense_attention(q16[g], K16, V16, n)
+        results.append(res)
+    return results
+
+
+def certified_decode_layer(q16, K16, V16, packed, n, G, **kw):
+    """All KV heads of one layer: q16 [H_q][128], K16/V16 [H_kv][n_cap][128]."""
+    out = []
+    for h in range(K16.shape[0]):
+        out.extend(certified_decode(q16[h * G:(h + 1) * G], K16[h], V16[h], packed, h, n, **kw))
+    return out
