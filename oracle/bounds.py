@@ -6,28 +6,31 @@ dot-product work; [A]: the scan is shared across a GQA group and reads every key
 The pages do not give the bound's formula.  Reading taken (test infrastructure
 only; the HIP scan follows the same written rules):
 
-For KV head h, block b, query g of the group (q fp16), channel t:
+Per call, query g (fp16 q_g):
+  Q1. qa_g = max_t |q_gt|; beta_g = 2^(e-11) with qa_g = f 2^e, f in [0.5, 1)
+      (beta_g = 0 and q~ = 0 when qa_g = 0); q~_gt = rint_half_even(q_gt / beta_g)
+      in [-2048, 2048], so |q_gt - beta_g q~_gt| <= beta_g / 2.
+  Q2. qn_g = smallest fp32 y with y^2 >= R1-sum_t q_gt^2 * (1 + 2^-40) (so qn_g >= |q_g|),
+      qnp_g = qn_g * (1 + 2^-40); qabs_g = R1-sum_t |q_gt|.
+Per KV head h, block b (kappa_b = 2^kexp_b, integer zero points z_bt, kscale_bt):
+  B1. One power-of-two step shared by the group: m_b = qmax_h * ksmax_b (fp32, exact)
+      with qmax_h = max |q| over the group and ksmax_b = max_t kscale_bt; alpha_b = 0
+      when m_b = 0, else alpha_b = 2^(x-11) with m_b = f 2^x, f in [0.5, 1).
+  B2. Integer weights a~_gbt = rint_half_even(fp32(q_gt * kscale_bt) * 2^(11-x)) in
+      [-2048, 2048]; |q_gt kscale_bt - alpha_b a~_gbt| <= alpha_b / 2.
+  B3. base_gb = (beta_g kappa_b) * sum_t q~_gt z_bt (exact integer times a power of two);
+      eb_gb = (beta_g / 2) kappa_b sum_t |z_bt| (exact).
+  B4. Kmax_b = max_t (|kappa_b z_bt| + 15 kscale_bt); pad_gb = (2^-40 qabs_g) Kmax_b.
+Per key i of block b:
+  K1. I_gi = sum_t a~_gbt c_it and C_i = sum_t c_it (exact integers).
+  K2. shat_i = (base_gb + alpha_b I_gi) * RSQRT_D,
+      slack_i = (((alpha_b/2 * C_i + qnp_g * kerr_i) + eb_gb) + pad_gb) * RSQRT_D,
+      UB_i = shat_i + slack_i,  LB_i = shat_i - slack_i   (fp64, in this order).
 
-1. a_gt = q_gt * kscale_bt, exact in fp32 (fp16 x fp16).
-2. One power-of-two step per (h, b), shared by the group: m_b = qmax_h * ksmax_b
-   (fp32, exact) with qmax_h = max |q| over the group and ksmax_b = max_t kscale_bt.
-   If m_b = 0 then alpha_b = 0 and every weight is 0; otherwise m_b = f 2^x with
-   f in [0.5, 1) and alpha_b = 2^(x-11).
-3. Integer weights a~_gt = rint_half_even(a_gt * 2^(11-x)) in [-2048, 2048]; then
-   |a_gt - alpha_b a~_gt| <= alpha_b / 2 for every channel.
-4. Per key: I_gi = sum_t a~_gt c_it and C_i = sum_t c_it (exact integers).
-5. base_gb = R1-sum_t q_gt kmin_bt (fp64, exact products).
-6. qn_g = smallest fp32 y with y^2 >= R1-sum_t q_gt^2 * (1 + 2^-40) (so qn_g >= |q_g|),
-   qnp_g = qn_g * (1 + 2^-40); qabs_g = R1-sum_t |q_gt|;
-   Kmax_b = max_t (|kmin_bt| + 15 kscale_bt); pad_gb = (2^-40 * qabs_g) * Kmax_b.
-7. shat_i = (base_gb + alpha_b I_gi) * RSQRT_D,
-   slack_i = ((alpha_b/2 * C_i + qnp_g * kerr_i) + pad_gb) * RSQRT_D,
-   UB_i = shat_i + slack_i,  LB_i = shat_i - slack_i   (fp64, in this order).
-
-Validity: q.k = q.k~ + q.(k - k~); q.k~ = base + sum_t a_t c_t; the quantization of
-a_t moves that by at most alpha/2 * C_i, Cauchy-Schwarz bounds |q.(k - k~)| by
-|q| kerr_i, and the pad terms dominate every fp64 rounding of this computation and
-of the exact score's, so LB_i <= s_i <= UB_i holds for the fp64 values.
+Validity: q.k = q.k~ + q.(k - k~) with q.k~ = sum_t q_t kappa z_t + sum_t q_t kscale_t c_t.
+The first sum is base up to eb (Q1), the second is alpha I up to alpha/2 C (B2),
+Cauchy-Schwarz bounds |q.(k - k~)| by |q| kerr_i, and the pad dominates every fp64
+rounding here and in the exact score, so LB_i <= s_i <= UB_i for the fp64 values.
 """
 
 import numpy as np
@@ -36,56 +39,62 @@ from .canon import PADF, RSQRT_D, csum128, fp32_sqrt_up
 
 
 def query_constants(q16: np.ndarray) -> dict:
-    """Per-query constants of step 6 for an array of queries [G][128]."""
+    """Q1 and Q2 for an array of queries [G][128]."""
     qd = q16.astype(np.float64)
     qn = fp32_sqrt_up(csum128(qd * qd) * (1.0 + PADF)).astype(np.float64)
     qnp = qn * (1.0 + PADF)
     qabs = csum128(np.abs(qd))
-    return {"qn": qn, "qnp": qnp, "qabs": qabs}
+    qa = np.abs(qd).max(axis=1)
+    _, e = np.frexp(qa)
+    beta = np.where(qa > 0, np.ldexp(1.0, e - 11), 0.0)
+    qint = np.where(qa[:, None] > 0, np.rint(qd / np.where(beta > 0, beta, 1.0)[:, None]), 0.0)
+    return {"qn": qn, "qnp": qnp, "qabs": qabs, "qbeta": beta, "qint": qint.astype(np.int64)}
 
 
-def block_constants(q16: np.ndarray, kmin16: np.ndarray, kscale16: np.ndarray) -> dict:
-    """Steps 1-3, 5 and the block part of 6 for one KV head.
-
-    q16 [G][128]; kmin16, kscale16 [nb][128].  Returns alpha [nb], integer weights
-    wts [G][nb][128] (int64), base [G][nb], pad [G][nb].
-    """
-    G = q16.shape[0]
+def block_constants(q16: np.ndarray, packed: dict, h: int, nb: int) -> dict:
+    """B1-B4 for blocks 0..nb-1 of KV head h and the group's queries q16 [G][128]."""
+    qc = query_constants(q16)
     qf = q16.astype(np.float32)
-    ksf = kscale16.astype(np.float32)
+    ks16 = packed["kscale"][h, :nb]
+    ksf = ks16.astype(np.float32)
     qmax = np.float32(np.abs(qf).max())
     ksmax = ksf.max(axis=1)                                   # [nb]
     m = (qmax * ksmax).astype(np.float32)                     # exact
-    _, x = np.frexp(m)                                        # m = f 2^x, f in [0.5, 1)
+    _, x = np.frexp(m)
     x = x.astype(np.int64)
-    alpha = np.where(m > 0, np.ldexp(1.0, x - 11), 0.0)       # fp64, exact powers of two
-    a = qf[:, None, :] * ksf[None, :, :]                      # [G][nb][128] fp32, exact
+    alpha = np.where(m > 0, np.ldexp(1.0, x - 11), 0.0)
     scale = np.where(m > 0, np.ldexp(np.float32(1.0), (11 - x).astype(np.int32)), np.float32(0.0))
-    scaled = (a * scale[None, :, None].astype(np.float32)).astype(np.float32)
-    wts = np.rint(scaled).astype(np.int64)
-    qd = q16.astype(np.float64)
-    kmind = kmin16.astype(np.float64)
-    base = csum128(qd[:, None, :] * kmind[None, :, :])       # [G][nb]
-    qc = query_constants(q16)
-    kmax_b = (np.abs(kmind) + 15.0 * kscale16.astype(np.float64)).max(axis=1)  # [nb]
+    a = qf[:, None, :] * ksf[None, :, :]                      # [G][nb][128] fp32, exact
+    wts = np.rint((a * scale[None, :, None].astype(np.float32)).astype(np.float32)).astype(np.int64)
+    z = packed["z"][h, :nb].astype(np.int64)                  # [nb][128]
+    kappa = np.ldexp(1.0, packed["kexp"][h, :nb])             # [nb]
+    Bint = qc["qint"] @ z.T                                   # [G][nb] exact
+    base = (qc["qbeta"][:, None] * kappa[None, :]) * Bint.astype(np.float64)
+    Z1 = np.abs(z).sum(axis=1)
+    eb = ((qc["qbeta"][:, None] / 2.0) * kappa[None, :]) * Z1[None, :].astype(np.float64)
+    kmin = kappa[:, None] * z.astype(np.float64)
+    kmax_b = (np.abs(kmin) + 15.0 * ks16.astype(np.float64)).max(axis=1)
     pad = (PADF * qc["qabs"])[:, None] * kmax_b[None, :]
-    return {"alpha": alpha, "wts": wts, "base": base, "pad": pad, **qc}
+    return {"alpha": alpha, "wts": wts, "base": base, "eb": eb, "pad": pad, "Bint": Bint,
+            "Kmax": kmax_b, "Z1": Z1, **qc}
 
 
 def scan_bounds(q16: np.ndarray, packed: dict, h: int, npool: int) -> dict:
-    """UB and LB [G][npool] for the pool keys 0..npool-1 of KV head h (step 7)."""
+    """UB and LB [G][npool] for the pool keys 0..npool-1 of KV head h (K1, K2)."""
     nb = (npool + 31) // 32
     codes = packed["codes"][h, :32 * nb].astype(np.int64).reshape(nb, 32, 128)
-    bc = block_constants(q16, packed["kmin"][h, :nb], packed["kscale"][h, :nb])
+    bc = block_constants(q16, packed, h, nb)
     I = np.einsum("gbt,bit->gbi", bc["wts"], codes)          # exact int64
     C = codes.sum(axis=2)                                     # [nb][32]
     kerr = packed["kerr"][h, :32 * nb].astype(np.float64).reshape(nb, 32)
     alpha = bc["alpha"][None, :, None]
     shat = (bc["base"][:, :, None] + alpha * I.astype(np.float64)) * RSQRT_D
-    slack = (((alpha / 2.0) * C[None, :, :].astype(np.float64)
-              + bc["qnp"][:, None, None] * kerr[None, :, :])
+    slack = ((((alpha / 2.0) * C[None, :, :].astype(np.float64)
+               + bc["qnp"][:, None, None] * kerr[None, :, :])
+              + bc["eb"][:, :, None])
              + bc["pad"][:, :, None]) * RSQRT_D
-    UB = (shat + slack).reshape(q16.shape[0], 32 * nb)[:, :npool]
-    LB = (shat - slack).reshape(q16.shape[0], 32 * nb)[:, :npool]
-    return {"UB": UB, "LB": LB, "I": I.reshape(q16.shape[0], -1)[:, :npool],
+    G = q16.shape[0]
+    UB = (shat + slack).reshape(G, 32 * nb)[:, :npool]
+    LB = (shat - slack).reshape(G, 32 * nb)[:, :npool]
+    return {"UB": UB, "LB": LB, "I": I.reshape(G, -1)[:, :npool],
             "C": C.reshape(-1)[:npool], "consts": bc}

@@ -6,14 +6,20 @@ Reading taken (test infrastructure only; the HIP pack follows the same rules):
 
 * blocks of 32 consecutive tokens, aligned at multiples of 32; only complete
   blocks are packed;
-* per block b and channel t: kmin = min_i k_it (an fp16 value, stored exactly),
-  kscale = fp16 round-to-nearest-even of the fp64 value (max - min) / 15;
-* code c_it = clamp(rint_half_even((k_it - kmin) / kscale), 0, 15) in fp64, and 0
-  when kscale = 0;
-* dequantized k~_it = kmin + kscale * c_it (exact in fp64);
+* zero points on a per-block power-of-two grid: with mn_t = min_i k_it (fp16) and
+  A = max_t |mn_t|, kappa = 2^(y - 11) where A = f 2^y, f in [0.5, 1) (kappa = 1 and
+  all z = 0 when A = 0); z_t = floor(mn_t / kappa), a 12-bit integer in
+  [-2048, 2047]; the zero point is kmin_t = kappa z_t <= mn_t (exact in fp64);
+* kscale_t = fp16 round-to-nearest-even of the fp64 value (max_i k_it - kmin_t) / 15;
+* code c_it = clamp(rint_half_even((k_it - kmin_t) / kscale_t), 0, 15) in fp64, and 0
+  when kscale_t = 0;
+* dequantized k~_it = kmin_t + kscale_t c_it (exact in fp64);
 * kerr_i = smallest fp16 h with h^2 >= R1-sum_t (k_it - k~_it)^2 * (1 + 2^-40), and
   vnorm_i = smallest fp16 h with h^2 >= R1-sum_t v_it^2 * (1 + 2^-40), so that
   kerr_i >= |k_i - k~_i| and vnorm_i >= |v_i| hold exactly.
+
+The integer zero points make the scan's offset term q.kmin an exact integer dot
+product once the query is put on its own power-of-two grid (see ``bounds``).
 """
 
 import numpy as np
@@ -27,15 +33,21 @@ def pack_kv_4bit(K16: np.ndarray, V16: np.ndarray, nblocks: int) -> dict:
     """Pack blocks 0..nblocks-1 of one layer.
 
     K16, V16: fp16 [H_kv][n_cap][128].  Returns logical arrays:
-    codes u8 [H_kv][32*nblocks][128], kmin and kscale fp16 [H_kv][nblocks][128],
-    kerr and vnorm fp16 [H_kv][32*nblocks].
+    codes u8 [H_kv][32*nblocks][128]; z int16 and kscale fp16 [H_kv][nblocks][128];
+    kexp int32 [H_kv][nblocks] (kappa = 2^kexp); kerr and vnorm fp16 [H_kv][32*nblocks].
     """
     H = K16.shape[0]
     ntok = BLOCK * nblocks
     Kb = K16[:, :ntok].astype(np.float64).reshape(H, nblocks, BLOCK, 128)
-    kmin = Kb.min(axis=2)
-    kmax = Kb.max(axis=2)
-    kscale16 = ((kmax - kmin) / 15.0).astype(np.float16)
+    mn = Kb.min(axis=2)
+    mx = Kb.max(axis=2)
+    A = np.abs(mn).max(axis=2)                                # [H][nb]
+    _, y = np.frexp(A)
+    kexp = np.where(A > 0, y - 11, 0).astype(np.int32)
+    kappa = np.ldexp(1.0, kexp)
+    z = np.where(A[..., None] > 0, np.floor(mn / kappa[..., None]), 0.0)
+    kmin = kappa[..., None] * z                               # exact
+    kscale16 = ((mx - kmin) / 15.0).astype(np.float16)
     ks = kscale16.astype(np.float64)
     num = Kb - kmin[:, :, None, :]
     safe = np.where(ks > 0, ks, 1.0)[:, :, None, :]
@@ -48,9 +60,15 @@ def pack_kv_4bit(K16: np.ndarray, V16: np.ndarray, nblocks: int) -> dict:
     vnorm = fp16_sqrt_up(csum128(Vd * Vd) * (1.0 + PADF))
     return {
         "codes": codes.astype(np.uint8).reshape(H, ntok, 128),
-        "kmin": kmin.astype(np.float16),
+        "z": z.astype(np.int16),
+        "kexp": kexp,
         "kscale": kscale16,
         "kerr": kerr.astype(np.float16),
         "vnorm": vnorm.astype(np.float16),
         "nblocks": nblocks,
     }
+
+
+def zero_points(packed: dict) -> np.ndarray:
+    """kmin = 2^kexp * z as fp64 [H][nb][128]."""
+    return np.ldexp(1.0, packed["kexp"])[..., None] * packed["z"].astype(np.float64)

@@ -18,6 +18,7 @@ import oracle
 import synth
 from oracle.bounds import block_constants
 from oracle.canon import fp16_sqrt_up, fp32_sqrt_up
+from oracle.pack import zero_points
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -56,11 +57,18 @@ def test_pack_codes_and_block_metadata(cfg1, cfg1_packed):
     pk = cfg1_packed
     K = cfg1.K[0].astype(np.float64).reshape(-1, 32, 128)
     codes = pk["codes"][0].reshape(-1, 32, 128).astype(np.float64)
-    kmin = pk["kmin"][0].astype(np.float64)
+    kmin = zero_points(pk)[0]
+    kappa = np.ldexp(1.0, pk["kexp"][0])[:, None]
     ks = pk["kscale"][0].astype(np.float64)
     assert codes.min() >= 0 and codes.max() <= 15
-    np.testing.assert_array_equal(kmin, K.min(axis=1))
-    # kscale is the fp16 value nearest to (max-min)/15: 15*kscale is within 15 half-ulps.
+    z = pk["z"][0].astype(np.int64)
+    assert z.min() >= -2048 and z.max() <= 2047
+    # zero point: the block minimum rounded down onto the block's power-of-two grid
+    mn = K.min(axis=1)
+    assert np.all(kmin <= mn) and np.all(mn - kmin < kappa)
+    # the grid is as fine as 12 bits allow: the largest |min| needs more than 10 bits
+    assert np.all(np.abs(mn).max(axis=1) >= 1024 * kappa[:, 0])
+    # kscale is the fp16 value nearest to (max - kmin)/15: within 15 half-ulps
     span = K.max(axis=1) - kmin
     ulp = np.spacing(pk["kscale"][0]).astype(np.float64)
     assert np.all(np.abs(15.0 * ks - span) <= 15.0 * ulp / 2 + 1e-30)
@@ -79,7 +87,8 @@ def test_pack_norm_bounds_exact_rational(cfg1, cfg1_packed):
     for i in toks:
         b = i // 32
         k = [Fraction(float(x)) for x in cfg1.K[0, i]]
-        kmin = [Fraction(float(x)) for x in pk["kmin"][0, b]]
+        kappa = Fraction(2) ** int(pk["kexp"][0, b])
+        kmin = [kappa * int(x) for x in pk["z"][0, b]]
         ks = [Fraction(float(x)) for x in pk["kscale"][0, b]]
         c = [int(x) for x in pk["codes"][0, i]]
         res2 = sum((k[t] - kmin[t] - ks[t] * c[t]) ** 2 for t in range(128))
@@ -148,14 +157,25 @@ def test_bounds_hold_for_every_key_config2():
 
 
 def test_bounds_integer_weights(cfg1, cfg1_packed):
-    """|q*kscale - alpha*w| <= alpha/2 with integer weights |w| <= 2048."""
+    """|q*kscale - alpha*w| <= alpha/2 with |w| <= 2048; |q - beta*q~| <= beta/2."""
     qg = cfg1.q
-    bc = block_constants(qg, cfg1_packed["kmin"][0], cfg1_packed["kscale"][0])
+    nb = cfg1.n // 32
+    bc = block_constants(qg, cfg1_packed, 0, nb)
     a = qg.astype(np.float64)[:, None, :] * cfg1_packed["kscale"][0].astype(np.float64)[None]
     alpha = bc["alpha"][None, :, None]
     assert np.abs(bc["wts"]).max() <= 2048
     assert np.all(np.abs(a - alpha * bc["wts"]) <= alpha / 2)
     assert np.abs(bc["wts"]).max() >= 512       # the step is not needlessly coarse
+    qd = qg.astype(np.float64)
+    beta = bc["qbeta"][:, None]
+    assert np.all(np.abs(qd - beta * bc["qint"]) <= beta / 2)
+    assert np.all(np.abs(bc["qint"]).max(axis=1) >= 1024)
+    # the offset term is exact: base equals q~ . kmin times beta, in exact arithmetic
+    kmin = zero_points(cfg1_packed)[0]
+    for g in range(cfg1.G):
+        for b in (0, 7, nb - 1):
+            exact = sum(Fraction(int(bc["qint"][g, t])) * Fraction(float(kmin[b, t])) for t in range(128))
+            assert Fraction(float(bc["base"][g, b])) == exact * Fraction(float(bc["qbeta"][g]))
 
 
 def test_bounds_planted_mistake_is_caught(cfg1, cfg1_packed):
