@@ -1,0 +1,17 @@
+"""Certified sparse attention via perturbed retrieval: one decode step of one layer
+on MI355X (gfx950), as hand-written HIP kernels behind the C ABI in include/csa.h.
+
+The Python layer only marshals torch tensors into the C ABI; the library must be
+built (``_build.build()``) and there is no CPU fallback.
+"""
+
+from .api import (  # noqa: F401
+    Event,
+    PackedKV,
+    allocate_workspace,
+    certified_decode_attention,
+    dense_decode_attention,
+    pack_kv_4bit,
+    scan_bounds,
+    workspace_bytes,
+)

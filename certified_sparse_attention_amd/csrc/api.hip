@@ -1,0 +1,432 @@
+// C ABI of the certified decode path (declarations and contracts in include/csa.h).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+// The launchers take the kernels' argument structs, so the kernel sources are
+// compiled as part of this one translation unit.
+#include "scan.hip"
+#include "select.hip"
+#include "certify.hip"
+#include "dense.hip"
+#include "pack.hip"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_shape(const csa_shape *s) {
+  if (!s) return fail(CSA_ERR_INVALID_ARGUMENT, "shape is null");
+  if (s->head_dim != csa::kD) return fail(CSA_ERR_INVALID_ARGUMENT, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->num_kv_heads < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "num_kv_heads must be >= 1");
+  if (s->group_size < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "group_size must be >= 1");
+  if (s->group_size > csa::kMaxG) return fail(CSA_ERR_UNSUPPORTED, "group_size must be <= %d", csa::kMaxG);
+  if (s->n_cap < 32 || s->n_cap % 32 != 0 || s->n_cap >= (int64_t(1) << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "n_cap must be a positive multiple of 32 below 2^31");
+  return CSA_OK;
+}
+
+int check_params(const csa_params *p) {
+  if (!p) return fail(CSA_ERR_INVALID_ARGUMENT, "params is null");
+  if (!(p->eps > 0.0) || !std::isfinite(p->eps)) return fail(CSA_ERR_INVALID_ARGUMENT, "eps must be > 0");
+  if (!(p->delta > 0.0 && p->delta < 1.0)) return fail(CSA_ERR_INVALID_ARGUMENT, "delta must lie in (0, 1)");
+  if (p->r < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "r must be >= 1");
+  if (p->J < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "J must be >= 0");
+  if (p->J > csa::kMaxJ) return fail(CSA_ERR_UNSUPPORTED, "J must be <= %d", csa::kMaxJ);
+  if (p->window < 32) return fail(CSA_ERR_UNSUPPORTED, "window must be >= 32");
+  if (p->measure < 0 || p->measure > 2) return fail(CSA_ERR_INVALID_ARGUMENT, "unknown measure %d", p->measure);
+  return CSA_OK;
+}
+
+csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
+  csa::Plan P;
+  P.H_kv = s->num_kv_heads;
+  P.G = s->group_size;
+  P.H_q = P.H_kv * P.G;
+  P.J = p->J;
+  P.W = p->window;
+  const int64_t npool = n_max > p->window ? n_max - p->window : 0;
+  P.npool_cap = npool > 0 ? npool : 1;
+  P.ntiles = (P.npool_cap + csa::kBucketTile - 1) / csa::kBucketTile;
+  const size_t Hq = (size_t)P.H_q, J1 = (size_t)P.J + 1, J2 = (size_t)P.J + 2, npc = (size_t)P.npool_cap;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  P.qf = take(Hq * csa::kD * sizeof(float));
+  P.qconst = take(Hq * csa::kQc * sizeof(double));
+  P.qA = take((size_t)P.H_kv * 2048);
+  P.lt = take(J1 * sizeof(double));
+  P.tau = take(J1 * sizeof(double));
+  P.prefix = take((size_t)P.H_kv * sizeof(uint64_t));
+  P.sR = take(Hq * (size_t)P.W * sizeof(double));
+  P.cR = 0;
+  P.clo = take(Hq * sizeof(unsigned long long));
+  P.cstar = take(Hq * sizeof(unsigned long long));
+  P.vmax = take((size_t)P.H_kv * sizeof(unsigned));
+  P.cmcnt = take(Hq * sizeof(int));
+  P.cmpos = take(Hq * npc * sizeof(int));
+  P.hist = take(Hq * J2 * sizeof(int));
+  P.tilecnt = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.ccount = take(Hq * sizeof(int));
+  P.pbuf = take(Hq * npc * sizeof(double));
+  P.ubuf = take(Hq * npc * sizeof(double));
+  P.lub = take(Hq * npc);
+  P.candpos = take(Hq * npc * sizeof(int));
+  P.rec_s = take(Hq * npc * sizeof(double));
+  P.rec_w = take(Hq * npc * sizeof(double));
+  P.rec_vsq = take(Hq * npc * sizeof(double));
+  P.rec_hl = take(Hq * npc * sizeof(int));
+  P.partial = take(Hq * csa::kNumSeg * J1 * csa::kStatW * sizeof(double));
+  P.stats = take(Hq * J1 * csa::kStatW * sizeof(double));
+  P.winsum = take(Hq * 130 * sizeof(double));
+  P.betalv = take(Hq * J1 * sizeof(double));
+  P.dhatlv = take(Hq * J1 * sizeof(double));
+  P.klv = take(Hq * J1 * sizeof(int));
+  P.flags = take(Hq * sizeof(int));
+  P.exactp = take(Hq * csa::kExactChunks * 130 * sizeof(double));
+  P.total = off;
+  return P;
+}
+
+template <class T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+int check_packed(const csa_packed *p) {
+  if (!p || !p->codes || !p->kscale || !p->zq || !p->bmeta || !p->kerr || !p->vnorm)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "packed arrays must all be non-null");
+  return CSA_OK;
+}
+
+// Prep + scan shared by the certified call and the bounds diagnostic.
+int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, const uint16_t *K,
+                  const csa_packed *pk, int64_t n, void *ws, const csa::Plan &P, double *lb_out,
+                  double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st) {
+  csa::PrepArgs pa;
+  pa.q = q;
+  pa.K = K;
+  pa.n_cap = s->n_cap;
+  pa.n = n;
+  pa.W = p->window;
+  pa.G = P.G;
+  pa.J = P.J;
+  pa.r = p->r;
+  pa.H_kv = P.H_kv;
+  pa.seed = p->seed;
+  pa.step = p->step;
+  pa.layer = p->layer;
+  pa.qf = at<float>(ws, P.qf);
+  pa.qconst = at<double>(ws, P.qconst);
+  pa.qA = at<int8_t>(ws, P.qA);
+  pa.lt = at<double>(ws, P.lt);
+  pa.tau = at<double>(ws, P.tau);
+  pa.prefix = at<uint64_t>(ws, P.prefix);
+  pa.sR = at<double>(ws, P.sR);
+  pa.clo = at<unsigned long long>(ws, P.clo);
+  pa.cstar = at<unsigned long long>(ws, P.cstar);
+  pa.vmax = at<unsigned>(ws, P.vmax);
+  pa.cmcnt = at<int>(ws, P.cmcnt);
+  pa.hist = at<int>(ws, P.hist);
+  pa.ccount = at<int>(ws, P.ccount);
+  pa.flags = at<int>(ws, P.flags);
+  hipError_t e = csa::launch_prep(pa, st);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  const int64_t npool = n - p->window;
+  if (npool <= 0) return CSA_OK;
+  csa::ScanArgs sa;
+  sa.codes = pk->codes;
+  sa.kscale = pk->kscale;
+  sa.zq = pk->zq;
+  sa.bmeta = reinterpret_cast<const csa::BlockMeta *>(pk->bmeta);
+  sa.kerr = pk->kerr;
+  sa.vnorm = pk->vnorm;
+  sa.n_cap = s->n_cap;
+  sa.nb_cap = s->n_cap / csa::kBlk;
+  sa.npool = npool;
+  sa.nb_pool = (npool + csa::kBlk - 1) / csa::kBlk;
+  sa.npool_cap = P.npool_cap;
+  sa.G = P.G;
+  sa.H_kv = P.H_kv;
+  sa.waves_per_head = (int)((sa.nb_pool + csa::kBlocksPerWave - 1) / csa::kBlocksPerWave);
+  sa.qf = pa.qf;
+  sa.qconst = pa.qconst;
+  sa.qA = pa.qA;
+  sa.prefix = pa.prefix;
+  sa.pbuf = at<double>(ws, P.pbuf);
+  sa.ubuf = at<double>(ws, P.ubuf);
+  sa.clo = pa.clo;
+  sa.vmax = pa.vmax;
+  sa.lb_out = lb_out;
+  sa.e_out = e_out;
+  if (ev0 && (e = hipEventRecord((hipEvent_t)ev0, st)) != hipSuccess) return hip_fail(e, "event");
+  e = csa::launch_scan(sa, st);
+  if (e != hipSuccess) return hip_fail(e, "scan");
+  if (ev1 && (e = hipEventRecord((hipEvent_t)ev1, st)) != hipSuccess) return hip_fail(e, "event");
+  if (ub_diag) {
+    e = hipMemcpy2DAsync(ub_diag, (size_t)npool * sizeof(double), sa.ubuf, (size_t)P.npool_cap * sizeof(double),
+                         (size_t)npool * sizeof(double), (size_t)P.H_q, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "copy UB");
+  }
+  return CSA_OK;
+}
+
+__global__ void trace_kernel(const double *qconst, const unsigned long long *clo,
+                             const unsigned long long *cstar, const int *cmcnt, const int *ccount,
+                             int Hq, double *c_R, double *c_lo, double *c_star, int *cm, int *cc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Hq) return;
+  if (c_R) c_R[i] = qconst[(int64_t)i * csa::kQc + csa::QC_CR];
+  if (c_lo) c_lo[i] = csa::dec_max(clo[i]);
+  if (c_star) c_star[i] = csa::dec_max(cstar[i]);
+  if (cm) cm[i] = cmcnt[i];
+  if (cc) cc[i] = ccount[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARGUMENT: return "CSA_ERR_INVALID_ARGUMENT";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+    default: return "CSA_ERR_UNKNOWN";
+  }
+}
+
+const char *csa_last_error(void) { return g_err; }
+
+int csa_pack_kv_4bit(const csa_shape *shape, const uint16_t *K, const uint16_t *V, int64_t block_begin,
+                     int64_t block_end, const csa_packed *out, csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!K || !V) return fail(CSA_ERR_INVALID_ARGUMENT, "K and V must be non-null");
+  if ((rc = check_packed(out))) return rc;
+  const int64_t nb = shape->n_cap / csa::kBlk;
+  if (block_begin < 0 || block_end < block_begin || block_end > nb)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "block range [%lld, %lld) outside [0, %lld]", (long long)block_begin,
+                (long long)block_end, (long long)nb);
+  hipError_t e = csa::launch_pack(*shape, K, V, block_begin, block_end, *out, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "pack");
+}
+
+size_t csa_workspace_bytes(const csa_shape *shape, const csa_params *params, int64_t n_max) {
+  if (check_shape(shape) || check_params(params) || n_max < 1) return 0;
+  return make_plan(shape, params, n_max).total;
+}
+
+int csa_scan_bounds(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
+                    const csa_packed *packed, int64_t n, void *workspace, size_t workspace_bytes, double *UB,
+                    double *LB, double *E, csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_shape(shape);
+  if (rc || (rc = check_params(params))) return rc;
+  if (!q || !K) return fail(CSA_ERR_INVALID_ARGUMENT, "q and K must be non-null");
+  if ((rc = check_packed(packed))) return rc;
+  if (n < 1 || n > shape->n_cap) return fail(CSA_ERR_INVALID_ARGUMENT, "n must lie in [1, n_cap]");
+  const csa::Plan P = make_plan(shape, params, n);
+  if (!workspace || workspace_bytes < P.total)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
+  return run_prep_scan(shape, params, q, K, packed, n, workspace, P, LB, E, UB, nullptr, nullptr,
+                       (hipStream_t)stream);
+}
+
+int csa_certified_decode_attention(const csa_shape *shape, const csa_params *params, const uint16_t *q,
+                                   const uint16_t *K, const uint16_t *V, const csa_packed *packed, int64_t n,
+                                   void *workspace, size_t workspace_bytes, float *o_hat, double *beta,
+                                   int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
+                                   csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_shape(shape);
+  if (rc || (rc = check_params(params))) return rc;
+  if (!q || !K || !V || !o_hat || !beta || !stop_level || !keys_read)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "q, K, V and every output must be non-null");
+  if (n < 1 || n > shape->n_cap) return fail(CSA_ERR_INVALID_ARGUMENT, "n must lie in [1, n_cap]");
+  const bool all_exact = n <= params->window;
+  if (!all_exact && (rc = check_packed(packed))) return rc;
+  const csa::Plan P = make_plan(shape, params, n);
+  if (!workspace || workspace_bytes < P.total)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
+  hipStream_t st = (hipStream_t)stream;
+  void *ev0 = trace ? trace->ev_scan_begin : nullptr;
+  void *ev1 = trace ? trace->ev_scan_end : nullptr;
+  rc = run_prep_scan(shape, params, q, K, packed, n, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
+  if (rc) return rc;
+  void *ws = workspace;
+  const int64_t npool = n - params->window;
+  hipError_t e;
+  if (!all_exact) {
+    csa::SelectArgs sa;
+    sa.K = K;
+    sa.V = V;
+    sa.n_cap = shape->n_cap;
+    sa.npool = npool;
+    sa.npool_cap = P.npool_cap;
+    sa.ntiles = (npool + csa::kBucketTile - 1) / csa::kBucketTile;
+    sa.G = P.G;
+    sa.J = P.J;
+    sa.qf = at<float>(ws, P.qf);
+    sa.lt = at<double>(ws, P.lt);
+    sa.prefix = at<uint64_t>(ws, P.prefix);
+    sa.pbuf = at<double>(ws, P.pbuf);
+    sa.ubuf = at<double>(ws, P.ubuf);
+    sa.clo = at<unsigned long long>(ws, P.clo);
+    sa.cstar = at<unsigned long long>(ws, P.cstar);
+    sa.cmcnt = at<int>(ws, P.cmcnt);
+    sa.cmpos = at<int>(ws, P.cmpos);
+    sa.hist = at<int>(ws, P.hist);
+    sa.tilecnt = at<int>(ws, P.tilecnt);
+    sa.tileoff = at<int>(ws, P.tileoff);
+    sa.ccount = at<int>(ws, P.ccount);
+    sa.lub = at<int8_t>(ws, P.lub);
+    sa.candpos = at<int>(ws, P.candpos);
+    sa.rec_s = at<double>(ws, P.rec_s);
+    sa.rec_w = at<double>(ws, P.rec_w);
+    sa.rec_vsq = at<double>(ws, P.rec_vsq);
+    sa.rec_hl = at<int>(ws, P.rec_hl);
+    if ((e = csa::launch_select(sa, P.H_q, st)) != hipSuccess) return hip_fail(e, "select");
+  }
+  csa::CertArgs ca;
+  ca.K = K;
+  ca.V = V;
+  ca.n_cap = shape->n_cap;
+  ca.n = n;
+  ca.npool = npool > 0 ? npool : 0;
+  ca.npool_cap = P.npool_cap;
+  ca.G = P.G;
+  ca.J = P.J;
+  ca.W = params->window;
+  ca.measure = params->measure;
+  ca.eps = params->eps;
+  {
+    const int tails = params->measure == CSA_MEASURE_DENOM ? 2 : (params->measure == CSA_MEASURE_OUTNORM ? 5 : 6);
+    ca.L = std::log((double)tails * (double)(params->J + 1) / params->delta);
+  }
+  ca.qf = at<float>(ws, P.qf);
+  ca.lt = at<double>(ws, P.lt);
+  ca.tau = at<double>(ws, P.tau);
+  ca.sR = at<double>(ws, P.sR);
+  ca.cstar = at<unsigned long long>(ws, P.cstar);
+  ca.vmax = at<unsigned>(ws, P.vmax);
+  ca.ccount = at<int>(ws, P.ccount);
+  ca.candpos = at<int>(ws, P.candpos);
+  ca.rec_hl = at<int>(ws, P.rec_hl);
+  ca.hist = at<int>(ws, P.hist);
+  ca.cmcnt = at<int>(ws, P.cmcnt);
+  ca.cmpos = at<int>(ws, P.cmpos);
+  ca.rec_w = at<double>(ws, P.rec_w);
+  ca.rec_vsq = at<double>(ws, P.rec_vsq);
+  ca.lub = at<int8_t>(ws, P.lub);
+  ca.partial = at<double>(ws, P.partial);
+  ca.stats = at<double>(ws, P.stats);
+  ca.winsum = at<double>(ws, P.winsum);
+  ca.betalv = at<double>(ws, P.betalv);
+  ca.dhatlv = at<double>(ws, P.dhatlv);
+  ca.klv = at<int>(ws, P.klv);
+  ca.flags = at<int>(ws, P.flags);
+  ca.exactp = at<double>(ws, P.exactp);
+  ca.o_hat = o_hat;
+  ca.beta = beta;
+  ca.stop = stop_level;
+  ca.keys_read = keys_read;
+  ca.all_exact = all_exact ? 1 : 0;
+  if ((e = csa::launch_certify(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");
+
+  if (trace) {
+    const int Hq = P.H_q;
+    hipLaunchKernelGGL(trace_kernel, dim3((Hq + 63) / 64), dim3(64), 0, st, at<double>(ws, P.qconst),
+                       at<unsigned long long>(ws, P.clo), at<unsigned long long>(ws, P.cstar),
+                       at<int>(ws, P.cmcnt), at<int>(ws, P.ccount), Hq, trace->c_R, trace->c_lo,
+                       trace->c_star, trace->cmax_count, trace->cand_count);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "trace");
+    const size_t J1 = (size_t)P.J + 1;
+    auto cp = [&](void *dst, size_t off, size_t bytes) -> hipError_t {
+      return dst ? hipMemcpyAsync(dst, at<char>(ws, off), bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
+    };
+    if (!all_exact) {
+      if ((e = cp(trace->bucket_count, P.hist, (size_t)Hq * (J1 + 1) * sizeof(int))) != hipSuccess ||
+          (e = cp(trace->beta_level, P.betalv, (size_t)Hq * J1 * sizeof(double))) != hipSuccess ||
+          (e = cp(trace->dhat_level, P.dhatlv, (size_t)Hq * J1 * sizeof(double))) != hipSuccess ||
+          (e = cp(trace->k_level, P.klv, (size_t)Hq * J1 * sizeof(int))) != hipSuccess ||
+          (e = cp(trace->logtau, P.lt, J1 * sizeof(double))) != hipSuccess)
+        return hip_fail(e, "trace copy");
+      if (trace->lub && npool > 0) {
+        e = hipMemcpy2DAsync(trace->lub, (size_t)npool, at<char>(ws, P.lub), (size_t)P.npool_cap, (size_t)npool,
+                             (size_t)Hq, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, "trace lub");
+      }
+    }
+  }
+  return CSA_OK;
+}
+
+size_t csa_dense_workspace_bytes(const csa_shape *shape, int64_t n_max) {
+  if (check_shape(shape) || n_max < 1) return 0;
+  return align_up((size_t)shape->num_kv_heads * shape->group_size * csa::dense_nsplit(n_max) * 130 * sizeof(float));
+}
+
+int csa_dense_decode_attention(const csa_shape *shape, const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                               int64_t n, void *workspace, size_t workspace_bytes, float *o, csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !K || !V || !o) return fail(CSA_ERR_INVALID_ARGUMENT, "q, K, V and o must be non-null");
+  if (n < 1 || n > shape->n_cap) return fail(CSA_ERR_INVALID_ARGUMENT, "n must lie in [1, n_cap]");
+  const size_t need = csa_dense_workspace_bytes(shape, n);
+  if (!workspace || workspace_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  csa::DenseArgs a;
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.n_cap = shape->n_cap;
+  a.n = n;
+  a.G = shape->group_size;
+  a.nsplit = csa::dense_nsplit(n);
+  a.part = static_cast<float *>(workspace);
+  a.o = o;
+  hipError_t e = csa::launch_dense(a, shape->num_kv_heads, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "dense");
+}
+
+int csa_event_create(void **event) {
+  if (!event) return fail(CSA_ERR_INVALID_ARGUMENT, "event is null");
+  hipEvent_t ev;
+  hipError_t e = hipEventCreate(&ev);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  *event = ev;
+  return CSA_OK;
+}
+
+int csa_event_destroy(void *event) {
+  hipError_t e = hipEventDestroy((hipEvent_t)event);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "hipEventDestroy");
+}
+
+int csa_event_elapsed_ms(void *begin, void *end, float *ms) {
+  if (!ms) return fail(CSA_ERR_INVALID_ARGUMENT, "ms is null");
+  hipError_t e = hipEventElapsedTime(ms, (hipEvent_t)begin, (hipEvent_t)end);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "hipEventElapsedTime");
+}
+
+}  // extern "C"

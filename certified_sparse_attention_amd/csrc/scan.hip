@@ -1,0 +1,385 @@
+// Per-call constants and the GQA-shared 4-bit scan.
+//
+// "Certified Sparse Attention via Perturbed Retrieval": summary page, Methodology >
+// Algorithm Components items 1 (window / pool split, Exp(1) perturbations from a
+// 53-bit hash) and 4 (4-bit keys give deterministic score bounds; candidates are
+// bucketed by their earliest possible inclusion level); authors' abstract (the scan
+// is shared across a GQA group and reads every key once).
+//
+// Bound per pool key i and query g (all integers exact; fp64 in this order):
+//   shat  = (base_gb + alpha_b I_gi) * RSQRT_D
+//   slack = (((alpha_b/2 C_i + qnp_g kerr_i) + eb_gb) + pad_gb) * RSQRT_D
+//   UB = shat + slack, LB = shat - slack, p = UB + E_i
+// with I_gi = sum_t a~_gbt c_it and C_i = sum_t c_it from one i8 MFMA chain, and
+// base_gb = beta_g kappa_b sum_t q~_gt z_bt from a second one.  The integer weights
+// a~ = rint(q kscale 2^(11-x)) lie in [-2048, 2048]; each is split a~ = 128 a1 + a0
+// (a1 in [-16, 16], a0 in [-64, 63]) into two int8 rows of the MFMA's A operand.
+//
+// MFMA operand rows (16): query g's high part at row 4(g%4) + 2(g/4), its low part
+// one row below; row 14 is all ones (gives C_i); row 15 is zero.  So G <= 7.
+// Output row 4k+i lands in register i of lanes 16k..16k+15, column = lane % 16.
+#include "common.h"
+
+namespace csa {
+
+__device__ inline int op_row(int g, int part) { return 4 * (g & 3) + 2 * (g >> 2) + part; }
+
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ prep
+struct PrepArgs {
+  const uint16_t *q, *K;
+  int64_t n_cap, n;
+  int W, G, J, r, H_kv;
+  uint64_t seed, step;
+  int layer;
+  float *qf;
+  double *qconst;
+  int8_t *qA;
+  double *lt, *tau;
+  uint64_t *prefix;
+  double *sR;
+  unsigned long long *clo, *cstar;
+  unsigned *vmax;
+  int *cmcnt, *hist, *ccount, *flags;
+};
+
+// One workgroup of 128 threads per KV head; thread t owns channel t.
+__global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
+  const int t = threadIdx.x;
+  const int h = blockIdx.x;
+  __shared__ double qd[kD];
+  __shared__ double red[kD];
+  __shared__ double smax[kD];
+  __shared__ uint32_t qAw[2 * 64 * 4];   // 2048 bytes as words
+
+  if (h == 0 && t <= a.J) {
+    double v = (-(double)t * kLn2) / (double)a.r;
+    a.lt[t] = v;
+    a.tau[t] = exp(v);
+  }
+  if (t == 0) {
+    a.prefix[h] = hash_prefix(a.seed, a.step, (uint64_t)(int64_t)a.layer, (uint64_t)h);
+    a.vmax[h] = 0u;
+  }
+  for (int i = t; i < 2 * 64 * 4; i += 128) qAw[i] = 0u;
+  __syncthreads();
+  uint8_t *qAb = reinterpret_cast<uint8_t *>(qAw);
+
+  const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
+  const int nw = (int)(a.n - w0);
+  for (int g = 0; g < a.G; ++g) {
+    const int hq = h * a.G + g;
+    const uint16_t qh = a.q[(int64_t)hq * kD + t];
+    const double qv = h2d(qh);
+    a.qf[(int64_t)hq * kD + t] = (float)qv;
+    qd[t] = qv;
+    __syncthreads();
+    if (t == 0) {
+      double ss = canon_sum([&](int c) { return qd[c] * qd[c]; });
+      double sa = canon_sum([&](int c) { return fabs(qd[c]); });
+      double qa = 0.0;
+      for (int c = 0; c < kD; ++c) qa = fmax(qa, fabs(qd[c]));
+      float qn = f32_sqrt_up(ss * (1.0 + kPadF));
+      double beta = 0.0;
+      if (qa > 0.0) {
+        int e;
+        (void)frexp(qa, &e);
+        beta = ldexp(1.0, e - 11);
+      }
+      double *qc = a.qconst + (int64_t)hq * kQc;
+      qc[QC_BETA] = beta;
+      qc[QC_QNP] = (double)qn * (1.0 + kPadF);
+      qc[QC_QABS] = sa;
+      qc[QC_QA] = qa;
+      qc[QC_QN] = (double)qn;
+      red[0] = beta;
+    }
+    __syncthreads();
+    {
+      const double beta = red[0];
+      const int qi = (beta > 0.0) ? (int)rint(qv / beta) : 0;   // exact scaling
+      const int q1 = (qi + 64) >> 7;
+      const int q0 = qi - 128 * q1;
+      const int kg = t >> 5, kh = (t >> 4) & 1, b = t & 15;
+      qAb[kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b] = (uint8_t)(int8_t)q1;
+      qAb[kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b] = (uint8_t)(int8_t)q0;
+    }
+    // window scores s_R and c_R = max
+    double m = -__builtin_huge_val();
+    for (int i = t; i < nw; i += kD) {
+      const uint16_t *krow = a.K + ((int64_t)h * a.n_cap + w0 + i) * kD;
+      double s = exact_score(qd, krow);
+      a.sR[(int64_t)hq * a.W + i] = s;
+      m = fmax(m, s);
+    }
+    smax[t] = m;
+    __syncthreads();
+    if (t == 0) {
+      double cr = -__builtin_huge_val();
+      for (int c = 0; c < kD; ++c) cr = fmax(cr, smax[c]);
+      a.qconst[(int64_t)hq * kQc + QC_CR] = cr;
+      a.clo[hq] = enc_max(cr);
+      a.cstar[hq] = enc_max(cr);
+      a.cmcnt[hq] = 0;
+      a.ccount[hq] = 0;
+      a.flags[hq] = 0;
+    }
+    for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
+    __syncthreads();
+  }
+  uint32_t *dst = reinterpret_cast<uint32_t *>(a.qA + (int64_t)h * 2048);
+  for (int i = t; i < 512; i += 128) dst[i] = qAw[i];
+}
+
+hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(prep_kernel, dim3(a.H_kv), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scan
+struct ScanArgs {
+  const uint8_t *codes;
+  const uint16_t *kscale;
+  const int8_t *zq;
+  const BlockMeta *bmeta;
+  const uint16_t *kerr, *vnorm;
+  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap;
+  int G, H_kv, waves_per_head;
+  const float *qf;
+  const double *qconst;
+  const int8_t *qA;
+  const uint64_t *prefix;
+  double *pbuf, *ubuf;
+  unsigned long long *clo;
+  unsigned *vmax;
+  double *lb_out, *e_out;   // diagnostics (may be null)
+};
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
+  if (gw >= (int64_t)a.H_kv * a.waves_per_head) return;
+  const int h = (int)(gw / a.waves_per_head);
+  const int64_t blk0 = (gw % a.waves_per_head) * kBlocksPerWave;
+  if (blk0 >= a.nb_pool) return;
+  const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
+  const int G = a.G;
+  const int n16 = lane & 15, grp = lane >> 4;
+
+  __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
+  __shared__ double cst_all[4][3][kBlocksPerWave][8];
+  uint8_t *Abuf = Abuf_all[wv];
+  double(*cst)[kBlocksPerWave][8] = cst_all[wv];
+
+  // ---- per-query constants held by this lane's finishing slots (g = grp, grp + 4)
+  const int gA = grp, gB = grp + 4;
+  const bool hasA = gA < G, hasB = gB < G;
+  const int hq0 = h * G;
+  double qnpA = 0, qnpB = 0;
+  if (hasA) qnpA = a.qconst[(int64_t)(hq0 + gA) * kQc + QC_QNP];
+  if (hasB) qnpB = a.qconst[(int64_t)(hq0 + gB) * kQc + QC_QNP];
+  float qmax = 0.0f;
+  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
+  // query values of this lane's two channels (2 lane, 2 lane + 1) for A construction
+  float qv0[kMaxG], qv1[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
+    qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
+  }
+
+  // ---- constant operand rows: zero everything, then the ones row (14)
+  {
+    uint4 *A4 = reinterpret_cast<uint4 *>(Abuf);
+    A4[lane] = make_uint4(0, 0, 0, 0);
+    A4[64 + lane] = make_uint4(0, 0, 0, 0);
+    wave_sync();
+    // row 14 for every channel group kg: lanes 14 + 16 kg
+    if ((lane & 15) == 14) {
+      A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+      A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+    }
+    wave_sync();
+  }
+
+  // ---- offset term for the wave's blocks: B_int = sum_t q~ z by MFMA (block = column)
+  {
+    v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
+    v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
+    v4i z1k0 = {0, 0, 0, 0}, z1k1 = {0, 0, 0, 0}, z0k0 = {0, 0, 0, 0}, z0k1 = {0, 0, 0, 0};
+    if (n16 < nblk) {
+      const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + n16) * 256;
+      z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
+      z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
+      z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
+      z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
+    }
+    v4i zero = {0, 0, 0, 0};
+    v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z1k0, zero, 0, 0, 0);
+    r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z1k1, r1, 0, 0, 0);
+    v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z0k0, zero, 0, 0, 0);
+    r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z0k1, r0, 0, 0, 0);
+    if (n16 < nblk) {
+      const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + n16];
+      const double kappa = ldexp(1.0, bm.kexp);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int g = grp + 4 * s;
+        if (g < G) {
+          // q~ z = 16384 q1 z1 + 128 (q1 z0 + q0 z1) + q0 z0
+          const int hi1 = s ? r1[2] : r1[0], lo1 = s ? r1[3] : r1[1];
+          const int hi0 = s ? r0[2] : r0[0], lo0 = s ? r0[3] : r0[1];
+          const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
+          const double *qc = a.qconst + (int64_t)(hq0 + g) * kQc;
+          const double beta = qc[QC_BETA];
+          cst[0][n16][g] = (beta * kappa) * (double)bint;
+          cst[1][n16][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
+          cst[2][n16][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
+        }
+      }
+    }
+    wave_sync();
+  }
+
+  const uint64_t prefix = a.prefix[h];
+  double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
+  unsigned vmx = 0u;
+  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
+
+  for (int c0 = 0; c0 < nblk; c0 += 2) {
+    const int64_t bA = blk0 + c0;
+    const int nb2 = min(2, nblk - c0);
+    const int64_t tok0 = bA * kBlk;
+    // per-token values for token tok0 + lane
+    const int64_t mypos = tok0 + lane;
+    double myE = 0.0;
+    uint32_t mykerr = 0;
+    if (lane < 32 * nb2 && mypos < a.npool) {
+      myE = perturbation(prefix, mypos);
+      mykerr = a.kerr[(int64_t)h * a.n_cap + mypos];
+      const unsigned vn = a.vnorm[(int64_t)h * a.n_cap + mypos];
+      vmx = max(vmx, vn);
+      if (a.e_out) a.e_out[(int64_t)h * a.npool + mypos] = myE;
+    }
+    // codes for the chunk's 4 half-block tiles
+    uint4 cw[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      cw[T] = make_uint4(0, 0, 0, 0);
+      if (T < 2 * nb2)
+        cw[T] = reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane];
+    }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      if (bi >= nb2) break;
+      const int64_t b = bA + bi;
+      const int bl = c0 + bi;
+      const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + b];
+      // power-of-two step shared by the group
+      const float m = qmax * bm.ksmax;
+      double alpha = 0.0;
+      float scale = 0.0f;
+      if (m > 0.0f) {
+        int x;
+        (void)frexpf(m, &x);
+        alpha = ldexp(1.0, x - 11);
+        scale = ldexpf(1.0f, 11 - x);
+      }
+      const double halpha = alpha / 2.0;
+      // integer weights for channels 2 lane, 2 lane + 1 -> operand rows
+      {
+        const uint32_t kk = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + b) * kD)[lane];
+        const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)), ks1 = h2f((uint16_t)(kk >> 16));
+        const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) {
+          if (g < G) {
+            const float x0 = (qv0[g] * ks0) * scale, x1 = (qv1[g] * ks1) * scale;
+            const int w0 = (int)rintf(x0), w1 = (int)rintf(x1);
+            const int h0 = (w0 + 64) >> 7, h1 = (w1 + 64) >> 7;
+            const int l0 = w0 - 128 * h0, l1 = w1 - 128 * h1;
+            const uint16_t hp = (uint16_t)((h0 & 0xFF) | ((h1 & 0xFF) << 8));
+            const uint16_t lp = (uint16_t)((l0 & 0xFF) | ((l1 & 0xFF) << 8));
+            *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = hp;
+            *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = lp;
+          }
+        }
+      }
+      wave_sync();
+      const v4i A0 = *reinterpret_cast<const v4i *>(Abuf + lane * 16);
+      const v4i A1 = *reinterpret_cast<const v4i *>(Abuf + 1024 + lane * 16);
+      wave_sync();
+      const double baseA = hasA ? cst[0][bl][gA] : 0.0, ebA = hasA ? cst[1][bl][gA] : 0.0,
+                   padA = hasA ? cst[2][bl][gA] : 0.0;
+      const double baseB = hasB ? cst[0][bl][gB] : 0.0, ebB = hasB ? cst[1][bl][gB] : 0.0,
+                   padB = hasB ? cst[2][bl][gB] : 0.0;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const uint4 w = cw[2 * bi + T];
+        v4i lo = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu), (int)(w.z & 0x0F0F0F0Fu),
+                  (int)(w.w & 0x0F0F0F0Fu)};
+        v4i hi = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
+                  (int)((w.z >> 4) & 0x0F0F0F0Fu), (int)((w.w >> 4) & 0x0F0F0F0Fu)};
+        v4i acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, hi, acc, 0, 0, 0);
+        const int Csum = bperm_i32(48 + n16, acc[2]);
+        const int tt = 32 * bi + 16 * T + n16;      // token within chunk
+        const int64_t pos = tok0 + tt;
+        const double E = bperm_f64(tt, myE);
+        const double kerr = h2d((uint16_t)bperm_i32(tt, (int)mykerr));
+        if (pos < a.npool) {
+          if (hasA) {
+            const int I = acc[0] * 128 + acc[1];
+            const double shat = (baseA + alpha * (double)I) * kRsqrtD;
+            const double slack = (((halpha * (double)Csum + qnpA * kerr) + ebA) + padA) * kRsqrtD;
+            const double ub = shat + slack, lb = shat - slack;
+            a.pbuf[rowA + pos] = ub + E;
+            a.ubuf[rowA + pos] = ub;
+            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gA) * a.npool + pos] = lb;
+            lbA = fmax(lbA, lb);
+          }
+          if (hasB) {
+            const int I = acc[2] * 128 + acc[3];
+            const double shat = (baseB + alpha * (double)I) * kRsqrtD;
+            const double slack = (((halpha * (double)Csum + qnpB * kerr) + ebB) + padB) * kRsqrtD;
+            const double ub = shat + slack, lb = shat - slack;
+            a.pbuf[rowB + pos] = ub + E;
+            a.ubuf[rowB + pos] = ub;
+            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gB) * a.npool + pos] = lb;
+            lbB = fmax(lbB, lb);
+          }
+        }
+      }
+    }
+  }
+  // reductions: max LB per query over the 16 lanes of a group; max vnorm over the wave
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
+    lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
+  }
+  if (n16 == 0) {
+    if (hasA) atomicMax(a.clo + hq0 + gA, enc_max(lbA));
+    if (hasB) atomicMax(a.clo + hq0 + gB, enc_max(lbB));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) vmx = max(vmx, (unsigned)__shfl_xor((int)vmx, off, 64));
+  if (lane == 0) atomicMax(a.vmax + h, vmx);
+}
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t st) {
+  const int64_t waves = (int64_t)a.H_kv * a.waves_per_head;
+  const unsigned wgs = (unsigned)((waves + 3) / 4);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(scan_kernel, dim3(wgs), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

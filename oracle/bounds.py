@@ -20,7 +20,8 @@ Per KV head h, block b (kappa_b = 2^kexp_b, integer zero points z_bt, kscale_bt)
       [-2048, 2048]; |q_gt kscale_bt - alpha_b a~_gbt| <= alpha_b / 2.
   B3. base_gb = (beta_g kappa_b) * sum_t q~_gt z_bt (exact integer times a power of two);
       eb_gb = (beta_g / 2) kappa_b sum_t |z_bt| (exact).
-  B4. Kmax_b = max_t (|kappa_b z_bt| + 15 kscale_bt); pad_gb = (2^-40 qabs_g) Kmax_b.
+  B4. Kmax_b = smallest fp32 value >= max_t (|kappa_b z_bt| + 15 kscale_bt);
+      pad_gb = (2^-40 qabs_g) Kmax_b.
 Per key i of block b:
   K1. I_gi = sum_t a~_gbt c_it and C_i = sum_t c_it (exact integers).
   K2. shat_i = (base_gb + alpha_b I_gi) * RSQRT_D,
@@ -36,6 +37,15 @@ rounding here and in the exact score, so LB_i <= s_i <= UB_i for the fp64 values
 import numpy as np
 
 from .canon import PADF, RSQRT_D, csum128, fp32_sqrt_up
+
+
+def fp32_up(x):
+    """Smallest fp32 value >= x, as fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    low = f.astype(np.float64) < x
+    f = np.where(low, np.nextafter(f, np.float32(np.inf)), f)
+    return f.astype(np.float64)
 
 
 def query_constants(q16: np.ndarray) -> dict:
@@ -73,7 +83,7 @@ def block_constants(q16: np.ndarray, packed: dict, h: int, nb: int) -> dict:
     Z1 = np.abs(z).sum(axis=1)
     eb = ((qc["qbeta"][:, None] / 2.0) * kappa[None, :]) * Z1[None, :].astype(np.float64)
     kmin = kappa[:, None] * z.astype(np.float64)
-    kmax_b = (np.abs(kmin) + 15.0 * ks16.astype(np.float64)).max(axis=1)
+    kmax_b = fp32_up((np.abs(kmin) + 15.0 * ks16.astype(np.float64)).max(axis=1))
     pad = (PADF * qc["qabs"])[:, None] * kmax_b[None, :]
     return {"alpha": alpha, "wts": wts, "base": base, "eb": eb, "pad": pad, "Bint": Bint,
             "Kmax": kmax_b, "Z1": Z1, **qc}

@@ -1,0 +1,252 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: packed codes and metadata, score bounds UB/LB, perturbations E, c_lo,
+c*, |C_max|, buckets l^ub (hence candidate sets), candidate counts, stop levels and
+keys read.  Floating point: beta and D^ at every level up to the stop within 1e-4
+relative, |o^_gpu - o^_cpu| <= 1e-3 M.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _csa():
+    import certified_sparse_attention_amd as csa
+    return csa
+
+
+def _to(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def decode_codes(codes: np.ndarray) -> np.ndarray:
+    """GPU code layout (include/csa.h) -> logical codes [H][nb*32][128]."""
+    H, nb, _ = codes.shape
+    a = codes.reshape(H, nb, 2, 4, 16, 16)            # T, g, n, j
+    lo, hi = a & 15, a >> 4
+    out = np.zeros((H, nb, 2, 16, 128), dtype=np.uint8)
+    for g in range(4):
+        out[:, :, :, :, 32 * g:32 * g + 16] = lo[:, :, :, g]
+        out[:, :, :, :, 32 * g + 16:32 * g + 32] = hi[:, :, :, g]
+    return out.reshape(H, nb * 32, 128)
+
+
+def _packed_numpy(p):
+    bm = p.bmeta.cpu().numpy().reshape(p.bmeta.shape[0], p.bmeta.shape[1], 16)
+    return {
+        "codes": decode_codes(p.codes.cpu().numpy()),
+        "kscale": p.kscale.cpu().numpy(),
+        "z": (128 * p.zq[:, :, 0].to(torch.int32) + p.zq[:, :, 1].to(torch.int32)).cpu().numpy(),
+        "ksmax": bm[..., 0:4].copy().view(np.float32)[..., 0],
+        "kexp": bm[..., 4:8].copy().view(np.int32)[..., 0],
+        "z1sum": bm[..., 8:12].copy().view(np.int32)[..., 0],
+        "kmax": bm[..., 12:16].copy().view(np.float32)[..., 0],
+        "kerr": p.kerr.cpu().numpy(),
+        "vnorm": p.vnorm.cpu().numpy(),
+    }
+
+
+WORKLOADS = {
+    "config1": synth.config1,
+    "config2": synth.config2,
+    "ragged_5000": lambda: synth.peaked_head(5000, seed=31, G=3),
+    "ragged_g7": lambda: synth.peaked_head(2100, seed=32, G=7, J=20),
+}
+
+
+def pad_cache(w):
+    """Give the cache a capacity that is a multiple of 32 (n itself stays ragged)."""
+    cap = -(-w.n_cap // 32) * 32
+    if cap != w.n_cap:
+        pad = ((0, 0), (0, cap - w.n_cap), (0, 0))
+        w.K = np.pad(w.K, pad)
+        w.V = np.pad(w.V, pad)
+    return w
+
+
+@pytest.fixture(scope="module", params=list(WORKLOADS))
+def case(request):
+    w = pad_cache(WORKLOADS[request.param]())
+    nb = w.n_cap // 32
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, nb)
+    q, K, V = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(K, V)
+    torch.cuda.synchronize()
+    return {"w": w, "pk_ref": pk_ref, "q": q, "K": K, "V": V, "packed": packed, "name": request.param}
+
+
+def test_pack_bit_exact(case):
+    w, ref = case["w"], case["pk_ref"]
+    got = _packed_numpy(case["packed"])
+    np.testing.assert_array_equal(got["codes"], ref["codes"])
+    np.testing.assert_array_equal(got["kscale"].view(np.uint16), ref["kscale"].view(np.uint16))
+    np.testing.assert_array_equal(got["z"], ref["z"].astype(np.int32))
+    np.testing.assert_array_equal(got["kexp"], ref["kexp"])
+    np.testing.assert_array_equal(got["kerr"].view(np.uint16), ref["kerr"].view(np.uint16))
+    np.testing.assert_array_equal(got["vnorm"].view(np.uint16), ref["vnorm"].view(np.uint16))
+    from oracle.bounds import block_constants
+    for h in range(w.H_kv):
+        bc = block_constants(w.q[h * w.G:(h + 1) * w.G], ref, h, w.n_cap // 32)
+        np.testing.assert_array_equal(got["z1sum"][h], bc["Z1"])
+        np.testing.assert_array_equal(got["kmax"][h].astype(np.float64), bc["Kmax"])
+        np.testing.assert_array_equal(got["ksmax"][h], ref["kscale"][h].astype(np.float32).max(axis=1))
+
+
+def test_scan_bounds_bit_exact(case):
+    w = case["w"]
+    UB, LB, E = _csa().scan_bounds(case["q"], case["K"], case["packed"], w.n, J=w.J, r=w.r,
+                                   window=w.window, seed=w.seed, step=w.step, layer=w.layer)
+    UB, LB, E = UB.cpu().numpy(), LB.cpu().numpy(), E.cpu().numpy()
+    npool = w.n - w.window
+    for h in range(w.H_kv):
+        b = oracle.scan_bounds(w.q[h * w.G:(h + 1) * w.G], case["pk_ref"], h, npool)
+        np.testing.assert_array_equal(UB[h * w.G:(h + 1) * w.G], b["UB"])
+        np.testing.assert_array_equal(LB[h * w.G:(h + 1) * w.G], b["LB"])
+        e_ref = oracle.perturbations(w.seed, w.step, w.layer, h, np.arange(npool))
+        np.testing.assert_array_equal(E[h], e_ref)
+
+
+def _compare_decode(w, pk_ref, res, tr, **kw):
+    o_hat, beta, stop, keys = (t.cpu().numpy() for t in res)
+    ref = oracle.certified_decode_layer(w.q, w.K, w.V, pk_ref, w.n, w.G, **kw)
+    trn = {k: v.cpu().numpy() for k, v in tr.items()}
+    for hq, r in enumerate(ref):
+        M = r["dense"]["M"]
+        t = r.get("trace")
+        assert int(stop[hq]) == r["stop_level"], (hq, int(stop[hq]), r["stop_level"])
+        assert int(keys[hq]) == r["keys_read"], (hq, int(keys[hq]), r["keys_read"])
+        assert np.linalg.norm(o_hat[hq].astype(np.float64) - r["o_hat"]) <= 1e-3 * M
+        if r["stop_level"] <= kw["J"]:
+            assert abs(beta[hq] - r["beta"]) <= 1e-4 * abs(r["beta"])
+        else:
+            assert beta[hq] == 0.0
+        if t is None:
+            continue
+        assert trn["c_R"][hq] == t["c_R"]
+        assert trn["c_lo"][hq] == t["c_lo"]
+        assert trn["c_star"][hq] == t["c_star"]
+        assert trn["cmax_count"][hq] == t["cmax_pos"].size
+        npool = w.n - kw["window"]
+        np.testing.assert_array_equal(trn["lub"][hq, :npool], t["lub"])
+        np.testing.assert_array_equal(trn["bucket_count"][hq],
+                                      np.bincount(t["lub"], minlength=kw["J"] + 2))
+        assert trn["cand_count"][hq] == t["cand"].size
+        for j, lv in enumerate(t["levels"]):
+            assert trn["k_level"][hq, j] == lv["k"], (hq, j)
+            assert abs(trn["dhat_level"][hq, j] - lv["D_hat"]) <= 1e-4 * lv["D_hat"]
+            b_ref = lv["beta"]
+            if np.isfinite(b_ref):
+                assert abs(trn["beta_level"][hq, j] - b_ref) <= 1e-4 * b_ref, (hq, j)
+            else:
+                assert not np.isfinite(trn["beta_level"][hq, j])
+    return ref
+
+
+def _kw(w, **over):
+    kw = dict(eps=w.eps, delta=w.delta, r=w.r, J=w.J, window=w.window, seed=w.seed, step=w.step,
+              layer=w.layer)
+    kw.update(over)
+    return kw
+
+
+def test_certified_decode_parity(case):
+    w = case["w"]
+    kw = _kw(w)
+    out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,
+                                            trace=True, **kw)
+    torch.cuda.synchronize()
+    _compare_decode(w, case["pk_ref"], out[:4], out[4], **kw)
+    lt = out[4]["logtau"].cpu().numpy()
+    np.testing.assert_array_equal(lt, oracle.logtau(w.r, w.J))
+
+
+def test_certified_decode_is_deterministic(case):
+    w = case["w"]
+    kw = _kw(w)
+    a = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n, **kw)
+    a = [t.clone() for t in a]
+    b = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("measure", ["denominator", "output_norm"])
+def test_other_measures(case, measure):
+    if case["name"] != "config1":
+        pytest.skip("one workload is enough for the measure switch")
+    w = case["w"]
+    kw = _kw(w)
+    out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,
+                                            trace=True, measure=measure, **kw)
+    torch.cuda.synchronize()
+    m = {"denominator": 0, "output_norm": 1}[measure]
+    _compare_decode(w, case["pk_ref"], out[:4], out[4], measure=m, **kw)
+
+
+def test_ragged_n_and_window_edges():
+    """n just above the window, n not a multiple of 32, and n inside the window."""
+    w = synth.peaked_head(4096, seed=41, G=4)
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, w.n_cap // 32)
+    q, K, V = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(K, V)
+    for n in (1, 40, 64, 65, 97, 1000, 4095):
+        kw = _kw(w)
+        out = _csa().certified_decode_attention(q, K, V, packed, n, trace=(n > 64), **kw)
+        torch.cuda.synchronize()
+        if n <= 64:
+            o_hat, beta, stop, keys = (t.cpu().numpy() for t in out)
+            for g in range(w.G):
+                d = oracle.dense_attention(w.q[g], w.K[0], w.V[0], n)
+                assert stop[g] == 0 and beta[g] == 0.0 and keys[g] == n
+                assert np.linalg.norm(o_hat[g] - d["o"]) <= 1e-6 * d["M"]
+        else:
+            w2 = synth.Workload(w.name, w.q, w.K, w.V, n, w.G, window=w.window, r=w.r, J=w.J,
+                                eps=w.eps, delta=w.delta)
+            _compare_decode(w2, pk_ref, out[:4], out[4], **kw)
+
+
+def test_fallback_paths():
+    """J = 0 or a tiny eps: no level certifies and the exact output comes back."""
+    w = synth.config1()
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, w.n_cap // 32)
+    q, K, V = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(K, V)
+    for over in (dict(J=0), dict(eps=1e-9)):
+        kw = _kw(w, **over)
+        out = _csa().certified_decode_attention(q, K, V, packed, w.n, trace=True, **kw)
+        torch.cuda.synchronize()
+        ref = _compare_decode(w, pk_ref, out[:4], out[4], **kw)
+        o_hat = out[0].cpu().numpy()
+        for hq, r in enumerate(ref):
+            assert r["stop_level"] == kw["J"] + 1
+            assert np.linalg.norm(o_hat[hq] - r["dense"]["o"]) <= 1e-6 * r["dense"]["M"]
+
+
+def test_fresh_perturbations_per_step():
+    """Another step gives other perturbations (and still matches the oracle)."""
+    w = synth.config1()
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, w.n_cap // 32)
+    q, K, V = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(K, V)
+    kw = _kw(w, step=7, layer=3)
+    out = _csa().certified_decode_attention(q, K, V, packed, w.n, trace=True, **kw)
+    torch.cuda.synchronize()
+    _compare_decode(w, pk_ref, out[:4], out[4], **kw)
+
+
+def test_dense_decode_matches_oracle(case):
+    w = case["w"]
+    o = _csa().dense_decode_attention(case["q"], case["K"], case["V"], w.n).cpu().numpy()
+    for hq in range(w.H_q):
+        h = hq // w.G
+        d = oracle.dense_attention(w.q[hq], w.K[h], w.V[h], w.n)
+        assert np.linalg.norm(o[hq] - d["o"]) <= 1e-4 * d["M"], hq

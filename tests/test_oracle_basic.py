@@ -241,3 +241,21 @@ def test_hash_uniform_and_exponential():
     # different steps, heads and layers give unrelated streams
     u2 = uniforms(0x5EED, 1, 0, 0, np.arange(200000))
     assert abs(np.corrcoef(u, u2)[0, 1]) < 0.02
+
+
+def test_log_spec_within_one_ulp_of_exact():
+    """ln by the written specification vs 40-digit decimal logarithms (correctly rounded)."""
+    from decimal import Decimal, getcontext
+    from oracle.perturb import log_spec, uniforms
+    getcontext().prec = 40
+    u = np.concatenate([uniforms(0x5EED, 0, 0, 0, np.arange(3000)),
+                        [1.0, 0.5, 0.25, 2.0 ** -53, 1 - 2.0 ** -53, 0.75, 1 - 2.0 ** -21, 1 - 2.0 ** -19]])
+    got = log_spec(u)
+    for x, g in zip(u, got):
+        exact = float(Decimal(float(x)).ln())          # correctly rounded to the nearest double
+        assert abs(g - exact) <= np.spacing(abs(exact)) or g == exact, (x, g, exact)
+    assert log_spec(np.array([1.0]))[0] == 0.0
+    assert log_spec(np.array([0.5]))[0] == -0.6931471805599453
+    # the Exp(1) law: mean and variance of E = -ln u stay 1 with this ln
+    E = -log_spec(uniforms(0x5EED, 0, 0, 0, np.arange(200000)))
+    assert abs(E.mean() - 1) < 4 / np.sqrt(E.size)
