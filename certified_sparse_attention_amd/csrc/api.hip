@@ -83,20 +83,23 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.cmcnt = take(Hq * sizeof(int));
   P.cmpos = take(Hq * npc * sizeof(int));
   P.hist = take(Hq * J2 * sizeof(int));
-  P.tilecnt = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.tilecnt = 0;
   P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.tileoff2 = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.tilehist = take(Hq * (size_t)P.ntiles * J2 * sizeof(int));
   P.ccount = take(Hq * sizeof(int));
+  P.ccount1 = take(Hq * sizeof(int));
+  P.jspec = take(Hq * sizeof(int));
   P.pbuf = take(Hq * npc * sizeof(double));
   P.ubuf = take(Hq * npc * sizeof(double));
   P.lub = take(Hq * npc);
+  P.live = take(Hq * (size_t)(P.npool_cap / 32 + 1) * sizeof(uint32_t));
   P.candpos = take(Hq * npc * sizeof(int));
   P.rec_s = take(Hq * npc * sizeof(double));
   P.rec_w = take(Hq * npc * sizeof(double));
   P.rec_vsq = take(Hq * npc * sizeof(double));
   P.rec_hl = take(Hq * npc * sizeof(int));
   P.partial = take(Hq * csa::kNumSeg * J1 * csa::kStatW * sizeof(double));
-  P.stats = take(Hq * J1 * csa::kStatW * sizeof(double));
-  P.winsum = take(Hq * 130 * sizeof(double));
   P.betalv = take(Hq * J1 * sizeof(double));
   P.dhatlv = take(Hq * J1 * sizeof(double));
   P.klv = take(Hq * J1 * sizeof(int));
@@ -118,7 +121,7 @@ int check_packed(const csa_packed *p) {
 // Prep + scan shared by the certified call and the bounds diagnostic.
 int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, const uint16_t *K,
                   const csa_packed *pk, int64_t n, void *ws, const csa::Plan &P, double *lb_out,
-                  double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st) {
+                  double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st, int diag = 0) {
   csa::PrepArgs pa;
   pa.q = q;
   pa.K = K;
@@ -146,6 +149,8 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.hist = at<int>(ws, P.hist);
   pa.ccount = at<int>(ws, P.ccount);
   pa.flags = at<int>(ws, P.flags);
+  pa.npool_cap = P.npool_cap;
+  pa.live = at<uint32_t>(ws, P.live);
   hipError_t e = csa::launch_prep(pa, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const int64_t npool = n - p->window;
@@ -175,6 +180,11 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.vmax = pa.vmax;
   sa.lb_out = lb_out;
   sa.e_out = e_out;
+  sa.nwords = P.npool_cap / 32 + 1;
+  sa.J = P.J;
+  sa.lt = pa.lt;
+  sa.live = pa.live;
+  sa.diag = diag;
   if (ev0 && (e = hipEventRecord((hipEvent_t)ev0, st)) != hipSuccess) return hip_fail(e, "event");
   e = csa::launch_scan(sa, st);
   if (e != hipSuccess) return hip_fail(e, "scan");
@@ -249,7 +259,7 @@ int csa_scan_bounds(const csa_shape *shape, const csa_params *params, const uint
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
   return run_prep_scan(shape, params, q, K, packed, n, workspace, P, LB, E, UB, nullptr, nullptr,
-                       (hipStream_t)stream);
+                       (hipStream_t)stream, 1);
 }
 
 int csa_certified_decode_attention(const csa_shape *shape, const csa_params *params, const uint16_t *q,
@@ -276,8 +286,9 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   void *ws = workspace;
   const int64_t npool = n - params->window;
   hipError_t e;
+  csa::SelectArgs sel{};
   if (!all_exact) {
-    csa::SelectArgs sa;
+    csa::SelectArgs &sa = sel;
     sa.K = K;
     sa.V = V;
     sa.n_cap = shape->n_cap;
@@ -296,8 +307,15 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.cmcnt = at<int>(ws, P.cmcnt);
     sa.cmpos = at<int>(ws, P.cmpos);
     sa.hist = at<int>(ws, P.hist);
-    sa.tilecnt = at<int>(ws, P.tilecnt);
+    sa.tilecnt = nullptr;
     sa.tileoff = at<int>(ws, P.tileoff);
+    sa.tileoff2 = at<int>(ws, P.tileoff2);
+    sa.tilehist = at<int>(ws, P.tilehist);
+    sa.ccount1 = at<int>(ws, P.ccount1);
+    sa.jspec = at<int>(ws, P.jspec);
+    sa.flags = at<int>(ws, P.flags);
+    sa.budget = params->cand_budget > 0 ? params->cand_budget : csa::kDefaultBudget;
+    sa.pass = 1;
     sa.ccount = at<int>(ws, P.ccount);
     sa.lub = at<int8_t>(ws, P.lub);
     sa.candpos = at<int>(ws, P.candpos);
@@ -305,6 +323,9 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.rec_w = at<double>(ws, P.rec_w);
     sa.rec_vsq = at<double>(ws, P.rec_vsq);
     sa.rec_hl = at<int>(ws, P.rec_hl);
+    sa.live = at<uint32_t>(ws, P.live);
+    sa.nwords = P.npool_cap / 32 + 1;
+    sa.full_lub = (trace && trace->lub) ? 1 : 0;
     if ((e = csa::launch_select(sa, P.H_q, st)) != hipSuccess) return hip_fail(e, "select");
   }
   csa::CertArgs ca;
@@ -339,8 +360,6 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.rec_vsq = at<double>(ws, P.rec_vsq);
   ca.lub = at<int8_t>(ws, P.lub);
   ca.partial = at<double>(ws, P.partial);
-  ca.stats = at<double>(ws, P.stats);
-  ca.winsum = at<double>(ws, P.winsum);
   ca.betalv = at<double>(ws, P.betalv);
   ca.dhatlv = at<double>(ws, P.dhatlv);
   ca.klv = at<int>(ws, P.klv);
@@ -351,7 +370,19 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.stop = stop_level;
   ca.keys_read = keys_read;
   ca.all_exact = all_exact ? 1 : 0;
-  if ((e = csa::launch_certify(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");
+  ca.ccount1 = at<int>(ws, P.ccount1);
+  ca.jspec = at<int>(ws, P.jspec);
+  if (all_exact) {
+    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");
+  } else {
+    // pass 1: levels up to the speculative level; pass 2: the heads that need all levels
+    if ((e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess ||
+        (e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess ||
+        (e = csa::launch_rescore(sel, 2, P.H_q, st)) != hipSuccess ||
+        (e = csa::launch_certify_pass(ca, 2, P.H_q, st)) != hipSuccess)
+      return hip_fail(e, "certify");
+  }
+  if ((e = csa::launch_exact(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "exact");
 
   if (trace) {
     const int Hq = P.H_q;

@@ -35,8 +35,10 @@ struct CertArgs {
   const int *ccount, *candpos, *rec_hl, *hist, *cmcnt, *cmpos;
   const double *rec_w, *rec_vsq;
   const int8_t *lub;
-  double *partial, *stats, *winsum, *betalv, *dhatlv;
+  double *partial, *betalv, *dhatlv;
   int *klv, *flags;
+  const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list
+  int pass;                     // 1: levels <= jspec; 2: all levels, heads flagged for extension
   double *exactp;
   float *o_hat;
   double *beta;
@@ -45,115 +47,116 @@ struct CertArgs {
   int all_exact;
 };
 
+constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
+constexpr int kStage = 64;        // candidates staged in LDS at a time
+
+// Candidates this pass accumulates for query head hq (-1: the head is not in this pass).
+__device__ inline int pass_count(const CertArgs &a, int hq) {
+  if (a.pass == 1) return a.ccount1[hq];
+  return (a.flags[hq] == 2) ? a.ccount[hq] : -1;
+}
+
 __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg) {
-  nseg = (count <= 0) ? 0 : min(kNumSeg, (count + 255) / 256);
+  nseg = (count <= kFusedMax) ? 0 : min(kNumSeg, (count + 1023) / 1024);
   if (seg >= nseg) { i0 = i1 = 0; return; }
   const int len = (count + nseg - 1) / nseg;
   i0 = seg * len;
   i1 = min(count, i0 + len);
 }
 
-// grid (H_q, kNumSeg, 2 channel slices); 64 threads, thread t owns channel 64 slice + t.
-__global__ __launch_bounds__(64) void accumulate_kernel(CertArgs a) {
-  extern __shared__ double sm[];
-  const int hq = blockIdx.x, seg = blockIdx.y, slice = blockIdx.z;
-  const int h = hq / a.G, t = threadIdx.x;
-  const int J1 = a.J + 1;
-  int i0, i1, nseg;
-  seg_range(a.ccount[hq], seg, i0, i1, nseg);
-  if (seg >= nseg) return;
-  double *accN = sm;                 // [J1][64]
-  double *accV = sm + J1 * 64;       // [J1][64]
-  double *scal = sm + 2 * J1 * 64;   // [J1][4]
-  for (int j = 0; j < J1; ++j) {
-    accN[j * 64 + t] = 0.0;
-    accV[j * 64 + t] = 0.0;
-    if (t < 4) scal[j * 4 + t] = 0.0;
-  }
+struct AccSmem {
+  double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
+  uint16_t vs[kStage][kD];              // staged V rows
+  int hl[kStage];
+  double w[kStage], vsq[kStage];
+};
+
+// Add candidates [i0, i1) of query head hq into s.acc (256 threads; fixed order).
+// Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light samples add (1, v, |v|^2)
+// at their entry level l and remove it at h, where they turn heavy.
+__device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+  const int t = threadIdx.x, h = hq / a.G;
   const int64_t base = (int64_t)hq * a.npool_cap;
-  const int ch = 64 * slice + t;
-  for (int i = i0; i < i1; ++i) {
-    const int hl = a.rec_hl[base + i];
-    const int hlev = hl & 0xFF, llev = hl >> 8;
-    if (llev > a.J) continue;
-    const int pos = a.candpos[base + i];
-    const double v = h2d(a.V[((int64_t)h * a.n_cap + pos) * kD + ch]);
-    const double w = a.rec_w[base + i];
-    if (hlev <= a.J) accN[hlev * 64 + t] += w * v;
-    if (llev < hlev) {
-      accV[llev * 64 + t] += v;
-      if (hlev <= a.J) accV[hlev * 64 + t] -= v;
+  for (int c0 = i0; c0 < i1; c0 += kStage) {
+    const int cnt = min(kStage, i1 - c0);
+    if (t < cnt) {
+      s.hl[t] = a.rec_hl[base + c0 + t];
+      s.w[t] = a.rec_w[base + c0 + t];
+      s.vsq[t] = a.rec_vsq[base + c0 + t];
     }
-    if (slice == 0 && t < 4) {
-      const double vsq = a.rec_vsq[base + i];
-      if (t == 0) {
-        if (hlev <= a.J) scal[hlev * 4 + 0] += w;
-      } else if (t == 1) {
-        if (hlev <= a.J) scal[hlev * 4 + 1] += w * vsq;
-      } else if (t == 2) {
+    __syncthreads();
+    // stage V rows of candidates that enter the sample at some level <= J
+    for (int e = t; e < cnt * 16; e += 256) {
+      const int r = e >> 4, part = e & 15;
+      if ((s.hl[r] >> 8) <= a.J) {
+        const int pos = a.candpos[base + c0 + r];
+        reinterpret_cast<uint4 *>(s.vs[r])[part] =
+            reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + pos) * kD)[part];
+      }
+    }
+    __syncthreads();
+    if (t < kD) {
+      for (int r = 0; r < cnt; ++r) {
+        const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
+        if (llev > a.J) continue;
+        const double v = h2d(s.vs[r][t]);
+        if (hlev <= a.J) s.acc[hlev][t] += s.w[r] * v;
         if (llev < hlev) {
-          scal[llev * 4 + 2] += 1.0;
-          if (hlev <= a.J) scal[hlev * 4 + 2] -= 1.0;
+          s.acc[llev][128 + t] += v;
+          if (hlev <= a.J) s.acc[hlev][128 + t] -= v;
         }
-      } else {
-        if (llev < hlev) {
-          scal[llev * 4 + 3] += vsq;
-          if (hlev <= a.J) scal[hlev * 4 + 3] -= vsq;
+      }
+    } else if (t < kD + 4) {
+      const int c = t - kD;
+      for (int r = 0; r < cnt; ++r) {
+        const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
+        if (llev > a.J) continue;
+        if (c == 0) {
+          if (hlev <= a.J) s.acc[hlev][256] += s.w[r];
+        } else if (c == 1) {
+          if (hlev <= a.J) s.acc[hlev][257] += s.w[r] * s.vsq[r];
+        } else if (c == 2) {
+          if (llev < hlev) {
+            s.acc[llev][258] += 1.0;
+            if (hlev <= a.J) s.acc[hlev][258] -= 1.0;
+          }
+        } else {
+          if (llev < hlev) {
+            s.acc[llev][259] += s.vsq[r];
+            if (hlev <= a.J) s.acc[hlev][259] -= s.vsq[r];
+          }
         }
       }
     }
-  }
-  double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
-  for (int j = 0; j < J1; ++j) {
-    out[j * kStatW + ch] = accN[j * 64 + t];
-    out[j * kStatW + 128 + ch] = accV[j * 64 + t];
-    if (slice == 0 && t < 4) out[j * kStatW + 256 + t] = scal[j * 4 + t];
+    __syncthreads();
   }
 }
 
-// grid H_q; thread c owns stats component c; fixed order over segments, then levels.
-__global__ __launch_bounds__(kStatW) void reduce_kernel(CertArgs a) {
-  const int hq = blockIdx.x, c = threadIdx.x;
-  const int J1 = a.J + 1;
+__device__ inline void zero_acc(AccSmem &s, int J1) {
+  for (int e = threadIdx.x; e < J1 * kStatW; e += blockDim.x) (&s.acc[0][0])[e] = 0.0;
+  __syncthreads();
+}
+
+constexpr int kSegWorkers = 8;   // workgroups per query head for the segmented accumulation
+
+// Heads with many candidates: grid (H_q, kSegWorkers); workgroup w accumulates
+// segments w, w + kSegWorkers, ... and writes each segment's increments.
+__global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
+  const int hq = blockIdx.x;
+  const int count = pass_count(a, hq);
+  if (count < 0) return;
   int i0, i1, nseg;
-  seg_range(a.ccount[hq], 0, i0, i1, nseg);
-  double run = 0.0;
-  for (int j = 0; j < J1; ++j) {
-    double inc = 0.0;
-    for (int s = 0; s < nseg; ++s) inc += a.partial[(((int64_t)hq * kNumSeg + s) * J1 + j) * kStatW + c];
-    run += inc;
-    a.stats[((int64_t)hq * J1 + j) * kStatW + c] = run;
-  }
-}
-
-// grid H_q, 128 threads: window sums N_R, D_R, Q_R relative to c*.
-__global__ __launch_bounds__(128) void window_kernel(CertArgs a) {
-  const int hq = blockIdx.x, h = hq / a.G, t = threadIdx.x;
-  __shared__ double wv[256], vq[256];
-  const int64_t w0 = (a.n > a.W) ? a.n - a.W : 0;
-  const int nw = (int)(a.n - w0);
-  const double cs = dec_max(a.cstar[hq]);
-  double accN = 0.0, accD = 0.0, accQ = 0.0;
-  for (int base = 0; base < nw; base += 256) {
-    const int cnt = min(256, nw - base);
-    for (int i = t; i < cnt; i += 128) {
-      wv[i] = exp(a.sR[(int64_t)hq * a.W + base + i] - cs);
-      vq[i] = row_sumsq(a.V + ((int64_t)h * a.n_cap + w0 + base + i) * kD);
-    }
+  seg_range(count, 0, i0, i1, nseg);
+  if ((int)blockIdx.y >= nseg) return;
+  __shared__ AccSmem s;
+  const int J1 = a.J + 1;
+  for (int seg = blockIdx.y; seg < nseg; seg += kSegWorkers) {
+    seg_range(count, seg, i0, i1, nseg);
+    zero_acc(s, J1);
+    accumulate_range(a, s, hq, i0, i1);
+    double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
+    for (int e = threadIdx.x; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
     __syncthreads();
-    for (int i = 0; i < cnt; ++i)
-      accN += wv[i] * h2d(a.V[((int64_t)h * a.n_cap + w0 + base + i) * kD + t]);
-    if (t == 0)
-      for (int i = 0; i < cnt; ++i) {
-        accD += wv[i];
-        accQ += wv[i] * vq[i];
-      }
-    __syncthreads();
-  }
-  a.winsum[(int64_t)hq * 130 + t] = accN;
-  if (t == 0) {
-    a.winsum[(int64_t)hq * 130 + 128] = accD;
-    a.winsum[(int64_t)hq * 130 + 129] = accQ;
   }
 }
 
@@ -187,64 +190,51 @@ __device__ inline double kl_lower(double x, double L) {
   return mu;
 }
 
-// grid H_q, 64 threads: lane j computes the certificate of level j.
-__global__ __launch_bounds__(64) void certificate_kernel(CertArgs a) {
-  const int hq = blockIdx.x, j = threadIdx.x, h = hq / a.G;
-  if (j > a.J) return;
-  const int J1 = a.J + 1;
-  const double *st = a.stats + ((int64_t)hq * J1 + j) * kStatW;
-  const double *ws = a.winsum + (int64_t)hq * 130;
-  const double tau = a.tau[j], L = a.L;
-  const double Vmax = h2d((uint16_t)a.vmax[h]);
-  const double D_det = ws[128] + st[256];
-  const double Q_det = ws[129] + st[257];
-  const double k = st[258], P = st[259];
+// Certificate of one level from the prefix sums and the level's four KL roots
+// (mu_hi, mu_lo of k; mu_G of y; mu_Q of P / Vmax^2), all in fp64.
+__device__ inline double level_beta(const CertArgs &a, double D_det, double Q_det, double k, double tau,
+                                    double Vmax, double cn2, double dn2, double on2, const double *root) {
+  const double L = a.L;
   const double D_hat = D_det + tau * k;
-  const double mu_hi = kl_upper(k, L), mu_lo = kl_lower(k, L);
+  const double mu_hi = root[0], mu_lo = root[1];
   const double dD = tau * fmax(k - mu_lo, mu_hi - k);
   const double D_hi = D_det + tau * mu_hi;
   const double inf = __builtin_huge_val();
-  double beta;
-  if (a.measure == CSA_MEASURE_DENOM) {
-    beta = (D_hat > dD) ? dD / (D_hat - dD) : inf;
-  } else {
-    double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
-    for (int t = 0; t < kD; ++t) {
-      const double nd = ws[t] + st[t];
-      const double c = nd / D_det;
-      const double o = (nd + tau * st[128 + t]) / D_hat;
-      cn2 += c * c;
-      cV += c * st[128 + t];
-      dn2 += (o - c) * (o - c);
-      on2 += o * o;
-    }
-    const double cn = sqrt(cn2), Rc = Vmax + cn;
-    const double y = (Rc > 0.0) ? fmax((P - 2.0 * cV + k * cn * cn) / (Rc * Rc), 0.0) : 0.0;
-    const double mu_G = kl_upper(y, L);
-    const double sigma2 = tau * tau * Rc * Rc * mu_G;
-    const double zeta = sqrt(2.0 * sigma2 * L) + (2.0 / 3.0) * (tau * Rc) * L;
-    const double dn = sqrt(dn2), on = sqrt(on2);
-    const double beta_abs = (D_hat > dD) ? (zeta + dn * dD) / (D_hat - dD) : inf;
-    if (a.measure == CSA_MEASURE_OUTNORM) {
-      beta = (on > beta_abs) ? beta_abs / (on - beta_abs) : inf;
-    } else {
-      const double yq = (Vmax > 0.0) ? P / (Vmax * Vmax) : 0.0;
-      const double mu_Q = kl_lower(yq, L);
-      const double Q_lo = Q_det + tau * Vmax * Vmax * mu_Q;
-      const double M_lo = fmax(on - beta_abs, sqrt(Q_lo / D_hi));
-      beta = (M_lo > 0.0 && beta_abs < inf) ? beta_abs / M_lo : inf;
-    }
-  }
-  a.betalv[(int64_t)hq * J1 + j] = beta;
-  a.dhatlv[(int64_t)hq * J1 + j] = D_hat;
-  a.klv[(int64_t)hq * J1 + j] = (int)k;
+  if (a.measure == CSA_MEASURE_DENOM) return (D_hat > dD) ? dD / (D_hat - dD) : inf;
+  const double cn = sqrt(cn2), Rc = Vmax + cn;
+  const double mu_G = root[2];
+  const double sigma2 = tau * tau * Rc * Rc * mu_G;
+  const double zeta = sqrt(2.0 * sigma2 * L) + (2.0 / 3.0) * (tau * Rc) * L;
+  const double dn = sqrt(dn2), on = sqrt(on2);
+  const double beta_abs = (D_hat > dD) ? (zeta + dn * dD) / (D_hat - dD) : inf;
+  if (a.measure == CSA_MEASURE_OUTNORM) return (on > beta_abs) ? beta_abs / (on - beta_abs) : inf;
+  const double mu_Q = root[3];
+  const double Q_lo = Q_det + tau * Vmax * Vmax * mu_Q;
+  const double M_lo = fmax(on - beta_abs, sqrt(Q_lo / D_hi));
+  return (M_lo > 0.0 && beta_abs < inf) ? beta_abs / M_lo : inf;
 }
 
-// grid H_q, 64 threads (one wavefront): the stop level and the outputs.
-__global__ __launch_bounds__(64) void finalize_kernel(CertArgs a) {
-  const int hq = blockIdx.x, lane = threadIdx.x;
+struct FinSmem {
+  AccSmem s;
+  double tau[kMaxJ + 1];
+  int hist[kMaxJ + 2];
+  double nr[kD];
+  double dr, qr;
+  double beta[kMaxJ + 1];
+  double dots[kMaxJ + 1][4];     // |c|^2, c.V, |o^ - c|^2, |o^|^2 per level
+  double root[kMaxJ + 1][4];
+  int jstar;
+  long long extra[4];
+};
+
+// One workgroup (256 threads) per query head: level sums (directly, or from the
+// segments' increments), window sums, prefix over levels, the certificate of every
+// level, the stop level and the outputs.
+__global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
+  const int hq = blockIdx.x, t = threadIdx.x, h = hq / a.G;
+  const int lane = t & 63, wv = t >> 6;
   if (a.all_exact) {
-    if (lane == 0) {
+    if (t == 0) {
       a.flags[hq] = 1;
       a.stop[hq] = 0;
       a.beta[hq] = 0.0;
@@ -252,41 +242,167 @@ __global__ __launch_bounds__(64) void finalize_kernel(CertArgs a) {
     }
     return;
   }
+  const int count = pass_count(a, hq);
+  if (count < 0) return;
+  const int jmax = (a.pass == 1) ? a.jspec[hq] : a.J;
+  __shared__ FinSmem f;
+  AccSmem &s = f.s;
   const int J1 = a.J + 1;
-  const bool ok = (lane <= a.J) && (a.betalv[(int64_t)hq * J1 + lane] <= a.eps);
-  const unsigned long long mask = __ballot(ok);
-  const int js = mask ? (__ffsll((long long)mask) - 1) : a.J + 1;
-  if (js > a.J) {
+  int i0, i1, nseg;
+  seg_range(count, 0, i0, i1, nseg);
+  for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
+  for (int j = t; j < a.J + 2; j += 256) f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
+  zero_acc(s, J1);
+  if (nseg == 0) {
+    accumulate_range(a, s, hq, 0, count);
+  } else {
+    for (int e = t; e < J1 * kStatW; e += 256) {
+      double v = 0.0;
+      for (int sg = 0; sg < nseg; ++sg) v += a.partial[((int64_t)hq * kNumSeg + sg) * J1 * kStatW + e];
+      (&s.acc[0][0])[e] = v;
+    }
+    __syncthreads();
+  }
+  // window sums relative to c*
+  const double cs = dec_max(a.cstar[hq]);
+  const int64_t w0 = a.n - a.W;
+  double nr = 0.0, dr = 0.0, qr = 0.0;
+  for (int c0 = 0; c0 < a.W; c0 += kStage) {
+    const int cnt = min(kStage, a.W - c0);
+    if (t < cnt) {
+      s.w[t] = exp(a.sR[(int64_t)hq * a.W + c0 + t] - cs);
+      s.vsq[t] = row_sumsq(a.V + ((int64_t)h * a.n_cap + w0 + c0 + t) * kD);
+    }
+    for (int e = t; e < cnt * 16; e += 256) {
+      const int r = e >> 4, part = e & 15;
+      reinterpret_cast<uint4 *>(s.vs[r])[part] =
+          reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + w0 + c0 + r) * kD)[part];
+    }
+    __syncthreads();
+    if (t < kD) {
+      for (int r = 0; r < cnt; ++r) nr += s.w[r] * h2d(s.vs[r][t]);
+    } else if (t == kD) {
+      for (int r = 0; r < cnt; ++r) dr += s.w[r];
+    } else if (t == kD + 1) {
+      for (int r = 0; r < cnt; ++r) qr += s.w[r] * s.vsq[r];
+    }
+    __syncthreads();
+  }
+  if (t < kD) f.nr[t] = nr;
+  if (t == kD) f.dr = dr;
+  if (t == kD + 1) f.qr = qr;
+  // prefix over levels
+  for (int c = t; c < kStatW; c += 256) {
+    double run = 0.0;
+    for (int j = 0; j < J1; ++j) {
+      run += s.acc[j][c];
+      s.acc[j][c] = run;
+    }
+  }
+  __syncthreads();
+  // certificate of every level up to jmax: dot products per level (wavefront wv takes
+  // levels wv, wv + 4, ...), then the four KL roots of every level in parallel, then beta
+  const double Vmax = h2d((uint16_t)a.vmax[h]);
+  for (int j = wv; j <= jmax; j += 4) {
+    const double tau = f.tau[j];
+    const double D_det = f.dr + s.acc[j][256];
+    const double D_hat = D_det + tau * s.acc[j][258];
+    double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
+    for (int c = lane; c < kD; c += 64) {
+      const double nd = f.nr[c] + s.acc[j][c];
+      const double cc = nd / D_det;
+      const double o = (nd + tau * s.acc[j][128 + c]) / D_hat;
+      cn2 += cc * cc;
+      cV += cc * s.acc[j][128 + c];
+      dn2 += (o - cc) * (o - cc);
+      on2 += o * o;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      cn2 += __shfl_xor(cn2, off, 64);
+      cV += __shfl_xor(cV, off, 64);
+      dn2 += __shfl_xor(dn2, off, 64);
+      on2 += __shfl_xor(on2, off, 64);
+    }
     if (lane == 0) {
-      a.flags[hq] = 1;
+      f.dots[j][0] = cn2;
+      f.dots[j][1] = cV;
+      f.dots[j][2] = dn2;
+      f.dots[j][3] = on2;
+    }
+  }
+  __syncthreads();
+  if (t < 4 * (jmax + 1)) {
+    const int j = t >> 2, r = t & 3;
+    const double k = s.acc[j][258], P = s.acc[j][259];
+    double x;
+    if (r < 2) {
+      x = k;
+    } else if (r == 2) {
+      const double cn2 = f.dots[j][0], cn = sqrt(cn2), Rc = Vmax + cn;
+      x = (Rc > 0.0) ? fmax((P - 2.0 * f.dots[j][1] + k * cn * cn) / (Rc * Rc), 0.0) : 0.0;
+    } else {
+      x = (Vmax > 0.0) ? P / (Vmax * Vmax) : 0.0;
+    }
+    f.root[j][r] = (r == 1 || r == 3) ? kl_lower(x, a.L) : kl_upper(x, a.L);
+  }
+  __syncthreads();
+  if (t <= jmax) {
+    const int j = t;
+    const double tau = f.tau[j];
+    const double D_det = f.dr + s.acc[j][256];
+    const double Q_det = f.qr + s.acc[j][257];
+    const double k = s.acc[j][258];
+    const double b = level_beta(a, D_det, Q_det, k, tau, Vmax, f.dots[j][0], f.dots[j][2], f.dots[j][3],
+                                f.root[j]);
+    f.beta[j] = b;
+    a.betalv[(int64_t)hq * J1 + j] = b;
+    a.dhatlv[(int64_t)hq * J1 + j] = D_det + tau * k;
+    a.klv[(int64_t)hq * J1 + j] = (int)k;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int js = a.J + 1;
+    for (int j = 0; j <= jmax; ++j)
+      if (f.beta[j] <= a.eps) { js = j; break; }
+    f.jstar = js;
+  }
+  __syncthreads();
+  const int js = f.jstar;
+  if (js > a.J || (js > jmax)) {
+    // no level up to jmax certifies: either the extension pass takes the rest of the
+    // levels, or (jmax = J) the head falls back to exact attention
+    if (t == 0) {
+      const bool extend = (jmax < a.J);
+      a.flags[hq] = extend ? 2 : 1;
       a.stop[hq] = a.J + 1;
       a.beta[hq] = 0.0;
       a.keys_read[hq] = a.n;
     }
     return;
   }
-  const double *st = a.stats + ((int64_t)hq * J1 + js) * kStatW;
-  const double *ws = a.winsum + (int64_t)hq * 130;
-  const double tau = a.tau[js];
-  const double D_hat = (ws[128] + st[256]) + tau * st[258];
-  for (int t = lane; t < kD; t += 64)
-    a.o_hat[(int64_t)hq * kD + t] = (float)(((ws[t] + st[t]) + tau * st[128 + t]) / D_hat);
   // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|
-  int64_t extra = 0;
+  long long extra = 0;
   const int ncm = a.cmcnt[hq];
-  for (int i = lane; i < ncm; i += 64) {
+  for (int i = t; i < ncm; i += 256) {
     const int pos = a.cmpos[(int64_t)hq * a.npool_cap + i];
     extra += (a.lub[(int64_t)hq * a.npool_cap + pos] > js);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) extra += __shfl_xor(extra, off, 64);
-  if (lane == 0) {
-    int64_t inb = 0;
-    for (int j = 0; j <= js; ++j) inb += a.hist[(int64_t)hq * (a.J + 2) + j];
+  if (lane == 0) f.extra[wv] = extra;
+  __syncthreads();
+  const double tau = f.tau[js];
+  const double D_hat = (f.dr + s.acc[js][256]) + tau * s.acc[js][258];
+  if (t < kD)
+    a.o_hat[(int64_t)hq * kD + t] = (float)(((f.nr[t] + s.acc[js][t]) + tau * s.acc[js][128 + t]) / D_hat);
+  if (t == 0) {
+    long long inb = 0;
+    for (int j = 0; j <= js; ++j) inb += f.hist[j];
     a.flags[hq] = 0;
     a.stop[hq] = js;
-    a.beta[hq] = a.betalv[(int64_t)hq * J1 + js];
-    a.keys_read[hq] = (int64_t)a.W + inb + extra;
+    a.beta[hq] = f.beta[js];
+    a.keys_read[hq] = (int64_t)a.W + inb + f.extra[0] + f.extra[1] + f.extra[2] + f.extra[3];
   }
 }
 
@@ -340,15 +456,14 @@ __global__ __launch_bounds__(128) void exact_final_kernel(CertArgs a) {
   a.o_hat[(int64_t)hq * kD + t] = (float)(N / Dn);
 }
 
-hipError_t launch_certify(const CertArgs &a, int H_q, hipStream_t st) {
-  if (!a.all_exact) {
-    const size_t shm = (size_t)(a.J + 1) * (2 * 64 + 4) * sizeof(double);
-    hipLaunchKernelGGL(accumulate_kernel, dim3(H_q, kNumSeg, 2), dim3(64), shm, st, a);
-    hipLaunchKernelGGL(reduce_kernel, dim3(H_q), dim3(kStatW), 0, st, a);
-    hipLaunchKernelGGL(window_kernel, dim3(H_q), dim3(128), 0, st, a);
-    hipLaunchKernelGGL(certificate_kernel, dim3(H_q), dim3(64), 0, st, a);
-  }
-  hipLaunchKernelGGL(finalize_kernel, dim3(H_q), dim3(64), 0, st, a);
+hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, hipStream_t st) {
+  a.pass = pass;
+  if (!a.all_exact) hipLaunchKernelGGL(accumulate_kernel, dim3(H_q, kSegWorkers), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(finish_kernel, dim3(H_q), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_exact(const CertArgs &a, int H_q, hipStream_t st) {
   hipLaunchKernelGGL(exact_partial_kernel, dim3(H_q, kExactChunks), dim3(128), 0, st, a);
   hipLaunchKernelGGL(exact_final_kernel, dim3(H_q), dim3(128), 0, st, a);
   return hipGetLastError();

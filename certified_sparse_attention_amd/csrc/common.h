@@ -271,16 +271,17 @@ struct Plan {
   int64_t ntiles;      // bucket tiles per query head
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
-  size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, ccount;
-  size_t pbuf, ubuf, lub, candpos, rec_s, rec_w, rec_vsq, rec_hl;
-  size_t partial, stats, winsum, betalv, dhatlv, klv, flags, exactp;
+  size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, ccount, ccount1, jspec;
+  size_t pbuf, ubuf, lub, live, candpos, rec_s, rec_w, rec_vsq, rec_hl;
+  size_t partial, betalv, dhatlv, klv, flags, exactp;
   size_t total;
 };
 
 // Per-query constants (fp64 slots in qconst[hq][kQc])
-enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, kQc = 8 };
+enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, QC_PILOT, kQc = 8 };
 
-constexpr int kBucketTile = 1024;
+constexpr int kBucketTile = 2048;   // positions per bucket tile (64 bitmap words)
+constexpr int kDefaultBudget = 4096; // candidates rescored before the first certificate pass
 constexpr int kExactChunks = 64;
 
 }  // namespace csa

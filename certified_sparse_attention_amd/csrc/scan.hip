@@ -31,9 +31,11 @@ __device__ inline void wave_sync() {
 }
 
 // ------------------------------------------------------------------ prep
+constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
+
 struct PrepArgs {
   const uint16_t *q, *K;
-  int64_t n_cap, n;
+  int64_t n_cap, n, npool_cap;
   int W, G, J, r, H_kv;
   uint64_t seed, step;
   int layer;
@@ -46,98 +48,119 @@ struct PrepArgs {
   unsigned long long *clo, *cstar;
   unsigned *vmax;
   int *cmcnt, *hist, *ccount, *flags;
+  uint32_t *live;     // [H_q][npool_cap / 32 + 1] bitmap, cleared here
 };
 
-// One workgroup of 128 threads per KV head; thread t owns channel t.
+// One workgroup of 128 threads per query head; thread t owns channel t.
 __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
-  const int t = threadIdx.x;
-  const int h = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int hq = blockIdx.x, h = hq / a.G, g = hq % a.G;
   __shared__ double qd[kD];
-  __shared__ double red[kD];
-  __shared__ double smax[kD];
-  __shared__ uint32_t qAw[2 * 64 * 4];   // 2048 bytes as words
+  __shared__ double part[16];
+  __shared__ double red[2];
+  __shared__ double smax[2];
 
-  if (h == 0 && t <= a.J) {
+  if (hq == 0 && t <= a.J) {
     double v = (-(double)t * kLn2) / (double)a.r;
     a.lt[t] = v;
     a.tau[t] = exp(v);
   }
-  if (t == 0) {
+  if (g == 0 && t == 0) {
     a.prefix[h] = hash_prefix(a.seed, a.step, (uint64_t)(int64_t)a.layer, (uint64_t)h);
     a.vmax[h] = 0u;
   }
-  for (int i = t; i < 2 * 64 * 4; i += 128) qAw[i] = 0u;
+  const double qv = h2d(a.q[(int64_t)hq * kD + t]);
+  a.qf[(int64_t)hq * kD + t] = (float)qv;
+  qd[t] = qv;
   __syncthreads();
-  uint8_t *qAb = reinterpret_cast<uint8_t *>(qAw);
-
+  // R1 sums: threads 0..7 own the partial sums of q^2, threads 8..15 those of |q|
+  if (t < 16) {
+    const int p = t & 7;
+    double acc = (t < 8) ? qd[16 * p] * qd[16 * p] : fabs(qd[16 * p]);
+    for (int c = 1; c < 16; ++c) acc = acc + ((t < 8) ? qd[16 * p + c] * qd[16 * p + c] : fabs(qd[16 * p + c]));
+    part[t] = acc;
+  }
+  double qa = fabs(qv);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) qa = fmax(qa, __shfl_xor(qa, off, 64));
+  if (lane == 0) smax[t >> 6] = qa;
+  __syncthreads();
+  qa = fmax(smax[0], smax[1]);
+  double beta = 0.0;
+  if (qa > 0.0) {
+    int e;
+    (void)frexp(qa, &e);
+    beta = ldexp(1.0, e - 11);
+  }
+  if (t == 0) {
+    const double ss = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    const double sa = ((part[8] + part[9]) + (part[10] + part[11])) + ((part[12] + part[13]) + (part[14] + part[15]));
+    const float qn = f32_sqrt_up(ss * (1.0 + kPadF));
+    double *qc = a.qconst + (int64_t)hq * kQc;
+    qc[QC_BETA] = beta;
+    qc[QC_QNP] = (double)qn * (1.0 + kPadF);
+    qc[QC_QABS] = sa;
+    qc[QC_QA] = qa;
+    qc[QC_QN] = (double)qn;
+  }
+  // operand rows of the offset-term MFMA: this query's two rows; query slot 0 clears
+  // the rows of the unused slots
+  {
+    const int qi = (beta > 0.0) ? (int)rint(qv / beta) : 0;   // exact scaling
+    const int q1 = (qi + 64) >> 7;
+    const int q0 = qi - 128 * q1;
+    const int kg = t >> 5, kh = (t >> 4) & 1, b = t & 15;
+    int8_t *A = a.qA + (int64_t)h * 2048;
+    A[kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b] = (int8_t)q1;
+    A[kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b] = (int8_t)q0;
+    if (g == 0)
+      for (int gs = a.G; gs < 8; ++gs) {
+        A[kh * 1024 + (op_row(gs, 0) + 16 * kg) * 16 + b] = 0;
+        A[kh * 1024 + (op_row(gs, 1) + 16 * kg) * 16 + b] = 0;
+      }
+  }
+  // window scores s_R, c_R; then a strided sample of the pool scored exactly
   const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
   const int nw = (int)(a.n - w0);
-  for (int g = 0; g < a.G; ++g) {
-    const int hq = h * a.G + g;
-    const uint16_t qh = a.q[(int64_t)hq * kD + t];
-    const double qv = h2d(qh);
-    a.qf[(int64_t)hq * kD + t] = (float)qv;
-    qd[t] = qv;
-    __syncthreads();
-    if (t == 0) {
-      double ss = canon_sum([&](int c) { return qd[c] * qd[c]; });
-      double sa = canon_sum([&](int c) { return fabs(qd[c]); });
-      double qa = 0.0;
-      for (int c = 0; c < kD; ++c) qa = fmax(qa, fabs(qd[c]));
-      float qn = f32_sqrt_up(ss * (1.0 + kPadF));
-      double beta = 0.0;
-      if (qa > 0.0) {
-        int e;
-        (void)frexp(qa, &e);
-        beta = ldexp(1.0, e - 11);
-      }
-      double *qc = a.qconst + (int64_t)hq * kQc;
-      qc[QC_BETA] = beta;
-      qc[QC_QNP] = (double)qn * (1.0 + kPadF);
-      qc[QC_QABS] = sa;
-      qc[QC_QA] = qa;
-      qc[QC_QN] = (double)qn;
-      red[0] = beta;
-    }
-    __syncthreads();
-    {
-      const double beta = red[0];
-      const int qi = (beta > 0.0) ? (int)rint(qv / beta) : 0;   // exact scaling
-      const int q1 = (qi + 64) >> 7;
-      const int q0 = qi - 128 * q1;
-      const int kg = t >> 5, kh = (t >> 4) & 1, b = t & 15;
-      qAb[kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b] = (uint8_t)(int8_t)q1;
-      qAb[kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b] = (uint8_t)(int8_t)q0;
-    }
-    // window scores s_R and c_R = max
-    double m = -__builtin_huge_val();
-    for (int i = t; i < nw; i += kD) {
-      const uint16_t *krow = a.K + ((int64_t)h * a.n_cap + w0 + i) * kD;
-      double s = exact_score(qd, krow);
-      a.sR[(int64_t)hq * a.W + i] = s;
-      m = fmax(m, s);
-    }
-    smax[t] = m;
-    __syncthreads();
-    if (t == 0) {
-      double cr = -__builtin_huge_val();
-      for (int c = 0; c < kD; ++c) cr = fmax(cr, smax[c]);
-      a.qconst[(int64_t)hq * kQc + QC_CR] = cr;
-      a.clo[hq] = enc_max(cr);
-      a.cstar[hq] = enc_max(cr);
-      a.cmcnt[hq] = 0;
-      a.ccount[hq] = 0;
-      a.flags[hq] = 0;
-    }
-    for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
-    __syncthreads();
+  double m = -__builtin_huge_val();
+  for (int i = t; i < nw; i += kD) {
+    const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + w0 + i) * kD);
+    a.sR[(int64_t)hq * a.W + i] = s;
+    m = fmax(m, s);
   }
-  uint32_t *dst = reinterpret_cast<uint32_t *>(a.qA + (int64_t)h * 2048);
-  for (int i = t; i < 512; i += 128) dst[i] = qAw[i];
+  double mp = -__builtin_huge_val();
+  if (w0 > 0) {
+    const int64_t stride = (w0 + kPilot - 1) / kPilot;
+    const int64_t pos = (int64_t)t * stride;
+    if (t < kPilot && pos < w0) mp = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    m = fmax(m, __shfl_xor(m, off, 64));
+    mp = fmax(mp, __shfl_xor(mp, off, 64));
+  }
+  __syncthreads();
+  if (lane == 0) { smax[t >> 6] = m; red[t >> 6] = mp; }
+  __syncthreads();
+  if (t == 0) {
+    const double cr = fmax(smax[0], smax[1]);
+    const double pilot = fmax(cr, fmax(red[0], red[1]));
+    double *qc = a.qconst + (int64_t)hq * kQc;
+    qc[QC_CR] = cr;
+    qc[QC_PILOT] = pilot;
+    a.clo[hq] = enc_max(cr);
+    a.cstar[hq] = enc_max(cr);
+    a.cmcnt[hq] = 0;
+    a.ccount[hq] = 0;
+    a.flags[hq] = 0;
+  }
+  for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
+  const int64_t nwords = a.npool_cap / 32 + 1;
+  for (int64_t i = t; i < nwords; i += kD) a.live[(int64_t)hq * nwords + i] = 0u;
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(prep_kernel, dim3(a.H_kv), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(prep_kernel, dim3(a.H_kv * a.G), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
@@ -148,17 +171,32 @@ struct ScanArgs {
   const int8_t *zq;
   const BlockMeta *bmeta;
   const uint16_t *kerr, *vnorm;
-  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap;
-  int G, H_kv, waves_per_head;
+  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap, nwords;
+  int G, H_kv, waves_per_head, J;
   const float *qf;
   const double *qconst;
   const int8_t *qA;
   const uint64_t *prefix;
+  const double *lt;
   double *pbuf, *ubuf;
+  uint32_t *live;
   unsigned long long *clo;
   unsigned *vmax;
+  int diag;                 // 1: every key is live and UB/LB/E are written for all keys
   double *lb_out, *e_out;   // diagnostics (may be null)
 };
+
+// Rigorous upper bound on E = -ln u with u = N 2^-53, N = (h >> 11) + 1, from N's
+// exponent k and leading mantissa bits f: ln(1 + f) >= f ln 2 on [0, 1], so
+// E <= (53 - k - f) ln 2.  (Only used to skip keys that cannot matter.)
+__device__ inline double perturbation_upper(uint64_t prefix, int64_t pos) {
+  const uint64_t N = (mix64(prefix ^ (uint64_t)pos) >> 11) + 1ull;
+  const int k = 63 - __clzll((long long)N);
+  const uint64_t top = (k >= 23) ? (N >> (k - 23)) : (N << (23 - k));   // in [2^23, 2^24)
+  const double f = (double)(top - (1ull << 23)) * 0x1p-23;             // <= mantissa fraction
+  const double x = (double)(53 - k) - f;
+  return (x * 0.69314718055994539725) * (1.0 + 0x1p-40) + 0x1p-40;    // ln 2 rounded up
+}
 
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int lane = lane_id();
@@ -174,25 +212,34 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
   __shared__ double cst_all[4][3][kBlocksPerWave][8];
+  __shared__ uint8_t flag_all[4][64];
   uint8_t *Abuf = Abuf_all[wv];
   double(*cst)[kBlocksPerWave][8] = cst_all[wv];
+  uint8_t *flag = flag_all[wv];
 
-  // ---- per-query constants held by this lane's finishing slots (g = grp, grp + 4)
+  // ---- per-query constants of this lane's finishing slots (g = grp, grp + 4)
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = gB < G;
   const int hq0 = h * G;
-  double qnpA = 0, qnpB = 0;
-  if (hasA) qnpA = a.qconst[(int64_t)(hq0 + gA) * kQc + QC_QNP];
-  if (hasB) qnpB = a.qconst[(int64_t)(hq0 + gB) * kQc + QC_QNP];
+  const int hqA = hq0 + gA, hqB = hq0 + gB;
+  double qnpA = 0, qnpB = 0, cRA = 0, cRB = 0, pilA = 0, pilB = 0;
+  if (hasA) {
+    const double *qc = a.qconst + (int64_t)hqA * kQc;
+    qnpA = qc[QC_QNP]; cRA = qc[QC_CR]; pilA = qc[QC_PILOT];
+  }
+  if (hasB) {
+    const double *qc = a.qconst + (int64_t)hqB * kQc;
+    qnpB = qc[QC_QNP]; cRB = qc[QC_CR]; pilB = qc[QC_PILOT];
+  }
   float qmax = 0.0f;
   for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
-  // query values of this lane's two channels (2 lane, 2 lane + 1) for A construction
   float qv0[kMaxG], qv1[kMaxG];
 #pragma unroll
   for (int g = 0; g < kMaxG; ++g) {
     qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
     qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
   }
+  const double ltJ = a.lt[a.J];
 
   // ---- constant operand rows: zero everything, then the ones row (14)
   {
@@ -200,7 +247,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     A4[lane] = make_uint4(0, 0, 0, 0);
     A4[64 + lane] = make_uint4(0, 0, 0, 0);
     wave_sync();
-    // row 14 for every channel group kg: lanes 14 + 16 kg
     if ((lane & 15) == 14) {
       A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
       A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
@@ -250,24 +296,29 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const uint64_t prefix = a.prefix[h];
   double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
   unsigned vmx = 0u;
-  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
+  const int64_t rowA = (int64_t)hqA * a.npool_cap, rowB = (int64_t)hqB * a.npool_cap;
 
   for (int c0 = 0; c0 < nblk; c0 += 2) {
     const int64_t bA = blk0 + c0;
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = bA * kBlk;
+    // running lower bounds: c_lo >= clo2 (c_R and maxima of LB seen so far), c* >= clo1
+    double clo2A = cRA, clo2B = cRB;
+    if (hasA) clo2A = fmax(fmax(clo2A, lbA), dec_max(__atomic_load_n(a.clo + hqA, __ATOMIC_RELAXED)));
+    if (hasB) clo2B = fmax(fmax(clo2B, lbB), dec_max(__atomic_load_n(a.clo + hqB, __ATOMIC_RELAXED)));
+    const double clo1A = fmax(clo2A, pilA), clo1B = fmax(clo2B, pilB);
+    const double thrA = clo1A + ltJ, thrB = clo1B + ltJ;
     // per-token values for token tok0 + lane
     const int64_t mypos = tok0 + lane;
-    double myE = 0.0;
+    const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
+    double myEup = 0.0;
     uint32_t mykerr = 0;
-    if (lane < 32 * nb2 && mypos < a.npool) {
-      myE = perturbation(prefix, mypos);
+    if (mine) {
+      myEup = perturbation_upper(prefix, mypos);
       mykerr = a.kerr[(int64_t)h * a.n_cap + mypos];
-      const unsigned vn = a.vnorm[(int64_t)h * a.n_cap + mypos];
-      vmx = max(vmx, vn);
-      if (a.e_out) a.e_out[(int64_t)h * a.npool + mypos] = myE;
+      vmx = max(vmx, (unsigned)a.vnorm[(int64_t)h * a.n_cap + mypos]);
     }
-    // codes for the chunk's 4 half-block tiles
+    flag[lane] = 0;
     uint4 cw[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -275,13 +326,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       if (T < 2 * nb2)
         cw[T] = reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane];
     }
+    double ubA[4], ubB[4];
+    uint32_t liveA = 0, liveB = 0;     // bit Tg: the key of tile Tg is live for slot A / B
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
       const int64_t b = bA + bi;
       const int bl = c0 + bi;
       const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + b];
-      // power-of-two step shared by the group
       const float m = qmax * bm.ksmax;
       double alpha = 0.0;
       float scale = 0.0f;
@@ -292,7 +344,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         scale = ldexpf(1.0f, 11 - x);
       }
       const double halpha = alpha / 2.0;
-      // integer weights for channels 2 lane, 2 lane + 1 -> operand rows
       {
         const uint32_t kk = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + b) * kD)[lane];
         const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)), ks1 = h2f((uint16_t)(kk >> 16));
@@ -321,7 +372,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
                    padB = hasB ? cst[2][bl][gB] : 0.0;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        const uint4 w = cw[2 * bi + T];
+        const int Tg = 2 * bi + T;
+        const uint4 w = cw[Tg];
         v4i lo = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu), (int)(w.z & 0x0F0F0F0Fu),
                   (int)(w.w & 0x0F0F0F0Fu)};
         v4i hi = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
@@ -330,44 +382,91 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, lo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, hi, acc, 0, 0, 0);
         const int Csum = bperm_i32(48 + n16, acc[2]);
-        const int tt = 32 * bi + 16 * T + n16;      // token within chunk
+        const int tt = 16 * Tg + n16;            // token within chunk
         const int64_t pos = tok0 + tt;
-        const double E = bperm_f64(tt, myE);
+        const double Eup = bperm_f64(tt, myEup);
         const double kerr = h2d((uint16_t)bperm_i32(tt, (int)mykerr));
+        ubA[Tg] = 0.0;
+        ubB[Tg] = 0.0;
         if (pos < a.npool) {
           if (hasA) {
             const int I = acc[0] * 128 + acc[1];
             const double shat = (baseA + alpha * (double)I) * kRsqrtD;
             const double slack = (((halpha * (double)Csum + qnpA * kerr) + ebA) + padA) * kRsqrtD;
             const double ub = shat + slack, lb = shat - slack;
-            a.pbuf[rowA + pos] = ub + E;
-            a.ubuf[rowA + pos] = ub;
-            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gA) * a.npool + pos] = lb;
+            ubA[Tg] = ub;
             lbA = fmax(lbA, lb);
+            if (a.lb_out) a.lb_out[(int64_t)hqA * a.npool + pos] = lb;
+            const double marg = 0x1p-40 * (fabs(ub) + fabs(thrA) + 1.0);
+            if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
           }
           if (hasB) {
             const int I = acc[2] * 128 + acc[3];
             const double shat = (baseB + alpha * (double)I) * kRsqrtD;
             const double slack = (((halpha * (double)Csum + qnpB * kerr) + ebB) + padB) * kRsqrtD;
             const double ub = shat + slack, lb = shat - slack;
-            a.pbuf[rowB + pos] = ub + E;
-            a.ubuf[rowB + pos] = ub;
-            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gB) * a.npool + pos] = lb;
+            ubB[Tg] = ub;
             lbB = fmax(lbB, lb);
+            if (a.lb_out) a.lb_out[(int64_t)hqB * a.npool + pos] = lb;
+            const double marg = 0x1p-40 * (fabs(ub) + fabs(thrB) + 1.0);
+            if (a.diag || ub + Eup >= thrB - marg || ub >= clo2B - marg) liveB |= 1u << Tg;
           }
+          if ((liveA | liveB) & (1u << Tg)) flag[tt] = 1;
         }
       }
     }
-  }
-  // reductions: max LB per query over the 16 lanes of a group; max vnorm over the wave
+    // exact perturbations for the chunk's live tokens (lane = token)
+    wave_sync();
+    double myE = 0.0;
+    if (__ballot((liveA | liveB) != 0)) {
+      if (mine && flag[lane]) {
+        myE = perturbation(prefix, mypos);
+        if (a.e_out) a.e_out[(int64_t)h * a.npool + mypos] = myE;
+      }
+    }
+    wave_sync();
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
-    lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
-  }
-  if (n16 == 0) {
-    if (hasA) atomicMax(a.clo + hq0 + gA, enc_max(lbA));
-    if (hasB) atomicMax(a.clo + hq0 + gB, enc_max(lbB));
+    for (int Tg = 0; Tg < 4; ++Tg) {
+      const int tt = 16 * Tg + n16;
+      const int64_t pos = tok0 + tt;
+      const bool la = (liveA >> Tg) & 1u, lbv = (liveB >> Tg) & 1u;
+      const unsigned long long mA = __ballot(la), mB = __ballot(lbv);
+      if (mA | mB) {
+        const double E = bperm_f64(tt, myE);
+        if (la) {
+          a.pbuf[rowA + pos] = ubA[Tg] + E;
+          a.ubuf[rowA + pos] = ubA[Tg];
+        }
+        if (lbv) {
+          a.pbuf[rowB + pos] = ubB[Tg] + E;
+          a.ubuf[rowB + pos] = ubB[Tg];
+        }
+      }
+      // live bitmap: one 32-bit word per (query, block); tiles 2k and 2k+1 fill it
+      if ((Tg & 1) == 1 && (Tg >> 1) < nb2) {
+        const unsigned long long pA = __ballot((liveA >> (Tg - 1)) & 1u);
+        const unsigned long long pB = __ballot((liveB >> (Tg - 1)) & 1u);
+        const int64_t blk = bA + (Tg >> 1);
+        if (n16 == 0) {
+          if (hasA)
+            a.live[(int64_t)hqA * a.nwords + blk] =
+                (uint32_t)((pA >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mA >> (16 * grp)) & 0xFFFFull) << 16);
+          if (hasB)
+            a.live[(int64_t)hqB * a.nwords + blk] =
+                (uint32_t)((pB >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mB >> (16 * grp)) & 0xFFFFull) << 16);
+        }
+      }
+    }
+    // share the running maxima of LB (16 lanes per query)
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
+      lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
+    }
+    if (n16 == 0) {
+      if (hasA && lbA > clo2A) atomicMax(a.clo + hqA, enc_max(lbA));
+      if (hasB && lbB > clo2B) atomicMax(a.clo + hqB, enc_max(lbB));
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) vmx = max(vmx, (unsigned)__shfl_xor((int)vmx, off, 64));

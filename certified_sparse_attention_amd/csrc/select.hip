@@ -29,9 +29,18 @@ struct SelectArgs {
   int *candpos;
   double *rec_s, *rec_w, *rec_vsq;
   int *rec_hl;
+  const uint32_t *live;   // [H_q][nwords] keys the scan kept (others have l^ub = J+1, UB < c_lo)
+  int64_t nwords;
+  int full_lub;           // write l^ub for every pool key (diagnostics)
+  int *tilehist;          // [H_q][ntiles][J+2] per-tile histograms of l^ub
+  int *tileoff2;          // [H_q][ntiles] offsets of the second range
+  int *ccount1, *jspec;   // [H_q]
+  const int *flags;
+  int budget;             // candidates rescored before the first certificate pass
+  int pass;
 };
 
-// ---- exact maximum over C_max
+// ---- exact maximum over C_max (only live keys can have UB >= c_lo)
 __global__ __launch_bounds__(256) void cmax_kernel(SelectArgs a) {
   const int hq = blockIdx.x;
   const int h = hq / a.G;
@@ -41,13 +50,19 @@ __global__ __launch_bounds__(256) void cmax_kernel(SelectArgs a) {
   __syncthreads();
   const double clo = dec_max(a.clo[hq]);
   double m = -__builtin_huge_val();
-  for (int64_t pos = (int64_t)blockIdx.y * 256 + threadIdx.x; pos < a.npool;
-       pos += (int64_t)gridDim.y * 256) {
-    if (a.ubuf[(int64_t)hq * a.npool_cap + pos] >= clo) {
-      const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-      m = fmax(m, s);
-      const int idx = atomicAdd(a.cmcnt + hq, 1);
-      a.cmpos[(int64_t)hq * a.npool_cap + idx] = (int)pos;
+  const int64_t nw = (a.npool + 31) / 32;
+  for (int64_t wi = (int64_t)blockIdx.y * 256 + threadIdx.x; wi < nw; wi += (int64_t)gridDim.y * 256) {
+    uint32_t bits = a.live[(int64_t)hq * a.nwords + wi];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int64_t pos = wi * 32 + b;
+      if (a.ubuf[(int64_t)hq * a.npool_cap + pos] >= clo) {
+        const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
+        m = fmax(m, s);
+        const int idx = atomicAdd(a.cmcnt + hq, 1);
+        a.cmpos[(int64_t)hq * a.npool_cap + idx] = (int)pos;
+      }
     }
   }
   red[threadIdx.x] = m;
@@ -59,69 +74,158 @@ __global__ __launch_bounds__(256) void cmax_kernel(SelectArgs a) {
   if (threadIdx.x == 0 && red[0] > -__builtin_huge_val()) atomicMax(a.cstar + hq, enc_max(red[0]));
 }
 
-// ---- buckets: count per tile and histogram of l^ub
-__global__ __launch_bounds__(256) void bucket_count_kernel(SelectArgs a) {
-  const int hq = blockIdx.x;
+// ---- buckets.  A tile is 64 bitmap words (2048 positions); one thread per word.
+__global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
+  const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
   __shared__ int hist[kMaxJ + 2];
-  __shared__ int cnt;
-  for (int j = threadIdx.x; j < a.J + 2; j += 256) hist[j] = 0;
-  if (threadIdx.x == 0) cnt = 0;
+  for (int j = lane; j < a.J + 2; j += 64) hist[j] = 0;
   __syncthreads();
   const double cs = dec_max(a.cstar[hq]);
-  int mine = 0;
-  for (int k = 0; k < 4; ++k) {
-    const int64_t pos = tile * kBucketTile + 4 * threadIdx.x + k;
-    if (pos < a.npool) {
-      const int l = first_level(a.pbuf[(int64_t)hq * a.npool_cap + pos] - cs, a.lt, a.J);
-      a.lub[(int64_t)hq * a.npool_cap + pos] = (int8_t)l;
+  const int64_t wi = tile * 64 + lane;
+  const int64_t p0 = wi * 32;
+  if (p0 < a.npool) {
+    const int valid = (int)min<int64_t>(32, a.npool - p0);
+    const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+    const uint32_t bits = a.live[(int64_t)hq * a.nwords + wi] & vmask;
+    const int dead = valid - __popc(bits);
+    if (dead) atomicAdd(&hist[a.J + 1], dead);
+    if (a.full_lub)
+      for (int b = 0; b < valid; ++b)
+        if (!((bits >> b) & 1u)) a.lub[(int64_t)hq * a.npool_cap + p0 + b] = (int8_t)(a.J + 1);
+    uint32_t rest = bits;
+    while (rest) {
+      const int b = __ffs(rest) - 1;
+      rest &= rest - 1u;
+      const int l = first_level(a.pbuf[(int64_t)hq * a.npool_cap + p0 + b] - cs, a.lt, a.J);
+      a.lub[(int64_t)hq * a.npool_cap + p0 + b] = (int8_t)l;
       atomicAdd(&hist[l], 1);
-      mine += (l <= a.J);
     }
   }
-  atomicAdd(&cnt, mine);
   __syncthreads();
-  for (int j = threadIdx.x; j < a.J + 2; j += 256)
-    if (hist[j]) atomicAdd(a.hist + (int64_t)hq * (a.J + 2) + j, hist[j]);
-  if (threadIdx.x == 0) a.tilecnt[(int64_t)hq * a.ntiles + tile] = cnt;
+  int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * (a.J + 2);
+  for (int j = lane; j < a.J + 2; j += 64) th[j] = hist[j];
 }
 
+// Per query head: the speculative level jspec (the deepest level whose cumulative
+// candidate count fits the budget), and tile offsets of the two candidate ranges
+// (l^ub <= jspec first, then jspec < l^ub <= J), each in position order.
 __global__ __launch_bounds__(64) void bucket_scan_kernel(SelectArgs a) {
-  const int hq = blockIdx.x;
-  if (threadIdx.x != 0) return;
-  int run = 0;
-  for (int64_t t = 0; t < a.ntiles; ++t) {
-    a.tileoff[(int64_t)hq * a.ntiles + t] = run;
-    run += a.tilecnt[(int64_t)hq * a.ntiles + t];
+  const int hq = blockIdx.x, lane = threadIdx.x;
+  const int J2 = a.J + 2;
+  __shared__ int js_sh;
+  __shared__ int c1[64], c2[64];
+  __shared__ int hh[kMaxJ + 2];
+  // level histogram of the head: each lane sums the rows of its tiles (independent
+  // loads into registers), then one wavefront reduction per level
+  int tot[kMaxJ + 2];
+#pragma unroll
+  for (int j = 0; j < kMaxJ + 2; ++j) tot[j] = 0;
+  for (int64_t tile = lane; tile < a.ntiles; tile += 64) {
+    const int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * J2;
+#pragma unroll
+    for (int j = 0; j < kMaxJ + 2; ++j)
+      if (j < J2) tot[j] += th[j];
   }
-  a.ccount[hq] = run;
-}
-
-// Stable compaction: thread k owns positions 4k..4k+3 of the tile.
-__global__ __launch_bounds__(256) void bucket_write_kernel(SelectArgs a) {
-  const int hq = blockIdx.x;
-  const int64_t tile = blockIdx.y;
-  __shared__ int pre[256];
-  int flags = 0, mine = 0;
-  for (int k = 0; k < 4; ++k) {
-    const int64_t pos = tile * kBucketTile + 4 * threadIdx.x + k;
-    if (pos < a.npool && a.lub[(int64_t)hq * a.npool_cap + pos] <= a.J) {
-      flags |= 1 << k;
-      ++mine;
+#pragma unroll
+  for (int j = 0; j < kMaxJ + 2; ++j) {
+    if (j < J2) {
+      int v = tot[j];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) {
+        hh[j] = v;
+        a.hist[(int64_t)hq * J2 + j] = v;
+      }
     }
   }
-  pre[threadIdx.x] = mine;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 256 counts
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = ((int)threadIdx.x >= off) ? pre[threadIdx.x - off] : 0;
-    __syncthreads();
-    pre[threadIdx.x] += v;
-    __syncthreads();
+  if (lane == 0) {
+    int cum = 0, js = 0;
+    for (int j = 0; j <= a.J; ++j) {
+      cum += hh[j];
+      if (cum <= a.budget || j == 0) js = j;
+    }
+    js_sh = js;
+    a.jspec[hq] = js;
   }
-  int out = a.tileoff[(int64_t)hq * a.ntiles + tile] + pre[threadIdx.x] - mine;
-  for (int k = 0; k < 4; ++k)
-    if (flags & (1 << k)) a.candpos[(int64_t)hq * a.npool_cap + out++] = (int)(tile * kBucketTile + 4 * threadIdx.x + k);
+  __syncthreads();
+  const int js = js_sh;
+  int run1 = 0, run2 = 0;
+  for (int64_t t0 = 0; t0 < a.ntiles; t0 += 64) {
+    const int64_t tile = t0 + lane;
+    int n1 = 0, n2 = 0;
+    if (tile < a.ntiles) {
+      const int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * J2;
+#pragma unroll
+      for (int j = 0; j < kMaxJ + 1; ++j) {
+        if (j <= a.J) {
+          const int v = th[j];
+          if (j <= js) n1 += v; else n2 += v;
+        }
+      }
+    }
+    // exclusive prefix over the 64 tiles of this chunk
+    int x1 = n1, x2 = n2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
+      if (lane >= off) { x1 += y1; x2 += y2; }
+    }
+    if (tile < a.ntiles) {
+      a.tileoff[(int64_t)hq * a.ntiles + tile] = run1 + x1 - n1;
+      a.tileoff2[(int64_t)hq * a.ntiles + tile] = run2 + x2 - n2;
+    }
+    run1 += __shfl(x1, 63, 64);
+    run2 += __shfl(x2, 63, 64);
+  }
+  if (lane == 0) {
+    a.ccount1[hq] = run1;
+    a.ccount[hq] = run1 + run2;
+  }
+}
+
+// Stable compaction of both ranges: thread = bitmap word, positions in order.
+__global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
+  const int hq = blockIdx.x, lane = threadIdx.x;
+  const int64_t tile = blockIdx.y;
+  const int js = a.jspec[hq];
+  const int64_t wi = tile * 64 + lane;
+  const int64_t p0 = wi * 32;
+  uint32_t m1 = 0, m2 = 0;
+  if (p0 < a.npool) {
+    const int valid = (int)min<int64_t>(32, a.npool - p0);
+    const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+    uint32_t rest = a.live[(int64_t)hq * a.nwords + wi] & vmask;
+    while (rest) {
+      const int b = __ffs(rest) - 1;
+      rest &= rest - 1u;
+      const int l = a.lub[(int64_t)hq * a.npool_cap + p0 + b];
+      if (l <= js) m1 |= 1u << b;
+      else if (l <= a.J) m2 |= 1u << b;
+    }
+  }
+  int n1 = __popc(m1), n2 = __popc(m2);
+  // exclusive prefix over the 64 lanes
+  int x1 = n1, x2 = n2;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
+    if (lane >= off) { x1 += y1; x2 += y2; }
+  }
+  int o1 = a.tileoff[(int64_t)hq * a.ntiles + tile] + x1 - n1;
+  int o2 = a.ccount1[hq] + a.tileoff2[(int64_t)hq * a.ntiles + tile] + x2 - n2;
+  int *dst = a.candpos + (int64_t)hq * a.npool_cap;
+  while (m1) {
+    const int b = __ffs(m1) - 1;
+    m1 &= m1 - 1u;
+    dst[o1++] = (int)(p0 + b);
+  }
+  while (m2) {
+    const int b = __ffs(m2) - 1;
+    m2 &= m2 - 1u;
+    dst[o2++] = (int)(p0 + b);
+  }
 }
 
 // ---- exact rescore of candidates (one lane per candidate)
@@ -131,10 +235,18 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
   __shared__ double qd[kD];
   if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
   __syncthreads();
-  const int cnt = a.ccount[hq];
+  int lo, hi;
+  if (a.pass == 1) {
+    lo = 0;
+    hi = a.ccount1[hq];
+  } else {
+    if (a.flags[hq] != 2) return;
+    lo = a.ccount1[hq];
+    hi = a.ccount[hq];
+  }
   const double cs = dec_max(a.cstar[hq]);
   const uint64_t prefix = a.prefix[h];
-  for (int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x; i < cnt; i += (int64_t)gridDim.y * 256) {
+  for (int64_t i = lo + (int64_t)blockIdx.y * 256 + threadIdx.x; i < hi; i += (int64_t)gridDim.y * 256) {
     const int64_t o = (int64_t)hq * a.npool_cap + i;
     const int pos = a.candpos[o];
     const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
@@ -151,12 +263,17 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
 }
 
 hipError_t launch_select(const SelectArgs &a, int H_q, hipStream_t st) {
-  const int64_t cmc = (a.npool + 255) / 256;
+  const int64_t cmc = ((a.npool + 31) / 32 + 255) / 256;
   const unsigned cm_chunks = (unsigned)(cmc < 64 ? cmc : 64);
   hipLaunchKernelGGL(cmax_kernel, dim3(H_q, cm_chunks), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(bucket_count_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bucket_count_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(H_q), dim3(64), 0, st, a);
-  hipLaunchKernelGGL(bucket_write_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bucket_write_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescore(SelectArgs a, int pass, int H_q, hipStream_t st) {
+  a.pass = pass;
   hipLaunchKernelGGL(rescore_kernel, dim3(H_q, 64), dim3(256), 0, st, a);
   return hipGetLastError();
 }

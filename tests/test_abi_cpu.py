@@ -53,7 +53,7 @@ def _shape(H=8, G=4, d=128, n_cap=4096):
 
 def _params(**kw):
     from certified_sparse_attention_amd import _lib
-    p = dict(eps=0.05, delta=0.01, r=2, J=30, window=64, measure=2, seed=1, step=0, layer=0, reserved=0)
+    p = dict(eps=0.05, delta=0.01, r=2, J=30, window=64, measure=2, seed=1, step=0, layer=0, cand_budget=0)
     p.update(kw)
     return _lib.Params(**p)
 

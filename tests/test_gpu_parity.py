@@ -250,3 +250,16 @@ def test_dense_decode_matches_oracle(case):
         h = hq // w.G
         d = oracle.dense_attention(w.q[hq], w.K[h], w.V[h], w.n)
         assert np.linalg.norm(o[hq] - d["o"]) <= 1e-4 * d["M"], hq
+
+
+@pytest.mark.parametrize("budget", [1, 16, 300])
+def test_speculative_budget_does_not_change_results(case, budget):
+    """A small candidate budget forces the second pass; results stay oracle-exact."""
+    if case["name"] == "config2" and budget != 16:
+        pytest.skip("one budget is enough for the large workload")
+    w = case["w"]
+    kw = _kw(w)
+    out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,
+                                            trace=True, cand_budget=budget, **kw)
+    torch.cuda.synchronize()
+    _compare_decode(w, case["pk_ref"], out[:4], out[4], **kw)
