@@ -11,6 +11,7 @@ Prints one JSON line (rank 0 only).  Only one GPU is used: --gpus above 1 exits.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -39,7 +40,41 @@ def parse():
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 4 times (reference for "
+                        "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": nbytes, "copy_bytes_written_per_launch": nbytes,
+                      "launches": 4}))
+
+
+def scan_traffic():
+    """HBM bytes per scan launch from the committed FETCH_SIZE/WRITE_SIZE summary, scaled by
+    the copy calibration; None once the scan's sources differ from those the counters saw."""
+    path = os.path.join(ROOT, "profiles", "scan_kernel_128k_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    src = b"".join(open(os.path.join(ROOT, "certified_sparse_attention_amd", "csrc", f), "rb").read()
+                   for f in ("scan.hip", "common.h"))
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def gen_layers(nlayers, chunk=8):
@@ -70,6 +105,9 @@ def cpu_baseline(w0):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU form in this build", file=sys.stderr)
@@ -91,6 +129,9 @@ def main():
         layers.append({"q": q, "K": K, "V": V, "packed": packed, "layer": w.layer})
         if w is not w0:
             del w
+        if len(layers) % 8 == 0 or len(layers) == L:
+            print(f"[bench] {len(layers)}/{L} layers generated and packed "
+                  f"({time.perf_counter() - t_gen:.0f} s)", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     kw = dict(eps=w0.eps, delta=w0.delta, r=w0.r, J=w0.J, window=w0.window, seed=w0.seed)
@@ -160,7 +201,7 @@ def main():
                                "hitters, eps=0.05, delta=0.01, r=2, J=48, window 64",
                    "n": N_CTX, "kv_heads": H_KV, "group": GQA, "layers_rotated": L},
         "roofline": {"bound": "hbm", "kernel": "scan_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic(),
                      "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": scan_avg_ms},
         "hbm_gbs_whole_step": scan_bytes / (ms_per_step * 1e-3) / 1e9,
         "dense_hip": {"ms_per_step": dense_ms, "steps_per_s": 1e3 / dense_ms,
@@ -173,6 +214,7 @@ def main():
                  "gpu": torch.cuda.get_device_name(0), "torch": torch.__version__},
     }
     if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w0)
     print(json.dumps(result))
 
