@@ -94,6 +94,7 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.ubuf = take(Hq * npc * sizeof(double));
   P.lub = take(Hq * npc);
   P.live = take(Hq * (size_t)(P.npool_cap / 32 + 1) * sizeof(uint32_t));
+  P.bmax = take(Hq * (size_t)((P.npool_cap + csa::kBlk - 1) / csa::kBlk) * 2 * sizeof(float));
   P.candpos = take(Hq * npc * sizeof(int));
   P.rec_s = take(Hq * npc * sizeof(double));
   P.rec_w = take(Hq * npc * sizeof(double));
@@ -169,7 +170,8 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.npool_cap = P.npool_cap;
   sa.G = P.G;
   sa.H_kv = P.H_kv;
-  sa.waves_per_head = (int)((sa.nb_pool + csa::kBlocksPerWave - 1) / csa::kBlocksPerWave);
+  sa.nbw = (P.npool_cap + csa::kBlk - 1) / csa::kBlk;
+  sa.bmax = at<float2>(ws, P.bmax);
   sa.qf = pa.qf;
   sa.qconst = pa.qconst;
   sa.qA = pa.qA;
@@ -189,6 +191,8 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   e = csa::launch_scan(sa, st);
   if (e != hipSuccess) return hip_fail(e, "scan");
   if (ev1 && (e = hipEventRecord((hipEvent_t)ev1, st)) != hipSuccess) return hip_fail(e, "event");
+  e = csa::launch_refine(sa, st);
+  if (e != hipSuccess) return hip_fail(e, "refine");
   if (ub_diag) {
     e = hipMemcpy2DAsync(ub_diag, (size_t)npool * sizeof(double), sa.ubuf, (size_t)P.npool_cap * sizeof(double),
                          (size_t)npool * sizeof(double), (size_t)P.H_q, hipMemcpyDeviceToDevice, st);

@@ -22,7 +22,7 @@ constexpr int kD = 128;
 constexpr int kBlk = 32;
 constexpr int kMaxJ = 60;
 constexpr int kMaxG = 7;
-constexpr int kBlocksPerWave = 8;                  // scan: blocks handled by one wavefront
+constexpr int kBlocksPerWave = 16;                 // scan: blocks handled by one wavefront
 constexpr int kNumSeg = 64;                        // accumulate: max segments per query
 constexpr int kStatW = 260;                        // per-level stats: N[128] V[128] D Q k P
 
@@ -272,7 +272,7 @@ struct Plan {
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
   size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, ccount, ccount1, jspec;
-  size_t pbuf, ubuf, lub, live, candpos, rec_s, rec_w, rec_vsq, rec_hl;
+  size_t pbuf, ubuf, lub, live, bmax, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
   size_t total;
 };

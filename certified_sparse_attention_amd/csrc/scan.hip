@@ -165,19 +165,32 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ scan
+//
+// The scan is two kernels.
+//   scan_kernel (streaming; reads every packed key once): for each block of 32 keys
+//     and query it keeps two fp32 numbers that are rigorous upper bounds of
+//     max_i UB_i and of max_i (UB_i + E^_i) over the block's keys (E^_i >= E_i from the
+//     hash's leading bits, no logarithm), and a rigorous lower bound of max_i LB_i that
+//     raises c_lo's running value.  Nothing is written per key.
+//   refine_kernel: once every block's maxima are known, c_lo and the pilot give tight
+//     lower bounds of c_lo and c*.  A block can hold a key of C_max (UB >= c_lo) or a
+//     key that is sampled at some level (UB + E >= c* + log tau_J) only if its maxima
+//     pass the same tests; the exact fp64 bounds, the exact perturbations and the
+//     per-key outputs are computed for those blocks only.
 struct ScanArgs {
   const uint8_t *codes;
   const uint16_t *kscale;
   const int8_t *zq;
   const BlockMeta *bmeta;
   const uint16_t *kerr, *vnorm;
-  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap, nwords;
-  int G, H_kv, waves_per_head, J;
+  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap, nwords, nbw;
+  int G, H_kv, J;
   const float *qf;
   const double *qconst;
   const int8_t *qA;
   const uint64_t *prefix;
   const double *lt;
+  float2 *bmax;             // [H_q][nbw]: per block, bounds of max UB and of max (UB + E)
   double *pbuf, *ubuf;
   uint32_t *live;
   unsigned long long *clo;
@@ -188,7 +201,7 @@ struct ScanArgs {
 
 // Rigorous upper bound on E = -ln u with u = N 2^-53, N = (h >> 11) + 1, from N's
 // exponent k and leading mantissa bits f: ln(1 + f) >= f ln 2 on [0, 1], so
-// E <= (53 - k - f) ln 2.  (Only used to skip keys that cannot matter.)
+// E <= (53 - k - f) ln 2.
 __device__ inline double perturbation_upper(uint64_t prefix, int64_t pos) {
   const uint64_t N = (mix64(prefix ^ (uint64_t)pos) >> 11) + 1ull;
   const int k = 63 - __clzll((long long)N);
@@ -198,39 +211,381 @@ __device__ inline double perturbation_upper(uint64_t prefix, int64_t pos) {
   return (x * 0.69314718055994539725) * (1.0 + 0x1p-40) + 0x1p-40;    // ln 2 rounded up
 }
 
+// fp32 bound that is >= perturbation_upper(): f is truncated to 16 bits (x grows and is
+// exact in fp32), ln 2 is taken as its fp32 rounding (which lies above ln 2), and the
+// relative and absolute pads exceed the fp64 ones plus every fp32 rounding.
+__device__ inline float perturbation_upper32(uint64_t prefix, int64_t pos) {
+  const uint64_t N = (mix64(prefix ^ (uint64_t)pos) >> 11) + 1ull;
+  const int k = 63 - __clzll((long long)N);
+  const uint32_t top = (uint32_t)((k >= 16) ? (N >> (k - 16)) : (N << (16 - k)));   // [2^16, 2^17)
+  const float x = (float)(53 - k) - (float)(top - (1u << 16)) * 0x1p-16f;
+  return (x * 0x1.62e430p-1f) * (1.0f + 0x1p-20f) + 0x1p-30f;
+}
+
+// Maximum over the 16 lanes of a row (all lanes get it), by DPP permutations.
+__device__ inline float row_max16(float v) {
+  int b = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));   // quad_perm 1032
+  b = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));   // quad_perm 2301
+  b = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  b = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false)));  // row_mirror
+  return v;
+}
+
+// Constant rows of the A operand: zero everything, then the ones row (14).
+__device__ inline void init_operand(uint8_t *Abuf, int lane) {
+  uint4 *A4 = reinterpret_cast<uint4 *>(Abuf);
+  A4[lane] = make_uint4(0, 0, 0, 0);
+  A4[64 + lane] = make_uint4(0, 0, 0, 0);
+  wave_sync();
+  if ((lane & 15) == 14) {
+    A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+    A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+  }
+  wave_sync();
+}
+
+// Offset term of up to 16 blocks (block = MFMA column): base = beta kappa sum_t q~ z,
+// eb = (beta/2) kappa sum_t |z|, pad = (2^-40 qabs) Kmax, into cst[0..2][block][g].
+__device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int nblk, int G, int lane,
+                                   double (*cst)[kBlocksPerWave][8]) {
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int hq0 = h * G;
+  v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
+  v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
+  v4i z1k0 = {0, 0, 0, 0}, z1k1 = {0, 0, 0, 0}, z0k0 = {0, 0, 0, 0}, z0k1 = {0, 0, 0, 0};
+  if (n16 < nblk) {
+    const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + n16) * 256;
+    z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
+    z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
+    z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
+    z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
+  }
+  v4i zero = {0, 0, 0, 0};
+  v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z1k0, zero, 0, 0, 0);
+  r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z1k1, r1, 0, 0, 0);
+  v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z0k0, zero, 0, 0, 0);
+  r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z0k1, r0, 0, 0, 0);
+  if (n16 < nblk) {
+    const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + n16];
+    const double kappa = ldexp(1.0, bm.kexp);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = grp + 4 * s;
+      if (g < G) {
+        // q~ z = 16384 q1 z1 + 128 (q1 z0 + q0 z1) + q0 z0
+        const int hi1 = s ? r1[2] : r1[0], lo1 = s ? r1[3] : r1[1];
+        const int hi0 = s ? r0[2] : r0[0], lo0 = s ? r0[3] : r0[1];
+        const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
+        const double *qc = a.qconst + (int64_t)(hq0 + g) * kQc;
+        const double beta = qc[QC_BETA];
+        cst[0][n16][g] = (beta * kappa) * (double)bint;
+        cst[1][n16][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
+        cst[2][n16][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
+      }
+    }
+  }
+  wave_sync();
+}
+
+// The query group's integer weights of one block, written into the A operand rows.
+// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0.
+template <int G>
+__device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const float *qv1, uint32_t kk,
+                                     float scale, int lane) {
+  const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)), ks1 = h2f((uint16_t)(kk >> 16));
+  const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float x0 = (qv0[g] * ks0) * scale, x1 = (qv1[g] * ks1) * scale;
+    const int w0 = (int)rintf(x0), w1 = (int)rintf(x1);
+    const int h0 = (w0 + 64) >> 7, h1 = (w1 + 64) >> 7;
+    const int l0 = w0 - 128 * h0, l1 = w1 - 128 * h1;
+    const uint16_t hp = (uint16_t)((h0 & 0xFF) | ((h1 & 0xFF) << 8));
+    const uint16_t lp = (uint16_t)((l0 & 0xFF) | ((l1 & 0xFF) << 8));
+    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = hp;
+    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = lp;
+  }
+}
+
+// Weight grid of one block: alpha = 2^(x - 11) with m = max_t |q_t| kscale_t = f 2^x.
+__device__ inline void block_grid(float qmax, float ksmax, double &alpha, float &scale) {
+  const float m = qmax * ksmax;
+  alpha = 0.0;
+  scale = 0.0f;
+  if (m > 0.0f) {
+    int x;
+    (void)frexpf(m, &x);
+    alpha = ldexp(1.0, x - 11);
+    scale = ldexpf(1.0f, 11 - x);
+  }
+}
+
+// fp32 bounds of one (query, key): ub >= UB, lb <= LB, ube >= UB + E^.  The fp64
+// bound rounds at most ~10 times with unit 2^-53 and this fp32 evaluation at most
+// ~12 times with unit 2^-24, each relative to M = (|base| + |alpha I|) R + slack, so a
+// pad of 2^-17 M (plus 2^-100 for subnormal results) covers both.
+struct Bound32 {
+  float ub, lb, ube;
+};
+__device__ inline Bound32 bound32(float base, float ebpad, float alpha, float halpha, float qnp, int I,
+                                  int C, float kerr, float eup) {
+  constexpr float R = 0x1.6a09e6p-4f;   // fp32 rounding of 2^-3.5
+  const float aI = alpha * (float)I;     // exact: |I| < 2^22, alpha a power of two
+  const float s = (base + aI) * R;
+  const float sl = __builtin_fmaf(halpha, (float)C, __builtin_fmaf(qnp, kerr, ebpad)) * R;
+  const float M = __builtin_fmaf(fabsf(base) + fabsf(aI), R, sl);
+  const float d = __builtin_fmaf(M, 0x1p-17f, 0x1p-100f);
+  Bound32 r;
+  r.ub = (s + sl) + d;
+  r.lb = (s - sl) - d;
+  const float t = r.ub + eup;
+  r.ube = __builtin_fmaf(fabsf(r.ub) + eup, 0x1p-20f, t);
+  return r;
+}
+
+template <int G>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  constexpr bool kTwo = G > 4;
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
+  const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
-  if (gw >= (int64_t)a.H_kv * a.waves_per_head) return;
-  const int h = (int)(gw / a.waves_per_head);
-  const int64_t blk0 = (gw % a.waves_per_head) * kBlocksPerWave;
-  if (blk0 >= a.nb_pool) return;
+  if (gw >= (int64_t)a.H_kv * wph) return;
+  const int h = (int)(gw / wph);
+  const int64_t blk0 = (gw % wph) * kBlocksPerWave;
+  const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
+  const int n16 = lane & 15, grp = lane >> 4;
+
+  __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
+  __shared__ double cst_all[4][3][kBlocksPerWave][8];
+  __shared__ float2 mx_all[4][kBlocksPerWave][8];
+  uint8_t *Abuf = Abuf_all[wv];
+  double(*cst)[kBlocksPerWave][8] = cst_all[wv];
+  float2(*mx)[8] = mx_all[wv];
+
+  const int gA = grp, gB = grp + 4;
+  const bool hasA = gA < G, hasB = kTwo && gB < G;
+  const int hq0 = h * G;
+  const float qnpA = hasA ? (float)a.qconst[(int64_t)(hq0 + gA) * kQc + QC_QNP] : 0.0f;
+  const float qnpB = hasB ? (float)a.qconst[(int64_t)(hq0 + gB) * kQc + QC_QNP] : 0.0f;
+  float qmax = 0.0f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
+  float qv0[G], qv1[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qv0[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane];
+    qv1[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
+  }
+
+  // Software pipeline: every global load of chunk c + 1 (two blocks) is issued before
+  // chunk c is computed.  The loop issues no global stores or atomics, so the waits
+  // for the prefetched loads never include other memory operations.
+  struct ChunkIn {
+    uint4 cw[4];
+    uint32_t kk[2];
+    float ksmax[2];
+    uint32_t kerr, vn;
+  };
+  auto load_chunk = [&](int c0, ChunkIn &in) {
+    const int64_t bA = blk0 + c0;
+    const int nb2 = min(2, nblk - c0);
+    const int64_t pos = bA * kBlk + lane;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      in.cw[T] = make_uint4(0, 0, 0, 0);
+      if (T < 2 * nb2)
+        in.cw[T] = reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane];
+    }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      in.kk[bi] = 0u;
+      in.ksmax[bi] = 0.0f;
+      if (bi < nb2) {
+        in.kk[bi] = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + bA + bi) * kD)[lane];
+        in.ksmax[bi] = a.bmeta[(int64_t)h * a.nb_cap + bA + bi].ksmax;
+      }
+    }
+    in.kerr = 0u;
+    in.vn = 0u;
+    if (lane < 32 * nb2 && pos < a.npool) {
+      in.kerr = a.kerr[(int64_t)h * a.n_cap + pos];
+      in.vn = a.vnorm[(int64_t)h * a.n_cap + pos];
+    }
+  };
+  ChunkIn nxt;
+  load_chunk(0, nxt);
+
+  init_operand(Abuf, lane);
+  offset_terms(a, h, blk0, nblk, G, lane, cst);
+
+  const uint64_t prefix = a.prefix[h];
+  float lbA = -__builtin_huge_valf(), lbB = -__builtin_huge_valf();
+  unsigned vmx = 0u;
+  constexpr float kNegInf = -__builtin_huge_valf();
+
+  for (int c0 = 0; c0 < nblk; c0 += 2) {
+    const ChunkIn cur = nxt;
+    if (c0 + 2 < nblk) load_chunk(c0 + 2, nxt);
+    const int nb2 = min(2, nblk - c0);
+    const int64_t tok0 = (blk0 + c0) * kBlk;
+    const int64_t mypos = tok0 + lane;
+    const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
+    float myEup = 0.0f;
+    if (mine) {
+      myEup = perturbation_upper32(prefix, mypos);
+      vmx = max(vmx, cur.vn);
+    }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      if (bi >= nb2) break;
+      const int bl = c0 + bi;
+      double alpha;
+      float scale;
+      block_grid(qmax, cur.ksmax[bi], alpha, scale);
+      const float alpha32 = (float)alpha, halpha32 = 0.5f * (float)alpha;
+      build_operand<G>(Abuf, qv0, qv1, cur.kk[bi], scale, lane);
+      wave_sync();
+      const v4i A0 = *reinterpret_cast<const v4i *>(Abuf + lane * 16);
+      const v4i A1 = *reinterpret_cast<const v4i *>(Abuf + 1024 + lane * 16);
+      wave_sync();
+      const float baseA = hasA ? (float)cst[0][bl][gA] : 0.0f;
+      const float ebpA = hasA ? (float)(cst[1][bl][gA] + cst[2][bl][gA]) : 0.0f;
+      const float baseB = hasB ? (float)cst[0][bl][gB] : 0.0f;
+      const float ebpB = hasB ? (float)(cst[1][bl][gB] + cst[2][bl][gB]) : 0.0f;
+      float uA = kNegInf, eA = kNegInf, uB = kNegInf, eB = kNegInf;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int Tg = 2 * bi + T;
+        const uint4 w = cur.cw[Tg];
+        v4i lo = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu), (int)(w.z & 0x0F0F0F0Fu),
+                  (int)(w.w & 0x0F0F0F0Fu)};
+        v4i hi = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
+                  (int)((w.z >> 4) & 0x0F0F0F0Fu), (int)((w.w >> 4) & 0x0F0F0F0Fu)};
+        v4i acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, hi, acc, 0, 0, 0);
+        const int tt = 16 * Tg + n16;            // token within chunk
+        const int Csum = bperm_i32(48 + n16, acc[2]);
+        const float eup = __int_as_float(bperm_i32(tt, __float_as_int(myEup)));
+        const float kerr = h2f((uint16_t)bperm_i32(tt, (int)cur.kerr));
+        const bool valid = tok0 + tt < a.npool;
+        if (hasA) {
+          const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
+          uA = fmaxf(uA, valid ? r.ub : kNegInf);
+          eA = fmaxf(eA, valid ? r.ube : kNegInf);
+          lbA = fmaxf(lbA, valid ? r.lb : kNegInf);
+        }
+        if (hasB) {
+          const Bound32 r = bound32(baseB, ebpB, alpha32, halpha32, qnpB, acc[2] * 128 + acc[3], Csum, kerr, eup);
+          uB = fmaxf(uB, valid ? r.ub : kNegInf);
+          eB = fmaxf(eB, valid ? r.ube : kNegInf);
+          lbB = fmaxf(lbB, valid ? r.lb : kNegInf);
+        }
+      }
+      uA = row_max16(uA);
+      eA = row_max16(eA);
+      if (kTwo) {
+        uB = row_max16(uB);
+        eB = row_max16(eB);
+      }
+      if (n16 == 0) {
+        if (hasA) mx[bl][gA] = make_float2(uA, eA);
+        if (hasB) mx[bl][gB] = make_float2(uB, eB);
+      }
+    }
+  }
+  wave_sync();
+  // per-block maxima of the wave: [query][block] rows of float2
+  for (int i = lane; i < G * kBlocksPerWave; i += 64) {
+    const int g = i / kBlocksPerWave, bl = i % kBlocksPerWave;
+    if (bl < nblk) a.bmax[(int64_t)(hq0 + g) * a.nbw + blk0 + bl] = mx[bl][g];
+  }
+  // c_lo >= every LB: publish the wave's lower bounds of max LB
+  lbA = row_max16(lbA);
+  if (kTwo) lbB = row_max16(lbB);
+  if (n16 == 0) {
+    if (hasA && lbA > kNegInf)
+      __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max((double)lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hasB && lbB > kNegInf)
+      __hip_atomic_fetch_max(a.clo + hq0 + gB, enc_max((double)lbB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) vmx = max(vmx, (unsigned)__shfl_xor((int)vmx, off, 64));
+  if (lane == 0) atomicMax(a.vmax + h, vmx);
+}
+
+__global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
+  if (gw >= (int64_t)a.H_kv * wph) return;
+  const int h = (int)(gw / wph);
+  const int64_t blk0 = (gw % wph) * kBlocksPerWave;
   const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
   const int G = a.G;
   const int n16 = lane & 15, grp = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
   __shared__ double cst_all[4][3][kBlocksPerWave][8];
+  __shared__ double clo_all[4][8];
   __shared__ uint8_t flag_all[4][64];
   uint8_t *Abuf = Abuf_all[wv];
   double(*cst)[kBlocksPerWave][8] = cst_all[wv];
   uint8_t *flag = flag_all[wv];
 
-  // ---- per-query constants of this lane's finishing slots (g = grp, grp + 4)
+  // one snapshot of c_lo's running value per query, shared by every test below
+  const int hq0 = h * G;
+  if (lane < G)
+    clo_all[wv][lane] = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  wave_sync();
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = gB < G;
-  const int hq0 = h * G;
-  const int hqA = hq0 + gA, hqB = hq0 + gB;
-  double qnpA = 0, qnpB = 0, cRA = 0, cRB = 0, pilA = 0, pilB = 0;
+  const double ltJ = a.lt[a.J];
+  double clo2A = 0, clo2B = 0, thrA = 0, thrB = 0, qnpA = 0, qnpB = 0;
   if (hasA) {
-    const double *qc = a.qconst + (int64_t)hqA * kQc;
-    qnpA = qc[QC_QNP]; cRA = qc[QC_CR]; pilA = qc[QC_PILOT];
+    const double *qc = a.qconst + (int64_t)(hq0 + gA) * kQc;
+    clo2A = clo_all[wv][gA];
+    thrA = fmax(clo2A, qc[QC_PILOT]) + ltJ;
+    qnpA = qc[QC_QNP];
   }
   if (hasB) {
-    const double *qc = a.qconst + (int64_t)hqB * kQc;
-    qnpB = qc[QC_QNP]; cRB = qc[QC_CR]; pilB = qc[QC_PILOT];
+    const double *qc = a.qconst + (int64_t)(hq0 + gB) * kQc;
+    clo2B = clo_all[wv][gB];
+    thrB = fmax(clo2B, qc[QC_PILOT]) + ltJ;
+    qnpB = qc[QC_QNP];
   }
+
+  // blocks whose maxima pass a test (lane = (query slot, block))
+  uint32_t alive = 0;
+  if (a.diag) {
+    alive = (nblk >= 32) ? 0xFFFFFFFFu : ((1u << nblk) - 1u);
+  } else {
+    bool pass = false;
+    if (n16 < nblk) {
+      if (hasA) {
+        const float2 m = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
+        const double u = m.x, e = m.y;
+        pass |= u >= clo2A - 0x1p-30 * (fabs(u) + fabs(clo2A) + 1.0);
+        pass |= e >= thrA - 0x1p-30 * (fabs(e) + fabs(thrA) + 1.0);
+      }
+      if (hasB) {
+        const float2 m = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
+        const double u = m.x, e = m.y;
+        pass |= u >= clo2B - 0x1p-30 * (fabs(u) + fabs(clo2B) + 1.0);
+        pass |= e >= thrB - 0x1p-30 * (fabs(e) + fabs(thrB) + 1.0);
+      }
+    }
+    const unsigned long long b = __ballot(pass);
+    alive = (uint32_t)((b | (b >> 16) | (b >> 32) | (b >> 48)) & 0xFFFFull);
+  }
+  if (alive == 0u) return;
+
   float qmax = 0.0f;
   for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
   float qv0[kMaxG], qv1[kMaxG];
@@ -239,76 +594,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
     qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
   }
-  const double ltJ = a.lt[a.J];
-
-  // ---- constant operand rows: zero everything, then the ones row (14)
-  {
-    uint4 *A4 = reinterpret_cast<uint4 *>(Abuf);
-    A4[lane] = make_uint4(0, 0, 0, 0);
-    A4[64 + lane] = make_uint4(0, 0, 0, 0);
-    wave_sync();
-    if ((lane & 15) == 14) {
-      A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
-      A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
-    }
-    wave_sync();
-  }
-
-  // ---- offset term for the wave's blocks: B_int = sum_t q~ z by MFMA (block = column)
-  {
-    v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
-    v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
-    v4i z1k0 = {0, 0, 0, 0}, z1k1 = {0, 0, 0, 0}, z0k0 = {0, 0, 0, 0}, z0k1 = {0, 0, 0, 0};
-    if (n16 < nblk) {
-      const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + n16) * 256;
-      z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
-      z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
-      z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
-      z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
-    }
-    v4i zero = {0, 0, 0, 0};
-    v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z1k0, zero, 0, 0, 0);
-    r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z1k1, r1, 0, 0, 0);
-    v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z0k0, zero, 0, 0, 0);
-    r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z0k1, r0, 0, 0, 0);
-    if (n16 < nblk) {
-      const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + n16];
-      const double kappa = ldexp(1.0, bm.kexp);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int g = grp + 4 * s;
-        if (g < G) {
-          // q~ z = 16384 q1 z1 + 128 (q1 z0 + q0 z1) + q0 z0
-          const int hi1 = s ? r1[2] : r1[0], lo1 = s ? r1[3] : r1[1];
-          const int hi0 = s ? r0[2] : r0[0], lo0 = s ? r0[3] : r0[1];
-          const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
-          const double *qc = a.qconst + (int64_t)(hq0 + g) * kQc;
-          const double beta = qc[QC_BETA];
-          cst[0][n16][g] = (beta * kappa) * (double)bint;
-          cst[1][n16][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
-          cst[2][n16][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
-        }
-      }
-    }
-    wave_sync();
-  }
+  init_operand(Abuf, lane);
+  offset_terms(a, h, blk0, nblk, G, lane, cst);
 
   const uint64_t prefix = a.prefix[h];
   double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
-  unsigned vmx = 0u;
-  const int64_t rowA = (int64_t)hqA * a.npool_cap, rowB = (int64_t)hqB * a.npool_cap;
+  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
 
   for (int c0 = 0; c0 < nblk; c0 += 2) {
+    if (((alive >> c0) & 3u) == 0u) continue;
     const int64_t bA = blk0 + c0;
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = bA * kBlk;
-    // running lower bounds: c_lo >= clo2 (c_R and maxima of LB seen so far), c* >= clo1
-    double clo2A = cRA, clo2B = cRB;
-    if (hasA) clo2A = fmax(fmax(clo2A, lbA), dec_max(__atomic_load_n(a.clo + hqA, __ATOMIC_RELAXED)));
-    if (hasB) clo2B = fmax(fmax(clo2B, lbB), dec_max(__atomic_load_n(a.clo + hqB, __ATOMIC_RELAXED)));
-    const double clo1A = fmax(clo2A, pilA), clo1B = fmax(clo2B, pilB);
-    const double thrA = clo1A + ltJ, thrB = clo1B + ltJ;
-    // per-token values for token tok0 + lane
     const int64_t mypos = tok0 + lane;
     const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
     double myEup = 0.0;
@@ -316,7 +613,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     if (mine) {
       myEup = perturbation_upper(prefix, mypos);
       mykerr = a.kerr[(int64_t)h * a.n_cap + mypos];
-      vmx = max(vmx, (unsigned)a.vnorm[(int64_t)h * a.n_cap + mypos]);
     }
     flag[lane] = 0;
     uint4 cw[4];
@@ -333,34 +629,19 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       if (bi >= nb2) break;
       const int64_t b = bA + bi;
       const int bl = c0 + bi;
-      const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + b];
-      const float m = qmax * bm.ksmax;
-      double alpha = 0.0;
-      float scale = 0.0f;
-      if (m > 0.0f) {
-        int x;
-        (void)frexpf(m, &x);
-        alpha = ldexp(1.0, x - 11);
-        scale = ldexpf(1.0f, 11 - x);
-      }
+      double alpha;
+      float scale;
+      block_grid(qmax, a.bmeta[(int64_t)h * a.nb_cap + b].ksmax, alpha, scale);
       const double halpha = alpha / 2.0;
-      {
-        const uint32_t kk = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + b) * kD)[lane];
-        const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)), ks1 = h2f((uint16_t)(kk >> 16));
-        const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
-#pragma unroll
-        for (int g = 0; g < kMaxG; ++g) {
-          if (g < G) {
-            const float x0 = (qv0[g] * ks0) * scale, x1 = (qv1[g] * ks1) * scale;
-            const int w0 = (int)rintf(x0), w1 = (int)rintf(x1);
-            const int h0 = (w0 + 64) >> 7, h1 = (w1 + 64) >> 7;
-            const int l0 = w0 - 128 * h0, l1 = w1 - 128 * h1;
-            const uint16_t hp = (uint16_t)((h0 & 0xFF) | ((h1 & 0xFF) << 8));
-            const uint16_t lp = (uint16_t)((l0 & 0xFF) | ((l1 & 0xFF) << 8));
-            *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = hp;
-            *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = lp;
-          }
-        }
+      const uint32_t kk = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + b) * kD)[lane];
+      switch (G) {
+        case 1: build_operand<1>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 2: build_operand<2>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 3: build_operand<3>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 4: build_operand<4>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 5: build_operand<5>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 6: build_operand<6>(Abuf, qv0, qv1, kk, scale, lane); break;
+        default: build_operand<7>(Abuf, qv0, qv1, kk, scale, lane); break;
       }
       wave_sync();
       const v4i A0 = *reinterpret_cast<const v4i *>(Abuf + lane * 16);
@@ -396,7 +677,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubA[Tg] = ub;
             lbA = fmax(lbA, lb);
-            if (a.lb_out) a.lb_out[(int64_t)hqA * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gA) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrA) + 1.0);
             if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
           }
@@ -407,7 +688,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubB[Tg] = ub;
             lbB = fmax(lbB, lb);
-            if (a.lb_out) a.lb_out[(int64_t)hqB * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gB) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrB) + 1.0);
             if (a.diag || ub + Eup >= thrB - marg || ub >= clo2B - marg) liveB |= 1u << Tg;
           }
@@ -449,35 +730,50 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         const int64_t blk = bA + (Tg >> 1);
         if (n16 == 0) {
           if (hasA)
-            a.live[(int64_t)hqA * a.nwords + blk] =
+            a.live[(int64_t)(hq0 + gA) * a.nwords + blk] =
                 (uint32_t)((pA >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mA >> (16 * grp)) & 0xFFFFull) << 16);
           if (hasB)
-            a.live[(int64_t)hqB * a.nwords + blk] =
+            a.live[(int64_t)(hq0 + gB) * a.nwords + blk] =
                 (uint32_t)((pB >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mB >> (16 * grp)) & 0xFFFFull) << 16);
         }
       }
     }
-    // share the running maxima of LB (16 lanes per query)
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
-      lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
-    }
-    if (n16 == 0) {
-      if (hasA && lbA > clo2A) atomicMax(a.clo + hqA, enc_max(lbA));
-      if (hasB && lbB > clo2B) atomicMax(a.clo + hqB, enc_max(lbB));
-    }
   }
+  // exact c_lo: the processed blocks hold every key whose LB can exceed the snapshot
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) vmx = max(vmx, (unsigned)__shfl_xor((int)vmx, off, 64));
-  if (lane == 0) atomicMax(a.vmax + h, vmx);
+  for (int off = 8; off >= 1; off >>= 1) {
+    lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
+    lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
+  }
+  if (n16 == 0) {
+    if (hasA && lbA > clo2A)
+      __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max(lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hasB && lbB > clo2B)
+      __hip_atomic_fetch_max(a.clo + hq0 + gB, enc_max(lbB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t st) {
-  const int64_t waves = (int64_t)a.H_kv * a.waves_per_head;
+  const int64_t waves = (int64_t)a.H_kv * ((a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
   const unsigned wgs = (unsigned)((waves + 3) / 4);
   if (wgs == 0) return hipSuccess;
-  hipLaunchKernelGGL(scan_kernel, dim3(wgs), dim3(256), 0, st, a);
+  switch (a.G) {
+    case 1: hipLaunchKernelGGL(scan_kernel<1>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(scan_kernel<2>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(scan_kernel<3>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(scan_kernel<4>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL(scan_kernel<5>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL(scan_kernel<6>, dim3(wgs), dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(scan_kernel<7>, dim3(wgs), dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_refine(const ScanArgs &a, hipStream_t st) {
+  const int64_t waves = (int64_t)a.H_kv * ((a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
+  const unsigned wgs = (unsigned)((waves + 3) / 4);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(refine_kernel, dim3(wgs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
