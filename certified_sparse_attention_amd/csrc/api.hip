@@ -157,6 +157,10 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   const int64_t npool = n - p->window;
   if (npool <= 0) return CSA_OK;
   csa::ScanArgs sa;
+  sa.K = K;
+  sa.cstar = pa.cstar;
+  sa.cmcnt = pa.cmcnt;
+  sa.cmpos = at<int>(ws, P.cmpos);
   sa.codes = pk->codes;
   sa.kscale = pk->kscale;
   sa.zq = pk->zq;
@@ -202,14 +206,20 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
 }
 
 __global__ void trace_kernel(const double *qconst, const unsigned long long *clo,
-                             const unsigned long long *cstar, const int *cmcnt, const int *ccount,
-                             int Hq, double *c_R, double *c_lo, double *c_star, int *cm, int *cc) {
+                             const unsigned long long *cstar, const int *cmcnt, const int *cmpos,
+                             const double *ubuf, int64_t npool_cap, const int *ccount, int Hq, double *c_R,
+                             double *c_lo, double *c_star, int *cm, int *cc) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= Hq) return;
+  const double cl = csa::dec_max(clo[i]);
   if (c_R) c_R[i] = qconst[(int64_t)i * csa::kQc + csa::QC_CR];
-  if (c_lo) c_lo[i] = csa::dec_max(clo[i]);
+  if (c_lo) c_lo[i] = cl;
   if (c_star) c_star[i] = csa::dec_max(cstar[i]);
-  if (cm) cm[i] = cmcnt[i];
+  if (cm) {
+    int k = 0;
+    for (int e = 0; e < cmcnt[i]; ++e) k += ubuf[(int64_t)i * npool_cap + cmpos[(int64_t)i * npool_cap + e]] >= cl;
+    cm[i] = k;
+  }
   if (cc) cc[i] = ccount[i];
 }
 
@@ -360,6 +370,8 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.hist = at<int>(ws, P.hist);
   ca.cmcnt = at<int>(ws, P.cmcnt);
   ca.cmpos = at<int>(ws, P.cmpos);
+  ca.ubuf = at<double>(ws, P.ubuf);
+  ca.clo = at<unsigned long long>(ws, P.clo);
   ca.rec_w = at<double>(ws, P.rec_w);
   ca.rec_vsq = at<double>(ws, P.rec_vsq);
   ca.lub = at<int8_t>(ws, P.lub);
@@ -392,7 +404,8 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     const int Hq = P.H_q;
     hipLaunchKernelGGL(trace_kernel, dim3((Hq + 63) / 64), dim3(64), 0, st, at<double>(ws, P.qconst),
                        at<unsigned long long>(ws, P.clo), at<unsigned long long>(ws, P.cstar),
-                       at<int>(ws, P.cmcnt), at<int>(ws, P.ccount), Hq, trace->c_R, trace->c_lo,
+                       at<int>(ws, P.cmcnt), at<int>(ws, P.cmpos), at<double>(ws, P.ubuf), P.npool_cap,
+                       at<int>(ws, P.ccount), Hq, trace->c_R, trace->c_lo,
                        trace->c_star, trace->cmax_count, trace->cand_count);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "trace");
     const size_t J1 = (size_t)P.J + 1;

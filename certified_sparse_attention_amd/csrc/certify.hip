@@ -30,7 +30,8 @@ struct CertArgs {
   double eps, L;
   const float *qf;
   const double *lt, *tau, *sR;
-  const unsigned long long *cstar;
+  const unsigned long long *cstar, *clo;
+  const double *ubuf;
   const unsigned *vmax;
   const int *ccount, *candpos, *rec_hl, *hist, *cmcnt, *cmpos;
   const double *rec_w, *rec_vsq;
@@ -381,12 +382,14 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     return;
   }
-  // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|
+  // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|; the list holds
+  // a superset of C_max, which is {UB >= c_lo}
   long long extra = 0;
   const int ncm = a.cmcnt[hq];
+  const double clo = dec_max(a.clo[hq]);
   for (int i = t; i < ncm; i += 256) {
     const int pos = a.cmpos[(int64_t)hq * a.npool_cap + i];
-    extra += (a.lub[(int64_t)hq * a.npool_cap + pos] > js);
+    extra += (a.ubuf[(int64_t)hq * a.npool_cap + pos] >= clo) && (a.lub[(int64_t)hq * a.npool_cap + pos] > js);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) extra += __shfl_xor(extra, off, 64);

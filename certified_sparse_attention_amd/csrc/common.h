@@ -135,6 +135,28 @@ __device__ inline double exact_score(const double *qd, const uint16_t *krow) {
   return (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) * kRsqrtD;
 }
 
+// The same exact score with the query given as fp32 values (each an exact fp16 value).
+__device__ inline double exact_score_qf(const float *qf, const uint16_t *krow) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(krow);
+  const float4 *q4 = reinterpret_cast<const float4 *>(qf);
+  double p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint4 a = src[2 * k], b = src[2 * k + 1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float4 qa = q4[4 * k], qb = q4[4 * k + 1], qc = q4[4 * k + 2], qe = q4[4 * k + 3];
+    float q[16] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w, qc.x, qc.y, qc.z, qc.w, qe.x, qe.y, qe.z, qe.w};
+    double acc = (double)q[0] * h2d((uint16_t)(w[0] & 0xFFFFu));
+#pragma unroll
+    for (int t = 1; t < 16; ++t) {
+      uint16_t hv = (uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu));
+      acc = acc + (double)q[t] * h2d(hv);
+    }
+    p[k] = acc;
+  }
+  return (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) * kRsqrtD;
+}
+
 // R1 sum of squares of one fp16 row.
 __device__ inline double row_sumsq(const uint16_t *row) {
   const uint4 *src = reinterpret_cast<const uint4 *>(row);

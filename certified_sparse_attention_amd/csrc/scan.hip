@@ -178,6 +178,7 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
 //     pass the same tests; the exact fp64 bounds, the exact perturbations and the
 //     per-key outputs are computed for those blocks only.
 struct ScanArgs {
+  const uint16_t *K;        // fp16 keys (exact scores of C_max candidates)
   const uint8_t *codes;
   const uint16_t *kscale;
   const int8_t *zq;
@@ -193,7 +194,8 @@ struct ScanArgs {
   float2 *bmax;             // [H_q][nbw]: per block, bounds of max UB and of max (UB + E)
   double *pbuf, *ubuf;
   uint32_t *live;
-  unsigned long long *clo;
+  unsigned long long *clo, *cstar;
+  int *cmcnt, *cmpos;       // keys with UB >= the c_lo snapshot (a superset of C_max)
   unsigned *vmax;
   int diag;                 // 1: every key is live and UB/LB/E are written for all keys
   double *lb_out, *e_out;   // diagnostics (may be null)
@@ -599,6 +601,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
 
   const uint64_t prefix = a.prefix[h];
   double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
+  double smA = -__builtin_huge_val(), smB = -__builtin_huge_val();   // max exact score of C_max candidates
   const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
 
   for (int c0 = 0; c0 < nblk; c0 += 2) {
@@ -624,6 +627,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     }
     double ubA[4], ubB[4];
     uint32_t liveA = 0, liveB = 0;     // bit Tg: the key of tile Tg is live for slot A / B
+    uint32_t cmA = 0, cmB = 0;         // bit Tg: UB >= c_lo snapshot (C_max candidate)
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
@@ -679,6 +683,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             lbA = fmax(lbA, lb);
             if (a.lb_out) a.lb_out[(int64_t)(hq0 + gA) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrA) + 1.0);
+            if (ub >= clo2A - marg) cmA |= 1u << Tg;
             if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
           }
           if (hasB) {
@@ -690,9 +695,27 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             lbB = fmax(lbB, lb);
             if (a.lb_out) a.lb_out[(int64_t)(hq0 + gB) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrB) + 1.0);
+            if (ub >= clo2B - marg) cmB |= 1u << Tg;
             if (a.diag || ub + Eup >= thrB - marg || ub >= clo2B - marg) liveB |= 1u << Tg;
           }
           if ((liveA | liveB) & (1u << Tg)) flag[tt] = 1;
+        }
+      }
+    }
+    // exact scores of C_max candidates: c* = max(c_R, max over them), since a key with
+    // UB < c_lo scores below c_lo <= c*; the list is filtered by the final c_lo later
+    if (__ballot((cmA | cmB) != 0)) {
+#pragma unroll 1
+      for (int sl = 0; sl < 2; ++sl) {
+        uint32_t m = sl ? cmB : cmA;
+        const int g = sl ? gB : gA;
+        while (m) {
+          const int Tg = __ffs(m) - 1;
+          m &= m - 1u;
+          const int64_t pos = tok0 + 16 * Tg + n16;
+          const double sc = exact_score_qf(a.qf + (int64_t)(hq0 + g) * kD, a.K + ((int64_t)h * a.n_cap + pos) * kD);
+          if (sl) smB = fmax(smB, sc); else smA = fmax(smA, sc);
+          a.cmpos[(int64_t)(hq0 + g) * a.npool_cap + atomicAdd(a.cmcnt + hq0 + g, 1)] = (int)pos;
         }
       }
     }
@@ -744,8 +767,14 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   for (int off = 8; off >= 1; off >>= 1) {
     lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
     lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
+    smA = fmax(smA, __shfl_xor(smA, off, 64));
+    smB = fmax(smB, __shfl_xor(smB, off, 64));
   }
   if (n16 == 0) {
+    if (hasA && smA > -__builtin_huge_val())
+      __hip_atomic_fetch_max(a.cstar + hq0 + gA, enc_max(smA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hasB && smB > -__builtin_huge_val())
+      __hip_atomic_fetch_max(a.cstar + hq0 + gB, enc_max(smB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (hasA && lbA > clo2A)
       __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max(lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (hasB && lbB > clo2B)

@@ -40,46 +40,23 @@ struct SelectArgs {
   int pass;
 };
 
-// ---- exact maximum over C_max (only live keys can have UB >= c_lo)
-__global__ __launch_bounds__(256) void cmax_kernel(SelectArgs a) {
-  const int hq = blockIdx.x;
-  const int h = hq / a.G;
-  __shared__ double qd[kD];
-  __shared__ double red[256];
-  if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
-  __syncthreads();
-  const double clo = dec_max(a.clo[hq]);
-  double m = -__builtin_huge_val();
-  const int64_t nw = (a.npool + 31) / 32;
-  for (int64_t wi = (int64_t)blockIdx.y * 256 + threadIdx.x; wi < nw; wi += (int64_t)gridDim.y * 256) {
-    uint32_t bits = a.live[(int64_t)hq * a.nwords + wi];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int64_t pos = wi * 32 + b;
-      if (a.ubuf[(int64_t)hq * a.npool_cap + pos] >= clo) {
-        const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-        m = fmax(m, s);
-        const int idx = atomicAdd(a.cmcnt + hq, 1);
-        a.cmpos[(int64_t)hq * a.npool_cap + idx] = (int)pos;
-      }
-    }
+// ---- buckets.  A tile is 64 bitmap words (2048 positions); one thread per word.
+__device__ inline int first_level_tab(double x, const double *lt, int J) {
+  int lo = 0, hi = J + 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (lt[mid] > x) lo = mid + 1; else hi = mid;
   }
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0 && red[0] > -__builtin_huge_val()) atomicMax(a.cstar + hq, enc_max(red[0]));
+  return lo;
 }
 
-// ---- buckets.  A tile is 64 bitmap words (2048 positions); one thread per word.
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
   __shared__ int hist[kMaxJ + 2];
+  __shared__ double lt[kMaxJ + 1];
   for (int j = lane; j < a.J + 2; j += 64) hist[j] = 0;
+  for (int j = lane; j <= a.J; j += 64) lt[j] = a.lt[j];
   __syncthreads();
   const double cs = dec_max(a.cstar[hq]);
   const int64_t wi = tile * 64 + lane;
@@ -90,16 +67,24 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     const uint32_t bits = a.live[(int64_t)hq * a.nwords + wi] & vmask;
     const int dead = valid - __popc(bits);
     if (dead) atomicAdd(&hist[a.J + 1], dead);
+    int8_t *lub = a.lub + (int64_t)hq * a.npool_cap + p0;
     if (a.full_lub)
       for (int b = 0; b < valid; ++b)
-        if (!((bits >> b) & 1u)) a.lub[(int64_t)hq * a.npool_cap + p0 + b] = (int8_t)(a.J + 1);
-    uint32_t rest = bits;
-    while (rest) {
-      const int b = __ffs(rest) - 1;
-      rest &= rest - 1u;
-      const int l = first_level(a.pbuf[(int64_t)hq * a.npool_cap + p0 + b] - cs, a.lt, a.J);
-      a.lub[(int64_t)hq * a.npool_cap + p0 + b] = (int8_t)l;
-      atomicAdd(&hist[l], 1);
+        if (!((bits >> b) & 1u)) lub[b] = (int8_t)(a.J + 1);
+    if (bits) {
+      // all loads of the word's live keys first, then the levels
+      const double *pb = a.pbuf + (int64_t)hq * a.npool_cap + p0;
+      double pv[32];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) pv[b] = ((bits >> b) & 1u) ? pb[b] : 0.0;
+#pragma unroll
+      for (int b = 0; b < 32; ++b) {
+        if ((bits >> b) & 1u) {
+          const int l = first_level_tab(pv[b] - cs, lt, a.J);
+          lub[b] = (int8_t)l;
+          atomicAdd(&hist[l], 1);
+        }
+      }
     }
   }
   __syncthreads();
@@ -110,76 +95,75 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
 // Per query head: the speculative level jspec (the deepest level whose cumulative
 // candidate count fits the budget), and tile offsets of the two candidate ranges
 // (l^ub <= jspec first, then jspec < l^ub <= J), each in position order.
-__global__ __launch_bounds__(64) void bucket_scan_kernel(SelectArgs a) {
-  const int hq = blockIdx.x, lane = threadIdx.x;
-  const int J2 = a.J + 2;
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(SelectArgs a) {
+  const int hq = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int J = a.J, J2 = J + 2;
+  __shared__ int part[4][64];
+  __shared__ int wsum1[4], wsum2[4];
   __shared__ int js_sh;
-  __shared__ int c1[64], c2[64];
-  __shared__ int hh[kMaxJ + 2];
-  // level histogram of the head: each lane sums the rows of its tiles (independent
-  // loads into registers), then one wavefront reduction per level
-  int tot[kMaxJ + 2];
-#pragma unroll
-  for (int j = 0; j < kMaxJ + 2; ++j) tot[j] = 0;
-  for (int64_t tile = lane; tile < a.ntiles; tile += 64) {
-    const int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * J2;
-#pragma unroll
-    for (int j = 0; j < kMaxJ + 2; ++j)
-      if (j < J2) tot[j] += th[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxJ + 2; ++j) {
-    if (j < J2) {
-      int v = tot[j];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) {
-        hh[j] = v;
-        a.hist[(int64_t)hq * J2 + j] = v;
-      }
-    }
+  const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
+  // level histogram: lane = level, wavefront wv sums tiles wv, wv + 4, ...
+  {
+    int v = 0;
+    if (lane < J2)
+      for (int64_t tile = wv; tile < a.ntiles; tile += 4) v += th0[tile * J2 + lane];
+    part[wv][lane] = v;
   }
   __syncthreads();
-  if (lane == 0) {
-    int cum = 0, js = 0;
-    for (int j = 0; j <= a.J; ++j) {
-      cum += hh[j];
-      if (cum <= a.budget || j == 0) js = j;
+  if (wv == 0) {
+    const int hv = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = hv;
+    int c = (lane <= J) ? hv : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(c, off, 64);
+      if (lane >= off) c += y;
     }
-    js_sh = js;
-    a.jspec[hq] = js;
+    // the levels that fit form a prefix 0..js (counts only grow with the level)
+    const unsigned long long fit = __ballot(lane <= J && (c <= a.budget || lane == 0));
+    if (lane == 0) {
+      js_sh = __popcll(fit) - 1;
+      a.jspec[hq] = js_sh;
+    }
   }
   __syncthreads();
   const int js = js_sh;
   int run1 = 0, run2 = 0;
-  for (int64_t t0 = 0; t0 < a.ntiles; t0 += 64) {
-    const int64_t tile = t0 + lane;
+  for (int64_t t0 = 0; t0 < a.ntiles; t0 += kScanThreads) {
+    const int64_t tile = t0 + t;
     int n1 = 0, n2 = 0;
     if (tile < a.ntiles) {
-      const int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * J2;
-#pragma unroll
-      for (int j = 0; j < kMaxJ + 1; ++j) {
-        if (j <= a.J) {
-          const int v = th[j];
-          if (j <= js) n1 += v; else n2 += v;
-        }
+      const int *th = th0 + tile * J2;
+      for (int j = 0; j <= J; ++j) {
+        const int v = th[j];
+        if (j <= js) n1 += v; else n2 += v;
       }
     }
-    // exclusive prefix over the 64 tiles of this chunk
     int x1 = n1, x2 = n2;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
       if (lane >= off) { x1 += y1; x2 += y2; }
     }
-    if (tile < a.ntiles) {
-      a.tileoff[(int64_t)hq * a.ntiles + tile] = run1 + x1 - n1;
-      a.tileoff2[(int64_t)hq * a.ntiles + tile] = run2 + x2 - n2;
+    if (lane == 63) { wsum1[wv] = x1; wsum2[wv] = x2; }
+    __syncthreads();
+    int b1 = 0, b2 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < wv) { b1 += wsum1[k]; b2 += wsum2[k]; }
+      s1 += wsum1[k];
+      s2 += wsum2[k];
     }
-    run1 += __shfl(x1, 63, 64);
-    run2 += __shfl(x2, 63, 64);
+    if (tile < a.ntiles) {
+      a.tileoff[(int64_t)hq * a.ntiles + tile] = run1 + b1 + x1 - n1;
+      a.tileoff2[(int64_t)hq * a.ntiles + tile] = run2 + b2 + x2 - n2;
+    }
+    run1 += s1;
+    run2 += s2;
+    __syncthreads();
   }
-  if (lane == 0) {
+  if (t == 0) {
     a.ccount1[hq] = run1;
     a.ccount[hq] = run1 + run2;
   }
@@ -233,7 +217,9 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
   const int hq = blockIdx.x;
   const int h = hq / a.G;
   __shared__ double qd[kD];
+  __shared__ double lt[kMaxJ + 1];
   if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
+  for (int j = threadIdx.x; j <= a.J; j += 256) lt[j] = a.lt[j];
   __syncthreads();
   int lo, hi;
   if (a.pass == 1) {
@@ -251,8 +237,8 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
     const int pos = a.candpos[o];
     const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
     const double E = perturbation(prefix, pos);
-    const int hl = first_level(s - cs, a.lt, a.J);
-    const int ll = first_level((s + E) - cs, a.lt, a.J);
+    const int hl = first_level_tab(s - cs, lt, a.J);
+    const int ll = first_level_tab((s + E) - cs, lt, a.J);
     double vsq = 0.0;
     if (ll <= a.J) vsq = row_sumsq(a.V + ((int64_t)h * a.n_cap + pos) * kD);
     a.rec_s[o] = s;
@@ -263,11 +249,8 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
 }
 
 hipError_t launch_select(const SelectArgs &a, int H_q, hipStream_t st) {
-  const int64_t cmc = ((a.npool + 31) / 32 + 255) / 256;
-  const unsigned cm_chunks = (unsigned)(cmc < 64 ? cmc : 64);
-  hipLaunchKernelGGL(cmax_kernel, dim3(H_q, cm_chunks), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bucket_count_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(H_q), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(H_q), dim3(kScanThreads), 0, st, a);
   hipLaunchKernelGGL(bucket_write_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
   return hipGetLastError();
 }
