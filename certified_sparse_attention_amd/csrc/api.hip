@@ -51,7 +51,8 @@ int check_params(const csa_params *p) {
   if (p->r < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "r must be >= 1");
   if (p->J < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "J must be >= 0");
   if (p->J > csa::kMaxJ) return fail(CSA_ERR_UNSUPPORTED, "J must be <= %d", csa::kMaxJ);
-  if (p->window < 32) return fail(CSA_ERR_UNSUPPORTED, "window must be >= 32");
+  if (p->window < 32 || p->window > csa::kMaxWin)
+    return fail(CSA_ERR_UNSUPPORTED, "window must lie in [32, %d]", csa::kMaxWin);
   if (p->measure < 0 || p->measure > 2) return fail(CSA_ERR_INVALID_ARGUMENT, "unknown measure %d", p->measure);
   return CSA_OK;
 }
@@ -95,6 +96,7 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.lub = take(Hq * npc);
   P.live = take(Hq * (size_t)(P.npool_cap / 32 + 1) * sizeof(uint32_t));
   P.bmax = take(Hq * (size_t)((P.npool_cap + csa::kBlk - 1) / csa::kBlk) * 2 * sizeof(float));
+  P.win = take(Hq * (size_t)csa::kWinW * sizeof(double));
   P.candpos = take(Hq * npc * sizeof(int));
   P.rec_s = take(Hq * npc * sizeof(double));
   P.rec_w = take(Hq * npc * sizeof(double));
@@ -121,7 +123,7 @@ int check_packed(const csa_packed *p) {
 
 // Prep + scan shared by the certified call and the bounds diagnostic.
 int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, const uint16_t *K,
-                  const csa_packed *pk, int64_t n, void *ws, const csa::Plan &P, double *lb_out,
+                  const uint16_t *V, const csa_packed *pk, int64_t n, void *ws, const csa::Plan &P, double *lb_out,
                   double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st, int diag = 0) {
   csa::PrepArgs pa;
   pa.q = q;
@@ -155,9 +157,13 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   hipError_t e = csa::launch_prep(pa, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const int64_t npool = n - p->window;
-  if (npool <= 0) return CSA_OK;
   csa::ScanArgs sa;
   sa.K = K;
+  sa.V = V;
+  sa.n = n;
+  sa.W = p->window;
+  sa.sR = pa.sR;
+  sa.win = at<double>(ws, P.win);
   sa.cstar = pa.cstar;
   sa.cmcnt = pa.cmcnt;
   sa.cmpos = at<int>(ws, P.cmpos);
@@ -169,8 +175,9 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.vnorm = pk->vnorm;
   sa.n_cap = s->n_cap;
   sa.nb_cap = s->n_cap / csa::kBlk;
-  sa.npool = npool;
-  sa.nb_pool = (npool + csa::kBlk - 1) / csa::kBlk;
+  sa.npool = npool > 0 ? npool : 0;
+  sa.nb_pool = (sa.npool + csa::kBlk - 1) / csa::kBlk;
+  sa.nstream = npool > 0 ? csa::scan_stream_wgs(P.H_kv, sa.nb_pool) : 0;
   sa.npool_cap = P.npool_cap;
   sa.G = P.G;
   sa.H_kv = P.H_kv;
@@ -195,6 +202,7 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   e = csa::launch_scan(sa, st);
   if (e != hipSuccess) return hip_fail(e, "scan");
   if (ev1 && (e = hipEventRecord((hipEvent_t)ev1, st)) != hipSuccess) return hip_fail(e, "event");
+  if (npool <= 0) return CSA_OK;
   e = csa::launch_refine(sa, st);
   if (e != hipSuccess) return hip_fail(e, "refine");
   if (ub_diag) {
@@ -272,7 +280,7 @@ int csa_scan_bounds(const csa_shape *shape, const csa_params *params, const uint
   const csa::Plan P = make_plan(shape, params, n);
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
-  return run_prep_scan(shape, params, q, K, packed, n, workspace, P, LB, E, UB, nullptr, nullptr,
+  return run_prep_scan(shape, params, q, K, nullptr, packed, n, workspace, P, LB, E, UB, nullptr, nullptr,
                        (hipStream_t)stream, 1);
 }
 
@@ -295,7 +303,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   hipStream_t st = (hipStream_t)stream;
   void *ev0 = trace ? trace->ev_scan_begin : nullptr;
   void *ev1 = trace ? trace->ev_scan_end : nullptr;
-  rc = run_prep_scan(shape, params, q, K, packed, n, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
+  rc = run_prep_scan(shape, params, q, K, V, packed, n, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
   if (rc) return rc;
   void *ws = workspace;
   const int64_t npool = n - params->window;
@@ -362,6 +370,8 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.lt = at<double>(ws, P.lt);
   ca.tau = at<double>(ws, P.tau);
   ca.sR = at<double>(ws, P.sR);
+  ca.win = at<double>(ws, P.win);
+  ca.qconst = at<double>(ws, P.qconst);
   ca.cstar = at<unsigned long long>(ws, P.cstar);
   ca.vmax = at<unsigned>(ws, P.vmax);
   ca.ccount = at<int>(ws, P.ccount);

@@ -30,6 +30,7 @@ struct CertArgs {
   double eps, L;
   const float *qf;
   const double *lt, *tau, *sR;
+  const double *win, *qconst;   // window sums relative to c_R; per-query constants (c_R)
   const unsigned long long *cstar, *clo;
   const double *ubuf;
   const unsigned *vmax;
@@ -223,6 +224,7 @@ struct FinSmem {
   double dr, qr;
   double beta[kMaxJ + 1];
   double dots[kMaxJ + 1][4];     // |c|^2, c.V, |o^ - c|^2, |o^|^2 per level
+  double dpart[kMaxJ + 1][4][4]; // the same over channel quarters
   double root[kMaxJ + 1][4];
   int jstar;
   long long extra[4];
@@ -264,38 +266,19 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     __syncthreads();
   }
-  // window sums relative to c*
-  const double cs = dec_max(a.cstar[hq]);
-  const int64_t w0 = a.n - a.W;
-  double nr = 0.0, dr = 0.0, qr = 0.0;
-  for (int c0 = 0; c0 < a.W; c0 += kStage) {
-    const int cnt = min(kStage, a.W - c0);
-    if (t < cnt) {
-      s.w[t] = exp(a.sR[(int64_t)hq * a.W + c0 + t] - cs);
-      s.vsq[t] = row_sumsq(a.V + ((int64_t)h * a.n_cap + w0 + c0 + t) * kD);
-    }
-    for (int e = t; e < cnt * 16; e += 256) {
-      const int r = e >> 4, part = e & 15;
-      reinterpret_cast<uint4 *>(s.vs[r])[part] =
-          reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + w0 + c0 + r) * kD)[part];
-    }
-    __syncthreads();
-    if (t < kD) {
-      for (int r = 0; r < cnt; ++r) nr += s.w[r] * h2d(s.vs[r][t]);
-    } else if (t == kD) {
-      for (int r = 0; r < cnt; ++r) dr += s.w[r];
-    } else if (t == kD + 1) {
-      for (int r = 0; r < cnt; ++r) qr += s.w[r] * s.vsq[r];
-    }
-    __syncthreads();
+  // window sums, rescaled from c_R to c*
+  {
+    const double cs = dec_max(a.cstar[hq]);
+    const double sc = exp(a.qconst[(int64_t)hq * kQc + QC_CR] - cs);
+    const double *wr = a.win + (int64_t)hq * kWinW;
+    if (t < kD) f.nr[t] = wr[t] * sc;
+    if (t == kD) f.dr = wr[kD] * sc;
+    if (t == kD + 1) f.qr = wr[kD + 1] * sc;
   }
-  if (t < kD) f.nr[t] = nr;
-  if (t == kD) f.dr = dr;
-  if (t == kD + 1) f.qr = qr;
   // prefix over levels
   for (int c = t; c < kStatW; c += 256) {
     double run = 0.0;
-    for (int j = 0; j < J1; ++j) {
+    for (int j = 0; j <= jmax; ++j) {
       run += s.acc[j][c];
       s.acc[j][c] = run;
     }
@@ -304,33 +287,32 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   // certificate of every level up to jmax: dot products per level (wavefront wv takes
   // levels wv, wv + 4, ...), then the four KL roots of every level in parallel, then beta
   const double Vmax = h2d((uint16_t)a.vmax[h]);
-  for (int j = wv; j <= jmax; j += 4) {
-    const double tau = f.tau[j];
-    const double D_det = f.dr + s.acc[j][256];
-    const double D_hat = D_det + tau * s.acc[j][258];
-    double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
-    for (int c = lane; c < kD; c += 64) {
-      const double nd = f.nr[c] + s.acc[j][c];
-      const double cc = nd / D_det;
-      const double o = (nd + tau * s.acc[j][128 + c]) / D_hat;
-      cn2 += cc * cc;
-      cV += cc * s.acc[j][128 + c];
-      dn2 += (o - cc) * (o - cc);
-      on2 += o * o;
+  {
+    const int j = t >> 2, qt = t & 3;
+    if (j <= jmax) {
+      const double tau = f.tau[j];
+      const double D_det = f.dr + s.acc[j][256];
+      const double D_hat = D_det + tau * s.acc[j][258];
+      double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
+      for (int c = 32 * qt; c < 32 * qt + 32; ++c) {
+        const double nd = f.nr[c] + s.acc[j][c];
+        const double cc = nd / D_det;
+        const double o = (nd + tau * s.acc[j][128 + c]) / D_hat;
+        cn2 += cc * cc;
+        cV += cc * s.acc[j][128 + c];
+        dn2 += (o - cc) * (o - cc);
+        on2 += o * o;
+      }
+      f.dpart[j][qt][0] = cn2;
+      f.dpart[j][qt][1] = cV;
+      f.dpart[j][qt][2] = dn2;
+      f.dpart[j][qt][3] = on2;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      cn2 += __shfl_xor(cn2, off, 64);
-      cV += __shfl_xor(cV, off, 64);
-      dn2 += __shfl_xor(dn2, off, 64);
-      on2 += __shfl_xor(on2, off, 64);
-    }
-    if (lane == 0) {
-      f.dots[j][0] = cn2;
-      f.dots[j][1] = cV;
-      f.dots[j][2] = dn2;
-      f.dots[j][3] = on2;
-    }
+  }
+  __syncthreads();
+  if (t < 4 * (jmax + 1)) {
+    const int j = t >> 2, r = t & 3;
+    f.dots[j][r] = (f.dpart[j][0][r] + f.dpart[j][1][r]) + (f.dpart[j][2][r] + f.dpart[j][3][r]);
   }
   __syncthreads();
   if (t < 4 * (jmax + 1)) {
@@ -362,11 +344,9 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     a.klv[(int64_t)hq * J1 + j] = (int)k;
   }
   __syncthreads();
-  if (t == 0) {
-    int js = a.J + 1;
-    for (int j = 0; j <= jmax; ++j)
-      if (f.beta[j] <= a.eps) { js = j; break; }
-    f.jstar = js;
+  if (wv == 0) {
+    const unsigned long long ok = __ballot(lane <= jmax && f.beta[lane] <= a.eps);
+    if (lane == 0) f.jstar = ok ? (__ffsll((long long)ok) - 1) : a.J + 1;
   }
   __syncthreads();
   const int js = f.jstar;

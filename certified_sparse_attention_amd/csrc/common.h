@@ -157,6 +157,44 @@ __device__ inline double exact_score_qf(const float *qf, const uint16_t *krow) {
   return (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) * kRsqrtD;
 }
 
+// Wavefront-cooperative R1 sums: lane 8s + k holds chunk k (16 channels, summed in
+// order) of item s; r1_combine8 returns ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7))
+// to all 8 lanes of the item (IEEE addition is commutative, so the butterfly forms
+// exactly those sums).
+__device__ inline double r1_combine8(double p) {
+  p = p + __shfl_xor(p, 1, 64);
+  p = p + __shfl_xor(p, 2, 64);
+  p = p + __shfl_xor(p, 4, 64);
+  return p;
+}
+// Chunk k of q . k for one fp16 key row (q given as doubles of the chunk).
+__device__ inline double score_chunk(const double *q16, const uint16_t *krow, int k) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(krow) + 2 * k;
+  const uint4 a = src[0], b = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  double acc = q16[0] * h2d((uint16_t)(w[0] & 0xFFFFu));
+#pragma unroll
+  for (int t = 1; t < 16; ++t) {
+    const uint16_t hv = (uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu));
+    acc = acc + q16[t] * h2d(hv);
+  }
+  return acc;
+}
+// Chunk k of |v|^2 for one fp16 row.
+__device__ inline double sumsq_chunk(const uint16_t *row, int k) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(row) + 2 * k;
+  const uint4 a = src[0], b = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const double v0 = h2d((uint16_t)(w[0] & 0xFFFFu));
+  double acc = v0 * v0;
+#pragma unroll
+  for (int t = 1; t < 16; ++t) {
+    const double v = h2d((uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu)));
+    acc = acc + v * v;
+  }
+  return acc;
+}
+
 // R1 sum of squares of one fp16 row.
 __device__ inline double row_sumsq(const uint16_t *row) {
   const uint4 *src = reinterpret_cast<const uint4 *>(row);
@@ -294,7 +332,7 @@ struct Plan {
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
   size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, ccount, ccount1, jspec;
-  size_t pbuf, ubuf, lub, live, bmax, candpos, rec_s, rec_w, rec_vsq, rec_hl;
+  size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
   size_t total;
 };
@@ -305,5 +343,7 @@ enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, QC_PILOT, kQc = 8 };
 constexpr int kBucketTile = 2048;   // positions per bucket tile (64 bitmap words)
 constexpr int kDefaultBudget = 4096; // candidates rescored before the first certificate pass
 constexpr int kExactChunks = 64;
+constexpr int kMaxWin = 1024;       // largest window (recent tokens read exactly)
+constexpr int kWinW = 130;          // window sums per query head: N[128], D, Q
 
 }  // namespace csa

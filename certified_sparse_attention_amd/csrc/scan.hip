@@ -31,7 +31,6 @@ __device__ inline void wave_sync() {
 }
 
 // ------------------------------------------------------------------ prep
-constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
 
 struct PrepArgs {
   const uint16_t *q, *K;
@@ -119,37 +118,10 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
         A[kh * 1024 + (op_row(gs, 1) + 16 * kg) * 16 + b] = 0;
       }
   }
-  // window scores s_R, c_R; then a strided sample of the pool scored exactly
-  const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
-  const int nw = (int)(a.n - w0);
-  double m = -__builtin_huge_val();
-  for (int i = t; i < nw; i += kD) {
-    const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + w0 + i) * kD);
-    a.sR[(int64_t)hq * a.W + i] = s;
-    m = fmax(m, s);
-  }
-  double mp = -__builtin_huge_val();
-  if (w0 > 0) {
-    const int64_t stride = (w0 + kPilot - 1) / kPilot;
-    const int64_t pos = (int64_t)t * stride;
-    if (t < kPilot && pos < w0) mp = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    m = fmax(m, __shfl_xor(m, off, 64));
-    mp = fmax(mp, __shfl_xor(mp, off, 64));
-  }
-  __syncthreads();
-  if (lane == 0) { smax[t >> 6] = m; red[t >> 6] = mp; }
-  __syncthreads();
+  // c_lo and c* start empty: the window work and the scan raise them
   if (t == 0) {
-    const double cr = fmax(smax[0], smax[1]);
-    const double pilot = fmax(cr, fmax(red[0], red[1]));
-    double *qc = a.qconst + (int64_t)hq * kQc;
-    qc[QC_CR] = cr;
-    qc[QC_PILOT] = pilot;
-    a.clo[hq] = enc_max(cr);
-    a.cstar[hq] = enc_max(cr);
+    a.clo[hq] = enc_max(-__builtin_huge_val());
+    a.cstar[hq] = enc_max(-__builtin_huge_val());
     a.cmcnt[hq] = 0;
     a.ccount[hq] = 0;
     a.flags[hq] = 0;
@@ -187,10 +159,17 @@ struct ScanArgs {
   int64_t n_cap, nb_cap, npool, nb_pool, npool_cap, nwords, nbw;
   int G, H_kv, J;
   const float *qf;
-  const double *qconst;
+  double *qconst;
   const int8_t *qA;
   const uint64_t *prefix;
   const double *lt;
+  // window work (extra workgroups of the streaming kernel, one per query head)
+  const uint16_t *V;
+  int64_t n;
+  int W;
+  int64_t nstream;          // workgroups of the streaming scan; the rest do window work
+  double *sR;               // [H_q][W] window scores
+  double *win;              // [H_q][kWinW]: sum_R e^(s - c_R) v, sum e^(s - c_R), sum e^(s - c_R) |v|^2
   float2 *bmax;             // [H_q][nbw]: per block, bounds of max UB and of max (UB + E)
   double *pbuf, *ubuf;
   uint32_t *live;
@@ -349,8 +328,110 @@ __device__ inline Bound32 bound32(float base, float ebpad, float alpha, float ha
   return r;
 }
 
+constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
+
+// Shared memory of the streaming kernel; its window workgroups reuse it.
+struct StreamSmem {
+  alignas(16) uint8_t Abuf[4][2 * 1024];
+  double cst[4][3][kBlocksPerWave][8];
+  float2 mx[4][kBlocksPerWave][8];
+};
+struct WindowSmem {
+  double sw[kMaxWin], vsq[kMaxWin];
+  double red[2][4];
+};
+union ScanSmem {
+  StreamSmem st;
+  WindowSmem win;
+};
+
+// Window work of query head hq (256 threads): exact window scores and c_R, a strided
+// sample of the pool scored exactly (a lower bound on c*), and the window's sums
+// relative to c_R, which the certificate rescales to c*.  All tokens are the window
+// when n <= window.  Scores are wavefront-cooperative: 8 keys per wavefront step.
+__device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int s8 = lane >> 3, k8 = lane & 7;
+  const int h = hq / a.G;
+  double q16[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
+  const int nw = (int)(a.n - w0);
+  const int64_t stride = (w0 + kPilot - 1) / kPilot;
+  const int npilot = (w0 > 0) ? kPilot : 0;
+  double m = -__builtin_huge_val(), mp = -__builtin_huge_val();
+  for (int e0 = 0; e0 < nw + npilot; e0 += 32) {
+    const int e = e0 + 8 * wv + s8;                       // the key of this lane's group
+    int64_t pos = -1;
+    if (e < nw) pos = w0 + e;
+    else if (e < nw + npilot && (int64_t)(e - nw) * stride < w0) pos = (int64_t)(e - nw) * stride;
+    double p = 0.0, v = 0.0;
+    if (pos >= 0) {
+      p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
+      if (e < nw && a.V) v = sumsq_chunk(a.V + ((int64_t)h * a.n_cap + pos) * kD, k8);
+    }
+    const double sc = r1_combine8(p) * kRsqrtD;
+    const double vs = r1_combine8(v);
+    if (pos >= 0 && k8 == 0) {
+      if (e < nw) {
+        a.sR[(int64_t)hq * a.W + e] = sc;
+        sm.sw[e] = sc;
+        sm.vsq[e] = vs;
+        m = fmax(m, sc);
+      } else {
+        mp = fmax(mp, sc);
+      }
+    }
+  }
+  m = wave_max_f64(m);
+  mp = wave_max_f64(mp);
+  if (lane == 0) { sm.red[0][wv] = m; sm.red[1][wv] = mp; }
+  __syncthreads();
+  const double cr = fmax(fmax(sm.red[0][0], sm.red[0][1]), fmax(sm.red[0][2], sm.red[0][3]));
+  const double pilot = fmax(cr, fmax(fmax(sm.red[1][0], sm.red[1][1]), fmax(sm.red[1][2], sm.red[1][3])));
+  for (int i = t; i < nw; i += 256) sm.sw[i] = exp(sm.sw[i] - cr);
+  __syncthreads();
+  double *out = a.win + (int64_t)hq * kWinW;
+  if (t < kD) {
+    if (a.V) {
+      const uint16_t *vcol = a.V + ((int64_t)h * a.n_cap + w0) * kD + t;
+      double acc = 0.0;
+      int i = 0;
+      for (; i + 8 <= nw; i += 8) {
+        uint16_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = vcol[(int64_t)(i + k) * kD];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += sm.sw[i + k] * h2d(v[k]);
+      }
+      for (; i < nw; ++i) acc += sm.sw[i] * h2d(vcol[(int64_t)i * kD]);
+      out[t] = acc;
+    }
+  } else if (t == kD) {
+    double d = 0.0;
+    for (int i = 0; i < nw; ++i) d += sm.sw[i];
+    out[kD] = d;
+  } else if (t == kD + 1) {
+    double q = 0.0;
+    for (int i = 0; i < nw; ++i) q += sm.sw[i] * sm.vsq[i];
+    out[kD + 1] = q;
+  } else if (t == kD + 2) {
+    double *qc = a.qconst + (int64_t)hq * kQc;
+    qc[QC_CR] = cr;
+    qc[QC_PILOT] = pilot;
+    __hip_atomic_fetch_max(a.clo + hq, enc_max(cr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(a.cstar + hq, enc_max(cr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  __shared__ ScanSmem sm;
+  if ((int64_t)blockIdx.x >= a.nstream) {
+    window_work(a, (int)((int64_t)blockIdx.x - a.nstream), sm.win);
+    return;
+  }
   constexpr bool kTwo = G > 4;
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
@@ -362,12 +443,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
   const int n16 = lane & 15, grp = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
-  __shared__ double cst_all[4][3][kBlocksPerWave][8];
-  __shared__ float2 mx_all[4][kBlocksPerWave][8];
-  uint8_t *Abuf = Abuf_all[wv];
-  double(*cst)[kBlocksPerWave][8] = cst_all[wv];
-  float2(*mx)[8] = mx_all[wv];
+  uint8_t *Abuf = sm.st.Abuf[wv];
+  double(*cst)[kBlocksPerWave][8] = sm.st.cst[wv];
+  float2(*mx)[8] = sm.st.mx[wv];
 
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = kTwo && gB < G;
@@ -537,12 +615,17 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   __shared__ double cst_all[4][3][kBlocksPerWave][8];
   __shared__ double clo_all[4][8];
   __shared__ uint8_t flag_all[4][64];
+  __shared__ int ent_all[4][64];
+  __shared__ unsigned long long smx_all[4][8];   // max exact score of C_max candidates per query
   uint8_t *Abuf = Abuf_all[wv];
   double(*cst)[kBlocksPerWave][8] = cst_all[wv];
   uint8_t *flag = flag_all[wv];
+  int *ent = ent_all[wv];
+  unsigned long long *smx = smx_all[wv];
 
   // one snapshot of c_lo's running value per query, shared by every test below
   const int hq0 = h * G;
+  if (lane < 8) smx[lane] = enc_max(-__builtin_huge_val());
   if (lane < G)
     clo_all[wv][lane] = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   wave_sync();
@@ -601,7 +684,6 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
 
   const uint64_t prefix = a.prefix[h];
   double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
-  double smA = -__builtin_huge_val(), smB = -__builtin_huge_val();   // max exact score of C_max candidates
   const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
 
   for (int c0 = 0; c0 < nblk; c0 += 2) {
@@ -703,19 +785,46 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       }
     }
     // exact scores of C_max candidates: c* = max(c_R, max over them), since a key with
-    // UB < c_lo scores below c_lo <= c*; the list is filtered by the final c_lo later
+    // UB < c_lo scores below c_lo <= c*; the list is filtered by the final c_lo later.
+    // Candidates are listed in LDS and scored 8 per wavefront step.
     if (__ballot((cmA | cmB) != 0)) {
 #pragma unroll 1
       for (int sl = 0; sl < 2; ++sl) {
-        uint32_t m = sl ? cmB : cmA;
-        const int g = sl ? gB : gA;
-        while (m) {
-          const int Tg = __ffs(m) - 1;
-          m &= m - 1u;
-          const int64_t pos = tok0 + 16 * Tg + n16;
-          const double sc = exact_score_qf(a.qf + (int64_t)(hq0 + g) * kD, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-          if (sl) smB = fmax(smB, sc); else smA = fmax(smA, sc);
-          a.cmpos[(int64_t)(hq0 + g) * a.npool_cap + atomicAdd(a.cmcnt + hq0 + g, 1)] = (int)pos;
+#pragma unroll 1
+        for (int Tg = 0; Tg < 4; ++Tg) {
+          const bool f = (((sl ? cmB : cmA) >> Tg) & 1u) != 0u;
+          const unsigned long long mk = __ballot(f);
+          if (!mk) continue;
+          if (f) {
+            const int idx = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+            ent[idx] = (16 * Tg + n16) | ((sl ? gB : gA) << 8);
+          }
+          wave_sync();
+          const int ne = __popcll(mk);
+          for (int e0 = 0; e0 < ne; e0 += 8) {
+            const int e = e0 + (lane >> 3), k8 = lane & 7;
+            int g2 = 0;
+            int64_t pos = -1;
+            if (e < ne) {
+              const int v = ent[e];
+              g2 = v >> 8;
+              pos = tok0 + (v & 0xFF);
+            }
+            double p = 0.0;
+            if (pos >= 0) {
+              double q16[16];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(hq0 + g2) * kD + 16 * k8 + i];
+              p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
+            }
+            const double sc = r1_combine8(p) * kRsqrtD;
+            if (pos >= 0 && k8 == 0) {
+              atomicMax(&smx[g2], enc_max(sc));
+              a.cmpos[(int64_t)(hq0 + g2) * a.npool_cap + atomicAdd(a.cmcnt + hq0 + g2, 1)] = (int)pos;
+            }
+          }
+          wave_sync();
         }
       }
     }
@@ -767,9 +876,10 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   for (int off = 8; off >= 1; off >>= 1) {
     lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
     lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
-    smA = fmax(smA, __shfl_xor(smA, off, 64));
-    smB = fmax(smB, __shfl_xor(smB, off, 64));
   }
+  wave_sync();
+  const double smA = hasA ? dec_max(smx[gA]) : -__builtin_huge_val();
+  const double smB = hasB ? dec_max(smx[gB]) : -__builtin_huge_val();
   if (n16 == 0) {
     if (hasA && smA > -__builtin_huge_val())
       __hip_atomic_fetch_max(a.cstar + hq0 + gA, enc_max(smA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -782,10 +892,15 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   }
 }
 
+// Streaming workgroups first, then one window workgroup per query head (a.nstream
+// must be the number of streaming workgroups, 0 when the pool is empty).
+int64_t scan_stream_wgs(int64_t H_kv, int64_t nb_pool) {
+  const int64_t waves = H_kv * ((nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
+  return (waves + 3) / 4;
+}
+
 hipError_t launch_scan(const ScanArgs &a, hipStream_t st) {
-  const int64_t waves = (int64_t)a.H_kv * ((a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
-  const unsigned wgs = (unsigned)((waves + 3) / 4);
-  if (wgs == 0) return hipSuccess;
+  const unsigned wgs = (unsigned)(a.nstream + (int64_t)a.H_kv * a.G);
   switch (a.G) {
     case 1: hipLaunchKernelGGL(scan_kernel<1>, dim3(wgs), dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(scan_kernel<2>, dim3(wgs), dim3(256), 0, st, a); break;
