@@ -82,6 +82,8 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.cstar = take(Hq * sizeof(unsigned long long));
   P.vmax = take((size_t)P.H_kv * sizeof(unsigned));
   P.cmcnt = take(Hq * sizeof(int));
+  P.bdone = take(Hq * sizeof(int));
+  P.exdone = take(Hq * sizeof(int));
   P.cmpos = take(Hq * npc * sizeof(int));
   P.hist = take(Hq * J2 * sizeof(int));
   P.tilecnt = 0;
@@ -152,6 +154,8 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.hist = at<int>(ws, P.hist);
   pa.ccount = at<int>(ws, P.ccount);
   pa.flags = at<int>(ws, P.flags);
+  pa.bdone = at<int>(ws, P.bdone);
+  pa.exdone = at<int>(ws, P.exdone);
   pa.npool_cap = P.npool_cap;
   pa.live = at<uint32_t>(ws, P.live);
   hipError_t e = csa::launch_prep(pa, st);
@@ -336,6 +340,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.ccount1 = at<int>(ws, P.ccount1);
     sa.jspec = at<int>(ws, P.jspec);
     sa.flags = at<int>(ws, P.flags);
+    sa.bdone = at<int>(ws, P.bdone);
     sa.budget = params->cand_budget > 0 ? params->cand_budget : csa::kDefaultBudget;
     sa.pass = 1;
     sa.ccount = at<int>(ws, P.ccount);
@@ -391,6 +396,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.klv = at<int>(ws, P.klv);
   ca.flags = at<int>(ws, P.flags);
   ca.exactp = at<double>(ws, P.exactp);
+  ca.exdone = at<int>(ws, P.exdone);
   ca.o_hat = o_hat;
   ca.beta = beta;
   ca.stop = stop_level;
@@ -399,24 +405,29 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.ccount1 = at<int>(ws, P.ccount1);
   ca.jspec = at<int>(ws, P.jspec);
   if (all_exact) {
-    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");
+    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, false, st)) != hipSuccess) return hip_fail(e, "certify");
   } else {
-    // pass 1: levels up to the speculative level; pass 2: the heads that need all levels
+    // pass 1: levels up to the speculative level (at most `budget` candidates, so the
+    // segmented accumulation is only needed when the budget exceeds the fused size);
+    // pass 2: the heads that need all levels
+    const bool seg1 = sel.budget > csa::kFusedMax;
     if ((e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess ||
-        (e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess ||
+        (e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess ||
         (e = csa::launch_rescore(sel, 2, P.H_q, st)) != hipSuccess ||
-        (e = csa::launch_certify_pass(ca, 2, P.H_q, st)) != hipSuccess)
+        (e = csa::launch_certify_pass(ca, 2, P.H_q, true, st)) != hipSuccess)
       return hip_fail(e, "certify");
   }
   if ((e = csa::launch_exact(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "exact");
 
   if (trace) {
     const int Hq = P.H_q;
-    hipLaunchKernelGGL(trace_kernel, dim3((Hq + 63) / 64), dim3(64), 0, st, at<double>(ws, P.qconst),
+    if (trace->c_R || trace->c_lo || trace->c_star || trace->cmax_count || trace->cand_count) {
+      hipLaunchKernelGGL(trace_kernel, dim3((Hq + 63) / 64), dim3(64), 0, st, at<double>(ws, P.qconst),
                        at<unsigned long long>(ws, P.clo), at<unsigned long long>(ws, P.cstar),
                        at<int>(ws, P.cmcnt), at<int>(ws, P.cmpos), at<double>(ws, P.ubuf), P.npool_cap,
                        at<int>(ws, P.ccount), Hq, trace->c_R, trace->c_lo,
                        trace->c_star, trace->cmax_count, trace->cand_count);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "trace");
     const size_t J1 = (size_t)P.J + 1;
     auto cp = [&](void *dst, size_t off, size_t bytes) -> hipError_t {

@@ -39,6 +39,7 @@ struct CertArgs {
   const int8_t *lub;
   double *partial, *betalv, *dhatlv;
   int *klv, *flags;
+  int *exdone;                  // [H_q] chunks of the exact fallback that have finished
   const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list
   int pass;                     // 1: levels <= jspec; 2: all levels, heads flagged for extension
   double *exactp;
@@ -97,37 +98,36 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
       }
     }
     __syncthreads();
+    // threads 0..127: heavy column t; threads 128..255: light column t - 128; lanes
+    // 64..67 also carry the four scalar columns (one or two read-modify-writes each)
     if (t < kD) {
+      const int c = t;
+      const int sc = t - 64;     // scalar column of lanes 64..67
       for (int r = 0; r < cnt; ++r) {
         const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
         if (llev > a.J) continue;
-        const double v = h2d(s.vs[r][t]);
-        if (hlev <= a.J) s.acc[hlev][t] += s.w[r] * v;
-        if (llev < hlev) {
-          s.acc[llev][128 + t] += v;
-          if (hlev <= a.J) s.acc[hlev][128 + t] -= v;
+        if (hlev <= a.J) s.acc[hlev][c] += s.w[r] * h2d(s.vs[r][c]);
+        if (sc >= 0 && sc < 4) {
+          if (sc == 0) {
+            if (hlev <= a.J) s.acc[hlev][256] += s.w[r];
+          } else if (sc == 1) {
+            if (hlev <= a.J) s.acc[hlev][257] += s.w[r] * s.vsq[r];
+          } else if (llev < hlev) {
+            const int col = (sc == 2) ? 258 : 259;
+            const double d = (sc == 2) ? 1.0 : s.vsq[r];
+            s.acc[llev][col] += d;
+            if (hlev <= a.J) s.acc[hlev][col] -= d;
+          }
         }
       }
-    } else if (t < kD + 4) {
+    } else {
       const int c = t - kD;
       for (int r = 0; r < cnt; ++r) {
         const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
-        if (llev > a.J) continue;
-        if (c == 0) {
-          if (hlev <= a.J) s.acc[hlev][256] += s.w[r];
-        } else if (c == 1) {
-          if (hlev <= a.J) s.acc[hlev][257] += s.w[r] * s.vsq[r];
-        } else if (c == 2) {
-          if (llev < hlev) {
-            s.acc[llev][258] += 1.0;
-            if (hlev <= a.J) s.acc[hlev][258] -= 1.0;
-          }
-        } else {
-          if (llev < hlev) {
-            s.acc[llev][259] += s.vsq[r];
-            if (hlev <= a.J) s.acc[hlev][259] -= s.vsq[r];
-          }
-        }
+        if (llev > a.J || llev >= hlev) continue;
+        const double v = h2d(s.vs[r][c]);
+        s.acc[llev][128 + c] += v;
+        if (hlev <= a.J) s.acc[hlev][128 + c] -= v;
       }
     }
     __syncthreads();
@@ -425,11 +425,14 @@ __global__ __launch_bounds__(128) void exact_partial_kernel(CertArgs a) {
     out[128] = accD;
     out[129] = accQ;
   }
-}
-
-__global__ __launch_bounds__(128) void exact_final_kernel(CertArgs a) {
-  const int hq = blockIdx.x, t = threadIdx.x;
-  if (a.flags[hq] == 0) return;
+  // the last chunk of the head to finish sums the chunks in a fixed order
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (t == 0) last = (atomicAdd(a.exdone + hq, 1) == kExactChunks - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
   double N = 0.0, Dn = 0.0;
   for (int c = 0; c < kExactChunks; ++c) {
     const double *p = a.exactp + ((int64_t)hq * kExactChunks + c) * 130;
@@ -439,16 +442,15 @@ __global__ __launch_bounds__(128) void exact_final_kernel(CertArgs a) {
   a.o_hat[(int64_t)hq * kD + t] = (float)(N / Dn);
 }
 
-hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, hipStream_t st) {
+hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, bool segmented, hipStream_t st) {
   a.pass = pass;
-  if (!a.all_exact) hipLaunchKernelGGL(accumulate_kernel, dim3(H_q, kSegWorkers), dim3(256), 0, st, a);
+  if (!a.all_exact && segmented) hipLaunchKernelGGL(accumulate_kernel, dim3(H_q, kSegWorkers), dim3(256), 0, st, a);
   hipLaunchKernelGGL(finish_kernel, dim3(H_q), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_exact(const CertArgs &a, int H_q, hipStream_t st) {
   hipLaunchKernelGGL(exact_partial_kernel, dim3(H_q, kExactChunks), dim3(128), 0, st, a);
-  hipLaunchKernelGGL(exact_final_kernel, dim3(H_q), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -332,6 +332,7 @@ struct Plan {
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
   size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, ccount, ccount1, jspec;
+  size_t bdone, exdone;  // per-head completion counters (last-workgroup reductions)
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
   size_t total;
@@ -341,7 +342,7 @@ struct Plan {
 enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, QC_PILOT, kQc = 8 };
 
 constexpr int kBucketTile = 2048;   // positions per bucket tile (64 bitmap words)
-constexpr int kDefaultBudget = 4096; // candidates rescored before the first certificate pass
+constexpr int kDefaultBudget = 256;  // candidates rescored before the first certificate pass
 constexpr int kExactChunks = 64;
 constexpr int kMaxWin = 1024;       // largest window (recent tokens read exactly)
 constexpr int kWinW = 130;          // window sums per query head: N[128], D, Q

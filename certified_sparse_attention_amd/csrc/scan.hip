@@ -47,6 +47,7 @@ struct PrepArgs {
   unsigned long long *clo, *cstar;
   unsigned *vmax;
   int *cmcnt, *hist, *ccount, *flags;
+  int *bdone, *exdone;   // per-head completion counters, cleared here
   uint32_t *live;     // [H_q][npool_cap / 32 + 1] bitmap, cleared here
 };
 
@@ -125,6 +126,8 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
     a.cmcnt[hq] = 0;
     a.ccount[hq] = 0;
     a.flags[hq] = 0;
+    a.bdone[hq] = 0;
+    a.exdone[hq] = 0;
   }
   for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
   const int64_t nwords = a.npool_cap / 32 + 1;

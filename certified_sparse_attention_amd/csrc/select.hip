@@ -35,6 +35,7 @@ struct SelectArgs {
   int *tilehist;          // [H_q][ntiles][J+2] per-tile histograms of l^ub
   int *tileoff2;          // [H_q][ntiles] offsets of the second range
   int *ccount1, *jspec;   // [H_q]
+  int *bdone;             // [H_q] tiles whose histogram is written
   const int *flags;
   int budget;             // candidates rescored before the first certificate pass
   int pass;
@@ -92,88 +93,70 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   for (int j = lane; j < a.J + 2; j += 64) th[j] = hist[j];
 }
 
-// Per query head: the speculative level jspec (the deepest level whose cumulative
-// candidate count fits the budget), and tile offsets of the two candidate ranges
-// (l^ub <= jspec first, then jspec < l^ub <= J), each in position order.
-constexpr int kScanThreads = 256;
-__global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(SelectArgs a) {
-  const int hq = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int J = a.J, J2 = J + 2;
-  __shared__ int part[4][64];
-  __shared__ int wsum1[4], wsum2[4];
-  __shared__ int js_sh;
-  const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
-  // level histogram: lane = level, wavefront wv sums tiles wv, wv + 4, ...
-  {
-    int v = 0;
-    if (lane < J2)
-      for (int64_t tile = wv; tile < a.ntiles; tile += 4) v += th0[tile * J2 + lane];
-    part[wv][lane] = v;
-  }
-  __syncthreads();
-  if (wv == 0) {
-    const int hv = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-    if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = hv;
-    int c = (lane <= J) ? hv : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(c, off, 64);
-      if (lane >= off) c += y;
-    }
-    // the levels that fit form a prefix 0..js (counts only grow with the level)
-    const unsigned long long fit = __ballot(lane <= J && (c <= a.budget || lane == 0));
-    if (lane == 0) {
-      js_sh = __popcll(fit) - 1;
-      a.jspec[hq] = js_sh;
-    }
-  }
-  __syncthreads();
-  const int js = js_sh;
-  int run1 = 0, run2 = 0;
-  for (int64_t t0 = 0; t0 < a.ntiles; t0 += kScanThreads) {
-    const int64_t tile = t0 + t;
-    int n1 = 0, n2 = 0;
-    if (tile < a.ntiles) {
-      const int *th = th0 + tile * J2;
-      for (int j = 0; j <= J; ++j) {
-        const int v = th[j];
-        if (j <= js) n1 += v; else n2 += v;
-      }
-    }
-    int x1 = n1, x2 = n2;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
-      if (lane >= off) { x1 += y1; x2 += y2; }
-    }
-    if (lane == 63) { wsum1[wv] = x1; wsum2[wv] = x2; }
-    __syncthreads();
-    int b1 = 0, b2 = 0, s1 = 0, s2 = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < wv) { b1 += wsum1[k]; b2 += wsum2[k]; }
-      s1 += wsum1[k];
-      s2 += wsum2[k];
-    }
-    if (tile < a.ntiles) {
-      a.tileoff[(int64_t)hq * a.ntiles + tile] = run1 + b1 + x1 - n1;
-      a.tileoff2[(int64_t)hq * a.ntiles + tile] = run2 + b2 + x2 - n2;
-    }
-    run1 += s1;
-    run2 += s2;
-    __syncthreads();
-  }
-  if (t == 0) {
-    a.ccount1[hq] = run1;
-    a.ccount[hq] = run1 + run2;
-  }
-}
-
-// Stable compaction of both ranges: thread = bitmap word, positions in order.
+// Stable compaction of both ranges (l^ub <= jspec first, then jspec < l^ub <= J, each in
+// position order): thread = bitmap word.  Every tile's workgroup sums the head's tile
+// histograms itself (they are small and L2-resident), which gives the level histogram,
+// the speculative level jspec (the deepest level whose cumulative candidate count fits
+// the budget) and the tile's offsets without a separate pass.
 __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
-  const int js = a.jspec[hq];
+  const int J = a.J, J2 = J + 2;
+  const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
+  // level histogram (lane = level)
+  int hv = 0;
+  if (lane < J2) {
+    int64_t tl = 0;
+    for (; tl + 8 <= a.ntiles; tl += 8) {
+      int v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = th0[(tl + k) * J2 + lane];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hv += v[k];
+    }
+    for (; tl < a.ntiles; ++tl) hv += th0[tl * J2 + lane];
+  }
+  int c = (lane <= J) ? hv : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(c, off, 64);
+    if (lane >= off) c += y;
+  }
+  // the levels that fit form a prefix 0..js (counts only grow with the level)
+  const unsigned long long fit = __ballot(lane <= J && (c <= a.budget || lane == 0));
+  const int js = __popcll(fit) - 1;
+  const int tot1 = __shfl(c, js, 64), totJ = __shfl(c, J, 64);
+  if (tile == 0) {
+    if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = hv;
+    if (lane == 0) {
+      a.jspec[hq] = js;
+      a.ccount1[hq] = tot1;
+      a.ccount[hq] = totJ;
+    }
+  }
+  // this tile's offsets: candidates of both ranges in the earlier tiles
+  int b1 = 0, b2 = 0;
+  for (int64_t t0 = 0; t0 < tile; t0 += 64) {
+    const int64_t tl = t0 + lane;
+    int n1 = 0, n2 = 0;
+    if (tl < tile) {
+      const int *th = th0 + tl * J2;
+      int v[kMaxJ + 1];
+#pragma unroll
+      for (int j = 0; j <= kMaxJ; ++j) v[j] = (j <= J) ? th[j] : 0;
+#pragma unroll
+      for (int j = 0; j <= kMaxJ; ++j) {
+        if (j <= js) n1 += v[j]; else n2 += v[j];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      n1 += __shfl_xor(n1, off, 64);
+      n2 += __shfl_xor(n2, off, 64);
+    }
+    b1 += n1;
+    b2 += n2;
+  }
   const int64_t wi = tile * 64 + lane;
   const int64_t p0 = wi * 32;
   uint32_t m1 = 0, m2 = 0;
@@ -186,7 +169,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       rest &= rest - 1u;
       const int l = a.lub[(int64_t)hq * a.npool_cap + p0 + b];
       if (l <= js) m1 |= 1u << b;
-      else if (l <= a.J) m2 |= 1u << b;
+      else if (l <= J) m2 |= 1u << b;
     }
   }
   int n1 = __popc(m1), n2 = __popc(m2);
@@ -197,8 +180,8 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
     if (lane >= off) { x1 += y1; x2 += y2; }
   }
-  int o1 = a.tileoff[(int64_t)hq * a.ntiles + tile] + x1 - n1;
-  int o2 = a.ccount1[hq] + a.tileoff2[(int64_t)hq * a.ntiles + tile] + x2 - n2;
+  int o1 = b1 + x1 - n1;
+  int o2 = tot1 + b2 + x2 - n2;
   int *dst = a.candpos + (int64_t)hq * a.npool_cap;
   while (m1) {
     const int b = __ffs(m1) - 1;
@@ -250,7 +233,6 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
 
 hipError_t launch_select(const SelectArgs &a, int H_q, hipStream_t st) {
   hipLaunchKernelGGL(bucket_count_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(H_q), dim3(kScanThreads), 0, st, a);
   hipLaunchKernelGGL(bucket_write_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
   return hipGetLastError();
 }

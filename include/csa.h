@@ -40,7 +40,7 @@ enum csa_status {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, head_dim != 128, n < 1, n > n_cap,
                                     r < 1, J < 0, eps <= 0, delta outside (0,1), ... */
-  CSA_ERR_UNSUPPORTED = -2,      /* group_size outside 1..7, window < 32, J > 60,
+  CSA_ERR_UNSUPPORTED = -2,      /* group_size outside 1..7, window outside 32..1024, J > 60,
                                     n_cap not a multiple of 32 or >= 2^31 */
   CSA_ERR_WORKSPACE = -3,        /* workspace missing or smaller than csa_workspace_bytes() */
   CSA_ERR_HIP = -4               /* a HIP runtime call failed; csa_last_error() has the text */
@@ -99,12 +99,12 @@ typedef struct {
   double delta;    /* failure probability per head and call, in (0,1) ([S] Theorem 4) */
   int32_t r;       /* grid tau_j = 2^(-j/r), j = 0..J ([S] Algorithm Components item 3) */
   int32_t J;       /* deepest level, 0..60 */
-  int32_t window;  /* recent tokens always read exactly ([S] item 1; 64 on the pages), >= 32 */
+  int32_t window;  /* recent tokens always read exactly ([S] item 1; 64 on the pages), 32..1024 */
   int32_t measure; /* enum csa_measure */
   uint64_t seed;   /* perturbation hash inputs ([S] item 1: 53-bit uniform hash) */
   uint64_t step;   /* decode step: fresh perturbations per step ([A]) */
   int32_t layer;
-  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 4096);
+  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 256);
                           heads that certify at no level up to that point get a second pass
                           over the remaining levels.  Results do not depend on it. */
 } csa_params;

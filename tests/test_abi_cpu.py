@@ -66,6 +66,8 @@ def test_workspace_bytes_validates(lib):
     assert lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params(J=61)), 4096) == 0
     assert lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params(delta=1.0)), 4096) == 0
     assert lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params(window=16)), 4096) == 0
+    assert lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params(window=1025)), 4096) == 0
+    assert lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params(window=1024)), 4096) > 0
     assert lib.csa_workspace_bytes(ctypes.byref(_shape(n_cap=100)), ctypes.byref(_params()), 64) == 0
     # grows with n and J
     a = lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params()), 2048)
@@ -75,7 +77,7 @@ def test_workspace_bytes_validates(lib):
 
 @pytest.mark.parametrize("bad", [
     dict(shape=None), dict(d=96), dict(G=0), dict(G=8), dict(eps=0.0), dict(eps=-1.0),
-    dict(delta=0.0), dict(r=0), dict(J=-1), dict(J=70), dict(window=8), dict(measure=5),
+    dict(delta=0.0), dict(r=0), dict(J=-1), dict(J=70), dict(window=8), dict(window=2048), dict(measure=5),
     dict(n=0), dict(n=5000), dict(null_q=True), dict(ws_small=True),
 ])
 def test_certified_call_rejects_bad_arguments(lib, bad):
