@@ -206,19 +206,6 @@ __device__ inline float perturbation_upper32(uint64_t prefix, int64_t pos) {
   return (x * 0x1.62e430p-1f) * (1.0f + 0x1p-20f) + 0x1p-30f;
 }
 
-// Maximum over the 16 lanes of a row (all lanes get it), by DPP permutations.
-__device__ inline float row_max16(float v) {
-  int b = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));   // quad_perm 1032
-  b = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false)));   // quad_perm 2301
-  b = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false)));  // row_half_mirror
-  b = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false)));  // row_mirror
-  return v;
-}
-
 // Constant rows of the A operand: zero everything, then the ones row (14).
 __device__ inline void init_operand(uint8_t *Abuf, int lane) {
   uint4 *A4 = reinterpret_cast<uint4 *>(Abuf);
@@ -234,15 +221,17 @@ __device__ inline void init_operand(uint8_t *Abuf, int lane) {
 
 // Offset term of up to 16 blocks (block = MFMA column): base = beta kappa sum_t q~ z,
 // eb = (beta/2) kappa sum_t |z|, pad = (2^-40 qabs) Kmax, into cst[0..2][block][g].
+template <int NB>
 __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int nblk, int G, int lane,
-                                   double (*cst)[kBlocksPerWave][8]) {
+                                   double (*cst)[NB][8], int col0 = 0) {
   const int n16 = lane & 15, grp = lane >> 4;
   const int hq0 = h * G;
   v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
   v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
   v4i z1k0 = {0, 0, 0, 0}, z1k1 = {0, 0, 0, 0}, z0k0 = {0, 0, 0, 0}, z0k1 = {0, 0, 0, 0};
-  if (n16 < nblk) {
-    const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + n16) * 256;
+  const int col = col0 + n16;
+  if (col < nblk) {
+    const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + col) * 256;
     z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
     z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
     z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
@@ -253,8 +242,8 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
   r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z1k1, r1, 0, 0, 0);
   v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z0k0, zero, 0, 0, 0);
   r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z0k1, r0, 0, 0, 0);
-  if (n16 < nblk) {
-    const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + n16];
+  if (col < nblk) {
+    const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + col];
     const double kappa = ldexp(1.0, bm.kexp);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -266,9 +255,9 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
         const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
         const double *qc = a.qconst + (int64_t)(hq0 + g) * kQc;
         const double beta = qc[QC_BETA];
-        cst[0][n16][g] = (beta * kappa) * (double)bint;
-        cst[1][n16][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
-        cst[2][n16][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
+        cst[0][col][g] = (beta * kappa) * (double)bint;
+        cst[1][col][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
+        cst[2][col][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
       }
     }
   }
@@ -332,12 +321,13 @@ __device__ inline Bound32 bound32(float base, float ebpad, float alpha, float ha
 }
 
 constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
+constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
 
 // Shared memory of the streaming kernel; its window workgroups reuse it.
 struct StreamSmem {
   alignas(16) uint8_t Abuf[4][2 * 1024];
-  double cst[4][3][kBlocksPerWave][8];
-  float2 mx[4][kBlocksPerWave][8];
+  double cst[4][3][kScanBlocks][8];
+  float2 mx[4][kScanBlocks][8];
 };
 struct WindowSmem {
   double sw[kMaxWin], vsq[kMaxWin];
@@ -428,6 +418,21 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   }
 }
 
+// Maximum over the 16 lanes of a row with integer DPP maxima on order-preserving keys.
+__device__ inline int fkey(float v) {
+  const int b = __float_as_int(v);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ inline float fkey_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+__device__ inline float row_max16k(float v) {
+  int k = fkey(v);
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0xB1, 0xF, 0xF, false));    // quad_perm 1032
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x4E, 0xF, 0xF, false));    // quad_perm 2301
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x140, 0xF, 0xF, false));   // row_mirror
+  return fkey_inv(k);
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   __shared__ ScanSmem sm;
@@ -437,17 +442,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
   constexpr bool kTwo = G > 4;
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
-  const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int64_t wph = (a.nb_pool + kScanBlocks - 1) / kScanBlocks;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
   if (gw >= (int64_t)a.H_kv * wph) return;
   const int h = (int)(gw / wph);
-  const int64_t blk0 = (gw % wph) * kBlocksPerWave;
-  const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
+  const int64_t blk0 = (gw % wph) * kScanBlocks;
+  const int nblk = (int)min((int64_t)kScanBlocks, a.nb_pool - blk0);
   const int n16 = lane & 15, grp = lane >> 4;
-
   uint8_t *Abuf = sm.st.Abuf[wv];
-  double(*cst)[kBlocksPerWave][8] = sm.st.cst[wv];
+  double(*cst)[kScanBlocks][8] = sm.st.cst[wv];
   float2(*mx)[8] = sm.st.mx[wv];
 
   const int gA = grp, gB = grp + 4;
@@ -465,55 +469,57 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     qv1[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
   }
 
-  // Software pipeline: every global load of chunk c + 1 (two blocks) is issued before
-  // chunk c is computed.  The loop issues no global stores or atomics, so the waits
-  // for the prefetched loads never include other memory operations.
+  // Software pipeline: the loads of chunks c + 1 and c + 2 (two blocks each) are in
+  // flight while chunk c is computed.  The loads are unconditional and the loop issues
+  // no global stores or atomics, so the compiler can wait for exactly the older loads.
   struct ChunkIn {
     uint4 cw[4];
     uint32_t kk[2];
     float ksmax[2];
     uint32_t kerr, vn;
   };
+  // Buffer resources over this wave's blocks only: offsets are a per-lane constant plus
+  // a wave-uniform chunk offset, and reads past the wave's blocks or the pool return 0.
+  const int64_t tokw = min((int64_t)nblk * kBlk, a.npool - blk0 * kBlk);
+  const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.codes + ((int64_t)h * a.nb_cap + blk0) * 2048), (short)0, nblk * 2048, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rs_ks = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.kscale + ((int64_t)h * a.nb_cap + blk0) * kD), (short)0, nblk * 2 * kD, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rs_bm = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.bmeta + (int64_t)h * a.nb_cap + blk0), (short)0, nblk * (int)sizeof(BlockMeta), kBufDword3);
+  const __amdgpu_buffer_rsrc_t rs_kerr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.kerr + (int64_t)h * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t rs_vn = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.vnorm + (int64_t)h * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
   auto load_chunk = [&](int c0, ChunkIn &in) {
-    const int64_t bA = blk0 + c0;
-    const int nb2 = min(2, nblk - c0);
-    const int64_t pos = bA * kBlk + lane;
+    c0 = __builtin_amdgcn_readfirstlane(c0);   // wave-uniform: offsets stay in SGPRs
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      in.cw[T] = make_uint4(0, 0, 0, 0);
-      if (T < 2 * nb2)
-        in.cw[T] = reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane];
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs_codes, lane * 16, c0 * 2048 + T * 1024, 0);
+      in.cw[T] = make_uint4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
-      in.kk[bi] = 0u;
-      in.ksmax[bi] = 0.0f;
-      if (bi < nb2) {
-        in.kk[bi] = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + bA + bi) * kD)[lane];
-        in.ksmax[bi] = a.bmeta[(int64_t)h * a.nb_cap + bA + bi].ksmax;
-      }
+      in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, lane * 4, (c0 + bi) * 2 * kD, 0);
+      in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, 0, (c0 + bi) * (int)sizeof(BlockMeta), 0));
     }
-    in.kerr = 0u;
-    in.vn = 0u;
-    if (lane < 32 * nb2 && pos < a.npool) {
-      in.kerr = a.kerr[(int64_t)h * a.n_cap + pos];
-      in.vn = a.vnorm[(int64_t)h * a.n_cap + pos];
-    }
+    in.kerr = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, lane * 2, c0 * kBlk * 2, 0);
+    in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, lane * 2, c0 * kBlk * 2, 0);
   };
-  ChunkIn nxt;
-  load_chunk(0, nxt);
 
   init_operand(Abuf, lane);
-  offset_terms(a, h, blk0, nblk, G, lane, cst);
+  static_assert(kScanBlocks % 16 == 0, "offset terms are formed 16 blocks at a time");
+#pragma unroll
+  for (int col0 = 0; col0 < kScanBlocks; col0 += 16)
+    if (col0 < nblk) offset_terms(a, h, blk0, nblk, G, lane, cst, col0);
 
   const uint64_t prefix = a.prefix[h];
   float lbA = -__builtin_huge_valf(), lbB = -__builtin_huge_valf();
   unsigned vmx = 0u;
   constexpr float kNegInf = -__builtin_huge_valf();
 
-  for (int c0 = 0; c0 < nblk; c0 += 2) {
-    const ChunkIn cur = nxt;
-    if (c0 + 2 < nblk) load_chunk(c0 + 2, nxt);
+  auto process = [&](const int c0, const ChunkIn &cur) {
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = (blk0 + c0) * kBlk;
     const int64_t mypos = tok0 + lane;
@@ -570,27 +576,41 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
           lbB = fmaxf(lbB, valid ? r.lb : kNegInf);
         }
       }
-      uA = row_max16(uA);
-      eA = row_max16(eA);
+      uA = row_max16k(uA);
+      eA = row_max16k(eA);
       if (kTwo) {
-        uB = row_max16(uB);
-        eB = row_max16(eB);
+        uB = row_max16k(uB);
+        eB = row_max16k(eB);
       }
       if (n16 == 0) {
         if (hasA) mx[bl][gA] = make_float2(uA, eA);
         if (hasB) mx[bl][gB] = make_float2(uB, eB);
       }
     }
+  };
+  // two chunks in flight ahead of the one being computed
+  ChunkIn buf0, buf1, buf2;
+  load_chunk(0, buf0);
+  load_chunk(2, buf1);
+  for (int c0 = 0; c0 < nblk; c0 += 6) {
+    load_chunk(c0 + 4, buf2);
+    process(c0, buf0);
+    if (c0 + 2 >= nblk) break;
+    load_chunk(c0 + 6, buf0);
+    process(c0 + 2, buf1);
+    if (c0 + 4 >= nblk) break;
+    load_chunk(c0 + 8, buf1);
+    process(c0 + 4, buf2);
   }
   wave_sync();
   // per-block maxima of the wave: [query][block] rows of float2
-  for (int i = lane; i < G * kBlocksPerWave; i += 64) {
-    const int g = i / kBlocksPerWave, bl = i % kBlocksPerWave;
+  for (int i = lane; i < G * kScanBlocks; i += 64) {
+    const int g = i / kScanBlocks, bl = i % kScanBlocks;
     if (bl < nblk) a.bmax[(int64_t)(hq0 + g) * a.nbw + blk0 + bl] = mx[bl][g];
   }
   // c_lo >= every LB: publish the wave's lower bounds of max LB
-  lbA = row_max16(lbA);
-  if (kTwo) lbB = row_max16(lbB);
+  lbA = row_max16k(lbA);
+  if (kTwo) lbB = row_max16k(lbB);
   if (n16 == 0) {
     if (hasA && lbA > kNegInf)
       __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max((double)lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -898,7 +918,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
 // Streaming workgroups first, then one window workgroup per query head (a.nstream
 // must be the number of streaming workgroups, 0 when the pool is empty).
 int64_t scan_stream_wgs(int64_t H_kv, int64_t nb_pool) {
-  const int64_t waves = H_kv * ((nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
+  const int64_t waves = H_kv * ((nb_pool + kScanBlocks - 1) / kScanBlocks);
   return (waves + 3) / 4;
 }
 
