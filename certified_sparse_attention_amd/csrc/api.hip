@@ -90,6 +90,8 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
   P.tileoff2 = take(Hq * (size_t)P.ntiles * sizeof(int));
   P.tilehist = take(Hq * (size_t)P.ntiles * J2 * sizeof(int));
+  P.tilecm = take(Hq * (size_t)P.ntiles * J2 * sizeof(int));
+  P.cmhist = take(Hq * J2 * sizeof(int));
   P.ccount = take(Hq * sizeof(int));
   P.ccount1 = take(Hq * sizeof(int));
   P.jspec = take(Hq * sizeof(int));
@@ -341,6 +343,8 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.jspec = at<int>(ws, P.jspec);
     sa.flags = at<int>(ws, P.flags);
     sa.bdone = at<int>(ws, P.bdone);
+    sa.tilecm = at<int>(ws, P.tilecm);
+    sa.cmhist = at<int>(ws, P.cmhist);
     sa.budget = params->cand_budget > 0 ? params->cand_budget : csa::kDefaultBudget;
     sa.pass = 1;
     sa.ccount = at<int>(ws, P.ccount);
@@ -397,6 +401,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.flags = at<int>(ws, P.flags);
   ca.exactp = at<double>(ws, P.exactp);
   ca.exdone = at<int>(ws, P.exdone);
+  ca.cmhist = at<int>(ws, P.cmhist);
   ca.o_hat = o_hat;
   ca.beta = beta;
   ca.stop = stop_level;

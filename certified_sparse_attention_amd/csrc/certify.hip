@@ -35,6 +35,7 @@ struct CertArgs {
   const double *ubuf;
   const unsigned *vmax;
   const int *ccount, *candpos, *rec_hl, *hist, *cmcnt, *cmpos;
+  const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
   const double *rec_w, *rec_vsq;
   const int8_t *lub;
   double *partial, *betalv, *dhatlv;
@@ -220,6 +221,7 @@ struct FinSmem {
   AccSmem s;
   double tau[kMaxJ + 1];
   int hist[kMaxJ + 2];
+  int cmh[kMaxJ + 2];            // C_max keys per bucket level
   double nr[kD];
   double dr, qr;
   double beta[kMaxJ + 1];
@@ -254,9 +256,12 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   int i0, i1, nseg;
   seg_range(count, 0, i0, i1, nseg);
   for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
-  for (int j = t; j < a.J + 2; j += 256) f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
-  zero_acc(s, J1);
+  for (int j = t; j < a.J + 2; j += 256) {
+    f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
+    f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
+  }
   if (nseg == 0) {
+    zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_range(a, s, hq, 0, count);
   } else {
     for (int e = t; e < J1 * kStatW; e += 256) {
@@ -293,11 +298,12 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
       const double tau = f.tau[j];
       const double D_det = f.dr + s.acc[j][256];
       const double D_hat = D_det + tau * s.acc[j][258];
+      const double iD = 1.0 / D_det, iDh = 1.0 / D_hat;
       double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
       for (int c = 32 * qt; c < 32 * qt + 32; ++c) {
         const double nd = f.nr[c] + s.acc[j][c];
-        const double cc = nd / D_det;
-        const double o = (nd + tau * s.acc[j][128 + c]) / D_hat;
+        const double cc = nd * iD;
+        const double o = (nd + tau * s.acc[j][128 + c]) * iDh;
         cn2 += cc * cc;
         cV += cc * s.acc[j][128 + c];
         dn2 += (o - cc) * (o - cc);
@@ -362,30 +368,31 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     return;
   }
-  // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|; the list holds
-  // a superset of C_max, which is {UB >= c_lo}
-  long long extra = 0;
-  const int ncm = a.cmcnt[hq];
-  const double clo = dec_max(a.clo[hq]);
-  for (int i = t; i < ncm; i += 256) {
-    const int pos = a.cmpos[(int64_t)hq * a.npool_cap + i];
-    extra += (a.ubuf[(int64_t)hq * a.npool_cap + pos] >= clo) && (a.lub[(int64_t)hq * a.npool_cap + pos] > js);
-  }
+  // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|
+  if (wv == 0) {
+    // C_max keys outside the sample's buckets, and candidates up to the stop level
+    int e = (lane > js && lane <= a.J + 1) ? f.cmh[lane] : 0;
+    int ib = (lane <= js) ? f.hist[lane] : 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) extra += __shfl_xor(extra, off, 64);
-  if (lane == 0) f.extra[wv] = extra;
+    for (int off = 32; off >= 1; off >>= 1) {
+      e += __shfl_xor(e, off, 64);
+      ib += __shfl_xor(ib, off, 64);
+    }
+    if (lane == 0) {
+      f.extra[0] = e;
+      f.extra[1] = ib;
+    }
+  }
   __syncthreads();
   const double tau = f.tau[js];
   const double D_hat = (f.dr + s.acc[js][256]) + tau * s.acc[js][258];
   if (t < kD)
     a.o_hat[(int64_t)hq * kD + t] = (float)(((f.nr[t] + s.acc[js][t]) + tau * s.acc[js][128 + t]) / D_hat);
   if (t == 0) {
-    long long inb = 0;
-    for (int j = 0; j <= js; ++j) inb += f.hist[j];
     a.flags[hq] = 0;
     a.stop[hq] = js;
     a.beta[hq] = f.beta[js];
-    a.keys_read[hq] = (int64_t)a.W + inb + f.extra[0] + f.extra[1] + f.extra[2] + f.extra[3];
+    a.keys_read[hq] = (int64_t)a.W + f.extra[1] + f.extra[0];
   }
 }
 

@@ -331,7 +331,8 @@ struct Plan {
   int64_t ntiles;      // bucket tiles per query head
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
-  size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, ccount, ccount1, jspec;
+  size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
+      jspec;
   size_t bdone, exdone;  // per-head completion counters (last-workgroup reductions)
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;

@@ -32,10 +32,12 @@ struct SelectArgs {
   const uint32_t *live;   // [H_q][nwords] keys the scan kept (others have l^ub = J+1, UB < c_lo)
   int64_t nwords;
   int full_lub;           // write l^ub for every pool key (diagnostics)
-  int *tilehist;          // [H_q][ntiles][J+2] per-tile histograms of l^ub
+  int *tilehist;          // [H_q][ntiles][J+2] per-tile cumulative counts of l^ub
   int *tileoff2;          // [H_q][ntiles] offsets of the second range
   int *ccount1, *jspec;   // [H_q]
   int *bdone;             // [H_q] tiles whose histogram is written
+  int *tilecm;            // [H_q][ntiles][J+2] C_max keys per level and tile
+  int *cmhist;            // [H_q][J+2] C_max keys per level
   const int *flags;
   int budget;             // candidates rescored before the first certificate pass
   int pass;
@@ -51,15 +53,21 @@ __device__ inline int first_level_tab(double x, const double *lt, int J) {
   return lo;
 }
 
+// Per tile: cumulative level counts tilehist[tile][j] = |{l^ub <= j}| (j = 0..J+1, the
+// last one counting every pool key of the tile) and the C_max keys per level.
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
-  __shared__ int hist[kMaxJ + 2];
+  __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2];
   __shared__ double lt[kMaxJ + 1];
-  for (int j = lane; j < a.J + 2; j += 64) hist[j] = 0;
+  for (int j = lane; j < a.J + 2; j += 64) {
+    hist[j] = 0;
+    cmh[j] = 0;
+  }
   for (int j = lane; j <= a.J; j += 64) lt[j] = a.lt[j];
   __syncthreads();
   const double cs = dec_max(a.cstar[hq]);
+  const double clo = dec_max(a.clo[hq]);
   const int64_t wi = tile * 64 + lane;
   const int64_t p0 = wi * 32;
   if (p0 < a.npool) {
@@ -75,22 +83,37 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     if (bits) {
       // all loads of the word's live keys first, then the levels
       const double *pb = a.pbuf + (int64_t)hq * a.npool_cap + p0;
-      double pv[32];
+      const double *ubp = a.ubuf + (int64_t)hq * a.npool_cap + p0;
+      double pv[32], uv[32];
 #pragma unroll
-      for (int b = 0; b < 32; ++b) pv[b] = ((bits >> b) & 1u) ? pb[b] : 0.0;
+      for (int b = 0; b < 32; ++b) {
+        const bool on = ((bits >> b) & 1u) != 0u;
+        pv[b] = on ? pb[b] : 0.0;
+        uv[b] = on ? ubp[b] : 0.0;
+      }
 #pragma unroll
       for (int b = 0; b < 32; ++b) {
         if ((bits >> b) & 1u) {
           const int l = first_level_tab(pv[b] - cs, lt, a.J);
           lub[b] = (int8_t)l;
           atomicAdd(&hist[l], 1);
+          if (uv[b] >= clo) atomicAdd(&cmh[l], 1);
         }
       }
     }
   }
   __syncthreads();
-  int *th = a.tilehist + ((int64_t)hq * a.ntiles + tile) * (a.J + 2);
-  for (int j = lane; j < a.J + 2; j += 64) th[j] = hist[j];
+  // inclusive prefix over levels (lane = level)
+  if (lane < a.J + 2) {
+    int c = hist[lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(c, off, 64);
+      if (lane >= off) c += y;
+    }
+    a.tilehist[((int64_t)hq * a.ntiles + tile) * (a.J + 2) + lane] = c;
+    a.tilecm[((int64_t)hq * a.ntiles + tile) * (a.J + 2) + lane] = cmh[lane];
+  }
 }
 
 // Stable compaction of both ranges (l^ub <= jspec first, then jspec < l^ub <= J, each in
@@ -103,8 +126,8 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int64_t tile = blockIdx.y;
   const int J = a.J, J2 = J + 2;
   const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
-  // level histogram (lane = level)
-  int hv = 0;
+  // cumulative level histogram of the head (lane = level)
+  int cum = 0;
   if (lane < J2) {
     int64_t tl = 0;
     for (; tl + 8 <= a.ntiles; tl += 8) {
@@ -112,26 +135,36 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = th0[(tl + k) * J2 + lane];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) hv += v[k];
+      for (int k = 0; k < 8; ++k) cum += v[k];
     }
-    for (; tl < a.ntiles; ++tl) hv += th0[tl * J2 + lane];
+    for (; tl < a.ntiles; ++tl) cum += th0[tl * J2 + lane];
   }
-  int c = (lane <= J) ? hv : 0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(c, off, 64);
-    if (lane >= off) c += y;
-  }
-  // the levels that fit form a prefix 0..js (counts only grow with the level)
-  const unsigned long long fit = __ballot(lane <= J && (c <= a.budget || lane == 0));
+  // the levels that fit form a prefix 0..js (cumulative counts only grow)
+  const unsigned long long fit = __ballot(lane <= J && (cum <= a.budget || lane == 0));
   const int js = __popcll(fit) - 1;
-  const int tot1 = __shfl(c, js, 64), totJ = __shfl(c, J, 64);
+  const int tot1 = __shfl(cum, js, 64), totJ = __shfl(cum, J, 64);
   if (tile == 0) {
-    if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = hv;
+    const int below = __shfl_up(cum, 1, 64);
+    if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = cum - (lane > 0 ? below : 0);
     if (lane == 0) {
       a.jspec[hq] = js;
       a.ccount1[hq] = tot1;
       a.ccount[hq] = totJ;
+    }
+    // C_max keys per bucket level
+    if (lane < J2) {
+      const int *cm0 = a.tilecm + (int64_t)hq * a.ntiles * J2;
+      int c = 0;
+      int64_t tl = 0;
+      for (; tl + 8 <= a.ntiles; tl += 8) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = cm0[(tl + k) * J2 + lane];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c += v[k];
+      }
+      for (; tl < a.ntiles; ++tl) c += cm0[tl * J2 + lane];
+      a.cmhist[(int64_t)hq * J2 + lane] = c;
     }
   }
   // this tile's offsets: candidates of both ranges in the earlier tiles
@@ -140,14 +173,9 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     const int64_t tl = t0 + lane;
     int n1 = 0, n2 = 0;
     if (tl < tile) {
-      const int *th = th0 + tl * J2;
-      int v[kMaxJ + 1];
-#pragma unroll
-      for (int j = 0; j <= kMaxJ; ++j) v[j] = (j <= J) ? th[j] : 0;
-#pragma unroll
-      for (int j = 0; j <= kMaxJ; ++j) {
-        if (j <= js) n1 += v[j]; else n2 += v[j];
-      }
+      const int c1 = th0[tl * J2 + js], cJ = th0[tl * J2 + J];
+      n1 = c1;
+      n2 = cJ - c1;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
