@@ -359,7 +359,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.full_lub = (trace && trace->lub) ? 1 : 0;
     if ((e = csa::launch_select(sa, P.H_q, st)) != hipSuccess) return hip_fail(e, "select");
   }
-  csa::CertArgs ca;
+  csa::CertArgs ca{};
   ca.K = K;
   ca.V = V;
   ca.n_cap = shape->n_cap;
@@ -392,6 +392,8 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.ubuf = at<double>(ws, P.ubuf);
   ca.clo = at<unsigned long long>(ws, P.clo);
   ca.rec_w = at<double>(ws, P.rec_w);
+  ca.rec_s = at<double>(ws, P.rec_s);
+  ca.prefix = at<uint64_t>(ws, P.prefix);
   ca.rec_vsq = at<double>(ws, P.rec_vsq);
   ca.lub = at<int8_t>(ws, P.lub);
   ca.partial = at<double>(ws, P.partial);
@@ -412,12 +414,14 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   if (all_exact) {
     if ((e = csa::launch_certify_pass(ca, 1, P.H_q, false, st)) != hipSuccess) return hip_fail(e, "certify");
   } else {
-    // pass 1: levels up to the speculative level (at most `budget` candidates, so the
-    // segmented accumulation is only needed when the budget exceeds the fused size);
-    // pass 2: the heads that need all levels
+    // pass 1: levels up to the speculative level (at most `budget` candidates).  With a
+    // budget within the fused size its rescoring runs inside the certificate kernel;
+    // otherwise a separate rescoring kernel and the segmented accumulation do it.
+    // pass 2: the heads that need all levels.
     const bool seg1 = sel.budget > csa::kFusedMax;
-    if ((e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess ||
-        (e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess ||
+    ca.fused_rescore = seg1 ? 0 : 1;
+    if (seg1 && (e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "rescore");
+    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess ||
         (e = csa::launch_rescore(sel, 2, P.H_q, st)) != hipSuccess ||
         (e = csa::launch_certify_pass(ca, 2, P.H_q, true, st)) != hipSuccess)
       return hip_fail(e, "certify");

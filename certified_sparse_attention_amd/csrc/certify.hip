@@ -34,15 +34,19 @@ struct CertArgs {
   const unsigned long long *cstar, *clo;
   const double *ubuf;
   const unsigned *vmax;
-  const int *ccount, *candpos, *rec_hl, *hist, *cmcnt, *cmpos;
+  const int *ccount, *candpos, *hist, *cmcnt, *cmpos;
+  int *rec_hl;                  // candidate records (written by the fused rescoring)
   const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
-  const double *rec_w, *rec_vsq;
+  double *rec_w, *rec_vsq;
   const int8_t *lub;
   double *partial, *betalv, *dhatlv;
   int *klv, *flags;
   int *exdone;                  // [H_q] chunks of the exact fallback that have finished
   const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list
   int pass;                     // 1: levels <= jspec; 2: all levels, heads flagged for extension
+  int fused_rescore;            // pass 1 rescoring happens in the certificate kernel
+  const uint64_t *prefix;       // per KV head hash prefixes
+  double *rec_s;
   double *exactp;
   float *o_hat;
   double *beta;
@@ -50,6 +54,15 @@ struct CertArgs {
   int64_t *keys_read;
   int all_exact;
 };
+
+__device__ inline int first_level_lt(double x, const double *lt, int J) {
+  int lo = 0, hi = J + 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (lt[mid] > x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
 
 constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
 constexpr int kStage = 64;        // candidates staged in LDS at a time
@@ -71,29 +84,24 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
 struct AccSmem {
   double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
   uint16_t vs[kStage][kD];              // staged V rows
-  int hl[kStage];
+  int hl[kStage], pos[kStage];
   double w[kStage], vsq[kStage];
 };
 
 // Add candidates [i0, i1) of query head hq into s.acc (256 threads; fixed order).
 // Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light samples add (1, v, |v|^2)
 // at their entry level l and remove it at h, where they turn heavy.
-__device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
-  const int t = threadIdx.x, h = hq / a.G;
-  const int64_t base = (int64_t)hq * a.npool_cap;
-  for (int c0 = i0; c0 < i1; c0 += kStage) {
-    const int cnt = min(kStage, i1 - c0);
-    if (t < cnt) {
-      s.hl[t] = a.rec_hl[base + c0 + t];
-      s.w[t] = a.rec_w[base + c0 + t];
-      s.vsq[t] = a.rec_vsq[base + c0 + t];
-    }
-    __syncthreads();
+// Add one staged group of candidates (records in s.hl/w/vsq/pos, cnt <= kStage) into
+// s.acc (256 threads; fixed order).  Heavy keys (h <= J) add (w, w v, w |v|^2) at level
+// h; light samples add (1, v, |v|^2) at their entry level l and remove it at h, where
+// they turn heavy.
+__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt) {
+  const int t = threadIdx.x;
     // stage V rows of candidates that enter the sample at some level <= J
     for (int e = t; e < cnt * 16; e += 256) {
       const int r = e >> 4, part = e & 15;
       if ((s.hl[r] >> 8) <= a.J) {
-        const int pos = a.candpos[base + c0 + r];
+        const int pos = s.pos[r];
         reinterpret_cast<uint4 *>(s.vs[r])[part] =
             reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + pos) * kD)[part];
       }
@@ -132,6 +140,77 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
       }
     }
     __syncthreads();
+}
+
+// Add candidates [i0, i1) of query head hq from their stored records.
+__device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+  const int t = threadIdx.x, h = hq / a.G;
+  const int64_t base = (int64_t)hq * a.npool_cap;
+  for (int c0 = i0; c0 < i1; c0 += kStage) {
+    const int cnt = min(kStage, i1 - c0);
+    if (t < cnt) {
+      s.hl[t] = a.rec_hl[base + c0 + t];
+      s.w[t] = a.rec_w[base + c0 + t];
+      s.vsq[t] = a.rec_vsq[base + c0 + t];
+      s.pos[t] = a.candpos[base + c0 + t];
+    }
+    __syncthreads();
+    accumulate_stage(a, s, h, cnt);
+  }
+}
+
+// Exact rescoring of candidates [0, count) of query head hq inside the certificate
+// workgroup (scores and |v|^2 eight lanes per key, one lane per key for E and the
+// levels), then accumulation.  The records are also stored for a second pass.
+__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, const double *lt, int hq, int count) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
+  const int s8 = lane >> 3, k8 = lane & 7;
+  const int64_t base = (int64_t)hq * a.npool_cap;
+  const double cs = dec_max(a.cstar[hq]);
+  const uint64_t prefix = a.prefix[h];
+  double q16[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  for (int c0 = 0; c0 < count; c0 += kStage) {
+    const int cnt = min(kStage, count - c0);
+    if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
+    __syncthreads();
+    // exact scores and |v|^2: wavefront wv takes keys 16 wv .. 16 wv + 15
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const int r = 16 * wv + 8 * step + s8;
+      double p = 0.0, v = 0.0;
+      if (r < cnt) {
+        const int64_t row = ((int64_t)h * a.n_cap + s.pos[r]) * kD;
+        p = score_chunk(q16, a.K + row, k8);
+        v = sumsq_chunk(a.V + row, k8);
+      }
+      const double sc = r1_combine8(p) * kRsqrtD;
+      const double vs = r1_combine8(v);
+      if (r < cnt && k8 == 0) {
+        s.w[r] = sc;       // the score for now; the weight below
+        s.vsq[r] = vs;
+      }
+    }
+    __syncthreads();
+    if (t < cnt) {
+      const int pos = s.pos[t];
+      const double sc = s.w[t];
+      const double E = perturbation(prefix, pos);
+      const int hl = first_level_lt(sc - cs, lt, a.J);
+      const int ll = first_level_lt((sc + E) - cs, lt, a.J);
+      const double w = exp(sc - cs);
+      const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
+      s.hl[t] = hl | (ll << 8);
+      s.w[t] = w;
+      s.vsq[t] = vsq;
+      a.rec_s[base + c0 + t] = sc;
+      a.rec_w[base + c0 + t] = w;
+      a.rec_vsq[base + c0 + t] = vsq;
+      a.rec_hl[base + c0 + t] = hl | (ll << 8);
+    }
+    __syncthreads();
+    accumulate_stage(a, s, h, cnt);
   }
 }
 
@@ -219,7 +298,7 @@ __device__ inline double level_beta(const CertArgs &a, double D_det, double Q_de
 
 struct FinSmem {
   AccSmem s;
-  double tau[kMaxJ + 1];
+  double tau[kMaxJ + 1], lt[kMaxJ + 1];
   int hist[kMaxJ + 2];
   int cmh[kMaxJ + 2];            // C_max keys per bucket level
   double nr[kD];
@@ -255,14 +334,20 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   const int J1 = a.J + 1;
   int i0, i1, nseg;
   seg_range(count, 0, i0, i1, nseg);
-  for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
+  for (int j = t; j < J1; j += 256) {
+    f.tau[j] = a.tau[j];
+    f.lt[j] = a.lt[j];
+  }
   for (int j = t; j < a.J + 2; j += 256) {
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
     f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
   }
   if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
-    accumulate_range(a, s, hq, 0, count);
+    if (a.pass == 1 && a.fused_rescore)
+      rescore_accumulate(a, s, f.lt, hq, count);
+    else
+      accumulate_range(a, s, hq, 0, count);
   } else {
     for (int e = t; e < J1 * kStatW; e += 256) {
       double v = 0.0;
