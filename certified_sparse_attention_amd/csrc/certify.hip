@@ -83,6 +83,7 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
 
 struct AccSmem {
   double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
+  double lt[kMaxJ + 1];                 // level table (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   int hl[kStage], pos[kStage];
   double w[kStage], vsq[kStage];
@@ -162,7 +163,8 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
 // Exact rescoring of candidates [0, count) of query head hq inside the certificate
 // workgroup (scores and |v|^2 eight lanes per key, one lane per key for E and the
 // levels), then accumulation.  The records are also stored for a second pass.
-__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, const double *lt, int hq, int count) {
+__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+  const double *lt = s.lt;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
@@ -171,8 +173,8 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, const double *
   double q16[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
-  for (int c0 = 0; c0 < count; c0 += kStage) {
-    const int cnt = min(kStage, count - c0);
+  for (int c0 = i0; c0 < i1; c0 += kStage) {
+    const int cnt = min(kStage, i1 - c0);
     if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
     __syncthreads();
     // exact scores and |v|^2: wavefront wv takes keys 16 wv .. 16 wv + 15
@@ -219,6 +221,20 @@ __device__ inline void zero_acc(AccSmem &s, int J1) {
   __syncthreads();
 }
 
+// Candidates [i0, i1): those below `split` from their stored records, the rest rescored
+// here (records stored), in index order.
+__device__ void accumulate_mixed(const CertArgs &a, AccSmem &s, int hq, int i0, int i1, int split) {
+  if (i0 < split) accumulate_range(a, s, hq, i0, min(i1, split));
+  if (i1 > split) rescore_accumulate(a, s, hq, max(i0, split), i1);
+}
+
+// Which candidates of this pass already have records: the first pass's, when a separate
+// kernel rescored them, and in the second pass the first pass's range.
+__device__ inline int record_split(const CertArgs &a, int hq, int count) {
+  if (a.pass == 1) return a.fused_rescore ? 0 : count;
+  return a.ccount1[hq];
+}
+
 constexpr int kSegWorkers = 8;   // workgroups per query head for the segmented accumulation
 
 // Heads with many candidates: grid (H_q, kSegWorkers); workgroup w accumulates
@@ -232,10 +248,12 @@ __global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
   if ((int)blockIdx.y >= nseg) return;
   __shared__ AccSmem s;
   const int J1 = a.J + 1;
+  for (int j = threadIdx.x; j < J1; j += 256) s.lt[j] = a.lt[j];
+  const int split = record_split(a, hq, count);
   for (int seg = blockIdx.y; seg < nseg; seg += kSegWorkers) {
     seg_range(count, seg, i0, i1, nseg);
     zero_acc(s, J1);
-    accumulate_range(a, s, hq, i0, i1);
+    accumulate_mixed(a, s, hq, i0, i1, split);
     double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
     for (int e = threadIdx.x; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
     __syncthreads();
@@ -298,7 +316,7 @@ __device__ inline double level_beta(const CertArgs &a, double D_det, double Q_de
 
 struct FinSmem {
   AccSmem s;
-  double tau[kMaxJ + 1], lt[kMaxJ + 1];
+  double tau[kMaxJ + 1];
   int hist[kMaxJ + 2];
   int cmh[kMaxJ + 2];            // C_max keys per bucket level
   double nr[kD];
@@ -336,7 +354,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   seg_range(count, 0, i0, i1, nseg);
   for (int j = t; j < J1; j += 256) {
     f.tau[j] = a.tau[j];
-    f.lt[j] = a.lt[j];
+    s.lt[j] = a.lt[j];
   }
   for (int j = t; j < a.J + 2; j += 256) {
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
@@ -344,10 +362,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   }
   if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
-    if (a.pass == 1 && a.fused_rescore)
-      rescore_accumulate(a, s, f.lt, hq, count);
-    else
-      accumulate_range(a, s, hq, 0, count);
+    accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
   } else {
     for (int e = t; e < J1 * kStatW; e += 256) {
       double v = 0.0;
