@@ -86,61 +86,141 @@ struct AccSmem {
   double lt[kMaxJ + 1];                 // level table (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   int hl[kStage], pos[kStage];
+  // the stage in level order (candidate index, level): heavy keys by h; light samples by
+  // entry level l and by h
+  int hIdx[kStage], hLev[kStage], aIdx[kStage], aLev[kStage], rIdx[kStage], rLev[kStage];
+  int nH, nA, nR;
   double w[kStage], vsq[kStage];
 };
 
-// Add candidates [i0, i1) of query head hq into s.acc (256 threads; fixed order).
-// Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light samples add (1, v, |v|^2)
-// at their entry level l and remove it at h, where they turn heavy.
+// Adds a level-sorted list of staged candidates into s.acc by runs of equal level: column
+// `col` gets sg * (sum of w v[vc]) (heavy) or sg * (sum of v[vc]) (light), and with `scal`
+// columns scol, scol + 1 get sg * (sum of w, sum of w |v|^2) or sg * (count, sum of |v|^2).
+// Eight entries are loaded at a time; each run's row is read and written once.
+// Adds one run into row L: x at column col, and (thread with `scal`) y, z at scol, scol + 1.
+// Every lane reads the scalar pair (the same address) so that one wait covers all reads.
+__device__ inline void flush_run(AccSmem &s, int L, int col, bool scal, int scol, double x, double y,
+                                 double z) {
+  const double a0 = s.acc[L][col];
+  const double a1 = s.acc[L][scol], a2 = s.acc[L][scol + 1];
+  s.acc[L][col] = a0 + x;
+  if (scal) {
+    s.acc[L][scol] = a1 + y;
+    s.acc[L][scol + 1] = a2 + z;
+  }
+}
+
+template <bool kHeavy>
+__device__ inline void level_runs(AccSmem &s, const int *idx, const int *lev, int n, int col, int vc,
+                                  bool scal, int scol, double sg) {
+  double run = 0.0, rb = 0.0, rd = 0.0;
+  int cur = -1;
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    double xa[8], xb[8], xd[8];
+    int L[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = min(i0 + k, n - 1);
+      const int r = idx[i];
+      L[k] = lev[i];
+      const double v = h2d(s.vs[r][vc]);
+      if (kHeavy) {
+        const double w = s.w[r];
+        xa[k] = w * v;
+        xb[k] = w;
+        xd[k] = w * s.vsq[r];
+      } else {
+        xa[k] = v;
+        xb[k] = 1.0;
+        xd[k] = s.vsq[r];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (i0 + k < n) {
+        if (L[k] != cur) {
+          if (cur >= 0) flush_run(s, cur, col, scal, scol, sg * run, sg * rb, sg * rd);
+          run = rb = rd = 0.0;
+          cur = L[k];
+        }
+        run = run + xa[k];
+        rb = rb + xb[k];
+        rd = rd + xd[k];
+      }
+    }
+  }
+  if (cur >= 0) flush_run(s, cur, col, scal, scol, sg * run, sg * rb, sg * rd);
+}
+
 // Add one staged group of candidates (records in s.hl/w/vsq/pos, cnt <= kStage) into
-// s.acc (256 threads; fixed order).  Heavy keys (h <= J) add (w, w v, w |v|^2) at level
-// h; light samples add (1, v, |v|^2) at their entry level l and remove it at h, where
-// they turn heavy.
-__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt) {
-  const int t = threadIdx.x;
-    // stage V rows of candidates that enter the sample at some level <= J
+// s.acc (256 threads).  Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light
+// samples (l < h) add (1, v, |v|^2) at their entry level l and remove it at h, where
+// they turn heavy.  The stage is put in a stable order by level first, so that every
+// column thread sums each level's run in registers (candidate order within a level)
+// and touches the level's row once.  V rows are fetched here unless `staged`.
+__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, bool staged) {
+  const int t = threadIdx.x, J = a.J;
+  if (!staged) {
+    // V rows of candidates that enter the sample at some level <= J
     for (int e = t; e < cnt * 16; e += 256) {
       const int r = e >> 4, part = e & 15;
-      if ((s.hl[r] >> 8) <= a.J) {
+      if ((s.hl[r] >> 8) <= J) {
         const int pos = s.pos[r];
         reinterpret_cast<uint4 *>(s.vs[r])[part] =
             reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + pos) * kD)[part];
       }
     }
-    __syncthreads();
-    // threads 0..127: heavy column t; threads 128..255: light column t - 128; lanes
-    // 64..67 also carry the four scalar columns (one or two read-modify-writes each)
-    if (t < kD) {
-      const int c = t;
-      const int sc = t - 64;     // scalar column of lanes 64..67
-      for (int r = 0; r < cnt; ++r) {
-        const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
-        if (llev > a.J) continue;
-        if (hlev <= a.J) s.acc[hlev][c] += s.w[r] * h2d(s.vs[r][c]);
-        if (sc >= 0 && sc < 4) {
-          if (sc == 0) {
-            if (hlev <= a.J) s.acc[hlev][256] += s.w[r];
-          } else if (sc == 1) {
-            if (hlev <= a.J) s.acc[hlev][257] += s.w[r] * s.vsq[r];
-          } else if (llev < hlev) {
-            const int col = (sc == 2) ? 258 : 259;
-            const double d = (sc == 2) ? 1.0 : s.vsq[r];
-            s.acc[llev][col] += d;
-            if (hlev <= a.J) s.acc[hlev][col] -= d;
-          }
-        }
-      }
-    } else {
-      const int c = t - kD;
-      for (int r = 0; r < cnt; ++r) {
-        const int hlev = s.hl[r] & 0xFF, llev = s.hl[r] >> 8;
-        if (llev > a.J || llev >= hlev) continue;
-        const double v = h2d(s.vs[r][c]);
-        s.acc[llev][128 + c] += v;
-        if (hlev <= a.J) s.acc[hlev][128 + c] -= v;
+  }
+  // stable ranks (wavefront 0, one candidate per lane): by (h, index) over all keys,
+  // by (l, index) and by (h, index) over the light samples
+  if (t < 64) {
+    const bool in = t < cnt;
+    const int me = in ? s.hl[t] : 0;
+    const int mh = me & 0xFF, ml = me >> 8;
+    const bool heavy = in && mh <= J;
+    const bool light = in && ml < mh;          // then l <= J, as l < h <= J + 1
+    const bool exits = light && mh <= J;
+    int rh = 0, ra = 0, rr = 0;
+    for (int u = 0; u < cnt; ++u) {
+      const int o = __builtin_amdgcn_readlane(me, u);
+      const int oh = o & 0xFF, ol = o >> 8;
+      const bool before = u < t;
+      rh += (oh < mh || (oh == mh && before)) ? 1 : 0;
+      if (ol < oh) {
+        ra += (ol < ml || (ol == ml && before)) ? 1 : 0;
+        rr += (oh < mh || (oh == mh && before)) ? 1 : 0;
       }
     }
-    __syncthreads();
+    if (heavy) {
+      s.hIdx[rh] = t;
+      s.hLev[rh] = mh;
+    }
+    if (light) {
+      s.aIdx[ra] = t;
+      s.aLev[ra] = ml;
+    }
+    if (exits) {
+      s.rIdx[rr] = t;
+      s.rLev[rr] = mh;
+    }
+    const unsigned long long bh = __ballot(heavy), bl = __ballot(light), br = __ballot(exits);
+    if (t == 0) {
+      s.nH = __popcll(bh);
+      s.nA = __popcll(bl);
+      s.nR = __popcll(br);
+    }
+  }
+  __syncthreads();
+  if (t < kD) {
+    // heavy: column t of N, and D, Q (thread 0)
+    level_runs<true>(s, s.hIdx, s.hLev, s.nH, t, t, t == 0, 256, 1.0);
+  } else {
+    // light: column t - 128 of V, and k, P (thread 128); entries, then exits
+    const int c = t - kD;
+    level_runs<false>(s, s.aIdx, s.aLev, s.nA, kD + c, c, c == 0, 258, 1.0);
+    level_runs<false>(s, s.rIdx, s.rLev, s.nR, kD + c, c, c == 0, 258, -1.0);
+  }
+  __syncthreads();
 }
 
 // Add candidates [i0, i1) of query head hq from their stored records.
@@ -156,7 +236,7 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
       s.pos[t] = a.candpos[base + c0 + t];
     }
     __syncthreads();
-    accumulate_stage(a, s, h, cnt);
+    accumulate_stage(a, s, h, cnt, false);
   }
 }
 
@@ -185,7 +265,13 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0
       if (r < cnt) {
         const int64_t row = ((int64_t)h * a.n_cap + s.pos[r]) * kD;
         p = score_chunk(q16, a.K + row, k8);
-        v = sumsq_chunk(a.V + row, k8);
+        // the V row is staged for the accumulation while its |v|^2 is formed
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + row) + 2 * k8;
+        const uint4 v0 = vsrc[0], v1 = vsrc[1];
+        uint4 *vdst = reinterpret_cast<uint4 *>(s.vs[r]) + 2 * k8;
+        vdst[0] = v0;
+        vdst[1] = v1;
+        v = sumsq_words(v0, v1);
       }
       const double sc = r1_combine8(p) * kRsqrtD;
       const double vs = r1_combine8(v);
@@ -212,7 +298,7 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0
       a.rec_hl[base + c0 + t] = hl | (ll << 8);
     }
     __syncthreads();
-    accumulate_stage(a, s, h, cnt);
+    accumulate_stage(a, s, h, cnt, true);
   }
 }
 
@@ -260,30 +346,30 @@ __global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
   }
 }
 
-__device__ inline double kl_div(double x, double mu) {
-  return (x > 0.0) ? (mu - x + x * log(x / mu)) : mu;
-}
-// Root of kl(x, mu) = L above x (Newton from above; convex increasing branch).
+// Root of kl(x, mu) = mu - x + x ln(x / mu) = L above x: Newton from above on the convex
+// increasing branch, stopped when a step no longer decreases mu.  The step is
+// mu - f mu / (mu - x) with f = (mu - x) + x (ln x - ln mu) - L.
 __device__ inline double kl_upper(double x, double L) {
   if (!(x > 0.0)) return L;
+  const double lx = log(x);
   double mu = x + L + sqrt(L * L + 2.0 * x * L);
   for (int it = 0; it < 100; ++it) {
-    const double f = kl_div(x, mu) - L;
-    const double d = 1.0 - x / mu;
-    const double nx = mu - f / d;
+    const double f = (mu - x) + x * (lx - log(mu)) - L;
+    const double nx = mu - f * mu / (mu - x);
     if (!(nx < mu)) break;
     mu = nx;
   }
   return mu;
 }
-// Root of kl(x, mu) = L below x (Newton from below; convex decreasing branch).
+// Root of kl(x, mu) = L below x (Newton from below on the convex decreasing branch).
 __device__ inline double kl_lower(double x, double L) {
   if (!(x > 0.0)) return 0.0;
+  const double lx = log(x);
   double mu = fmax(x - sqrt(2.0 * x * L), x * exp(-1.0 - L / x));
+  if (!(mu > 0.0)) return 0.0;
   for (int it = 0; it < 100; ++it) {
-    const double f = kl_div(x, mu) - L;
-    const double d = 1.0 - x / mu;
-    const double nx = mu - f / d;
+    const double f = (mu - x) + x * (lx - log(mu)) - L;
+    const double nx = mu - f * mu / (mu - x);
     if (!(nx > mu) || !(nx < x)) break;
     mu = nx;
   }
@@ -360,6 +446,15 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
     f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
   }
+  // window sums, rescaled from c_R to c*
+  {
+    const double cs = dec_max(a.cstar[hq]);
+    const double sc = exp(a.qconst[(int64_t)hq * kQc + QC_CR] - cs);
+    const double *wr = a.win + (int64_t)hq * kWinW;
+    if (t < kD) f.nr[t] = wr[t] * sc;
+    if (t == kD) f.dr = wr[kD] * sc;
+    if (t == kD + 1) f.qr = wr[kD + 1] * sc;
+  }
   if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
@@ -371,21 +466,36 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     __syncthreads();
   }
-  // window sums, rescaled from c_R to c*
+  // prefix over levels: columns 0..255 one per thread (eight rows at a time), the four
+  // scalar columns by wavefront 3 with the levels across its lanes
   {
-    const double cs = dec_max(a.cstar[hq]);
-    const double sc = exp(a.qconst[(int64_t)hq * kQc + QC_CR] - cs);
-    const double *wr = a.win + (int64_t)hq * kWinW;
-    if (t < kD) f.nr[t] = wr[t] * sc;
-    if (t == kD) f.dr = wr[kD] * sc;
-    if (t == kD + 1) f.qr = wr[kD + 1] * sc;
-  }
-  // prefix over levels
-  for (int c = t; c < kStatW; c += 256) {
     double run = 0.0;
-    for (int j = 0; j <= jmax; ++j) {
-      run += s.acc[j][c];
-      s.acc[j][c] = run;
+    int j = 0;
+    for (; j + 8 <= jmax + 1; j += 8) {
+      double v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = s.acc[j + i][t];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        run += v[i];
+        s.acc[j + i][t] = run;
+      }
+    }
+    for (; j <= jmax; ++j) {
+      run += s.acc[j][t];
+      s.acc[j][t] = run;
+    }
+    if (wv == 3) {
+#pragma unroll
+      for (int c = 2 * kD; c < 2 * kD + 4; ++c) {
+        double v = (lane <= jmax) ? s.acc[lane][c] : 0.0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const double u = __shfl_up(v, off, 64);
+          if (lane >= off) v += u;
+        }
+        if (lane <= jmax) s.acc[lane][c] = v;
+      }
     }
   }
   __syncthreads();
@@ -421,19 +531,24 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     f.dots[j][r] = (f.dpart[j][0][r] + f.dpart[j][1][r]) + (f.dpart[j][2][r] + f.dpart[j][3][r]);
   }
   __syncthreads();
-  if (t < 4 * (jmax + 1)) {
-    const int j = t >> 2, r = t & 3;
-    const double k = s.acc[j][258], P = s.acc[j][259];
-    double x;
-    if (r < 2) {
-      x = k;
-    } else if (r == 2) {
-      const double cn2 = f.dots[j][0], cn = sqrt(cn2), Rc = Vmax + cn;
-      x = (Rc > 0.0) ? fmax((P - 2.0 * f.dots[j][1] + k * cn * cn) / (Rc * Rc), 0.0) : 0.0;
-    } else {
-      x = (Vmax > 0.0) ? P / (Vmax * Vmax) : 0.0;
+  {
+    // roots: wavefronts 0-1 the upper ones (r = 0: of k; r = 2: of the G statistic),
+    // wavefronts 2-3 the lower ones (r = 1: of k; r = 3: of P / Vmax^2)
+    const bool upper = t < 128;
+    const int u = t & 127, j = u >> 1, r = (upper ? 0 : 1) + 2 * (u & 1);
+    if (j <= jmax) {
+      const double k = s.acc[j][258], P = s.acc[j][259];
+      double x;
+      if (r < 2) {
+        x = k;
+      } else if (r == 2) {
+        const double cn2 = f.dots[j][0], cn = sqrt(cn2), Rc = Vmax + cn;
+        x = (Rc > 0.0) ? fmax((P - 2.0 * f.dots[j][1] + k * cn * cn) / (Rc * Rc), 0.0) : 0.0;
+      } else {
+        x = (Vmax > 0.0) ? P / (Vmax * Vmax) : 0.0;
+      }
+      f.root[j][r] = upper ? kl_upper(x, a.L) : kl_lower(x, a.L);
     }
-    f.root[j][r] = (r == 1 || r == 3) ? kl_lower(x, a.L) : kl_upper(x, a.L);
   }
   __syncthreads();
   if (t <= jmax) {

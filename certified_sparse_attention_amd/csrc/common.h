@@ -24,7 +24,9 @@ constexpr int kMaxJ = 60;
 constexpr int kMaxG = 7;
 constexpr int kBlocksPerWave = 16;                 // scan: blocks handled by one wavefront
 constexpr int kNumSeg = 64;                        // accumulate: max segments per query
-constexpr int kStatW = 260;                        // per-level stats: N[128] V[128] D Q k P
+constexpr int kStatW = 261;                        // per-level stats N[128] V[128] D Q k P, and a
+                                                   // pad column (rows 522 dwords apart: level-
+                                                   // strided LDS reads spread over the banks)
 
 struct BlockMeta {   // 16 bytes per packed block
   float ksmax;
@@ -180,10 +182,8 @@ __device__ inline double score_chunk(const double *q16, const uint16_t *krow, in
   }
   return acc;
 }
-// Chunk k of |v|^2 for one fp16 row.
-__device__ inline double sumsq_chunk(const uint16_t *row, int k) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(row) + 2 * k;
-  const uint4 a = src[0], b = src[1];
+// |v|^2 of the sixteen fp16 values held in two 16-byte words, in index order.
+__device__ inline double sumsq_words(uint4 a, uint4 b) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   const double v0 = h2d((uint16_t)(w[0] & 0xFFFFu));
   double acc = v0 * v0;
@@ -193,6 +193,11 @@ __device__ inline double sumsq_chunk(const uint16_t *row, int k) {
     acc = acc + v * v;
   }
   return acc;
+}
+// Chunk k of |v|^2 for one fp16 row.
+__device__ inline double sumsq_chunk(const uint16_t *row, int k) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(row) + 2 * k;
+  return sumsq_words(src[0], src[1]);
 }
 
 // R1 sum of squares of one fp16 row.
