@@ -55,13 +55,14 @@ struct CertArgs {
   int all_exact;
 };
 
-__device__ inline int first_level_lt(double x, const double *lt, int J) {
-  int lo = 0, hi = J + 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (lt[mid] > x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
+// First level j in [0, J + 1] with lt[j] <= x (J + 1 if none), for the table
+// lt[j] = j lt[1]: an estimate from x / lt[1], then steps to the exact answer.
+__device__ inline int level_of(double x, const double *lt, int J, double inv_l1) {
+  const double e = ceil(x * inv_l1);
+  int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
+  while (j <= J && lt[j] > x) ++j;
+  while (j > 0 && lt[j - 1] <= x) --j;
+  return j;
 }
 
 constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
@@ -246,6 +247,7 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
 __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
   const double *lt = s.lt;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
+  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
   const double cs = dec_max(a.cstar[hq]);
@@ -285,8 +287,8 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0
       const int pos = s.pos[t];
       const double sc = s.w[t];
       const double E = perturbation(prefix, pos);
-      const int hl = first_level_lt(sc - cs, lt, a.J);
-      const int ll = first_level_lt((sc + E) - cs, lt, a.J);
+      const int hl = level_of(sc - cs, lt, a.J, inv_l1);
+      const int ll = level_of((sc + E) - cs, lt, a.J, inv_l1);
       const double w = exp(sc - cs);
       const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
       s.hl[t] = hl | (ll << 8);
@@ -406,6 +408,7 @@ struct FinSmem {
   int hist[kMaxJ + 2];
   int cmh[kMaxJ + 2];            // C_max keys per bucket level
   double nr[kD];
+  double vmax;
   double dr, qr;
   double beta[kMaxJ + 1];
   double dots[kMaxJ + 1][4];     // |c|^2, c.V, |o^ - c|^2, |o^|^2 per level
@@ -430,14 +433,12 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     return;
   }
-  const int count = pass_count(a, hq);
-  if (count < 0) return;
-  const int jmax = (a.pass == 1) ? a.jspec[hq] : a.J;
   __shared__ FinSmem f;
   AccSmem &s = f.s;
   const int J1 = a.J + 1;
-  int i0, i1, nseg;
-  seg_range(count, 0, i0, i1, nseg);
+  // every load that does not depend on the candidate count is issued before it is used
+  const int count = pass_count(a, hq);
+  const int jmax = (a.pass == 1) ? a.jspec[hq] : a.J;
   for (int j = t; j < J1; j += 256) {
     f.tau[j] = a.tau[j];
     s.lt[j] = a.lt[j];
@@ -446,6 +447,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
     f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
   }
+  if (t == 255) f.vmax = h2d((uint16_t)a.vmax[h]);
   // window sums, rescaled from c_R to c*
   {
     const double cs = dec_max(a.cstar[hq]);
@@ -455,6 +457,9 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     if (t == kD) f.dr = wr[kD] * sc;
     if (t == kD + 1) f.qr = wr[kD + 1] * sc;
   }
+  if (count < 0) return;
+  int i0, i1, nseg;
+  seg_range(count, 0, i0, i1, nseg);
   if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
@@ -466,42 +471,38 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     __syncthreads();
   }
-  // prefix over levels: columns 0..255 one per thread (eight rows at a time), the four
-  // scalar columns by wavefront 3 with the levels across its lanes
+  // prefix over levels, eight rows at a time: thread t takes column t and, for t < 4, the
+  // scalar column 256 + t as a second chain (the others run it on the pad column)
   {
-    double run = 0.0;
+    const int c2 = (t < 4) ? 2 * kD + t : kStatW - 1;
+    double run = 0.0, run2 = 0.0;
     int j = 0;
     for (; j + 8 <= jmax + 1; j += 8) {
-      double v[8];
+      double v[8], v2[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = s.acc[j + i][t];
+      for (int i = 0; i < 8; ++i) {
+        v[i] = s.acc[j + i][t];
+        v2[i] = s.acc[j + i][c2];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         run += v[i];
+        run2 += v2[i];
         s.acc[j + i][t] = run;
+        s.acc[j + i][c2] = run2;
       }
     }
     for (; j <= jmax; ++j) {
       run += s.acc[j][t];
+      run2 += s.acc[j][c2];
       s.acc[j][t] = run;
-    }
-    if (wv == 3) {
-#pragma unroll
-      for (int c = 2 * kD; c < 2 * kD + 4; ++c) {
-        double v = (lane <= jmax) ? s.acc[lane][c] : 0.0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const double u = __shfl_up(v, off, 64);
-          if (lane >= off) v += u;
-        }
-        if (lane <= jmax) s.acc[lane][c] = v;
-      }
+      s.acc[j][c2] = run2;
     }
   }
   __syncthreads();
   // certificate of every level up to jmax: dot products per level (wavefront wv takes
   // levels wv, wv + 4, ...), then the four KL roots of every level in parallel, then beta
-  const double Vmax = h2d((uint16_t)a.vmax[h]);
+  const double Vmax = f.vmax;
   {
     const int j = t >> 2, qt = t & 3;
     if (j <= jmax) {
