@@ -417,16 +417,14 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     // pass 1: levels up to the speculative level (at most `budget` candidates).  With a
     // budget within the fused size its rescoring runs inside the certificate kernel;
     // otherwise a separate rescoring kernel and the segmented accumulation do it.
-    // pass 2: the heads that need all levels (their remaining candidates are rescored
-    // inside the certificate or segmented-accumulation kernel).
     const bool seg1 = sel.budget > csa::kFusedMax;
     ca.fused_rescore = seg1 ? 0 : 1;
     if (seg1 && (e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "rescore");
-    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess ||
-        (e = csa::launch_certify_pass(ca, 2, P.H_q, true, st)) != hipSuccess)
-      return hip_fail(e, "certify");
+    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess) return hip_fail(e, "certify");
   }
-  if ((e = csa::launch_exact(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "exact");
+  // the tail: pass 2 for the heads that need all levels (their remaining candidates are
+  // rescored there) and the exact fallback, in one launch that certified heads leave at once
+  if ((e = csa::launch_tail(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "tail");
 
   if (trace) {
     const int Hq = P.H_q;

@@ -418,22 +418,14 @@ struct FinSmem {
   long long extra[4];
 };
 
-// One workgroup (256 threads) per query head: level sums (directly, or from the
-// segments' increments), window sums, prefix over levels, the certificate of every
-// level, the stop level and the outputs.
-__global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
-  const int hq = blockIdx.x, t = threadIdx.x, h = hq / a.G;
+// The certificate of query head hq in pass a.pass, by one workgroup of 256 threads: level
+// sums (directly, or from the segments' increments), window sums, prefix over levels, the
+// certificate of every level up to the pass's last level, the stop level and the outputs.
+// Returns true when a level certifies (outputs written); otherwise the head is flagged
+// for the extension pass (2) or for the exact fallback (1).  Uniform across the group.
+__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
+  const int t = threadIdx.x, h = hq / a.G;
   const int lane = t & 63, wv = t >> 6;
-  if (a.all_exact) {
-    if (t == 0) {
-      a.flags[hq] = 1;
-      a.stop[hq] = 0;
-      a.beta[hq] = 0.0;
-      a.keys_read[hq] = a.n;
-    }
-    return;
-  }
-  __shared__ FinSmem f;
   AccSmem &s = f.s;
   const int J1 = a.J + 1;
   // every load that does not depend on the candidate count is issued before it is used
@@ -457,7 +449,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     if (t == kD) f.dr = wr[kD] * sc;
     if (t == kD + 1) f.qr = wr[kD + 1] * sc;
   }
-  if (count < 0) return;
+  if (count < 0) return false;
   int i0, i1, nseg;
   seg_range(count, 0, i0, i1, nseg);
   if (nseg == 0) {
@@ -582,7 +574,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
       a.beta[hq] = 0.0;
       a.keys_read[hq] = a.n;
     }
-    return;
+    return false;
   }
   // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|
   if (wv == 0) {
@@ -610,59 +602,122 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     a.beta[hq] = f.beta[js];
     a.keys_read[hq] = (int64_t)a.W + f.extra[1] + f.extra[0];
   }
+  return true;
 }
 
-// Exact attention for heads flagged for the fallback: grid (H_q, kExactChunks), 128 threads.
-__global__ __launch_bounds__(128) void exact_partial_kernel(CertArgs a) {
-  const int hq = blockIdx.x, ch = blockIdx.y, t = threadIdx.x, h = hq / a.G;
-  if (a.flags[hq] == 0) return;
-  __shared__ double qd[kD];
-  __shared__ double wv[128], wq[128];
-  qd[t] = (double)a.qf[(int64_t)hq * kD + t];
-  __syncthreads();
+// Pass 1, one workgroup per query head (heads with n <= W go straight to exact attention).
+__global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
+  const int hq = blockIdx.x;
+  if (a.all_exact) {
+    if (threadIdx.x == 0) {
+      a.flags[hq] = 1;
+      a.stop[hq] = 0;
+      a.beta[hq] = 0.0;
+      a.keys_read[hq] = a.n;
+    }
+    return;
+  }
+  __shared__ FinSmem f;
+  certify_head(a, f, hq);
+}
+
+struct ExactSmem {
+  double qd[kD];
+  double w[256];
+  double half[kD];
+  double dsum[4];
+};
+
+// Exact attention sums over keys [i0, i1) of query head hq relative to c*: N[c] (out[c])
+// and D (out[kD]), 256 threads.  Keys in batches of 256: one key per thread for its score
+// and weight, then two halves of the batch over the 128 channels.
+__device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0, int64_t i1, double *out) {
+  const int t = threadIdx.x, h = hq / a.G, c = t & (kD - 1), hf = t >> 7;
+  if (t < kD) e.qd[t] = (double)a.qf[(int64_t)hq * kD + t];
   const double cs = dec_max(a.cstar[hq]);
-  const int64_t len = (a.n + kExactChunks - 1) / kExactChunks;
-  const int64_t i0 = ch * len, i1 = min(a.n, i0 + len);
-  double accN = 0.0, accD = 0.0, accQ = 0.0;
-  for (int64_t b = i0; b < i1; b += 128) {
-    const int cnt = (int)min<int64_t>(128, i1 - b);
+  __syncthreads();
+  double accN = 0.0, accD = 0.0;
+  for (int64_t b = i0; b < i1; b += 256) {
+    const int cnt = (int)min<int64_t>(256, i1 - b);
     if (t < cnt) {
-      const int64_t pos = b + t;
-      const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-      const double w = exp(s - cs);
-      wv[t] = w;
-      wq[t] = w * row_sumsq(a.V + ((int64_t)h * a.n_cap + pos) * kD);
+      const double sc = exact_score(e.qd, a.K + ((int64_t)h * a.n_cap + b + t) * kD);
+      const double w = exp(sc - cs);
+      e.w[t] = w;
+      accD += w;
     }
     __syncthreads();
-    for (int i = 0; i < cnt; ++i) accN += wv[i] * h2d(a.V[((int64_t)h * a.n_cap + b + i) * kD + t]);
-    if (t == 0)
-      for (int i = 0; i < cnt; ++i) {
-        accD += wv[i];
-        accQ += wq[i];
-      }
+    for (int i = 128 * hf; i < min(cnt, 128 * hf + 128); ++i)
+      accN += e.w[i] * h2d(a.V[((int64_t)h * a.n_cap + b + i) * kD + c]);
     __syncthreads();
   }
-  double *out = a.exactp + ((int64_t)hq * kExactChunks + ch) * 130;
-  out[t] = accN;
-  if (t == 0) {
-    out[128] = accD;
-    out[129] = accQ;
-  }
-  // the last chunk of the head to finish sums the chunks in a fixed order
+  // D: wavefront sums, then the four in order; N: the two halves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) accD += __shfl_xor(accD, off, 64);
+  if ((t & 63) == 0) e.dsum[t >> 6] = accD;
+  if (hf == 1) e.half[c] = accN;
+  __syncthreads();
+  if (t < kD) out[t] = accN + e.half[t];
+  if (t == 0) out[kD] = (e.dsum[0] + e.dsum[1]) + (e.dsum[2] + e.dsum[3]);
+}
+
+constexpr int kTailWG = kExactChunks;   // workgroups per query head in the tail
+
+// Everything after pass 1, for the heads pass 1 did not certify; grid (H_q, kTailWG), 256
+// threads.  Heads flagged for the extension pass: workgroup y accumulates segments y,
+// y + kTailWG, ... of the long candidate lists; every flagged head: workgroup y sums the
+// exact attention over the y-th chunk of the keys (for extended heads ahead of knowing
+// whether the extension certifies).  The last workgroup of a head to finish (a counter
+// behind a device-wide fence) runs the extension certificate, and where no level
+// certifies, writes the exact output from the chunks.  Certified heads exit at once.
+__global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
+  const int hq = blockIdx.x, y = blockIdx.y, t = threadIdx.x;
+  const int fl = a.flags[hq];
+  if (fl == 0) return;
+  __shared__ union {
+    FinSmem f;
+    ExactSmem e;
+  } u;
   __shared__ int last;
+  AccSmem &s = u.f.s;
+  if (fl == 2) {
+    const int count = a.ccount[hq];
+    int i0, i1, nseg;
+    seg_range(count, 0, i0, i1, nseg);
+    if (nseg > 0) {
+      const int J1 = a.J + 1;
+      for (int j = t; j < J1; j += 256) s.lt[j] = a.lt[j];
+      const int split = record_split(a, hq, count);
+      for (int seg = y; seg < nseg; seg += kTailWG) {
+        seg_range(count, seg, i0, i1, nseg);
+        zero_acc(s, J1);
+        accumulate_mixed(a, s, hq, i0, i1, split);
+        double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
+        for (int e = t; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
+        __syncthreads();
+      }
+    }
+  }
+  {
+    const int64_t len = (a.n + kTailWG - 1) / kTailWG;
+    const int64_t i0 = y * len, i1 = min<int64_t>(a.n, i0 + len);
+    exact_chunk(a, u.e, hq, i0, i1, a.exactp + ((int64_t)hq * kExactChunks + y) * 130);
+  }
   __threadfence();
   __syncthreads();
-  if (t == 0) last = (atomicAdd(a.exdone + hq, 1) == kExactChunks - 1);
+  if (t == 0) last = (atomicAdd(a.exdone + hq, 1) == kTailWG - 1);
   __syncthreads();
   if (!last) return;
   __threadfence();
-  double N = 0.0, Dn = 0.0;
-  for (int c = 0; c < kExactChunks; ++c) {
-    const double *p = a.exactp + ((int64_t)hq * kExactChunks + c) * 130;
-    N += p[t];
-    Dn += p[128];
+  if (fl == 2 && certify_head(a, u.f, hq)) return;
+  if (t < kD) {
+    double N = 0.0, Dn = 0.0;
+    for (int c = 0; c < kTailWG; ++c) {
+      const double *p = a.exactp + ((int64_t)hq * kExactChunks + c) * 130;
+      N += p[t];
+      Dn += p[kD];
+    }
+    a.o_hat[(int64_t)hq * kD + t] = (float)(N / Dn);
   }
-  a.o_hat[(int64_t)hq * kD + t] = (float)(N / Dn);
 }
 
 hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, bool segmented, hipStream_t st) {
@@ -672,8 +727,9 @@ hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, bool segmented, hi
   return hipGetLastError();
 }
 
-hipError_t launch_exact(const CertArgs &a, int H_q, hipStream_t st) {
-  hipLaunchKernelGGL(exact_partial_kernel, dim3(H_q, kExactChunks), dim3(128), 0, st, a);
+hipError_t launch_tail(CertArgs a, int H_q, hipStream_t st) {
+  a.pass = 2;
+  hipLaunchKernelGGL(tail_kernel, dim3(H_q, kTailWG), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
