@@ -81,10 +81,8 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.clo = take(Hq * sizeof(unsigned long long));
   P.cstar = take(Hq * sizeof(unsigned long long));
   P.vmax = take((size_t)P.H_kv * sizeof(unsigned));
-  P.cmcnt = take(Hq * sizeof(int));
   P.bdone = take(Hq * sizeof(int));
   P.exdone = take(Hq * sizeof(int));
-  P.cmpos = take(Hq * npc * sizeof(int));
   P.hist = take(Hq * J2 * sizeof(int));
   P.tilecnt = 0;
   P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
@@ -152,7 +150,6 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.clo = at<unsigned long long>(ws, P.clo);
   pa.cstar = at<unsigned long long>(ws, P.cstar);
   pa.vmax = at<unsigned>(ws, P.vmax);
-  pa.cmcnt = at<int>(ws, P.cmcnt);
   pa.hist = at<int>(ws, P.hist);
   pa.ccount = at<int>(ws, P.ccount);
   pa.flags = at<int>(ws, P.flags);
@@ -171,8 +168,6 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.sR = pa.sR;
   sa.win = at<double>(ws, P.win);
   sa.cstar = pa.cstar;
-  sa.cmcnt = pa.cmcnt;
-  sa.cmpos = at<int>(ws, P.cmpos);
   sa.codes = pk->codes;
   sa.kscale = pk->kscale;
   sa.zq = pk->zq;
@@ -204,10 +199,8 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.lt = pa.lt;
   sa.live = pa.live;
   sa.diag = diag;
-  if (ev0 && (e = hipEventRecord((hipEvent_t)ev0, st)) != hipSuccess) return hip_fail(e, "event");
-  e = csa::launch_scan(sa, st);
+  e = csa::launch_scan(sa, st, (hipEvent_t)ev0, (hipEvent_t)ev1);
   if (e != hipSuccess) return hip_fail(e, "scan");
-  if (ev1 && (e = hipEventRecord((hipEvent_t)ev1, st)) != hipSuccess) return hip_fail(e, "event");
   if (npool <= 0) return CSA_OK;
   e = csa::launch_refine(sa, st);
   if (e != hipSuccess) return hip_fail(e, "refine");
@@ -219,22 +212,38 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   return CSA_OK;
 }
 
-__global__ void trace_kernel(const double *qconst, const unsigned long long *clo,
-                             const unsigned long long *cstar, const int *cmcnt, const int *cmpos,
-                             const double *ubuf, int64_t npool_cap, const int *ccount, int Hq, double *c_R,
-                             double *c_lo, double *c_star, int *cm, int *cc) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Hq) return;
+// Trace values of a certified call, one workgroup (256 threads) per query head.  |C_max|
+// counts the live keys whose stored UB reaches the final c_lo: every such key is live
+// (its block passed the snapshot test and the key itself the UB >= snapshot test).
+__global__ __launch_bounds__(256) void trace_kernel(const double *qconst, const unsigned long long *clo,
+                                                    const unsigned long long *cstar, const uint32_t *live,
+                                                    int64_t nwords, int64_t nblocks, const double *ubuf,
+                                                    int64_t npool_cap, const int *ccount, double *c_R,
+                                                    double *c_lo, double *c_star, int *cm, int *cc) {
+  const int i = blockIdx.x, t = threadIdx.x;
   const double cl = csa::dec_max(clo[i]);
-  if (c_R) c_R[i] = qconst[(int64_t)i * csa::kQc + csa::QC_CR];
-  if (c_lo) c_lo[i] = cl;
-  if (c_star) c_star[i] = csa::dec_max(cstar[i]);
-  if (cm) {
-    int k = 0;
-    for (int e = 0; e < cmcnt[i]; ++e) k += ubuf[(int64_t)i * npool_cap + cmpos[(int64_t)i * npool_cap + e]] >= cl;
-    cm[i] = k;
+  if (t == 0) {
+    if (c_R) c_R[i] = qconst[(int64_t)i * csa::kQc + csa::QC_CR];
+    if (c_lo) c_lo[i] = cl;
+    if (c_star) c_star[i] = csa::dec_max(cstar[i]);
+    if (cc) cc[i] = ccount[i];
   }
-  if (cc) cc[i] = ccount[i];
+  if (!cm) return;
+  __shared__ int part[4];
+  int k = 0;
+  for (int64_t w = t; w < nblocks; w += 256) {
+    uint32_t bits = live[(int64_t)i * nwords + w];
+    while (bits) {
+      const int b = __ffs((int)bits) - 1;
+      bits &= bits - 1u;
+      k += (ubuf[(int64_t)i * npool_cap + 32 * w + b] >= cl) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) k += __shfl_xor(k, off, 64);
+  if ((t & 63) == 0) part[t >> 6] = k;
+  __syncthreads();
+  if (t == 0) cm[i] = part[0] + part[1] + part[2] + part[3];
 }
 
 }  // namespace
@@ -332,8 +341,6 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     sa.ubuf = at<double>(ws, P.ubuf);
     sa.clo = at<unsigned long long>(ws, P.clo);
     sa.cstar = at<unsigned long long>(ws, P.cstar);
-    sa.cmcnt = at<int>(ws, P.cmcnt);
-    sa.cmpos = at<int>(ws, P.cmpos);
     sa.hist = at<int>(ws, P.hist);
     sa.tilecnt = nullptr;
     sa.tileoff = at<int>(ws, P.tileoff);
@@ -387,8 +394,6 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.candpos = at<int>(ws, P.candpos);
   ca.rec_hl = at<int>(ws, P.rec_hl);
   ca.hist = at<int>(ws, P.hist);
-  ca.cmcnt = at<int>(ws, P.cmcnt);
-  ca.cmpos = at<int>(ws, P.cmpos);
   ca.ubuf = at<double>(ws, P.ubuf);
   ca.clo = at<unsigned long long>(ws, P.clo);
   ca.rec_w = at<double>(ws, P.rec_w);
@@ -429,11 +434,12 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   if (trace) {
     const int Hq = P.H_q;
     if (trace->c_R || trace->c_lo || trace->c_star || trace->cmax_count || trace->cand_count) {
-      hipLaunchKernelGGL(trace_kernel, dim3((Hq + 63) / 64), dim3(64), 0, st, at<double>(ws, P.qconst),
+      const int64_t nblocks = npool > 0 ? (npool + 31) / 32 : 0;
+      hipLaunchKernelGGL(trace_kernel, dim3(Hq), dim3(256), 0, st, at<double>(ws, P.qconst),
                        at<unsigned long long>(ws, P.clo), at<unsigned long long>(ws, P.cstar),
-                       at<int>(ws, P.cmcnt), at<int>(ws, P.cmpos), at<double>(ws, P.ubuf), P.npool_cap,
-                       at<int>(ws, P.ccount), Hq, trace->c_R, trace->c_lo,
-                       trace->c_star, trace->cmax_count, trace->cand_count);
+                       at<uint32_t>(ws, P.live), (int64_t)(P.npool_cap / 32 + 1), nblocks,
+                       at<double>(ws, P.ubuf), P.npool_cap, at<int>(ws, P.ccount), trace->c_R,
+                       trace->c_lo, trace->c_star, trace->cmax_count, trace->cand_count);
     }
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "trace");
     const size_t J1 = (size_t)P.J + 1;

@@ -34,7 +34,7 @@ struct CertArgs {
   const unsigned long long *cstar, *clo;
   const double *ubuf;
   const unsigned *vmax;
-  const int *ccount, *candpos, *hist, *cmcnt, *cmpos;
+  const int *ccount, *candpos, *hist;
   int *rec_hl;                  // candidate records (written by the fused rescoring)
   const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
   double *rec_w, *rec_vsq;

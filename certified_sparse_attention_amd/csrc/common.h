@@ -9,6 +9,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "../../include/csa.h"
@@ -336,7 +337,7 @@ struct Plan {
   int64_t ntiles;      // bucket tiles per query head
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
-  size_t clo, cstar, vmax, cmcnt, cmpos, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
+  size_t clo, cstar, vmax, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
       jspec;
   size_t bdone, exdone;  // per-head completion counters (last-workgroup reductions)
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;

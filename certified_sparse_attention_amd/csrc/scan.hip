@@ -46,7 +46,7 @@ struct PrepArgs {
   double *sR;
   unsigned long long *clo, *cstar;
   unsigned *vmax;
-  int *cmcnt, *hist, *ccount, *flags;
+  int *hist, *ccount, *flags;
   int *bdone, *exdone;   // per-head completion counters, cleared here
   uint32_t *live;     // [H_q][npool_cap / 32 + 1] bitmap, cleared here
 };
@@ -123,7 +123,6 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
   if (t == 0) {
     a.clo[hq] = enc_max(-__builtin_huge_val());
     a.cstar[hq] = enc_max(-__builtin_huge_val());
-    a.cmcnt[hq] = 0;
     a.ccount[hq] = 0;
     a.flags[hq] = 0;
     a.bdone[hq] = 0;
@@ -177,7 +176,6 @@ struct ScanArgs {
   double *pbuf, *ubuf;
   uint32_t *live;
   unsigned long long *clo, *cstar;
-  int *cmcnt, *cmpos;       // keys with UB >= the c_lo snapshot (a superset of C_max)
   unsigned *vmax;
   int diag;                 // 1: every key is live and UB/LB/E are written for all keys
   double *lb_out, *e_out;   // diagnostics (may be null)
@@ -622,49 +620,89 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   if (lane == 0) atomicMax(a.vmax + h, vmx);
 }
 
+// Everything one chunk (two blocks) of the refinement reads from the packed cache: its
+// codes (four tiles), the key-error code of the lane's key and both blocks' scale maximum
+// and channel scales of the lane's two channels.
+struct ChunkLoads {
+  uint4 cw[4];
+  uint32_t kerr;
+  float ksmax[2];
+  uint32_t kk[2];
+};
+
+__device__ inline void load_chunk(const ScanArgs &a, int h, int64_t bA, int nb2, int lane, ChunkLoads &L) {
+  const int64_t mypos = bA * kBlk + lane;
+  L.kerr = (lane < 32 * nb2 && mypos < a.npool) ? (uint32_t)a.kerr[(int64_t)h * a.n_cap + mypos] : 0u;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+    L.cw[T] = (T < 2 * nb2)
+                  ? reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane]
+                  : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    L.ksmax[bi] = (bi < nb2) ? a.bmeta[(int64_t)h * a.nb_cap + bA + bi].ksmax : 0.0f;
+    L.kk[bi] = (bi < nb2) ? reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + bA + bi) * kD)[lane]
+                          : 0u;
+  }
+}
+
 __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
+  // four wave slots of kBlocksPerWave blocks per workgroup; a workgroup never spans two
+  // KV heads (slots past a head's last block have none)
   const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
-  if (gw >= (int64_t)a.H_kv * wph) return;
-  const int h = (int)(gw / wph);
-  const int64_t blk0 = (gw % wph) * kBlocksPerWave;
-  const int nblk = (int)min((int64_t)kBlocksPerWave, a.nb_pool - blk0);
+  const int64_t wgh = (wph + 3) / 4;
+  const int h = (int)(blockIdx.x / wgh);
+  const int64_t wbase = (int64_t)(blockIdx.x % wgh) * 4;
+  const int64_t blk0 = (wbase + wv) * kBlocksPerWave;
+  const int nblk = (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, a.nb_pool - blk0));
   const int G = a.G;
   const int n16 = lane & 15, grp = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
   __shared__ double cst_all[4][3][kBlocksPerWave][8];
-  __shared__ double clo_all[4][8];
+  __shared__ double clo_wg[8];
+  __shared__ uint32_t wchunks[4];
   __shared__ uint8_t flag_all[4][64];
-  __shared__ int ent_all[4][64];
+  __shared__ int ent_all[4][2 * 4 * 64];
   __shared__ unsigned long long smx_all[4][8];   // max exact score of C_max candidates per query
   uint8_t *Abuf = Abuf_all[wv];
-  double(*cst)[kBlocksPerWave][8] = cst_all[wv];
   uint8_t *flag = flag_all[wv];
   int *ent = ent_all[wv];
   unsigned long long *smx = smx_all[wv];
 
-  // one snapshot of c_lo's running value per query, shared by every test below
+  // one snapshot of c_lo's running value per query for the whole workgroup, shared by
+  // every test below; the block maxima and the query values are loaded together with it
   const int hq0 = h * G;
-  if (lane < 8) smx[lane] = enc_max(-__builtin_huge_val());
-  if (lane < G)
-    clo_all[wv][lane] = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  wave_sync();
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = gB < G;
+  float2 mxA = make_float2(0.0f, 0.0f), mxB = make_float2(0.0f, 0.0f);
+  if (n16 < nblk && hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
+  if (n16 < nblk && hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
+  float qv0[kMaxG], qv1[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
+    qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
+  }
+  float qmax = 0.0f;
+  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
+  if (lane < 8) smx[lane] = enc_max(-__builtin_huge_val());
+  if (wv == 0 && lane < G)
+    clo_wg[lane] = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  __syncthreads();
   const double ltJ = a.lt[a.J];
   double clo2A = 0, clo2B = 0, thrA = 0, thrB = 0, qnpA = 0, qnpB = 0;
   if (hasA) {
     const double *qc = a.qconst + (int64_t)(hq0 + gA) * kQc;
-    clo2A = clo_all[wv][gA];
+    clo2A = clo_wg[gA];
     thrA = fmax(clo2A, qc[QC_PILOT]) + ltJ;
     qnpA = qc[QC_QNP];
   }
   if (hasB) {
     const double *qc = a.qconst + (int64_t)(hq0 + gB) * kQc;
-    clo2B = clo_all[wv][gB];
+    clo2B = clo_wg[gB];
     thrB = fmax(clo2B, qc[QC_PILOT]) + ltJ;
     qnpB = qc[QC_QNP];
   }
@@ -677,14 +715,12 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     bool pass = false;
     if (n16 < nblk) {
       if (hasA) {
-        const float2 m = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
-        const double u = m.x, e = m.y;
+        const double u = mxA.x, e = mxA.y;
         pass |= u >= clo2A - 0x1p-30 * (fabs(u) + fabs(clo2A) + 1.0);
         pass |= e >= thrA - 0x1p-30 * (fabs(e) + fabs(thrA) + 1.0);
       }
       if (hasB) {
-        const float2 m = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
-        const double u = m.x, e = m.y;
+        const double u = mxB.x, e = mxB.y;
         pass |= u >= clo2B - 0x1p-30 * (fabs(u) + fabs(clo2B) + 1.0);
         pass |= e >= thrB - 0x1p-30 * (fabs(e) + fabs(thrB) + 1.0);
       }
@@ -692,44 +728,54 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     const unsigned long long b = __ballot(pass);
     alive = (uint32_t)((b | (b >> 16) | (b >> 32) | (b >> 48)) & 0xFFFFull);
   }
-  if (alive == 0u) return;
-
-  float qmax = 0.0f;
-  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
-  float qv0[kMaxG], qv1[kMaxG];
-#pragma unroll
-  for (int g = 0; g < kMaxG; ++g) {
-    qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
-    qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
-  }
+  // chunks (two blocks) with a block that passed
+  uint32_t chunks = 0;
+  for (int c = 0; 2 * c < nblk; ++c)
+    if ((alive >> (2 * c)) & 3u) chunks |= 1u << c;
+  if (lane == 0) wchunks[wv] = chunks;
+  __syncthreads();
+  const uint32_t allm = wchunks[0] | (wchunks[1] << 8) | (wchunks[2] << 16) | (wchunks[3] << 24);
+  if (allm == 0u) return;
+  if (chunks) offset_terms(a, h, blk0, nblk, G, lane, cst_all[wv]);
   init_operand(Abuf, lane);
-  offset_terms(a, h, blk0, nblk, G, lane, cst);
+  __syncthreads();   // every slot's offset terms are in LDS
 
+  // the workgroup's chunks in order, the k-th to wavefront k mod 4 (job bit 8 w + c: chunk
+  // c of slot w); each job's loads are issued before the previous job is processed
+  uint32_t jobs = 0;
+  {
+    uint32_t m = allm;
+    for (int k = 0; m; ++k) {
+      const uint32_t bit = m & (0u - m);
+      if ((k & 3) == wv) jobs |= bit;
+      m ^= bit;
+    }
+  }
   const uint64_t prefix = a.prefix[h];
   double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
   const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
+  auto job_blk = [&](int j) { return (wbase + (j >> 3)) * kBlocksPerWave + 2 * (j & 7); };
+  auto job_nb2 = [&](int j) { return (int)min<int64_t>(2, a.nb_pool - job_blk(j)); };
+  int cc = jobs ? __ffs((int)jobs) - 1 : -1;
+  ChunkLoads cur, nxt;
+  if (cc >= 0) load_chunk(a, h, job_blk(cc), job_nb2(cc), lane, cur);
 
-  for (int c0 = 0; c0 < nblk; c0 += 2) {
-    if (((alive >> c0) & 3u) == 0u) continue;
-    const int64_t bA = blk0 + c0;
-    const int nb2 = min(2, nblk - c0);
+  while (cc >= 0) {
+    jobs &= jobs - 1u;
+    const int cn = jobs ? __ffs((int)jobs) - 1 : -1;
+    if (cn >= 0) load_chunk(a, h, job_blk(cn), job_nb2(cn), lane, nxt);
+    double(*cst)[kBlocksPerWave][8] = cst_all[cc >> 3];
+    const int c0 = 2 * (cc & 7);          // first block of the chunk within its slot
+    const int64_t bA = job_blk(cc);
+    const int nb2 = job_nb2(cc);
     const int64_t tok0 = bA * kBlk;
     const int64_t mypos = tok0 + lane;
     const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
     double myEup = 0.0;
-    uint32_t mykerr = 0;
-    if (mine) {
-      myEup = perturbation_upper(prefix, mypos);
-      mykerr = a.kerr[(int64_t)h * a.n_cap + mypos];
-    }
+    if (mine) myEup = perturbation_upper(prefix, mypos);
+    const uint32_t mykerr = cur.kerr;
     flag[lane] = 0;
-    uint4 cw[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      cw[T] = make_uint4(0, 0, 0, 0);
-      if (T < 2 * nb2)
-        cw[T] = reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane];
-    }
+    const uint4 *cw = cur.cw;
     double ubA[4], ubB[4];
     uint32_t liveA = 0, liveB = 0;     // bit Tg: the key of tile Tg is live for slot A / B
     uint32_t cmA = 0, cmB = 0;         // bit Tg: UB >= c_lo snapshot (C_max candidate)
@@ -740,9 +786,9 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       const int bl = c0 + bi;
       double alpha;
       float scale;
-      block_grid(qmax, a.bmeta[(int64_t)h * a.nb_cap + b].ksmax, alpha, scale);
+      block_grid(qmax, cur.ksmax[bi], alpha, scale);
       const double halpha = alpha / 2.0;
-      const uint32_t kk = reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + b) * kD)[lane];
+      const uint32_t kk = cur.kk[bi];
       switch (G) {
         case 1: build_operand<1>(Abuf, qv0, qv1, kk, scale, lane); break;
         case 2: build_operand<2>(Abuf, qv0, qv1, kk, scale, lane); break;
@@ -808,48 +854,45 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       }
     }
     // exact scores of C_max candidates: c* = max(c_R, max over them), since a key with
-    // UB < c_lo scores below c_lo <= c*; the list is filtered by the final c_lo later.
-    // Candidates are listed in LDS and scored 8 per wavefront step.
+    // UB < c_lo scores below c_lo <= c*.  Every candidate of the chunk (both slots, all
+    // tiles) is listed in LDS first, then they are scored eight lanes per key.
     if (__ballot((cmA | cmB) != 0)) {
-#pragma unroll 1
+      int ne = 0;
+#pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
-#pragma unroll 1
+#pragma unroll
         for (int Tg = 0; Tg < 4; ++Tg) {
           const bool f = (((sl ? cmB : cmA) >> Tg) & 1u) != 0u;
           const unsigned long long mk = __ballot(f);
-          if (!mk) continue;
           if (f) {
             const int idx = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-            ent[idx] = (16 * Tg + n16) | ((sl ? gB : gA) << 8);
+            ent[ne + idx] = (16 * Tg + n16) | ((sl ? gB : gA) << 8);
           }
-          wave_sync();
-          const int ne = __popcll(mk);
-          for (int e0 = 0; e0 < ne; e0 += 8) {
-            const int e = e0 + (lane >> 3), k8 = lane & 7;
-            int g2 = 0;
-            int64_t pos = -1;
-            if (e < ne) {
-              const int v = ent[e];
-              g2 = v >> 8;
-              pos = tok0 + (v & 0xFF);
-            }
-            double p = 0.0;
-            if (pos >= 0) {
-              double q16[16];
-#pragma unroll
-              for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(hq0 + g2) * kD + 16 * k8 + i];
-              p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
-            }
-            const double sc = r1_combine8(p) * kRsqrtD;
-            if (pos >= 0 && k8 == 0) {
-              atomicMax(&smx[g2], enc_max(sc));
-              a.cmpos[(int64_t)(hq0 + g2) * a.npool_cap + atomicAdd(a.cmcnt + hq0 + g2, 1)] = (int)pos;
-            }
-          }
-          wave_sync();
+          ne += __popcll(mk);
         }
       }
+      wave_sync();
+      for (int e0 = 0; e0 < ne; e0 += 8) {
+        const int e = e0 + (lane >> 3), k8 = lane & 7;
+        int g2 = 0;
+        int64_t pos = -1;
+        if (e < ne) {
+          const int v = ent[e];
+          g2 = v >> 8;
+          pos = tok0 + (v & 0xFF);
+        }
+        double p = 0.0;
+        if (pos >= 0) {
+          double q16[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(hq0 + g2) * kD + 16 * k8 + i];
+          p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
+        }
+        const double sc = r1_combine8(p) * kRsqrtD;
+        if (pos >= 0 && k8 == 0) atomicMax(&smx[g2], enc_max(sc));
+      }
+      wave_sync();
     }
     // exact perturbations for the chunk's live tokens (lane = token)
     wave_sync();
@@ -893,6 +936,8 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         }
       }
     }
+    cc = cn;
+    if (cc >= 0) cur = nxt;
   }
   // exact c_lo: the processed blocks hold every key whose LB can exceed the snapshot
 #pragma unroll
@@ -922,23 +967,25 @@ int64_t scan_stream_wgs(int64_t H_kv, int64_t nb_pool) {
   return (waves + 3) / 4;
 }
 
-hipError_t launch_scan(const ScanArgs &a, hipStream_t st) {
+// With events given, they take the kernel's own start and end times from its dispatch (no
+// separate marker packets around it).
+hipError_t launch_scan(const ScanArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
   const unsigned wgs = (unsigned)(a.nstream + (int64_t)a.H_kv * a.G);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL(scan_kernel<1>, dim3(wgs), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(scan_kernel<2>, dim3(wgs), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(scan_kernel<3>, dim3(wgs), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(scan_kernel<4>, dim3(wgs), dim3(256), 0, st, a); break;
-    case 5: hipLaunchKernelGGL(scan_kernel<5>, dim3(wgs), dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL(scan_kernel<6>, dim3(wgs), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(scan_kernel<7>, dim3(wgs), dim3(256), 0, st, a); break;
+    case 1: hipExtLaunchKernelGGL(scan_kernel<1>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL(scan_kernel<2>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    case 3: hipExtLaunchKernelGGL(scan_kernel<3>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL(scan_kernel<4>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    case 5: hipExtLaunchKernelGGL(scan_kernel<5>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    case 6: hipExtLaunchKernelGGL(scan_kernel<6>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
+    default: hipExtLaunchKernelGGL(scan_kernel<7>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_refine(const ScanArgs &a, hipStream_t st) {
-  const int64_t waves = (int64_t)a.H_kv * ((a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave);
-  const unsigned wgs = (unsigned)((waves + 3) / 4);
+  const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
+  const unsigned wgs = (unsigned)((int64_t)a.H_kv * ((wph + 3) / 4));
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(refine_kernel, dim3(wgs), dim3(256), 0, st, a);
   return hipGetLastError();

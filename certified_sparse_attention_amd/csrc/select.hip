@@ -23,7 +23,6 @@ struct SelectArgs {
   const uint64_t *prefix;
   const double *pbuf, *ubuf;
   unsigned long long *clo, *cstar;
-  int *cmcnt, *cmpos;
   int *hist, *tilecnt, *tileoff, *ccount;
   int8_t *lub;
   int *candpos;

@@ -121,8 +121,9 @@ typedef struct {
  *   beta_level, dhat_level fp64 [H_q][J+1]: beta_j and D^_j at every level.
  *   k_level             int32 [H_q][J+1]: light sample count k_j.
  *   logtau              fp64 [J+1]: the level table used.
- *   ev_scan_begin/end   hipEvent_t recorded on the call's stream right before and
- *                       after the 4-bit scan kernel (for timing it alone).
+ *   ev_scan_begin/end   hipEvent_t that take the start and end times of the 4-bit
+ *                       scan kernel's own dispatch (for timing it alone; no marker
+ *                       packets are added to the stream).
  */
 typedef struct {
   double *c_R, *c_lo, *c_star;
