@@ -323,7 +323,7 @@ constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
 
 // Shared memory of the streaming kernel; its window workgroups reuse it.
 struct StreamSmem {
-  alignas(16) uint8_t Abuf[4][2 * 1024];
+  alignas(16) uint8_t Abuf[4][2][2 * 1024];   // per wavefront, one operand per block of a chunk
   double cst[4][3][kScanBlocks][8];
   float2 mx[4][kScanBlocks][8];
 };
@@ -448,7 +448,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int64_t blk0 = (gw % wph) * kScanBlocks;
   const int nblk = (int)min((int64_t)kScanBlocks, a.nb_pool - blk0);
   const int n16 = lane & 15, grp = lane >> 4;
-  uint8_t *Abuf = sm.st.Abuf[wv];
+  uint8_t *Abuf = sm.st.Abuf[wv][0];
+  uint8_t *Abuf1 = sm.st.Abuf[wv][1];
   double(*cst)[kScanBlocks][8] = sm.st.cst[wv];
   float2(*mx)[8] = sm.st.mx[wv];
 
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     qv1[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
   }
 
-  // Software pipeline: the loads of chunks c + 1 and c + 2 (two blocks each) are in
+  // Software pipeline: the loads of chunks c + 1 .. c + 3 (two blocks each) are in
   // flight while chunk c is computed.  The loads are unconditional and the loop issues
   // no global stores or atomics, so the compiler can wait for exactly the older loads.
   struct ChunkIn {
@@ -506,7 +507,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, lane * 2, c0 * kBlk * 2, 0);
   };
 
+  // the first three chunks' loads are in flight while the offset terms are formed
+  ChunkIn buf0, buf1, buf2, buf3;
+  load_chunk(0, buf0);
+  load_chunk(2, buf1);
+  load_chunk(4, buf2);
   init_operand(Abuf, lane);
+  init_operand(Abuf1, lane);
   static_assert(kScanBlocks % 16 == 0, "offset terms are formed 16 blocks at a time");
 #pragma unroll
   for (int col0 = 0; col0 < kScanBlocks; col0 += 16)
@@ -527,19 +534,31 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       myEup = perturbation_upper32(prefix, mypos);
       vmx = max(vmx, cur.vn);
     }
+    // both blocks' operands are built before either is read (one wavefront sync per
+    // chunk; the next chunk's writes follow these reads in the wavefront's LDS order)
+    float alpha32s[2], scales[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      double alpha;
+      block_grid(qmax, cur.ksmax[bi], alpha, scales[bi]);
+      alpha32s[bi] = (float)alpha;
+    }
+    build_operand<G>(Abuf, qv0, qv1, cur.kk[0], scales[0], lane);
+    if (nb2 > 1) build_operand<G>(Abuf1, qv0, qv1, cur.kk[1], scales[1], lane);
+    wave_sync();
+    v4i Aop[2][2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const uint8_t *Ab = bi ? Abuf1 : Abuf;
+      Aop[bi][0] = *reinterpret_cast<const v4i *>(Ab + lane * 16);
+      Aop[bi][1] = *reinterpret_cast<const v4i *>(Ab + 1024 + lane * 16);
+    }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
       const int bl = c0 + bi;
-      double alpha;
-      float scale;
-      block_grid(qmax, cur.ksmax[bi], alpha, scale);
-      const float alpha32 = (float)alpha, halpha32 = 0.5f * (float)alpha;
-      build_operand<G>(Abuf, qv0, qv1, cur.kk[bi], scale, lane);
-      wave_sync();
-      const v4i A0 = *reinterpret_cast<const v4i *>(Abuf + lane * 16);
-      const v4i A1 = *reinterpret_cast<const v4i *>(Abuf + 1024 + lane * 16);
-      wave_sync();
+      const float alpha32 = alpha32s[bi], halpha32 = 0.5f * alpha32s[bi];
+      const v4i A0 = Aop[bi][0], A1 = Aop[bi][1];
       const float baseA = hasA ? (float)cst[0][bl][gA] : 0.0f;
       const float ebpA = hasA ? (float)(cst[1][bl][gA] + cst[2][bl][gA]) : 0.0f;
       const float baseB = hasB ? (float)cst[0][bl][gB] : 0.0f;
@@ -586,19 +605,19 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
     }
   };
-  // two chunks in flight ahead of the one being computed
-  ChunkIn buf0, buf1, buf2;
-  load_chunk(0, buf0);
-  load_chunk(2, buf1);
-  for (int c0 = 0; c0 < nblk; c0 += 6) {
-    load_chunk(c0 + 4, buf2);
+  // three chunks in flight ahead of the one being computed
+  for (int c0 = 0; c0 < nblk; c0 += 8) {
+    load_chunk(c0 + 6, buf3);
     process(c0, buf0);
     if (c0 + 2 >= nblk) break;
-    load_chunk(c0 + 6, buf0);
+    load_chunk(c0 + 8, buf0);
     process(c0 + 2, buf1);
     if (c0 + 4 >= nblk) break;
-    load_chunk(c0 + 8, buf1);
+    load_chunk(c0 + 10, buf1);
     process(c0 + 4, buf2);
+    if (c0 + 6 >= nblk) break;
+    load_chunk(c0 + 12, buf2);
+    process(c0 + 6, buf3);
   }
   wave_sync();
   // per-block maxima of the wave: [query][block] rows of float2
