@@ -185,6 +185,21 @@ def main():
 
     npool = N_CTX - WINDOW
     scan_bytes = SCAN_BYTES_PER_TOKEN * npool * H_KV
+
+    # context for the roofline: a plain read (16-byte loads, no arithmetic) of the scan's
+    # byte count, rotating over L separate buffers so each read is as cold as the scan's
+    nb = int(scan_bytes)
+    rbufs = torch.empty((L, nb), dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        csa.stream_read(rbufs[i % L], sink=sink)
+    rev = [(csa.Event(), csa.Event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        csa.stream_read(rbufs[(args.warmup + i) % L], sink=sink, events=(rev[i][0].handle, rev[i][1].handle))
+    torch.cuda.synchronize()
+    read_ms = float(np.mean([a.elapsed_ms(b) for a, b in rev]))
+    del rbufs
     achieved = scan_bytes / (scan_avg_ms * 1e-3) / 1e9
     dense_bytes = DENSE_BYTES_PER_TOKEN * N_CTX * H_KV
     result = {
@@ -208,6 +223,10 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic(),
                      "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": scan_avg_ms,
                      "timed_launches": len(scan_ms), "timed_every": EVENT_EVERY},
+        "read_ceiling": {"kernel": "stream_read_kernel (16-byte loads only, 4096 workgroups)",
+                         "bytes": nb, "avg_launch_ms": read_ms, "GB/s": nb / (read_ms * 1e-3) / 1e9,
+                         "frac": nb / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "scan_over_read": scan_avg_ms / read_ms},
         "hbm_gbs_whole_step": scan_bytes / (ms_per_step * 1e-3) / 1e9,
         "dense_hip": {"ms_per_step": dense_ms, "steps_per_s": 1e3 / dense_ms,
                       "gbs": dense_bytes / (dense_ms * 1e-3) / 1e9},

@@ -13,5 +13,6 @@ from .api import (  # noqa: F401
     dense_decode_attention,
     pack_kv_4bit,
     scan_bounds,
+    stream_read,
     workspace_bytes,
 )

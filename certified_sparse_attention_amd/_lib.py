@@ -55,6 +55,7 @@ SYMBOLS = {
                                            c_void_p, c_size_t, c_void_p, c_void_p]),
     "csa_status_string": (ctypes.c_char_p, [c_int]),
     "csa_last_error": (ctypes.c_char_p, []),
+    "csa_stream_read": (c_int, [c_void_p, ctypes.c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "csa_event_create": (c_int, [ctypes.POINTER(c_void_p)]),
     "csa_event_destroy": (c_int, [c_void_p]),
     "csa_event_elapsed_ms": (c_int, [c_void_p, c_void_p, ctypes.POINTER(ctypes.c_float)]),

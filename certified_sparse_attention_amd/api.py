@@ -230,6 +230,22 @@ def dense_decode_attention(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, n:
     return out
 
 
+def stream_read(buf: torch.Tensor, workgroups: int = 4096, sink: torch.Tensor | None = None, events=None):
+    """Read a contiguous device buffer once (a measurement helper, not part of the certified
+    path); returns the per-workgroup XOR of its 32-bit words.  `events` = (begin, end)
+    Event handles take the kernel's own dispatch times."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    lib = _lib.load()
+    ev0, ev1 = events if events is not None else (None, None)
+    _lib.check(lib.csa_stream_read(_ptr(buf), int(nbytes), int(workgroups), _ptr(sink), ev0, ev1, _stream()),
+               "csa_stream_read")
+    return sink
+
+
 class Event:
     """A hipEvent_t created through the library (for timing one kernel on a stream)."""
 

@@ -246,6 +246,27 @@ __global__ __launch_bounds__(256) void trace_kernel(const double *qconst, const 
   if (t == 0) cm[i] = part[0] + part[1] + part[2] + part[3];
 }
 
+// One read of a buffer (16-byte loads; workgroup w streams the w-th contiguous slice) and
+// the XOR of its 32-bit words per workgroup.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *src, int64_t n16, int64_t per,
+                                                          uint32_t *sink) {
+  const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(n16, b0 + per);
+  uint32_t acc = 0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 4 * 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (i + 256 * k < b1) ? src[i + 256 * k] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,6 +510,19 @@ int csa_dense_decode_attention(const csa_shape *shape, const uint16_t *q, const 
   a.o = o;
   hipError_t e = csa::launch_dense(a, shape->num_kv_heads, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "dense");
+}
+
+int csa_stream_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *ev_begin,
+                    void *ev_end, void *stream) {
+  if (!buf || !sink) return fail(CSA_ERR_INVALID_ARGUMENT, "buf and sink must be device pointers");
+  if (bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
+  if (workgroups < 1 || workgroups > 65536) return fail(CSA_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65536]");
+  const int64_t n16 = bytes / 16, per = (n16 + workgroups - 1) / workgroups;
+  hipExtLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                        (hipEvent_t)ev_begin, (hipEvent_t)ev_end, 0, (const uint4 *)buf, n16, per, sink);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "stream read");
 }
 
 int csa_event_create(void **event) {

@@ -198,6 +198,16 @@ const char *csa_status_string(int status);
 /* Detail of the calling thread's last failed call (static per thread; "" if none). */
 const char *csa_last_error(void);
 
+/* Measurement helper (not part of the certified path): reads `bytes` of device memory at
+ * `buf` once with 16-byte loads, `workgroups` workgroups of 256 threads each streaming one
+ * contiguous slice, and writes each workgroup's XOR of the 32-bit words it read to
+ * sink[workgroup] (uint32, device, `workgroups` entries).  It times the plain read of a
+ * given byte count on the caller's stream: ev_begin/ev_end (hipEvent_t or NULL) take the
+ * kernel's own dispatch start and end.  bytes must be a multiple of 16 and buf 16-byte
+ * aligned; workgroups in [1, 65536].  Returns CSA_ERR_INVALID_ARGUMENT otherwise. */
+int csa_stream_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *ev_begin,
+                    void *ev_end, void *stream);
+
 /* Event helpers for timing on the caller's stream (host side; events are hipEvent_t). */
 int csa_event_create(void **event);
 int csa_event_destroy(void *event);

@@ -112,3 +112,12 @@ def test_dense_rejects_bad_arguments(lib):
     assert lib.csa_dense_decode_attention(ctypes.byref(sh), fake, fake, fake, 0, fake, 1 << 30, fake, None) == -1
     assert lib.csa_dense_decode_attention(ctypes.byref(sh), fake, fake, fake, 64, fake, 4, fake, None) == -3
     assert lib.csa_dense_workspace_bytes(ctypes.byref(sh), 4096) > 0
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.csa_stream_read(None, 1024, 4, fake, None, None, None) == -1            # null buffer
+    assert lib.csa_stream_read(fake, 1000, 4, fake, None, None, None) == -1            # not a multiple of 16
+    assert lib.csa_stream_read(ctypes.c_void_p(0x1004), 1024, 4, fake, None, None, None) == -1   # misaligned
+    assert lib.csa_stream_read(fake, 1024, 0, fake, None, None, None) == -1            # no workgroups
+    assert lib.csa_stream_read(fake, 1024, 70000, fake, None, None, None) == -1        # too many

@@ -252,6 +252,21 @@ def test_dense_decode_matches_oracle(case):
         assert np.linalg.norm(o[hq] - d["o"]) <= 1e-4 * d["M"], hq
 
 
+def test_stream_read_checksum():
+    """The read helper visits every 32-bit word once: per-workgroup XORs match the host's."""
+    rng = np.random.default_rng(5)
+    for nbytes, wgs in ((16 * 1000, 7), (1 << 20, 64), (16 * 4097, 300)):
+        host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+        sink = _csa().stream_read(torch.from_numpy(host.view(np.int32)).to(DEV), workgroups=wgs)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        n16 = nbytes // 16
+        per = -(-n16 // wgs)
+        for w in range(wgs):
+            part = host[4 * min(n16, w * per):4 * min(n16, (w + 1) * per)]
+            assert got[w] == (np.bitwise_xor.reduce(part) if part.size else 0), (nbytes, wgs, w)
+
+
 @pytest.mark.parametrize("budget", [1, 16, 300])
 def test_speculative_budget_does_not_change_results(case, budget):
     """A small candidate budget forces the second pass; results stay oracle-exact."""
