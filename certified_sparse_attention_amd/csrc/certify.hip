@@ -55,16 +55,6 @@ struct CertArgs {
   int all_exact;
 };
 
-// First level j in [0, J + 1] with lt[j] <= x (J + 1 if none), for the table
-// lt[j] = j lt[1]: an estimate from x / lt[1], then steps to the exact answer.
-__device__ inline int level_of(double x, const double *lt, int J, double inv_l1) {
-  const double e = ceil(x * inv_l1);
-  int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
-  while (j <= J && lt[j] > x) ++j;
-  while (j > 0 && lt[j - 1] <= x) --j;
-  return j;
-}
-
 constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
 constexpr int kStage = 64;        // candidates staged in LDS at a time
 

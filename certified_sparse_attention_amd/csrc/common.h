@@ -201,6 +201,16 @@ __device__ inline double sumsq_chunk(const uint16_t *row, int k) {
   return sumsq_words(src[0], src[1]);
 }
 
+// First level j in [0, J + 1] with lt[j] <= x (J + 1 if none), for the table
+// lt[j] = j lt[1]: an estimate from x / lt[1], then steps to the exact answer.
+__device__ inline int level_of(double x, const double *lt, int J, double inv_l1) {
+  const double e = ceil(x * inv_l1);
+  int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
+  while (j <= J && lt[j] > x) ++j;
+  while (j > 0 && lt[j - 1] <= x) --j;
+  return j;
+}
+
 // R1 sum of squares of one fp16 row.
 __device__ inline double row_sumsq(const uint16_t *row) {
   const uint4 *src = reinterpret_cast<const uint4 *>(row);

@@ -43,15 +43,6 @@ struct SelectArgs {
 };
 
 // ---- buckets.  A tile is 64 bitmap words (2048 positions); one thread per word.
-__device__ inline int first_level_tab(double x, const double *lt, int J) {
-  int lo = 0, hi = J + 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (lt[mid] > x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 // Per tile: cumulative level counts tilehist[tile][j] = |{l^ub <= j}| (j = 0..J+1, the
 // last one counting every pool key of the tile) and the C_max keys per level.
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
@@ -67,6 +58,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   __syncthreads();
   const double cs = dec_max(a.cstar[hq]);
   const double clo = dec_max(a.clo[hq]);
+  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
   const int64_t wi = tile * 64 + lane;
   const int64_t p0 = wi * 32;
   if (p0 < a.npool) {
@@ -93,7 +85,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
 #pragma unroll
       for (int b = 0; b < 32; ++b) {
         if ((bits >> b) & 1u) {
-          const int l = first_level_tab(pv[b] - cs, lt, a.J);
+          const int l = level_of(pv[b] - cs, lt, a.J, inv_l1);
           lub[b] = (int8_t)l;
           atomicAdd(&hist[l], 1);
           if (uv[b] >= clo) atomicAdd(&cmh[l], 1);
@@ -231,6 +223,7 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
   if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
   for (int j = threadIdx.x; j <= a.J; j += 256) lt[j] = a.lt[j];
   __syncthreads();
+  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
   int lo, hi;
   if (a.pass == 1) {
     lo = 0;
@@ -247,8 +240,8 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
     const int pos = a.candpos[o];
     const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
     const double E = perturbation(prefix, pos);
-    const int hl = first_level_tab(s - cs, lt, a.J);
-    const int ll = first_level_tab((s + E) - cs, lt, a.J);
+    const int hl = level_of(s - cs, lt, a.J, inv_l1);
+    const int ll = level_of((s + E) - cs, lt, a.J, inv_l1);
     double vsq = 0.0;
     if (ll <= a.J) vsq = row_sumsq(a.V + ((int64_t)h * a.n_cap + pos) * kD);
     a.rec_s[o] = s;
