@@ -65,7 +65,9 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.J = p->J;
   P.W = p->window;
   const int64_t npool = n_max > p->window ? n_max - p->window : 0;
-  P.npool_cap = npool > 0 ? npool : 1;
+  // per-head pool capacity, a multiple of 32 (rows of per-key arrays start 32-byte aligned
+  // and every 32-key word of them lies inside its row)
+  P.npool_cap = npool > 0 ? (npool + 31) / 32 * 32 : 32;
   P.ntiles = (P.npool_cap + csa::kBucketTile - 1) / csa::kBucketTile;
   const size_t Hq = (size_t)P.H_q, J1 = (size_t)P.J + 1, J2 = (size_t)P.J + 2, npc = (size_t)P.npool_cap;
   size_t off = 0;

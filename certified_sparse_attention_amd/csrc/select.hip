@@ -107,6 +107,21 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   }
 }
 
+// Sum over the ntiles tiles of entry `lane` of rows of width w (eight loads at a time).
+__device__ inline int sum_tiles(const int *base, int64_t ntiles, int w, int lane) {
+  int cum = 0;
+  int64_t tl = 0;
+  for (; tl + 8 <= ntiles; tl += 8) {
+    int v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = base[(tl + k) * w + lane];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cum += v[k];
+  }
+  for (; tl < ntiles; ++tl) cum += base[tl * w + lane];
+  return cum;
+}
+
 // Stable compaction of both ranges (l^ub <= jspec first, then jspec < l^ub <= J, each in
 // position order): thread = bitmap word.  Every tile's workgroup sums the head's tile
 // histograms itself (they are small and L2-resident), which gives the level histogram,
@@ -119,17 +134,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
   // cumulative level histogram of the head (lane = level)
   int cum = 0;
-  if (lane < J2) {
-    int64_t tl = 0;
-    for (; tl + 8 <= a.ntiles; tl += 8) {
-      int v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = th0[(tl + k) * J2 + lane];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) cum += v[k];
-    }
-    for (; tl < a.ntiles; ++tl) cum += th0[tl * J2 + lane];
-  }
+  if (lane < J2) cum = sum_tiles(th0, a.ntiles, J2, lane);
   // the levels that fit form a prefix 0..js (cumulative counts only grow)
   const unsigned long long fit = __ballot(lane <= J && (cum <= a.budget || lane == 0));
   const int js = __popcll(fit) - 1;
@@ -143,20 +148,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       a.ccount[hq] = totJ;
     }
     // C_max keys per bucket level
-    if (lane < J2) {
-      const int *cm0 = a.tilecm + (int64_t)hq * a.ntiles * J2;
-      int c = 0;
-      int64_t tl = 0;
-      for (; tl + 8 <= a.ntiles; tl += 8) {
-        int v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = cm0[(tl + k) * J2 + lane];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) c += v[k];
-      }
-      for (; tl < a.ntiles; ++tl) c += cm0[tl * J2 + lane];
-      a.cmhist[(int64_t)hq * J2 + lane] = c;
-    }
+    if (lane < J2) a.cmhist[(int64_t)hq * J2 + lane] = sum_tiles(a.tilecm + (int64_t)hq * a.ntiles * J2, a.ntiles, J2, lane);
   }
   // this tile's offsets: candidates of both ranges in the earlier tiles
   int b1 = 0, b2 = 0;
@@ -182,13 +174,21 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   if (p0 < a.npool) {
     const int valid = (int)min<int64_t>(32, a.npool - p0);
     const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-    uint32_t rest = a.live[(int64_t)hq * a.nwords + wi] & vmask;
-    while (rest) {
-      const int b = __ffs(rest) - 1;
-      rest &= rest - 1u;
-      const int l = a.lub[(int64_t)hq * a.npool_cap + p0 + b];
-      if (l <= js) m1 |= 1u << b;
-      else if (l <= J) m2 |= 1u << b;
+    const uint32_t bits = a.live[(int64_t)hq * a.nwords + wi] & vmask;
+    if (bits) {
+      // the word's 32 levels in two 16-byte loads (entries of keys that are not live are
+      // not read as levels)
+      const uint4 *lw = reinterpret_cast<const uint4 *>(a.lub + (int64_t)hq * a.npool_cap + p0);
+      const uint4 lv0 = lw[0], lv1 = lw[1];
+      const uint32_t wds[8] = {lv0.x, lv0.y, lv0.z, lv0.w, lv1.x, lv1.y, lv1.z, lv1.w};
+#pragma unroll
+      for (int b = 0; b < 32; ++b) {
+        if ((bits >> b) & 1u) {
+          const int l = (int)(int8_t)((wds[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+          if (l <= js) m1 |= 1u << b;
+          else if (l <= J) m2 |= 1u << b;
+        }
+      }
     }
   }
   int n1 = __popc(m1), n2 = __popc(m2);
