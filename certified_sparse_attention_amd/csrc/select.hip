@@ -135,10 +135,12 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   // cumulative level histogram of the head (lane = level)
   int cum = 0;
   if (lane < J2) cum = sum_tiles(th0, a.ntiles, J2, lane);
-  // the levels that fit form a prefix 0..js (cumulative counts only grow)
-  const unsigned long long fit = __ballot(lane <= J && (cum <= a.budget || lane == 0));
+  // the levels that fit form a prefix 0..js (cumulative counts only grow); js = -1 when
+  // level 0 alone exceeds the budget, and the first pass then has no candidates
+  const unsigned long long fit = __ballot(lane <= J && cum <= a.budget);
   const int js = __popcll(fit) - 1;
-  const int tot1 = __shfl(cum, js, 64), totJ = __shfl(cum, J, 64);
+  const int tot1v = __shfl(cum, max(js, 0), 64), totJ = __shfl(cum, J, 64);
+  const int tot1 = (js >= 0) ? tot1v : 0;
   if (tile == 0) {
     const int below = __shfl_up(cum, 1, 64);
     if (lane < J2) a.hist[(int64_t)hq * J2 + lane] = cum - (lane > 0 ? below : 0);
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     const int64_t tl = t0 + lane;
     int n1 = 0, n2 = 0;
     if (tl < tile) {
-      const int c1 = th0[tl * J2 + js], cJ = th0[tl * J2 + J];
+      const int c1 = (js >= 0) ? th0[tl * J2 + js] : 0, cJ = th0[tl * J2 + J];
       n1 = c1;
       n2 = cJ - c1;
     }

@@ -252,6 +252,23 @@ def test_dense_decode_matches_oracle(case):
         assert np.linalg.norm(o[hq] - d["o"]) <= 1e-4 * d["M"], hq
 
 
+def test_level_zero_over_the_budget():
+    """A near-flat head whose level-0 bucket alone holds more candidates than the fused
+    first pass takes: the first pass is empty and the second pass takes every level."""
+    rng = np.random.default_rng(77)
+    _, q, K, V = synth.recipe_layer(rng, 1, 4, 12288, sink=3.5, q_scale=0.1)
+    w = pad_cache(synth.Workload("flat12k", q, K, V, 12288, 4, window=64, r=2, J=30, eps=0.1, delta=0.01))
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, w.n_cap // 32)
+    qg, Kg, Vg = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(Kg, Vg)
+    kw = _kw(w)
+    out = _csa().certified_decode_attention(qg, Kg, Vg, packed, w.n, trace=True, **kw)
+    torch.cuda.synchronize()
+    ref = _compare_decode(w, pk_ref, out[:4], out[4], **kw)
+    level0 = [int((r["trace"]["lub"] == 0).sum()) for r in ref]
+    assert max(level0) > 2048, level0
+
+
 def test_stream_read_checksum():
     """The read helper visits every 32-bit word once: per-workgroup XORs match the host's."""
     rng = np.random.default_rng(5)
