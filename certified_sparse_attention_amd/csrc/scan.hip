@@ -204,13 +204,16 @@ __device__ inline float perturbation_upper32(uint64_t prefix, int64_t pos) {
   return (x * 0x1.62e430p-1f) * (1.0f + 0x1p-20f) + 0x1p-30f;
 }
 
-// Constant rows of the A operand: zero everything, then the ones row (14).
-__device__ inline void init_operand(uint8_t *Abuf, int lane) {
+// Constant rows of the A operand: zero everything, then the ones row (14); with
+// `every_group` (groups of at most four queries, which leave rows 4k + 2 and 4k + 3
+// free) also rows 2, 6 and 10, so that every lane group of the result holds the code
+// sums of its tokens.
+__device__ inline void init_operand(uint8_t *Abuf, int lane, bool every_group = false) {
   uint4 *A4 = reinterpret_cast<uint4 *>(Abuf);
   A4[lane] = make_uint4(0, 0, 0, 0);
   A4[64 + lane] = make_uint4(0, 0, 0, 0);
   wave_sync();
-  if ((lane & 15) == 14) {
+  if ((lane & 15) == 14 || (every_group && (lane & 3) == 2)) {
     A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
     A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
   }
@@ -475,7 +478,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     uint4 cw[4];
     uint32_t kk[2];
     float ksmax[2];
-    uint32_t kerr, vn;
+    uint32_t kerr[4];   // key-error codes of the lane's key in each of the chunk's four tiles
+    uint32_t vn;
   };
   // Buffer resources over this wave's blocks only: offsets are a per-lane constant plus
   // a wave-uniform chunk offset, and reads past the wave's blocks or the pool return 0.
@@ -503,7 +507,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, lane * 4, (c0 + bi) * 2 * kD, 0);
       in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, 0, (c0 + bi) * (int)sizeof(BlockMeta), 0));
     }
-    in.kerr = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, lane * 2, c0 * kBlk * 2, 0);
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      in.kerr[T] = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, n16 * 2, (c0 * kBlk + 16 * T) * 2, 0);
     in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, lane * 2, c0 * kBlk * 2, 0);
   };
 
@@ -512,8 +518,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   load_chunk(0, buf0);
   load_chunk(2, buf1);
   load_chunk(4, buf2);
-  init_operand(Abuf, lane);
-  init_operand(Abuf1, lane);
+  init_operand(Abuf, lane, !kTwo);
+  init_operand(Abuf1, lane, !kTwo);
   static_assert(kScanBlocks % 16 == 0, "offset terms are formed 16 blocks at a time");
 #pragma unroll
   for (int col0 = 0; col0 < kScanBlocks; col0 += 16)
@@ -576,9 +582,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, lo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, hi, acc, 0, 0, 0);
         const int tt = 16 * Tg + n16;            // token within chunk
-        const int Csum = bperm_i32(48 + n16, acc[2]);
+        // code sums: every lane group's own ones row for groups of up to four queries
+        const int Csum = kTwo ? bperm_i32(48 + n16, acc[2]) : acc[2];
         const float eup = __int_as_float(bperm_i32(tt, __float_as_int(myEup)));
-        const float kerr = h2f((uint16_t)bperm_i32(tt, (int)cur.kerr));
+        const float kerr = h2f((uint16_t)cur.kerr[Tg]);
         const bool valid = tok0 + tt < a.npool;
         if (hasA) {
           const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
