@@ -614,8 +614,8 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
 struct ExactSmem {
   double qd[kD];
   double w[256];
-  double half[kD];
-  double dsum[4];
+  double half[kD];   // after the call: N[c] of the whole range
+  double dsum[4];    // after the call: dsum[0] = D of the whole range
 };
 
 // Exact attention sums over keys [i0, i1) of query head hq relative to c*: N[c] (out[c])
@@ -646,19 +646,29 @@ __device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0,
   if ((t & 63) == 0) e.dsum[t >> 6] = accD;
   if (hf == 1) e.half[c] = accN;
   __syncthreads();
-  if (t < kD) out[t] = accN + e.half[t];
-  if (t == 0) out[kD] = (e.dsum[0] + e.dsum[1]) + (e.dsum[2] + e.dsum[3]);
+  if (t < kD) {
+    const double N = accN + e.half[t];
+    out[t] = N;
+    e.half[t] = N;
+  }
+  if (t == 0) {
+    const double D = (e.dsum[0] + e.dsum[1]) + (e.dsum[2] + e.dsum[3]);
+    out[kD] = D;
+    e.dsum[0] = D;
+  }
+  __syncthreads();
 }
 
 constexpr int kTailWG = kExactChunks;   // workgroups per query head in the tail
 
 // Everything after pass 1, for the heads pass 1 did not certify; grid (H_q, kTailWG), 256
 // threads.  Heads flagged for the extension pass: workgroup y accumulates segments y,
-// y + kTailWG, ... of the long candidate lists; every flagged head: workgroup y sums the
-// exact attention over the y-th chunk of the keys (for extended heads ahead of knowing
-// whether the extension certifies).  The last workgroup of a head to finish (a counter
-// behind a device-wide fence) runs the extension certificate, and where no level
-// certifies, writes the exact output from the chunks.  Certified heads exit at once.
+// y + kTailWG, ... of the long candidate lists, and the last workgroup of the head to
+// finish (a counter behind a device-wide fence) runs the extension certificate; if no
+// level certifies, that workgroup computes the exact output over all keys by itself.
+// Heads flagged for the exact fallback by pass 1: workgroup y sums the exact attention
+// over the y-th chunk of the keys and the last one combines the chunks.  Certified
+// heads exit at once.
 __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
   const int hq = blockIdx.x, y = blockIdx.y, t = threadIdx.x;
   const int fl = a.flags[hq];
@@ -686,8 +696,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
         __syncthreads();
       }
     }
-  }
-  {
+  } else {
     const int64_t len = (a.n + kTailWG - 1) / kTailWG;
     const int64_t i0 = y * len, i1 = min<int64_t>(a.n, i0 + len);
     exact_chunk(a, u.e, hq, i0, i1, a.exactp + ((int64_t)hq * kExactChunks + y) * 130);
@@ -698,7 +707,13 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
   __syncthreads();
   if (!last) return;
   __threadfence();
-  if (fl == 2 && certify_head(a, u.f, hq)) return;
+  if (fl == 2) {
+    if (certify_head(a, u.f, hq)) return;
+    __syncthreads();
+    exact_chunk(a, u.e, hq, 0, a.n, a.exactp + (int64_t)hq * kExactChunks * 130);
+    if (t < kD) a.o_hat[(int64_t)hq * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);
+    return;
+  }
   if (t < kD) {
     double N = 0.0, Dn = 0.0;
     for (int c = 0; c < kTailWG; ++c) {
