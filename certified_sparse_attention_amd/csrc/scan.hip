@@ -222,30 +222,45 @@ __device__ inline void init_operand(uint8_t *Abuf, int lane, bool every_group = 
 
 // Offset term of up to 16 blocks (block = MFMA column): base = beta kappa sum_t q~ z,
 // eb = (beta/2) kappa sum_t |z|, pad = (2^-40 qabs) Kmax, into cst[0..2][block][g].
-template <int NB>
-__device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int nblk, int G, int lane,
-                                   double (*cst)[NB][8], int col0 = 0) {
+// The packed data the offset terms of blocks col0 .. col0 + 15 read (lane = (block
+// column n16, channel group)): zero-point rows and the block record.
+struct OffsetIn {
+  v4i z1k0, z1k1, z0k0, z0k1;
+  BlockMeta bm;
+};
+
+__device__ inline void offset_load(const ScanArgs &a, int h, int64_t blk0, int nblk, int lane, int col0,
+                                   OffsetIn &in) {
   const int n16 = lane & 15, grp = lane >> 4;
-  const int hq0 = h * G;
-  v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
-  v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
-  v4i z1k0 = {0, 0, 0, 0}, z1k1 = {0, 0, 0, 0}, z0k0 = {0, 0, 0, 0}, z0k1 = {0, 0, 0, 0};
+  in.z1k0 = in.z1k1 = in.z0k0 = in.z0k1 = v4i{0, 0, 0, 0};
+  in.bm = BlockMeta{};
   const int col = col0 + n16;
   if (col < nblk) {
     const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + col) * 256;
-    z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
-    z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
-    z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
-    z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
+    in.z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
+    in.z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
+    in.z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
+    in.z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
+    in.bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + col];
   }
+}
+
+// Offset term of up to 16 blocks (block = MFMA column): base = beta kappa sum_t q~ z,
+// eb = (beta/2) kappa sum_t |z|, pad = (2^-40 qabs) Kmax, into cst[0..2][block][g].
+// qa0/qa1: the group's operand rows; beta/qabs: the lane's two query slots' constants.
+template <int NB>
+__device__ inline void offset_compute(const OffsetIn &in, v4i qa0, v4i qa1, const double *beta,
+                                      const double *qabs, int nblk, int G, int lane, double (*cst)[NB][8],
+                                      int col0) {
+  const int n16 = lane & 15, grp = lane >> 4;
   v4i zero = {0, 0, 0, 0};
-  v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z1k0, zero, 0, 0, 0);
-  r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z1k1, r1, 0, 0, 0);
-  v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, z0k0, zero, 0, 0, 0);
-  r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, z0k1, r0, 0, 0, 0);
+  v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, in.z1k0, zero, 0, 0, 0);
+  r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, in.z1k1, r1, 0, 0, 0);
+  v4i r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, in.z0k0, zero, 0, 0, 0);
+  r0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, in.z0k1, r0, 0, 0, 0);
+  const int col = col0 + n16;
   if (col < nblk) {
-    const BlockMeta bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + col];
-    const double kappa = ldexp(1.0, bm.kexp);
+    const double kappa = ldexp(1.0, in.bm.kexp);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = grp + 4 * s;
@@ -254,15 +269,36 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
         const int hi1 = s ? r1[2] : r1[0], lo1 = s ? r1[3] : r1[1];
         const int hi0 = s ? r0[2] : r0[0], lo0 = s ? r0[3] : r0[1];
         const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
-        const double *qc = a.qconst + (int64_t)(hq0 + g) * kQc;
-        const double beta = qc[QC_BETA];
-        cst[0][col][g] = (beta * kappa) * (double)bint;
-        cst[1][col][g] = ((beta / 2.0) * kappa) * (double)bm.z1sum;
-        cst[2][col][g] = (kPadF * qc[QC_QABS]) * (double)bm.kmax;
+        cst[0][col][g] = (beta[s] * kappa) * (double)bint;
+        cst[1][col][g] = ((beta[s] / 2.0) * kappa) * (double)in.bm.z1sum;
+        cst[2][col][g] = (kPadF * qabs[s]) * (double)in.bm.kmax;
       }
     }
   }
   wave_sync();
+}
+
+// The lane's query-slot constants for the offset terms.
+__device__ inline void offset_consts(const ScanArgs &a, int h, int G, int lane, double *beta, double *qabs) {
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int g = grp + 4 * s;
+    beta[s] = (g < G) ? a.qconst[(int64_t)(h * G + g) * kQc + QC_BETA] : 0.0;
+    qabs[s] = (g < G) ? a.qconst[(int64_t)(h * G + g) * kQc + QC_QABS] : 0.0;
+  }
+}
+
+template <int NB>
+__device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int nblk, int G, int lane,
+                                   double (*cst)[NB][8], int col0 = 0) {
+  const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
+  const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
+  double beta[2], qabs[2];
+  offset_consts(a, h, G, lane, beta, qabs);
+  OffsetIn in;
+  offset_load(a, h, blk0, nblk, lane, col0, in);
+  offset_compute<NB>(in, qa0, qa1, beta, qabs, nblk, G, lane, cst, col0);
 }
 
 // The query group's integer weights of one block, written into the A operand rows.
@@ -513,17 +549,24 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, lane * 2, c0 * kBlk * 2, 0);
   };
 
-  // the first three chunks' loads are in flight while the offset terms are formed
+  // The offset terms of blocks 0..15 are formed before the stream starts and those of
+  // blocks 16..31 during its first chunks; the loads of both and of the first three
+  // chunks are all in flight before the first wait.
+  static_assert(kScanBlocks == 32, "offset terms are formed 16 blocks at a time, in two halves");
+  const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
+  const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
+  double obeta[2], oqabs[2];
+  offset_consts(a, h, G, lane, obeta, oqabs);
+  OffsetIn off0, off1;
+  offset_load(a, h, blk0, nblk, lane, 0, off0);
   ChunkIn buf0, buf1, buf2, buf3;
   load_chunk(0, buf0);
   load_chunk(2, buf1);
   load_chunk(4, buf2);
+  offset_load(a, h, blk0, nblk, lane, 16, off1);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
-  static_assert(kScanBlocks % 16 == 0, "offset terms are formed 16 blocks at a time");
-#pragma unroll
-  for (int col0 = 0; col0 < kScanBlocks; col0 += 16)
-    if (col0 < nblk) offset_terms(a, h, blk0, nblk, G, lane, cst, col0);
+  offset_compute<kScanBlocks>(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 0);
 
   const uint64_t prefix = a.prefix[h];
   float lbA = -__builtin_huge_valf(), lbB = -__builtin_huge_valf();
@@ -614,6 +657,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   };
   // three chunks in flight ahead of the one being computed
   for (int c0 = 0; c0 < nblk; c0 += 8) {
+    if (c0 == 8) offset_compute<kScanBlocks>(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 16);
     load_chunk(c0 + 6, buf3);
     process(c0, buf0);
     if (c0 + 2 >= nblk) break;
