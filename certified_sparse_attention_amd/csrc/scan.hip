@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // The offset terms of blocks 0..15 are formed before the stream starts and those of
   // blocks 16..31 during its first chunks; the loads of both and of the first three
   // chunks are all in flight before the first wait.
-  static_assert(kScanBlocks == 32, "offset terms are formed 16 blocks at a time, in two halves");
+  static_assert(kScanBlocks == 16 || kScanBlocks == 32, "offset terms are formed 16 blocks at a time");
   const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
   const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
   double obeta[2], oqabs[2];
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   load_chunk(0, buf0);
   load_chunk(2, buf1);
   load_chunk(4, buf2);
-  offset_load(a, h, blk0, nblk, lane, 16, off1);
+  if (kScanBlocks > 16) offset_load(a, h, blk0, nblk, lane, 16, off1);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
   offset_compute<kScanBlocks>(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 0);
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   };
   // three chunks in flight ahead of the one being computed
   for (int c0 = 0; c0 < nblk; c0 += 8) {
-    if (c0 == 8) offset_compute<kScanBlocks>(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 16);
+    if (kScanBlocks > 16 && c0 == 8) offset_compute<kScanBlocks>(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 16);
     load_chunk(c0 + 6, buf3);
     process(c0, buf0);
     if (c0 + 2 >= nblk) break;
