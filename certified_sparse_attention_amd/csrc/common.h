@@ -202,12 +202,16 @@ __device__ inline double sumsq_chunk(const uint16_t *row, int k) {
 }
 
 // First level j in [0, J + 1] with lt[j] <= x (J + 1 if none), for the table
-// lt[j] = j lt[1]: an estimate from x / lt[1], then steps to the exact answer.
+// lt[j] = (-j ln 2) / r.  The estimate e = ceil(x / lt[1]) differs from the true
+// threshold x / lt[1] by a few ulps of a number below J + 2, far less than one level,
+// so the answer is e - 1, e or e + 1; both neighbours are read at once and one step
+// (no loop) settles it.
 __device__ inline int level_of(double x, const double *lt, int J, double inv_l1) {
   const double e = ceil(x * inv_l1);
-  int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
-  while (j <= J && lt[j] > x) ++j;
-  while (j > 0 && lt[j - 1] <= x) --j;
+  const int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
+  const double here = lt[min(j, J)], below = lt[max(j - 1, 0)];
+  if (j <= J && here > x) return j + 1;
+  if (j > 0 && below <= x) return j - 1;
   return j;
 }
 

@@ -42,7 +42,7 @@ struct SelectArgs {
   int pass;
 };
 
-// ---- buckets.  A tile is 64 bitmap words (2048 positions); one thread per word.
+// ---- buckets.  A tile is 64 bitmap words (2048 positions).
 // Per tile: cumulative level counts tilehist[tile][j] = |{l^ub <= j}| (j = 0..J+1, the
 // last one counting every pool key of the tile) and the C_max keys per level.
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
@@ -59,37 +59,50 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const double cs = dec_max(a.cstar[hq]);
   const double clo = dec_max(a.clo[hq]);
   const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
-  const int64_t wi = tile * 64 + lane;
-  const int64_t p0 = wi * 32;
-  if (p0 < a.npool) {
-    const int valid = (int)min<int64_t>(32, a.npool - p0);
+  // this lane's bitmap word (tile word `lane`), for the dead count and for the bits the
+  // lanes read below through shuffles
+  const int64_t p_tile = tile * 2048;
+  uint32_t word = 0;
+  int dead = 0;
+  if (p_tile + 32 * lane < a.npool) {
+    const int valid = (int)min<int64_t>(32, a.npool - p_tile - 32 * lane);
     const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-    const uint32_t bits = a.live[(int64_t)hq * a.nwords + wi] & vmask;
-    const int dead = valid - __popc(bits);
-    if (dead) atomicAdd(&hist[a.J + 1], dead);
-    int8_t *lub = a.lub + (int64_t)hq * a.npool_cap + p0;
-    if (a.full_lub)
-      for (int b = 0; b < valid; ++b)
-        if (!((bits >> b) & 1u)) lub[b] = (int8_t)(a.J + 1);
-    if (bits) {
-      // all loads of the word's live keys first, then the levels
-      const double *pb = a.pbuf + (int64_t)hq * a.npool_cap + p0;
-      const double *ubp = a.ubuf + (int64_t)hq * a.npool_cap + p0;
-      double pv[32], uv[32];
+    word = a.live[(int64_t)hq * a.nwords + tile * 64 + lane] & vmask;
+    dead = valid - __popc(word);
+  }
+  if (dead) atomicAdd(&hist[a.J + 1], dead);
+  // positions p_tile + 64 k + lane, k = 0..31: lane reads bit (lane & 31) of tile word
+  // 2k + (lane >> 5), so every load and store of a round covers 64 consecutive keys
+  const bool any = __ballot(word != 0u) != 0ull;
+  if (any || a.full_lub) {
+    const double *pb = a.pbuf + (int64_t)hq * a.npool_cap + p_tile;
+    const double *ubp = a.ubuf + (int64_t)hq * a.npool_cap + p_tile;
+    int8_t *lub = a.lub + (int64_t)hq * a.npool_cap + p_tile;
+    const int64_t left = a.npool - p_tile;
+    uint32_t on = 0;
 #pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        const bool on = ((bits >> b) & 1u) != 0u;
-        pv[b] = on ? pb[b] : 0.0;
-        uv[b] = on ? ubp[b] : 0.0;
-      }
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t wk = (uint32_t)__shfl((int)word, 2 * k + (lane >> 5), 64);
+      on |= ((wk >> (lane & 31)) & 1u) << k;
+    }
+    // all loads of the lane's live keys first, then the levels
+    double pv[32], uv[32];
 #pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        if ((bits >> b) & 1u) {
-          const int l = level_of(pv[b] - cs, lt, a.J, inv_l1);
-          lub[b] = (int8_t)l;
-          atomicAdd(&hist[l], 1);
-          if (uv[b] >= clo) atomicAdd(&cmh[l], 1);
-        }
+    for (int k = 0; k < 32; ++k) {
+      const bool o = ((on >> k) & 1u) != 0u;
+      pv[k] = o ? pb[64 * k + lane] : 0.0;
+      uv[k] = o ? ubp[64 * k + lane] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int i = 64 * k + lane;
+      if ((on >> k) & 1u) {
+        const int l = level_of(pv[k] - cs, lt, a.J, inv_l1);
+        lub[i] = (int8_t)l;
+        atomicAdd(&hist[l], 1);
+        if (uv[k] >= clo) atomicAdd(&cmh[l], 1);
+      } else if (a.full_lub && i < left) {
+        lub[i] = (int8_t)(a.J + 1);
       }
     }
   }
