@@ -76,79 +76,19 @@ struct AccSmem {
   double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
   double lt[kMaxJ + 1];                 // level table (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
-  int hl[kStage], pos[kStage];
-  // the stage in level order (candidate index, level): heavy keys by h; light samples by
-  // entry level l and by h
-  int hIdx[kStage], hLev[kStage], aIdx[kStage], aLev[kStage], rIdx[kStage], rLev[kStage];
-  int nH, nA, nR;
+  alignas(16) int hl[kStage];           // read eight at a time
+  int pos[kStage];
   double w[kStage], vsq[kStage];
 };
-
-// Adds a level-sorted list of staged candidates into s.acc by runs of equal level: column
-// `col` gets sg * (sum of w v[vc]) (heavy) or sg * (sum of v[vc]) (light), and with `scal`
-// columns scol, scol + 1 get sg * (sum of w, sum of w |v|^2) or sg * (count, sum of |v|^2).
-// Eight entries are loaded at a time; each run's row is read and written once.
-// Adds one run into row L: x at column col, and (thread with `scal`) y, z at scol, scol + 1.
-// Every lane reads the scalar pair (the same address) so that one wait covers all reads.
-__device__ inline void flush_run(AccSmem &s, int L, int col, bool scal, int scol, double x, double y,
-                                 double z) {
-  const double a0 = s.acc[L][col];
-  const double a1 = s.acc[L][scol], a2 = s.acc[L][scol + 1];
-  s.acc[L][col] = a0 + x;
-  if (scal) {
-    s.acc[L][scol] = a1 + y;
-    s.acc[L][scol + 1] = a2 + z;
-  }
-}
-
-template <bool kHeavy>
-__device__ inline void level_runs(AccSmem &s, const int *idx, const int *lev, int n, int col, int vc,
-                                  bool scal, int scol, double sg) {
-  double run = 0.0, rb = 0.0, rd = 0.0;
-  int cur = -1;
-  for (int i0 = 0; i0 < n; i0 += 8) {
-    double xa[8], xb[8], xd[8];
-    int L[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = min(i0 + k, n - 1);
-      const int r = idx[i];
-      L[k] = lev[i];
-      const double v = h2d(s.vs[r][vc]);
-      if (kHeavy) {
-        const double w = s.w[r];
-        xa[k] = w * v;
-        xb[k] = w;
-        xd[k] = w * s.vsq[r];
-      } else {
-        xa[k] = v;
-        xb[k] = 1.0;
-        xd[k] = s.vsq[r];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (i0 + k < n) {
-        if (L[k] != cur) {
-          if (cur >= 0) flush_run(s, cur, col, scal, scol, sg * run, sg * rb, sg * rd);
-          run = rb = rd = 0.0;
-          cur = L[k];
-        }
-        run = run + xa[k];
-        rb = rb + xb[k];
-        rd = rd + xd[k];
-      }
-    }
-  }
-  if (cur >= 0) flush_run(s, cur, col, scal, scol, sg * run, sg * rb, sg * rd);
-}
 
 // Add one staged group of candidates (records in s.hl/w/vsq/pos, cnt <= kStage) into
 // s.acc (256 threads).  Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light
 // samples (l < h) add (1, v, |v|^2) at their entry level l and remove it at h, where
-// they turn heavy.  The stage is put in a stable order by level first, so that every
-// column thread sums each level's run in registers (candidate order within a level)
-// and touches the level's row once.  V rows are fetched here unless `staged`.
+// they turn heavy.  Thread t < 128 owns column t of N (thread 0 also D and Q), thread
+// 128 + c column c of the light V sums (thread 128 also k and P); each adds its
+// candidates' terms in candidate order with LDS atomics that return nothing, so no cell
+// is shared between threads and nothing waits on the sums.  V rows are fetched here
+// unless `staged`.
 __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, bool staged) {
   const int t = threadIdx.x, J = a.J;
   if (!staged) {
@@ -161,55 +101,57 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
             reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + pos) * kD)[part];
       }
     }
+    __syncthreads();
   }
-  // stable ranks (wavefront 0, one candidate per lane): by (h, index) over all keys,
-  // by (l, index) and by (h, index) over the light samples
-  if (t < 64) {
-    const bool in = t < cnt;
-    const int me = in ? s.hl[t] : 0;
-    const int mh = me & 0xFF, ml = me >> 8;
-    const bool heavy = in && mh <= J;
-    const bool light = in && ml < mh;          // then l <= J, as l < h <= J + 1
-    const bool exits = light && mh <= J;
-    int rh = 0, ra = 0, rr = 0;
-    for (int u = 0; u < cnt; ++u) {
-      const int o = __builtin_amdgcn_readlane(me, u);
-      const int oh = o & 0xFF, ol = o >> 8;
-      const bool before = u < t;
-      rh += (oh < mh || (oh == mh && before)) ? 1 : 0;
-      if (ol < oh) {
-        ra += (ol < ml || (ol == ml && before)) ? 1 : 0;
-        rr += (oh < mh || (oh == mh && before)) ? 1 : 0;
+  const bool heavy_col = t < kD;
+  const int c = heavy_col ? t : t - kD;
+  const bool scal = c == 0;
+  for (int e0 = 0; e0 < cnt; e0 += 8) {
+    // eight records at once (slots past cnt hold stale values and are not used)
+    const int4 h0 = *reinterpret_cast<const int4 *>(&s.hl[e0]);
+    const int4 h1 = *reinterpret_cast<const int4 *>(&s.hl[e0 + 4]);
+    const int raw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    int hl[8];
+    double v[8], w[8], q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = e0 + k;
+      v[k] = h2d(s.vs[e][c]);
+      w[k] = s.w[e];
+      q[k] = s.vsq[e];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      // the same for every thread: kept in scalar registers, so the tests below are
+      // scalar branches (not a candidate: h = l = 255)
+      hl[k] = (e0 + k < cnt) ? __builtin_amdgcn_readfirstlane(raw[k]) : 0xFFFF;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int hk = hl[k] & 0xFF, lk = hl[k] >> 8;
+      if (heavy_col) {
+        if (hk <= J) {
+          atomicAdd(&s.acc[hk][t], w[k] * v[k]);
+          if (scal) {
+            atomicAdd(&s.acc[hk][2 * kD], w[k]);
+            atomicAdd(&s.acc[hk][2 * kD + 1], w[k] * q[k]);
+          }
+        }
+      } else if (lk < hk) {
+        atomicAdd(&s.acc[lk][t], v[k]);
+        if (scal) {
+          atomicAdd(&s.acc[lk][2 * kD + 2], 1.0);
+          atomicAdd(&s.acc[lk][2 * kD + 3], q[k]);
+        }
+        if (hk <= J) {
+          atomicAdd(&s.acc[hk][t], -v[k]);
+          if (scal) {
+            atomicAdd(&s.acc[hk][2 * kD + 2], -1.0);
+            atomicAdd(&s.acc[hk][2 * kD + 3], -q[k]);
+          }
+        }
       }
     }
-    if (heavy) {
-      s.hIdx[rh] = t;
-      s.hLev[rh] = mh;
-    }
-    if (light) {
-      s.aIdx[ra] = t;
-      s.aLev[ra] = ml;
-    }
-    if (exits) {
-      s.rIdx[rr] = t;
-      s.rLev[rr] = mh;
-    }
-    const unsigned long long bh = __ballot(heavy), bl = __ballot(light), br = __ballot(exits);
-    if (t == 0) {
-      s.nH = __popcll(bh);
-      s.nA = __popcll(bl);
-      s.nR = __popcll(br);
-    }
-  }
-  __syncthreads();
-  if (t < kD) {
-    // heavy: column t of N, and D, Q (thread 0)
-    level_runs<true>(s, s.hIdx, s.hLev, s.nH, t, t, t == 0, 256, 1.0);
-  } else {
-    // light: column t - 128 of V, and k, P (thread 128); entries, then exits
-    const int c = t - kD;
-    level_runs<false>(s, s.aIdx, s.aLev, s.nA, kD + c, c, c == 0, 258, 1.0);
-    level_runs<false>(s, s.rIdx, s.rLev, s.nR, kD + c, c, c == 0, 258, -1.0);
   }
   __syncthreads();
 }

@@ -363,7 +363,7 @@ struct Plan {
 enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, QC_PILOT, kQc = 8 };
 
 constexpr int kBucketTile = 2048;   // positions per bucket tile (64 bitmap words)
-constexpr int kDefaultBudget = 256;  // candidates rescored before the first certificate pass
+constexpr int kDefaultBudget = 32;   // candidates rescored before the first certificate pass
 constexpr int kExactChunks = 8;                    // tail: workgroups (exact chunks) per query head
 constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 for gfx9-family raw loads
 constexpr int kMaxWin = 1024;       // largest window (recent tokens read exactly)

@@ -104,7 +104,7 @@ typedef struct {
   uint64_t seed;   /* perturbation hash inputs ([S] item 1: 53-bit uniform hash) */
   uint64_t step;   /* decode step: fresh perturbations per step ([A]) */
   int32_t layer;
-  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 256);
+  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 32);
                           heads that certify at no level up to that point get a second pass
                           over the remaining levels.  Results do not depend on it. */
 } csa_params;
