@@ -170,10 +170,9 @@ __device__ inline double r1_combine8(double p) {
   p = p + __shfl_xor(p, 4, 64);
   return p;
 }
-// Chunk k of q . k for one fp16 key row (q given as doubles of the chunk).
-__device__ inline double score_chunk(const double *q16, const uint16_t *krow, int k) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(krow) + 2 * k;
-  const uint4 a = src[0], b = src[1];
+// q . k over sixteen fp16 values held in two 16-byte words (q given as doubles), in
+// index order.
+__device__ inline double score_words(const double *q16, uint4 a, uint4 b) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   double acc = q16[0] * h2d((uint16_t)(w[0] & 0xFFFFu));
 #pragma unroll
@@ -182,6 +181,11 @@ __device__ inline double score_chunk(const double *q16, const uint16_t *krow, in
     acc = acc + q16[t] * h2d(hv);
   }
   return acc;
+}
+// Chunk k of q . k for one fp16 key row (q given as doubles of the chunk).
+__device__ inline double score_chunk(const double *q16, const uint16_t *krow, int k) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(krow) + 2 * k;
+  return score_words(q16, src[0], src[1]);
 }
 // |v|^2 of the sixteen fp16 values held in two 16-byte words, in index order.
 __device__ inline double sumsq_words(uint4 a, uint4 b) {

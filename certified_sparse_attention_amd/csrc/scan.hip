@@ -302,22 +302,26 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
 }
 
 // The query group's integer weights of one block, written into the A operand rows.
-// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0.
+// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0.  The
+// power-of-two scale is applied to kscale first (exact, and the product rounds the same
+// way); the split of both channels' weights runs on packed 16-bit integers (|a~| <= 2048).
+typedef short short2v __attribute__((ext_vector_type(2)));
 template <int G>
 __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const float *qv1, uint32_t kk,
                                      float scale, int lane) {
-  const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)), ks1 = h2f((uint16_t)(kk >> 16));
+  const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)) * scale, ks1 = h2f((uint16_t)(kk >> 16)) * scale;
   const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float x0 = (qv0[g] * ks0) * scale, x1 = (qv1[g] * ks1) * scale;
-    const int w0 = (int)rintf(x0), w1 = (int)rintf(x1);
-    const int h0 = (w0 + 64) >> 7, h1 = (w1 + 64) >> 7;
-    const int l0 = w0 - 128 * h0, l1 = w1 - 128 * h1;
-    const uint16_t hp = (uint16_t)((h0 & 0xFF) | ((h1 & 0xFF) << 8));
-    const uint16_t lp = (uint16_t)((l0 & 0xFF) | ((l1 & 0xFF) << 8));
-    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = hp;
-    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = lp;
+    const int w0 = (int)rintf(qv0[g] * ks0), w1 = (int)rintf(qv1[g] * ks1);
+    const short2v w = {(short)w0, (short)w1};
+    const short2v a1 = (w + (short)64) >> (short)7;   // rounded a~ / 128
+    const short2v a0 = w - (a1 << (short)7);           // in [-64, 63]
+    // bytes: a1 of both channels (row part 0), then a0 of both channels (row part 1)
+    const uint32_t pk = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                                              0x06040200u);
+    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = (uint16_t)pk;
+    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = (uint16_t)(pk >> 16);
   }
 }
 
@@ -378,39 +382,74 @@ union ScanSmem {
 // Window work of query head hq (256 threads): exact window scores and c_R, a strided
 // sample of the pool scored exactly (a lower bound on c*), and the window's sums
 // relative to c_R, which the certificate rescales to c*.  All tokens are the window
-// when n <= window.  Scores are wavefront-cooperative: 8 keys per wavefront step.
+// when n <= window.  Scores are wavefront-cooperative: 8 keys per wavefront step.  The
+// workgroup shares the GPU with the streaming scan, so its reads are issued in few
+// batches: the V columns of the first window rows up front, and the key rows of three
+// steps at a time (more would raise the kernel's register count).
+constexpr int kWinVPre = 64;   // window rows whose V columns are read up front
+constexpr int kWinGrp = 3;     // wavefront steps whose rows are read together
 __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int h = hq / a.G;
-  double q16[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
   const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
   const int nw = (int)(a.n - w0);
   const int64_t stride = (w0 + kPilot - 1) / kPilot;
   const int npilot = (w0 > 0) ? kPilot : 0;
-  double m = -__builtin_huge_val(), mp = -__builtin_huge_val();
-  for (int e0 = 0; e0 < nw + npilot; e0 += 32) {
-    const int e = e0 + 8 * wv + s8;                       // the key of this lane's group
-    int64_t pos = -1;
-    if (e < nw) pos = w0 + e;
-    else if (e < nw + npilot && (int64_t)(e - nw) * stride < w0) pos = (int64_t)(e - nw) * stride;
-    double p = 0.0, v = 0.0;
-    if (pos >= 0) {
-      p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
-      if (e < nw && a.V) v = sumsq_chunk(a.V + ((int64_t)h * a.n_cap + pos) * kD, k8);
+  const bool vcols = (t < kD) && a.V != nullptr && nw > 0;
+  const uint16_t *vcol = vcols ? a.V + ((int64_t)h * a.n_cap + w0) * kD + t : nullptr;
+  typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+  ushort2v vpre[kWinVPre / 2];   // two rows per register (half-register loads)
+  if (vcols) {
+#pragma unroll
+    for (int i = 0; i < kWinVPre / 2; ++i) {
+      vpre[i].x = vcol[(int64_t)min(2 * i, nw - 1) * kD];
+      vpre[i].y = vcol[(int64_t)min(2 * i + 1, nw - 1) * kD];
     }
-    const double sc = r1_combine8(p) * kRsqrtD;
-    const double vs = r1_combine8(v);
-    if (pos >= 0 && k8 == 0) {
-      if (e < nw) {
-        a.sR[(int64_t)hq * a.W + e] = sc;
-        sm.sw[e] = sc;
-        sm.vsq[e] = vs;
-        m = fmax(m, sc);
+  }
+  double q16[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  const uint16_t *Kh = a.K + (int64_t)h * a.n_cap * kD;
+  const uint16_t *Vh = a.V ? a.V + (int64_t)h * a.n_cap * kD : nullptr;
+  double m = -__builtin_huge_val(), mp = -__builtin_huge_val();
+  for (int g0 = 0; g0 < nw + npilot; g0 += 32 * kWinGrp) {
+    int64_t pos[kWinGrp];
+    uint4 kw[kWinGrp][2], vw[kWinGrp][2];
+#pragma unroll
+    for (int j = 0; j < kWinGrp; ++j) {
+      const int e = g0 + 32 * j + 8 * wv + s8;             // the key of this lane's group
+      pos[j] = -1;
+      if (e < nw) pos[j] = w0 + e;
+      else if (e < nw + npilot && (int64_t)(e - nw) * stride < w0) pos[j] = (int64_t)(e - nw) * stride;
+      const int64_t row = (pos[j] >= 0) ? pos[j] : 0;       // rows read by keys past the end: unused
+      const uint4 *ks = reinterpret_cast<const uint4 *>(Kh + row * kD) + 2 * k8;
+      kw[j][0] = ks[0];
+      kw[j][1] = ks[1];
+      if (Vh != nullptr && e < nw) {
+        const uint4 *vs = reinterpret_cast<const uint4 *>(Vh + row * kD) + 2 * k8;
+        vw[j][0] = vs[0];
+        vw[j][1] = vs[1];
       } else {
-        mp = fmax(mp, sc);
+        vw[j][0] = vw[j][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kWinGrp; ++j) {
+      const int e = g0 + 32 * j + 8 * wv + s8;
+      const double p = (pos[j] >= 0) ? score_words(q16, kw[j][0], kw[j][1]) : 0.0;
+      const double v = (pos[j] >= 0 && e < nw && Vh != nullptr) ? sumsq_words(vw[j][0], vw[j][1]) : 0.0;
+      const double sc = r1_combine8(p) * kRsqrtD;
+      const double vs = r1_combine8(v);
+      if (pos[j] >= 0 && k8 == 0) {
+        if (e < nw) {
+          a.sR[(int64_t)hq * a.W + e] = sc;
+          sm.sw[e] = sc;
+          sm.vsq[e] = vs;
+          m = fmax(m, sc);
+        } else {
+          mp = fmax(mp, sc);
+        }
       }
     }
   }
@@ -425,9 +464,14 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   double *out = a.win + (int64_t)hq * kWinW;
   if (t < kD) {
     if (a.V) {
-      const uint16_t *vcol = a.V + ((int64_t)h * a.n_cap + w0) * kD + t;
       double acc = 0.0;
       int i = 0;
+      if (vcols) {
+#pragma unroll
+        for (int k = 0; k < kWinVPre; ++k)
+          if (k < nw) acc += sm.sw[k] * h2d((k & 1) ? vpre[k >> 1].y : vpre[k >> 1].x);
+        i = min(nw, kWinVPre);
+      }
       for (; i + 8 <= nw; i += 8) {
         uint16_t v[8];
 #pragma unroll
