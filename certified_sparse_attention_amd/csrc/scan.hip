@@ -850,12 +850,10 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   __syncthreads();
   const uint32_t allm = wchunks[0] | (wchunks[1] << 8) | (wchunks[2] << 16) | (wchunks[3] << 24);
   if (allm == 0u) return;
-  if (chunks) offset_terms(a, h, blk0, nblk, G, lane, cst_all[wv]);
-  init_operand(Abuf, lane);
-  __syncthreads();   // every slot's offset terms are in LDS
 
   // the workgroup's chunks in order, the k-th to wavefront k mod 4 (job bit 8 w + c: chunk
-  // c of slot w); each job's loads are issued before the previous job is processed
+  // c of slot w); each job's loads are issued before the previous job is processed, and
+  // the first job's before the offset terms are formed
   uint32_t jobs = 0;
   {
     uint32_t m = allm;
@@ -865,14 +863,18 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       m ^= bit;
     }
   }
-  const uint64_t prefix = a.prefix[h];
-  double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
-  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
   auto job_blk = [&](int j) { return (wbase + (j >> 3)) * kBlocksPerWave + 2 * (j & 7); };
   auto job_nb2 = [&](int j) { return (int)min<int64_t>(2, a.nb_pool - job_blk(j)); };
   int cc = jobs ? __ffs((int)jobs) - 1 : -1;
   ChunkLoads cur, nxt;
   if (cc >= 0) load_chunk(a, h, job_blk(cc), job_nb2(cc), lane, cur);
+  if (chunks) offset_terms(a, h, blk0, nblk, G, lane, cst_all[wv]);
+  init_operand(Abuf, lane);
+  __syncthreads();   // every slot's offset terms are in LDS
+
+  const uint64_t prefix = a.prefix[h];
+  double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
+  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
 
   while (cc >= 0) {
     jobs &= jobs - 1u;

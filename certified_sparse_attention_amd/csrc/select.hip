@@ -120,39 +120,57 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   }
 }
 
-// Sum over the ntiles tiles of entry `lane` of rows of width w (eight loads at a time).
-__device__ inline int sum_tiles(const int *base, int64_t ntiles, int w, int lane) {
-  int cum = 0;
-  int64_t tl = 0;
-  for (; tl + 8 <= ntiles; tl += 8) {
-    int v[8];
+// Entry `lane` of rows of width w, summed over the ntiles tiles (*all) and over the tiles
+// before `upto` (*before).  Buffer loads keep 64 tiles' loads in flight at a time; the
+// per-lane offset carries the tile, so reads past the last tile are out of the buffer's
+// range and return 0.
+__device__ inline void sum_tiles(const int *base, int64_t ntiles, int w, int lane, int64_t upto, int *all,
+                                 int *before) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)(ntiles * w * 4), kBufDword3);
+  int cum = 0, pre = 0;
+  for (int64_t g0 = 0; g0 < ntiles; g0 += 64) {
+    int v[64];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = base[(tl + k) * w + lane];
+    for (int k = 0; k < 64; ++k)
+      v[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((g0 + k) * w * 4) + lane * 4, 0, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) cum += v[k];
+    for (int k = 0; k < 64; ++k) {
+      cum += v[k];
+      pre += (g0 + k < upto) ? v[k] : 0;
+    }
   }
-  for (; tl < ntiles; ++tl) cum += base[tl * w + lane];
-  return cum;
+  *all = cum;
+  *before = pre;
 }
 
 // Stable compaction of both ranges (l^ub <= jspec first, then jspec < l^ub <= J, each in
 // position order): thread = bitmap word.  Every tile's workgroup sums the head's tile
 // histograms itself (they are small and L2-resident), which gives the level histogram,
 // the speculative level jspec (the deepest level whose cumulative candidate count fits
-// the budget) and the tile's offsets without a separate pass.
+// the budget) and, from the tiles before it, the tile's offsets without a separate pass.
 __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
   const int J = a.J, J2 = J + 2;
   const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
-  // cumulative level histogram of the head (lane = level)
-  int cum = 0;
-  if (lane < J2) cum = sum_tiles(th0, a.ntiles, J2, lane);
+  // this lane's bitmap word and its 32 levels are read together with the histograms (the
+  // levels of keys that are not live are read too, and not used)
+  const int64_t wi = tile * 64 + lane;
+  const int64_t p0 = wi * 32;
+  // unconditional loads at clamped positions; words past the pool are masked out below
+  const uint32_t word = a.live[(int64_t)hq * a.nwords + min(wi, a.nwords - 1)];
+  const uint4 *lw = reinterpret_cast<const uint4 *>(a.lub + (int64_t)hq * a.npool_cap + min(p0, a.npool_cap - 32));
+  const uint4 lv0 = lw[0], lv1 = lw[1];
+  // cumulative level histogram of the head and of the tiles before this one (lane = level)
+  int cum = 0, pre = 0;
+  if (lane < J2) sum_tiles(th0, a.ntiles, J2, lane, tile, &cum, &pre);
   // the levels that fit form a prefix 0..js (cumulative counts only grow); js = -1 when
   // level 0 alone exceeds the budget, and the first pass then has no candidates
   const unsigned long long fit = __ballot(lane <= J && cum <= a.budget);
   const int js = __popcll(fit) - 1;
   const int tot1v = __shfl(cum, max(js, 0), 64), totJ = __shfl(cum, J, 64);
+  const int pre1v = __shfl(pre, max(js, 0), 64), preJ = __shfl(pre, J, 64);
   const int tot1 = (js >= 0) ? tot1v : 0;
   if (tile == 0) {
     const int below = __shfl_up(cum, 1, 64);
@@ -163,46 +181,26 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       a.ccount[hq] = totJ;
     }
     // C_max keys per bucket level
-    if (lane < J2) a.cmhist[(int64_t)hq * J2 + lane] = sum_tiles(a.tilecm + (int64_t)hq * a.ntiles * J2, a.ntiles, J2, lane);
+    if (lane < J2) {
+      int cm = 0, unused = 0;
+      sum_tiles(a.tilecm + (int64_t)hq * a.ntiles * J2, a.ntiles, J2, lane, 0, &cm, &unused);
+      a.cmhist[(int64_t)hq * J2 + lane] = cm;
+    }
   }
   // this tile's offsets: candidates of both ranges in the earlier tiles
-  int b1 = 0, b2 = 0;
-  for (int64_t t0 = 0; t0 < tile; t0 += 64) {
-    const int64_t tl = t0 + lane;
-    int n1 = 0, n2 = 0;
-    if (tl < tile) {
-      const int c1 = (js >= 0) ? th0[tl * J2 + js] : 0, cJ = th0[tl * J2 + J];
-      n1 = c1;
-      n2 = cJ - c1;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      n1 += __shfl_xor(n1, off, 64);
-      n2 += __shfl_xor(n2, off, 64);
-    }
-    b1 += n1;
-    b2 += n2;
-  }
-  const int64_t wi = tile * 64 + lane;
-  const int64_t p0 = wi * 32;
+  const int b1 = (js >= 0) ? pre1v : 0;
+  const int b2 = preJ - b1;
+  const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p0));
+  const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
   uint32_t m1 = 0, m2 = 0;
-  if (p0 < a.npool) {
-    const int valid = (int)min<int64_t>(32, a.npool - p0);
-    const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-    const uint32_t bits = a.live[(int64_t)hq * a.nwords + wi] & vmask;
-    if (bits) {
-      // the word's 32 levels in two 16-byte loads (entries of keys that are not live are
-      // not read as levels)
-      const uint4 *lw = reinterpret_cast<const uint4 *>(a.lub + (int64_t)hq * a.npool_cap + p0);
-      const uint4 lv0 = lw[0], lv1 = lw[1];
-      const uint32_t wds[8] = {lv0.x, lv0.y, lv0.z, lv0.w, lv1.x, lv1.y, lv1.z, lv1.w};
+  if (bits) {
+    const uint32_t wds[8] = {lv0.x, lv0.y, lv0.z, lv0.w, lv1.x, lv1.y, lv1.z, lv1.w};
 #pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        if ((bits >> b) & 1u) {
-          const int l = (int)(int8_t)((wds[b >> 2] >> (8 * (b & 3))) & 0xFFu);
-          if (l <= js) m1 |= 1u << b;
-          else if (l <= J) m2 |= 1u << b;
-        }
+    for (int b = 0; b < 32; ++b) {
+      if ((bits >> b) & 1u) {
+        const int l = (int)(int8_t)((wds[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+        if (l <= js) m1 |= 1u << b;
+        else if (l <= J) m2 |= 1u << b;
       }
     }
   }
