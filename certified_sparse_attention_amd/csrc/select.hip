@@ -50,26 +50,24 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int64_t tile = blockIdx.y;
   __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2];
   __shared__ double lt[kMaxJ + 1];
+  // this lane's bitmap word (tile word `lane`, read at a clamped position and masked
+  // below), c* and c_lo are read together with the level table
+  const int64_t p_tile = tile * 2048;
+  const uint32_t rawword = a.live[(int64_t)hq * a.nwords + min(tile * 64 + lane, a.nwords - 1)];
+  const unsigned long long cs_enc = a.cstar[hq], clo_enc = a.clo[hq];
   for (int j = lane; j < a.J + 2; j += 64) {
     hist[j] = 0;
     cmh[j] = 0;
   }
   for (int j = lane; j <= a.J; j += 64) lt[j] = a.lt[j];
   __syncthreads();
-  const double cs = dec_max(a.cstar[hq]);
-  const double clo = dec_max(a.clo[hq]);
+  const double cs = dec_max(cs_enc);
+  const double clo = dec_max(clo_enc);
   const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
-  // this lane's bitmap word (tile word `lane`), for the dead count and for the bits the
-  // lanes read below through shuffles
-  const int64_t p_tile = tile * 2048;
-  uint32_t word = 0;
-  int dead = 0;
-  if (p_tile + 32 * lane < a.npool) {
-    const int valid = (int)min<int64_t>(32, a.npool - p_tile - 32 * lane);
-    const uint32_t vmask = (valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-    word = a.live[(int64_t)hq * a.nwords + tile * 64 + lane] & vmask;
-    dead = valid - __popc(word);
-  }
+  // the word gives the dead count and the bits the lanes read below through shuffles
+  const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p_tile - 32 * lane));
+  const uint32_t word = rawword & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
+  const int dead = valid - __popc(word);
   if (dead) atomicAdd(&hist[a.J + 1], dead);
   // positions p_tile + 64 k + lane, k = 0..31: lane reads bit (lane & 31) of tile word
   // 2k + (lane >> 5), so every load and store of a round covers 64 consecutive keys
