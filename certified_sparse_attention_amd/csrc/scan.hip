@@ -760,66 +760,77 @@ __device__ inline void load_chunk(const ScanArgs &a, int h, int64_t bA, int nb2,
   }
 }
 
+// Per wave slot: the KV head's values every wavefront of the workgroup needs when it takes
+// one of the slot's chunks.
+struct RefineSlot {
+  float q[kMaxG][kD];              // the group's query values
+  double clo[8], thr[8], qnp[8];   // c_lo snapshot, sampling threshold, |q| pad per query
+  uint64_t prefix;
+  float qmax;
+  int h;
+};
+
 __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
-  // four wave slots of kBlocksPerWave blocks per workgroup; a workgroup never spans two
-  // KV heads (slots past a head's last block have none)
+  // wave slots of kBlocksPerWave blocks, interleaved over the KV heads: global slot s is
+  // local slot s / H_kv of head s % H_kv, so one head's slots fall to different
+  // workgroups and a head with many passing blocks shares them with the others' waves
   const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t wgh = (wph + 3) / 4;
-  const int h = (int)(blockIdx.x / wgh);
-  const int64_t wbase = (int64_t)(blockIdx.x % wgh) * 4;
-  const int64_t blk0 = (wbase + wv) * kBlocksPerWave;
-  const int nblk = (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, a.nb_pool - blk0));
+  const int64_t nslots = (int64_t)a.H_kv * wph;
+  auto slot_head = [&](int w) { return (int)(((int64_t)blockIdx.x * 4 + w) % a.H_kv); };
+  auto slot_blk0 = [&](int w) { return (((int64_t)blockIdx.x * 4 + w) / a.H_kv) * kBlocksPerWave; };
+  const int64_t gs = (int64_t)blockIdx.x * 4 + wv;
+  const int h = slot_head(wv);
+  const int64_t blk0 = slot_blk0(wv);
+  const int nblk = (gs < nslots) ? (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, a.nb_pool - blk0)) : 0;
   const int G = a.G;
   const int n16 = lane & 15, grp = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) uint8_t Abuf_all[4][2 * 1024];
   __shared__ double cst_all[4][3][kBlocksPerWave][8];
-  __shared__ double clo_wg[8];
+  __shared__ RefineSlot slot_all[4];
   __shared__ uint32_t wchunks[4];
   __shared__ uint8_t flag_all[4][64];
   __shared__ int ent_all[4][2 * 4 * 64];
-  __shared__ unsigned long long smx_all[4][8];   // max exact score of C_max candidates per query
   uint8_t *Abuf = Abuf_all[wv];
   uint8_t *flag = flag_all[wv];
   int *ent = ent_all[wv];
-  unsigned long long *smx = smx_all[wv];
+  RefineSlot &me = slot_all[wv];
 
-  // one snapshot of c_lo's running value per query for the whole workgroup, shared by
-  // every test below; the block maxima and the query values are loaded together with it
+  // this slot's values: one snapshot of c_lo's running value per query, shared by every
+  // test of the slot's blocks; the block maxima are loaded together with it
   const int hq0 = h * G;
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = gB < G;
   float2 mxA = make_float2(0.0f, 0.0f), mxB = make_float2(0.0f, 0.0f);
   if (n16 < nblk && hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
   if (n16 < nblk && hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
-  float qv0[kMaxG], qv1[kMaxG];
-#pragma unroll
-  for (int g = 0; g < kMaxG; ++g) {
-    qv0[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
-    qv1[g] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
-  }
-  float qmax = 0.0f;
-  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
-  if (lane < 8) smx[lane] = enc_max(-__builtin_huge_val());
-  if (wv == 0 && lane < G)
-    clo_wg[lane] = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  __syncthreads();
   const double ltJ = a.lt[a.J];
-  double clo2A = 0, clo2B = 0, thrA = 0, thrB = 0, qnpA = 0, qnpB = 0;
-  if (hasA) {
-    const double *qc = a.qconst + (int64_t)(hq0 + gA) * kQc;
-    clo2A = clo_wg[gA];
-    thrA = fmax(clo2A, qc[QC_PILOT]) + ltJ;
-    qnpA = qc[QC_QNP];
+  for (int g = 0; g < G; ++g) {
+    me.q[g][2 * lane] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane];
+    me.q[g][2 * lane + 1] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
   }
-  if (hasB) {
-    const double *qc = a.qconst + (int64_t)(hq0 + gB) * kQc;
-    clo2B = clo_wg[gB];
-    thrB = fmax(clo2B, qc[QC_PILOT]) + ltJ;
-    qnpB = qc[QC_QNP];
+  if (lane < 8) {
+    double clo = 0.0, thr = 0.0, qnp = 0.0;
+    if (lane < G) {
+      const double *qc = a.qconst + (int64_t)(hq0 + lane) * kQc;
+      clo = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      thr = fmax(clo, qc[QC_PILOT]) + ltJ;
+      qnp = qc[QC_QNP];
+    }
+    me.clo[lane] = clo;
+    me.thr[lane] = thr;
+    me.qnp[lane] = qnp;
   }
+  if (lane == 0) {
+    float qm = 0.0f;
+    for (int g = 0; g < G; ++g) qm = fmaxf(qm, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
+    me.qmax = qm;
+    me.prefix = a.prefix[h];
+    me.h = h;
+  }
+  wave_sync();
 
   // blocks whose maxima pass a test (lane = (query slot, block))
   uint32_t alive = 0;
@@ -829,14 +840,14 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     bool pass = false;
     if (n16 < nblk) {
       if (hasA) {
-        const double u = mxA.x, e = mxA.y;
-        pass |= u >= clo2A - 0x1p-30 * (fabs(u) + fabs(clo2A) + 1.0);
-        pass |= e >= thrA - 0x1p-30 * (fabs(e) + fabs(thrA) + 1.0);
+        const double u = mxA.x, e = mxA.y, clo2 = me.clo[gA], thr = me.thr[gA];
+        pass |= u >= clo2 - 0x1p-30 * (fabs(u) + fabs(clo2) + 1.0);
+        pass |= e >= thr - 0x1p-30 * (fabs(e) + fabs(thr) + 1.0);
       }
       if (hasB) {
-        const double u = mxB.x, e = mxB.y;
-        pass |= u >= clo2B - 0x1p-30 * (fabs(u) + fabs(clo2B) + 1.0);
-        pass |= e >= thrB - 0x1p-30 * (fabs(e) + fabs(thrB) + 1.0);
+        const double u = mxB.x, e = mxB.y, clo2 = me.clo[gB], thr = me.thr[gB];
+        pass |= u >= clo2 - 0x1p-30 * (fabs(u) + fabs(clo2) + 1.0);
+        pass |= e >= thr - 0x1p-30 * (fabs(e) + fabs(thr) + 1.0);
       }
     }
     const unsigned long long b = __ballot(pass);
@@ -863,23 +874,34 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       m ^= bit;
     }
   }
-  auto job_blk = [&](int j) { return (wbase + (j >> 3)) * kBlocksPerWave + 2 * (j & 7); };
+  auto job_blk = [&](int j) { return slot_blk0(j >> 3) + 2 * (j & 7); };
   auto job_nb2 = [&](int j) { return (int)min<int64_t>(2, a.nb_pool - job_blk(j)); };
   int cc = jobs ? __ffs((int)jobs) - 1 : -1;
   ChunkLoads cur, nxt;
-  if (cc >= 0) load_chunk(a, h, job_blk(cc), job_nb2(cc), lane, cur);
+  if (cc >= 0) load_chunk(a, slot_head(cc >> 3), job_blk(cc), job_nb2(cc), lane, cur);
   if (chunks) offset_terms(a, h, blk0, nblk, G, lane, cst_all[wv]);
   init_operand(Abuf, lane);
-  __syncthreads();   // every slot's offset terms are in LDS
-
-  const uint64_t prefix = a.prefix[h];
-  double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
-  const int64_t rowA = (int64_t)(hq0 + gA) * a.npool_cap, rowB = (int64_t)(hq0 + gB) * a.npool_cap;
+  __syncthreads();   // every slot's offset terms and values are in LDS
 
   while (cc >= 0) {
     jobs &= jobs - 1u;
     const int cn = jobs ? __ffs((int)jobs) - 1 : -1;
-    if (cn >= 0) load_chunk(a, h, job_blk(cn), job_nb2(cn), lane, nxt);
+    if (cn >= 0) load_chunk(a, slot_head(cn >> 3), job_blk(cn), job_nb2(cn), lane, nxt);
+    // the job's slot: its head's values
+    RefineSlot &S = slot_all[cc >> 3];
+    const int jh = slot_head(cc >> 3), jhq0 = jh * G;
+    float qv0[kMaxG], qv1[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) {
+      qv0[g] = (g < G) ? S.q[g][2 * lane] : 0.0f;
+      qv1[g] = (g < G) ? S.q[g][2 * lane + 1] : 0.0f;
+    }
+    const float qmax = S.qmax;
+    const uint64_t prefix = S.prefix;
+    const double clo2A = hasA ? S.clo[gA] : 0.0, thrA = hasA ? S.thr[gA] : 0.0, qnpA = hasA ? S.qnp[gA] : 0.0;
+    const double clo2B = hasB ? S.clo[gB] : 0.0, thrB = hasB ? S.thr[gB] : 0.0, qnpB = hasB ? S.qnp[gB] : 0.0;
+    const int64_t rowA = (int64_t)(jhq0 + gA) * a.npool_cap, rowB = (int64_t)(jhq0 + gB) * a.npool_cap;
+    double lbA = -__builtin_huge_val(), lbB = -__builtin_huge_val();
     double(*cst)[kBlocksPerWave][8] = cst_all[cc >> 3];
     const int c0 = 2 * (cc & 7);          // first block of the chunk within its slot
     const int64_t bA = job_blk(cc);
@@ -948,7 +970,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubA[Tg] = ub;
             lbA = fmax(lbA, lb);
-            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gA) * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gA) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrA) + 1.0);
             if (ub >= clo2A - marg) cmA |= 1u << Tg;
             if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
@@ -960,7 +982,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubB[Tg] = ub;
             lbB = fmax(lbB, lb);
-            if (a.lb_out) a.lb_out[(int64_t)(hq0 + gB) * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gB) * a.npool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrB) + 1.0);
             if (ub >= clo2B - marg) cmB |= 1u << Tg;
             if (a.diag || ub + Eup >= thrB - marg || ub >= clo2B - marg) liveB |= 1u << Tg;
@@ -1002,11 +1024,13 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         if (pos >= 0) {
           double q16[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(hq0 + g2) * kD + 16 * k8 + i];
-          p = score_chunk(q16, a.K + ((int64_t)h * a.n_cap + pos) * kD, k8);
+          for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(jhq0 + g2) * kD + 16 * k8 + i];
+          p = score_chunk(q16, a.K + ((int64_t)jh * a.n_cap + pos) * kD, k8);
         }
         const double sc = r1_combine8(p) * kRsqrtD;
-        if (pos >= 0 && k8 == 0) atomicMax(&smx[g2], enc_max(sc));
+        // c* = max(c_R, these exact scores)
+        if (pos >= 0 && k8 == 0)
+          __hip_atomic_fetch_max(a.cstar + jhq0 + g2, enc_max(sc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       wave_sync();
     }
@@ -1016,7 +1040,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     if (__ballot((liveA | liveB) != 0)) {
       if (mine && flag[lane]) {
         myE = perturbation(prefix, mypos);
-        if (a.e_out) a.e_out[(int64_t)h * a.npool + mypos] = myE;
+        if (a.e_out) a.e_out[(int64_t)jh * a.npool + mypos] = myE;
       }
     }
     wave_sync();
@@ -1044,35 +1068,28 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         const int64_t blk = bA + (Tg >> 1);
         if (n16 == 0) {
           if (hasA)
-            a.live[(int64_t)(hq0 + gA) * a.nwords + blk] =
+            a.live[(int64_t)(jhq0 + gA) * a.nwords + blk] =
                 (uint32_t)((pA >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mA >> (16 * grp)) & 0xFFFFull) << 16);
           if (hasB)
-            a.live[(int64_t)(hq0 + gB) * a.nwords + blk] =
+            a.live[(int64_t)(jhq0 + gB) * a.nwords + blk] =
                 (uint32_t)((pB >> (16 * grp)) & 0xFFFFull) | ((uint32_t)((mB >> (16 * grp)) & 0xFFFFull) << 16);
         }
       }
     }
+    // exact c_lo: the processed blocks hold every key whose LB can exceed the snapshot
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
+      lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
+    }
+    if (n16 == 0) {
+      if (hasA && lbA > clo2A)
+        __hip_atomic_fetch_max(a.clo + jhq0 + gA, enc_max(lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (hasB && lbB > clo2B)
+        __hip_atomic_fetch_max(a.clo + jhq0 + gB, enc_max(lbB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     cc = cn;
     if (cc >= 0) cur = nxt;
-  }
-  // exact c_lo: the processed blocks hold every key whose LB can exceed the snapshot
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    lbA = fmax(lbA, __shfl_xor(lbA, off, 64));
-    lbB = fmax(lbB, __shfl_xor(lbB, off, 64));
-  }
-  wave_sync();
-  const double smA = hasA ? dec_max(smx[gA]) : -__builtin_huge_val();
-  const double smB = hasB ? dec_max(smx[gB]) : -__builtin_huge_val();
-  if (n16 == 0) {
-    if (hasA && smA > -__builtin_huge_val())
-      __hip_atomic_fetch_max(a.cstar + hq0 + gA, enc_max(smA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hasB && smB > -__builtin_huge_val())
-      __hip_atomic_fetch_max(a.cstar + hq0 + gB, enc_max(smB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hasA && lbA > clo2A)
-      __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max(lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hasB && lbB > clo2B)
-      __hip_atomic_fetch_max(a.clo + hq0 + gB, enc_max(lbB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1101,7 +1118,7 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t st, hipEvent_t ev0 = nullp
 
 hipError_t launch_refine(const ScanArgs &a, hipStream_t st) {
   const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
-  const unsigned wgs = (unsigned)((int64_t)a.H_kv * ((wph + 3) / 4));
+  const unsigned wgs = (unsigned)(((int64_t)a.H_kv * wph + 3) / 4);
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(refine_kernel, dim3(wgs), dim3(256), 0, st, a);
   return hipGetLastError();
