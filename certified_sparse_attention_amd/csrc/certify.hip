@@ -74,7 +74,7 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
 
 struct AccSmem {
   double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
-  double lt[kMaxJ + 1];                 // level table (for rescoring)
+  double2 ltp[kMaxJ + 2];               // level table in neighbour pairs (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   alignas(16) int hl[kStage];           // read eight at a time
   int pos[kStage];
@@ -177,9 +177,9 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
 // workgroup (scores and |v|^2 eight lanes per key, one lane per key for E and the
 // levels), then accumulation.  The records are also stored for a second pass.
 __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
-  const double *lt = s.lt;
+  const double2 *ltp = s.ltp;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
-  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
+  const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
   const double cs = dec_max(a.cstar[hq]);
@@ -219,8 +219,8 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0
       const int pos = s.pos[t];
       const double sc = s.w[t];
       const double E = perturbation(prefix, pos);
-      const int hl = level_of(sc - cs, lt, a.J, inv_l1);
-      const int ll = level_of((sc + E) - cs, lt, a.J, inv_l1);
+      const int hl = level_of_pairs(sc - cs, ltp, a.J, inv_l1);
+      const int ll = level_of_pairs((sc + E) - cs, ltp, a.J, inv_l1);
       const double w = exp(sc - cs);
       const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
       s.hl[t] = hl | (ll << 8);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
   if ((int)blockIdx.y >= nseg) return;
   __shared__ AccSmem s;
   const int J1 = a.J + 1;
-  for (int j = threadIdx.x; j < J1; j += 256) s.lt[j] = a.lt[j];
+  fill_level_pairs(s.ltp, a.lt, a.J, threadIdx.x, 256);
   const int split = record_split(a, hq, count);
   for (int seg = blockIdx.y; seg < nseg; seg += kSegWorkers) {
     seg_range(count, seg, i0, i1, nseg);
@@ -363,10 +363,8 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
   // every load that does not depend on the candidate count is issued before it is used
   const int count = pass_count(a, hq);
   const int jmax = (a.pass == 1) ? a.jspec[hq] : a.J;
-  for (int j = t; j < J1; j += 256) {
-    f.tau[j] = a.tau[j];
-    s.lt[j] = a.lt[j];
-  }
+  for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
+  fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
   for (int j = t; j < a.J + 2; j += 256) {
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
     f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
@@ -627,7 +625,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
     seg_range(count, 0, i0, i1, nseg);
     if (nseg > 0) {
       const int J1 = a.J + 1;
-      for (int j = t; j < J1; j += 256) s.lt[j] = a.lt[j];
+      fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
       const int split = record_split(a, hq, count);
       for (int seg = y; seg < nseg; seg += kTailWG) {
         seg_range(count, seg, i0, i1, nseg);

@@ -208,15 +208,21 @@ __device__ inline double sumsq_chunk(const uint16_t *row, int k) {
 // First level j in [0, J + 1] with lt[j] <= x (J + 1 if none), for the table
 // lt[j] = (-j ln 2) / r.  The estimate e = ceil(x / lt[1]) differs from the true
 // threshold x / lt[1] by a few ulps of a number below J + 2, far less than one level,
-// so the answer is e - 1, e or e + 1; both neighbours are read at once and one step
-// (no loop) settles it.
-__device__ inline int level_of(double x, const double *lt, int J, double inv_l1) {
+// so the answer is e - 1, e or e + 1, settled by one step from the neighbour pair
+// ltp[e] = (lt[e - 1], lt[e]) read at once (ltp[j] for j = 0..J+1, with lt[-1] = +inf
+// and lt[J + 1] = -inf; fill_level_pairs writes that table).
+__device__ inline void fill_level_pairs(double2 *ltp, const double *lt, int J, int t, int nt) {
+  for (int j = t; j <= J + 1; j += nt)
+    ltp[j] = make_double2(j > 0 ? lt[j - 1] : __builtin_huge_val(), j <= J ? lt[j] : -__builtin_huge_val());
+}
+__device__ inline int level_of_pairs(double x, const double2 *ltp, int J, double inv_l1) {
   const double e = ceil(x * inv_l1);
   const int j = !(e > 0.0) ? 0 : (!(e < (double)(J + 1)) ? J + 1 : (int)e);
-  const double here = lt[min(j, J)], below = lt[max(j - 1, 0)];
-  if (j <= J && here > x) return j + 1;
-  if (j > 0 && below <= x) return j - 1;
-  return j;
+  double below = ltp[j].x, here = ltp[j].y;
+  // both values are taken as they are read (so the compiler keeps one read, not a second
+  // one behind a branch)
+  __asm__ volatile("" : "+v"(below), "+v"(here));
+  return (here > x) ? j + 1 : ((below <= x) ? j - 1 : j);
 }
 
 // R1 sum of squares of one fp16 row.

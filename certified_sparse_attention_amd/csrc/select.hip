@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
   __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2];
-  __shared__ double lt[kMaxJ + 1];
+  __shared__ double2 ltp[kMaxJ + 2];
   // this lane's bitmap word (tile word `lane`, read at a clamped position and masked
   // below), c* and c_lo are read together with the level table
   const int64_t p_tile = tile * 2048;
@@ -59,11 +59,11 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     hist[j] = 0;
     cmh[j] = 0;
   }
-  for (int j = lane; j <= a.J; j += 64) lt[j] = a.lt[j];
+  fill_level_pairs(ltp, a.lt, a.J, lane, 64);
   __syncthreads();
   const double cs = dec_max(cs_enc);
   const double clo = dec_max(clo_enc);
-  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
+  const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
   // the word gives the dead count and the bits the lanes read below through shuffles
   const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p_tile - 32 * lane));
   const uint32_t word = rawword & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     for (int k = 0; k < 32; ++k) {
       const int i = 64 * k + lane;
       if ((on >> k) & 1u) {
-        const int l = level_of(pv[k] - cs, lt, a.J, inv_l1);
+        const int l = level_of_pairs(pv[k] - cs, ltp, a.J, inv_l1);
         lub[i] = (int8_t)l;
         atomicAdd(&hist[l], 1);
         if (uv[k] >= clo) atomicAdd(&cmh[l], 1);
@@ -230,11 +230,11 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
   const int hq = blockIdx.x;
   const int h = hq / a.G;
   __shared__ double qd[kD];
-  __shared__ double lt[kMaxJ + 1];
+  __shared__ double2 ltp[kMaxJ + 2];
   if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
-  for (int j = threadIdx.x; j <= a.J; j += 256) lt[j] = a.lt[j];
+  fill_level_pairs(ltp, a.lt, a.J, threadIdx.x, 256);
   __syncthreads();
-  const double inv_l1 = (a.J >= 1) ? 1.0 / lt[1] : 0.0;
+  const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
   int lo, hi;
   if (a.pass == 1) {
     lo = 0;
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
     const int pos = a.candpos[o];
     const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
     const double E = perturbation(prefix, pos);
-    const int hl = level_of(s - cs, lt, a.J, inv_l1);
-    const int ll = level_of((s + E) - cs, lt, a.J, inv_l1);
+    const int hl = level_of_pairs(s - cs, ltp, a.J, inv_l1);
+    const int ll = level_of_pairs((s + E) - cs, ltp, a.J, inv_l1);
     double vsq = 0.0;
     if (ll <= a.J) vsq = row_sumsq(a.V + ((int64_t)h * a.n_cap + pos) * kD);
     a.rec_s[o] = s;
