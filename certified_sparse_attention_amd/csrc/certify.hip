@@ -84,11 +84,11 @@ struct AccSmem {
 // Add one staged group of candidates (records in s.hl/w/vsq/pos, cnt <= kStage) into
 // s.acc (256 threads).  Heavy keys (h <= J) add (w, w v, w |v|^2) at level h; light
 // samples (l < h) add (1, v, |v|^2) at their entry level l and remove it at h, where
-// they turn heavy.  Thread t < 128 owns column t of N (thread 0 also D and Q), thread
-// 128 + c column c of the light V sums (thread 128 also k and P); each adds its
+// they turn heavy.  Thread t < 128 owns column t of N (threads 0, 1 also D, Q), thread
+// 128 + c column c of the light V sums (threads 128, 129 also k, P); each adds its
 // candidates' terms in candidate order with LDS atomics that return nothing, so no cell
-// is shared between threads and nothing waits on the sums.  V rows are fetched here
-// unless `staged`.
+// is shared between threads and nothing waits on the sums.
+// V rows are fetched here unless `staged`.
 __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, bool staged) {
   const int t = threadIdx.x, J = a.J;
   if (!staged) {
@@ -105,7 +105,6 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
   }
   const bool heavy_col = t < kD;
   const int c = heavy_col ? t : t - kD;
-  const bool scal = c == 0;
   for (int e0 = 0; e0 < cnt; e0 += 8) {
     // eight records at once (slots past cnt hold stale values and are not used)
     const int4 h0 = *reinterpret_cast<const int4 *>(&s.hl[e0]);
@@ -132,23 +131,17 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
       if (heavy_col) {
         if (hk <= J) {
           atomicAdd(&s.acc[hk][t], w[k] * v[k]);
-          if (scal) {
-            atomicAdd(&s.acc[hk][2 * kD], w[k]);
-            atomicAdd(&s.acc[hk][2 * kD + 1], w[k] * q[k]);
-          }
+          // D and Q: threads 0 and 1, one instruction
+          if (t < 2) atomicAdd(&s.acc[hk][2 * kD + t], (t == 0) ? w[k] : w[k] * q[k]);
         }
       } else if (lk < hk) {
         atomicAdd(&s.acc[lk][t], v[k]);
-        if (scal) {
-          atomicAdd(&s.acc[lk][2 * kD + 2], 1.0);
-          atomicAdd(&s.acc[lk][2 * kD + 3], q[k]);
-        }
-        if (hk <= J) {
-          atomicAdd(&s.acc[hk][t], -v[k]);
-          if (scal) {
-            atomicAdd(&s.acc[hk][2 * kD + 2], -1.0);
-            atomicAdd(&s.acc[hk][2 * kD + 3], -q[k]);
-          }
+        if (hk <= J) atomicAdd(&s.acc[hk][t], -v[k]);
+        // k and P: threads 128, 129 add (1, |v|^2) at l and remove them at h
+        if (c < 2) {
+          const double x = c ? q[k] : 1.0;
+          atomicAdd(&s.acc[lk][2 * kD + 2 + c], x);
+          if (hk <= J) atomicAdd(&s.acc[hk][2 * kD + 2 + c], -x);
         }
       }
     }
