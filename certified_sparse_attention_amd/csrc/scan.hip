@@ -863,7 +863,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   if (allm == 0u) return;
 
   // the workgroup's chunks in order, the k-th to wavefront k mod 4 (job bit 8 w + c: chunk
-  // c of slot w); each job's loads are issued before the previous job is processed, and
+  // c of slot w); each job's loads are issued while the previous job finishes, and
   // the first job's before the offset terms are formed
   uint32_t jobs = 0;
   {
@@ -886,7 +886,6 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   while (cc >= 0) {
     jobs &= jobs - 1u;
     const int cn = jobs ? __ffs((int)jobs) - 1 : -1;
-    if (cn >= 0) load_chunk(a, slot_head(cn >> 3), job_blk(cn), job_nb2(cn), lane, nxt);
     // the job's slot: its head's values
     RefineSlot &S = slot_all[cc >> 3];
     const int jh = slot_head(cc >> 3), jhq0 = jh * G;
@@ -991,6 +990,10 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         }
       }
     }
+    // the next job's loads go out once this chunk's packed data has been used (vector
+    // stores share the load counter, so loads issued before this job's stores would be
+    // waited for together with them)
+    if (cn >= 0) load_chunk(a, slot_head(cn >> 3), job_blk(cn), job_nb2(cn), lane, nxt);
     // exact scores of C_max candidates: c* = max(c_R, max over them), since a key with
     // UB < c_lo scores below c_lo <= c*.  Every candidate of the chunk (both slots, all
     // tiles) is listed in LDS first, then they are scored eight lanes per key.
