@@ -43,6 +43,7 @@ struct SelectArgs {
 };
 
 // ---- buckets.  A tile is 64 bitmap words (2048 positions).
+constexpr int kDenseTile = 512;   // live keys above which a tile's candidates are written in rounds
 // Per tile: cumulative level counts tilehist[tile][j] = |{l^ub <= j}| (j = 0..J+1, the
 // last one counting every pool key of the tile) and the C_max keys per level.
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
@@ -152,11 +153,12 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int64_t tile = blockIdx.y;
   const int J = a.J, J2 = J + 2;
   const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
-  // this lane's bitmap word and its 32 levels are read together with the histograms (the
-  // levels of keys that are not live are read too, and not used)
+  // this lane's bitmap word (tile word `lane`) and its 32 levels are read together with
+  // the histograms (unconditional reads at clamped positions; words past the pool are
+  // masked out below, and the levels of keys that are not live are not used)
   const int64_t wi = tile * 64 + lane;
   const int64_t p0 = wi * 32;
-  // unconditional loads at clamped positions; words past the pool are masked out below
+  const int64_t p_tile = tile * 2048;
   const uint32_t word = a.live[(int64_t)hq * a.nwords + min(wi, a.nwords - 1)];
   const uint4 *lw = reinterpret_cast<const uint4 *>(a.lub + (int64_t)hq * a.npool_cap + min(p0, a.npool_cap - 32));
   const uint4 lv0 = lw[0], lv1 = lw[1];
@@ -190,6 +192,40 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int b2 = preJ - b1;
   const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p0));
   const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
+  int *dst = a.candpos + (int64_t)hq * a.npool_cap;
+  int tile_live = __popc(bits);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tile_live += __shfl_xor(tile_live, off, 64);
+  if (tile_live > kDenseTile) {
+    // a dense tile (a near-flat head): round k, lane i takes position p_tile + 64 k + i,
+    // whose bit is bit (i & 31) of tile word 2k + (i >> 5); each round's candidates of
+    // either range are consecutive in position order and go out in one store instruction.
+    // The levels are read again in that layout (byte buffer loads, range checked).
+    const __amdgpu_buffer_rsrc_t rs_lub = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.lub + (int64_t)hq * a.npool_cap + p_tile), (short)0,
+        (int)max<int64_t>(0, a.npool_cap - p_tile), kBufDword3);
+    int lv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) lv[k] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs_lub, 64 * k + lane, 0, 0);
+    int o1 = b1, o2 = tot1 + b2;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t wk = (uint32_t)__shfl((int)bits, 2 * k + (lane >> 5), 64);
+      const bool on = ((wk >> (lane & 31)) & 1u) != 0u;
+      const int l = lv[k];
+      const bool in1 = on && l <= js, in2 = on && l > js && l <= J;
+      const unsigned long long m1 = __ballot(in1), m2 = __ballot(in2);
+      const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
+      const int r2 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m2, 0u));
+      const int pos = (int)(p_tile + 64 * k + lane);
+      if (in1) dst[o1 + r1] = pos;
+      if (in2) dst[o2 + r2] = pos;
+      o1 += __popcll(m1);
+      o2 += __popcll(m2);
+    }
+    return;
+  }
+  // a sparse tile: thread = bitmap word, its candidates in bit order after the earlier words'
   uint32_t m1 = 0, m2 = 0;
   if (bits) {
     const uint32_t wds[8] = {lv0.x, lv0.y, lv0.z, lv0.w, lv1.x, lv1.y, lv1.z, lv1.w};
@@ -202,7 +238,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       }
     }
   }
-  int n1 = __popc(m1), n2 = __popc(m2);
+  const int n1 = __popc(m1), n2 = __popc(m2);
   // exclusive prefix over the 64 lanes
   int x1 = n1, x2 = n2;
 #pragma unroll
@@ -212,7 +248,6 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   }
   int o1 = b1 + x1 - n1;
   int o2 = tot1 + b2 + x2 - n2;
-  int *dst = a.candpos + (int64_t)hq * a.npool_cap;
   while (m1) {
     const int b = __ffs(m1) - 1;
     m1 &= m1 - 1u;
