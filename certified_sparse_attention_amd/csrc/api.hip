@@ -158,7 +158,6 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.bdone = at<int>(ws, P.bdone);
   pa.exdone = at<int>(ws, P.exdone);
   pa.npool_cap = P.npool_cap;
-  pa.live = at<uint32_t>(ws, P.live);
   hipError_t e = csa::launch_prep(pa, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const int64_t npool = n - p->window;
@@ -199,7 +198,7 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.nwords = P.npool_cap / 32 + 1;
   sa.J = P.J;
   sa.lt = pa.lt;
-  sa.live = pa.live;
+  sa.live = at<uint32_t>(ws, P.live);
   sa.diag = diag;
   e = csa::launch_scan(sa, st, (hipEvent_t)ev0, (hipEvent_t)ev1);
   if (e != hipSuccess) return hip_fail(e, "scan");

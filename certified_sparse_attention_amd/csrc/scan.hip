@@ -48,7 +48,6 @@ struct PrepArgs {
   unsigned *vmax;
   int *hist, *ccount, *flags;
   int *bdone, *exdone;   // per-head completion counters, cleared here
-  uint32_t *live;     // [H_q][npool_cap / 32 + 1] bitmap, cleared here
 };
 
 // One workgroup of 128 threads per query head; thread t owns channel t.
@@ -129,8 +128,6 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
     a.exdone[hq] = 0;
   }
   for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
-  const int64_t nwords = a.npool_cap / 32 + 1;
-  for (int64_t i = t; i < nwords; i += kD) a.live[(int64_t)hq * nwords + i] = 0u;
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
@@ -767,7 +764,6 @@ struct RefineSlot {
   double clo[8], thr[8], qnp[8];   // c_lo snapshot, sampling threshold, |q| pad per query
   uint64_t prefix;
   float qmax;
-  int h;
 };
 
 __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
@@ -828,7 +824,6 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     for (int g = 0; g < G; ++g) qm = fmaxf(qm, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
     me.qmax = qm;
     me.prefix = a.prefix[h];
-    me.h = h;
   }
   wave_sync();
 
@@ -858,6 +853,12 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   for (int c = 0; 2 * c < nblk; ++c)
     if ((alive >> (2 * c)) & 3u) chunks |= 1u << c;
   if (lane == 0) wchunks[wv] = chunks;
+  // the live words of blocks in chunks that are not processed (the processed ones are
+  // written by their job): every pool block's word is written by this launch
+  if (n16 < nblk && !((chunks >> (n16 >> 1)) & 1u)) {
+    if (hasA) a.live[(int64_t)(hq0 + gA) * a.nwords + blk0 + n16] = 0u;
+    if (hasB) a.live[(int64_t)(hq0 + gB) * a.nwords + blk0 + n16] = 0u;
+  }
   __syncthreads();
   const uint32_t allm = wchunks[0] | (wchunks[1] << 8) | (wchunks[2] << 16) | (wchunks[3] << 24);
   if (allm == 0u) return;
