@@ -274,8 +274,9 @@ __global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
 }
 
 // Root of kl(x, mu) = mu - x + x ln(x / mu) = L above x: Newton from above on the convex
-// increasing branch, stopped when a step no longer decreases mu.  The step is
-// mu - f mu / (mu - x) with f = (mu - x) + x (ln x - ln mu) - L.
+// increasing branch, stopped when a step no longer decreases mu or moves it by at most
+// 2^-44 of itself (every iterate stays above the root, so the bound stays valid).  The
+// step is mu - f mu / (mu - x) with f = (mu - x) + x (ln x - ln mu) - L.
 __device__ inline double kl_upper(double x, double L) {
   if (!(x > 0.0)) return L;
   const double lx = log(x);
@@ -284,7 +285,9 @@ __device__ inline double kl_upper(double x, double L) {
     const double f = (mu - x) + x * (lx - log(mu)) - L;
     const double nx = mu - f * mu / (mu - x);
     if (!(nx < mu)) break;
+    const bool small = mu - nx <= 0x1p-44 * mu;   // converged: the iterate stays above the root
     mu = nx;
+    if (small) break;
   }
   return mu;
 }
@@ -298,7 +301,9 @@ __device__ inline double kl_lower(double x, double L) {
     const double f = (mu - x) + x * (lx - log(mu)) - L;
     const double nx = mu - f * mu / (mu - x);
     if (!(nx > mu) || !(nx < x)) break;
+    const bool small = nx - mu <= 0x1p-44 * mu;   // converged: the iterate stays below the root
     mu = nx;
+    if (small) break;
   }
   return mu;
 }
