@@ -302,6 +302,9 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
 // Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0.  The
 // power-of-two scale is applied to kscale first (exact, and the product rounds the same
 // way); the split of both channels' weights runs on packed 16-bit integers (|a~| <= 2048).
+// rint is the add of 1.5 2^23: for |p| < 2^22 the sum lies in [2^23, 2^24), where the
+// spacing is 1, so it rounds p to the nearest integer, ties to even, and its low 16 bits
+// hold that integer modulo 2^16 (the constant's own low 16 bits are zero).
 typedef short short2v __attribute__((ext_vector_type(2)));
 template <int G>
 __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const float *qv1, uint32_t kk,
@@ -310,8 +313,9 @@ __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const floa
   const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int w0 = (int)rintf(qv0[g] * ks0), w1 = (int)rintf(qv1[g] * ks1);
-    const short2v w = {(short)w0, (short)w1};
+    const float p0 = qv0[g] * ks0, p1 = qv1[g] * ks1;
+    const short2v w = __builtin_bit_cast(
+        short2v, __builtin_amdgcn_perm(__float_as_uint(p1 + 0x1.8p23f), __float_as_uint(p0 + 0x1.8p23f), 0x05040100u));
     const short2v a1 = (w + (short)64) >> (short)7;   // rounded a~ / 128
     const short2v a0 = w - (a1 << (short)7);           // in [-64, 63]
     // bytes: a1 of both channels (row part 0), then a0 of both channels (row part 1)
@@ -502,6 +506,26 @@ __device__ inline int fkey(float v) {
   return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
 __device__ inline float fkey_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+// Maxima over the 16 lanes of each row of two values at once: four DPP steps (swap
+// neighbours, swap pairs, mirror half-rows, mirror rows), each a max with the moved
+// value.  Every source lane lies in the row, so the masks are full and no lane keeps an
+// old value; every lane must be active.  The nops give the two wait states a DPP read
+// needs after a VALU write of its operand.
+__device__ inline void row_max16x2(float &u, float &v) {
+  __asm__("s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
+          : "+v"(u), "+v"(v));
+}
 __device__ inline float row_max16k(float v) {
   int k = fkey(v);
   k = max(k, __builtin_amdgcn_update_dpp(k, k, 0xB1, 0xF, 0xF, false));    // quad_perm 1032
@@ -684,12 +708,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
           lbB = fmaxf(lbB, valid ? r.lb : kNegInf);
         }
       }
-      uA = row_max16k(uA);
-      eA = row_max16k(eA);
-      if (kTwo) {
-        uB = row_max16k(uB);
-        eB = row_max16k(eB);
-      }
+      row_max16x2(uA, eA);
+      if (kTwo) row_max16x2(uB, eB);
       if (n16 == 0) {
         if (hasA) mx[bl][gA] = make_float2(uA, eA);
         if (hasB) mx[bl][gB] = make_float2(uB, eB);
