@@ -299,7 +299,8 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
 }
 
 // The query group's integer weights of one block, written into the A operand rows.
-// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0.  The
+// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0 with
+// a1 = floor(a~ / 128) in [-16, 16] and a0 in [0, 127], both signed bytes.  The
 // power-of-two scale is applied to kscale first (exact, and the product rounds the same
 // way); the split of both channels' weights runs on packed 16-bit integers (|a~| <= 2048).
 // rint is the add of 1.5 2^23: for |p| < 2^22 the sum lies in [2^23, 2^24), where the
@@ -316,8 +317,8 @@ __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const floa
     const float p0 = qv0[g] * ks0, p1 = qv1[g] * ks1;
     const short2v w = __builtin_bit_cast(
         short2v, __builtin_amdgcn_perm(__float_as_uint(p1 + 0x1.8p23f), __float_as_uint(p0 + 0x1.8p23f), 0x05040100u));
-    const short2v a1 = (w + (short)64) >> (short)7;   // rounded a~ / 128
-    const short2v a0 = w - (a1 << (short)7);           // in [-64, 63]
+    const short2v a1 = w >> (short)7;
+    const short2v a0 = w & (short)127;
     // bytes: a1 of both channels (row part 0), then a0 of both channels (row part 1)
     const uint32_t pk = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
                                               0x06040200u);
@@ -368,6 +369,7 @@ constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
 // Shared memory of the streaming kernel; its window workgroups reuse it.
 struct StreamSmem {
   alignas(16) uint8_t Abuf[4][2][2 * 1024];   // per wavefront, one operand per block of a chunk
+  alignas(16) float ep[4][64];                 // per wavefront, E^ of the chunk's keys by (n16, tile)
   double cst[4][3][kScanBlocks][8];
   float2 mx[4][kScanBlocks][8];
 };
@@ -556,6 +558,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   uint8_t *Abuf1 = sm.st.Abuf[wv][1];
   double(*cst)[kScanBlocks][8] = sm.st.cst[wv];
   float2(*mx)[8] = sm.st.mx[wv];
+  float *ep = sm.st.ep[wv];
 
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = kTwo && gB < G;
@@ -641,13 +644,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   auto process = [&](const int c0, const ChunkIn &cur) {
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = (blk0 + c0) * kBlk;
-    const int64_t mypos = tok0 + lane;
-    const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
+    const int nval = (int)min((int64_t)(32 * nb2), a.npool - tok0);   // keys of the chunk in the pool
     float myEup = 0.0f;
-    if (mine) {
-      myEup = perturbation_upper32(prefix, mypos);
+    if (lane < nval) {
+      myEup = perturbation_upper32(prefix, tok0 + lane);
       vmx = max(vmx, cur.vn);
     }
+    // key 16 T + n goes to ep[4 n + T]: a lane reads its token's four tiles at once
+    ep[4 * (lane & 15) + (lane >> 4)] = myEup;
     // both blocks' operands are built before either is read (one wavefront sync per
     // chunk; the next chunk's writes follow these reads in the wavefront's LDS order)
     float alpha32s[2], scales[2];
@@ -667,12 +671,25 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       Aop[bi][0] = *reinterpret_cast<const v4i *>(Ab + lane * 16);
       Aop[bi][1] = *reinterpret_cast<const v4i *>(Ab + 1024 + lane * 16);
     }
+    const float4 eup4 = *reinterpret_cast<const float4 *>(ep + 4 * n16);
+    // all four tiles' products first, so that the matrix operations overlap
+    v4i accs[4];
+#pragma unroll
+    for (int Tg = 0; Tg < 4; ++Tg) {
+      const uint4 w = cur.cw[Tg];
+      v4i lo = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu), (int)(w.z & 0x0F0F0F0Fu),
+                (int)(w.w & 0x0F0F0F0Fu)};
+      v4i hi = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
+                (int)((w.z >> 4) & 0x0F0F0F0Fu), (int)((w.w >> 4) & 0x0F0F0F0Fu)};
+      v4i acc = {0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[Tg >> 1][0], lo, acc, 0, 0, 0);
+      accs[Tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[Tg >> 1][1], hi, acc, 0, 0, 0);
+    }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
       const int bl = c0 + bi;
       const float alpha32 = alpha32s[bi], halpha32 = 0.5f * alpha32s[bi];
-      const v4i A0 = Aop[bi][0], A1 = Aop[bi][1];
       const float baseA = hasA ? (float)cst[0][bl][gA] : 0.0f;
       const float ebpA = hasA ? (float)(cst[1][bl][gA] + cst[2][bl][gA]) : 0.0f;
       const float baseB = hasB ? (float)cst[0][bl][gB] : 0.0f;
@@ -681,30 +698,23 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         const int Tg = 2 * bi + T;
-        const uint4 w = cur.cw[Tg];
-        v4i lo = {(int)(w.x & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu), (int)(w.z & 0x0F0F0F0Fu),
-                  (int)(w.w & 0x0F0F0F0Fu)};
-        v4i hi = {(int)((w.x >> 4) & 0x0F0F0F0Fu), (int)((w.y >> 4) & 0x0F0F0F0Fu),
-                  (int)((w.z >> 4) & 0x0F0F0F0Fu), (int)((w.w >> 4) & 0x0F0F0F0Fu)};
-        v4i acc = {0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, lo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, hi, acc, 0, 0, 0);
+        const v4i acc = accs[Tg];
         const int tt = 16 * Tg + n16;            // token within chunk
         // code sums: every lane group's own ones row for groups of up to four queries
         const int Csum = kTwo ? bperm_i32(48 + n16, acc[2]) : acc[2];
-        const float eup = __int_as_float(bperm_i32(tt, __float_as_int(myEup)));
+        const float eup = Tg == 0 ? eup4.x : (Tg == 1 ? eup4.y : (Tg == 2 ? eup4.z : eup4.w));
         const float kerr = h2f((uint16_t)cur.kerr[Tg]);
-        const bool valid = tok0 + tt < a.npool;
+        const bool valid = tt < nval;
         if (hasA) {
           const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
-          uA = fmaxf(uA, valid ? r.ub : kNegInf);
-          eA = fmaxf(eA, valid ? r.ube : kNegInf);
+          uA = T ? fmaxf(uA, valid ? r.ub : kNegInf) : (valid ? r.ub : kNegInf);
+          eA = T ? fmaxf(eA, valid ? r.ube : kNegInf) : (valid ? r.ube : kNegInf);
           lbA = fmaxf(lbA, valid ? r.lb : kNegInf);
         }
         if (hasB) {
           const Bound32 r = bound32(baseB, ebpB, alpha32, halpha32, qnpB, acc[2] * 128 + acc[3], Csum, kerr, eup);
-          uB = fmaxf(uB, valid ? r.ub : kNegInf);
-          eB = fmaxf(eB, valid ? r.ube : kNegInf);
+          uB = T ? fmaxf(uB, valid ? r.ub : kNegInf) : (valid ? r.ub : kNegInf);
+          eB = T ? fmaxf(eB, valid ? r.ube : kNegInf) : (valid ? r.ube : kNegInf);
           lbB = fmaxf(lbB, valid ? r.lb : kNegInf);
         }
       }
