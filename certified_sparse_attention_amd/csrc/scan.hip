@@ -244,11 +244,11 @@ __device__ inline void offset_load(const ScanArgs &a, int h, int64_t blk0, int n
 
 // Offset term of up to 16 blocks (block = MFMA column): base = beta kappa sum_t q~ z,
 // eb = (beta/2) kappa sum_t |z|, pad = (2^-40 qabs) Kmax, into cst[0..2][block][g].
-// qa0/qa1: the group's operand rows; beta/qabs: the lane's two query slots' constants.
-template <int NB>
+// qa0/qa1: the group's operand rows; beta/qabs: the lane's two query slots' constants;
+// store(col, g, base, eb, pad) keeps the three terms.
+template <typename Store>
 __device__ inline void offset_compute(const OffsetIn &in, v4i qa0, v4i qa1, const double *beta,
-                                      const double *qabs, int nblk, int G, int lane, double (*cst)[NB][8],
-                                      int col0) {
+                                      const double *qabs, int nblk, int G, int lane, Store &&store, int col0) {
   const int n16 = lane & 15, grp = lane >> 4;
   v4i zero = {0, 0, 0, 0};
   v4i r1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, in.z1k0, zero, 0, 0, 0);
@@ -266,9 +266,8 @@ __device__ inline void offset_compute(const OffsetIn &in, v4i qa0, v4i qa1, cons
         const int hi1 = s ? r1[2] : r1[0], lo1 = s ? r1[3] : r1[1];
         const int hi0 = s ? r0[2] : r0[0], lo0 = s ? r0[3] : r0[1];
         const int bint = 16384 * hi1 + 128 * (hi0 + lo1) + lo0;
-        cst[0][col][g] = (beta[s] * kappa) * (double)bint;
-        cst[1][col][g] = ((beta[s] / 2.0) * kappa) * (double)in.bm.z1sum;
-        cst[2][col][g] = (kPadF * qabs[s]) * (double)in.bm.kmax;
+        store(col, g, (beta[s] * kappa) * (double)bint, ((beta[s] / 2.0) * kappa) * (double)in.bm.z1sum,
+              (kPadF * qabs[s]) * (double)in.bm.kmax);
       }
     }
   }
@@ -295,7 +294,14 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
   offset_consts(a, h, G, lane, beta, qabs);
   OffsetIn in;
   offset_load(a, h, blk0, nblk, lane, col0, in);
-  offset_compute<NB>(in, qa0, qa1, beta, qabs, nblk, G, lane, cst, col0);
+  offset_compute(
+      in, qa0, qa1, beta, qabs, nblk, G, lane,
+      [&](int col, int g, double base, double eb, double pad) {
+        cst[0][col][g] = base;
+        cst[1][col][g] = eb;
+        cst[2][col][g] = pad;
+      },
+      col0);
 }
 
 // The query group's integer weights of one block, written into the A operand rows.
@@ -370,7 +376,7 @@ constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
 struct StreamSmem {
   alignas(16) uint8_t Abuf[4][2][2 * 1024];   // per wavefront, one operand per block of a chunk
   alignas(16) float ep[4][64];                 // per wavefront, E^ of the chunk's keys by (n16, tile)
-  double cst[4][3][kScanBlocks][8];
+  float2 cst[4][kScanBlocks][8];                // per block and query: fp32 base, eb + pad
   float2 mx[4][kScanBlocks][8];
 };
 struct WindowSmem {
@@ -556,7 +562,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int n16 = lane & 15, grp = lane >> 4;
   uint8_t *Abuf = sm.st.Abuf[wv][0];
   uint8_t *Abuf1 = sm.st.Abuf[wv][1];
-  double(*cst)[kScanBlocks][8] = sm.st.cst[wv];
+  float2(*cst)[8] = sm.st.cst[wv];
+  auto keep_offsets = [&](int col, int g, double base, double eb, double pad) {
+    cst[col][g] = make_float2((float)base, (float)(eb + pad));
+  };
   float2(*mx)[8] = sm.st.mx[wv];
   float *ep = sm.st.ep[wv];
 
@@ -634,36 +643,55 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   if (kScanBlocks > 16) offset_load(a, h, blk0, nblk, lane, 16, off1);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
-  offset_compute<kScanBlocks>(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 0);
+  offset_compute(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 0);
 
   const uint64_t prefix = a.prefix[h];
   float lbA = -__builtin_huge_valf(), lbB = -__builtin_huge_valf();
   unsigned vmx = 0u;
   constexpr float kNegInf = -__builtin_huge_valf();
 
-  auto process = [&](const int c0, const ChunkIn &cur) {
+  // Staging a chunk: E^ of the lane's key (hash_chunk), then E^ into ep and both blocks'
+  // operands into Abuf, Abuf1 (stage); al gets each block's fp32 grid step.
+  auto hash_chunk = [&](const int c0, const ChunkIn &in) {
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = (blk0 + c0) * kBlk;
-    const int nval = (int)min((int64_t)(32 * nb2), a.npool - tok0);   // keys of the chunk in the pool
+    const int nval = (int)min((int64_t)(32 * nb2), a.npool - tok0);
     float myEup = 0.0f;
     if (lane < nval) {
       myEup = perturbation_upper32(prefix, tok0 + lane);
-      vmx = max(vmx, cur.vn);
+      vmx = max(vmx, in.vn);
     }
+    return myEup;
+  };
+  auto stage = [&](const int c0, const ChunkIn &in, float myEup, float *al) {
+    const int nb2 = min(2, nblk - c0);
     // key 16 T + n goes to ep[4 n + T]: a lane reads its token's four tiles at once
     ep[4 * (lane & 15) + (lane >> 4)] = myEup;
-    // both blocks' operands are built before either is read (one wavefront sync per
-    // chunk; the next chunk's writes follow these reads in the wavefront's LDS order)
-    float alpha32s[2], scales[2];
+    float scales[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       double alpha;
-      block_grid(qmax, cur.ksmax[bi], alpha, scales[bi]);
-      alpha32s[bi] = (float)alpha;
+      block_grid(qmax, in.ksmax[bi], alpha, scales[bi]);
+      al[bi] = (float)alpha;
     }
-    build_operand<G>(Abuf, qv0, qv1, cur.kk[0], scales[0], lane);
-    if (nb2 > 1) build_operand<G>(Abuf1, qv0, qv1, cur.kk[1], scales[1], lane);
+    build_operand<G>(Abuf, qv0, qv1, in.kk[0], scales[0], lane);
+    if (nb2 > 1) build_operand<G>(Abuf1, qv0, qv1, in.kk[1], scales[1], lane);
+  };
+  // process(c0, cur, nxt): bounds of the chunk staged before, with the next chunk hashed
+  // while the operand reads are in flight and staged while the products run.  The
+  // wavefront's LDS operations run in order, so the reads see the staged chunk and the
+  // next chunk's writes leave them be; the syncs only keep the compiler from moving LDS
+  // accesses (and the writes before the products) across them.
+  auto process = [&](const int c0, const ChunkIn &cur, const ChunkIn &nxt, const float *alpha32s, float *alnext) {
+    const int nb2 = min(2, nblk - c0);
+    const int nval = (int)min((int64_t)(32 * nb2), a.npool - (blk0 + c0) * kBlk);
     wave_sync();
+    float2 cA[2], cB[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      cA[bi] = hasA ? cst[c0 + bi][gA] : make_float2(0.0f, 0.0f);
+      cB[bi] = hasB ? cst[c0 + bi][gB] : make_float2(0.0f, 0.0f);
+    }
     v4i Aop[2][2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
@@ -672,6 +700,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       Aop[bi][1] = *reinterpret_cast<const v4i *>(Ab + 1024 + lane * 16);
     }
     const float4 eup4 = *reinterpret_cast<const float4 *>(ep + 4 * n16);
+    wave_sync();
+    const bool more = c0 + 2 < nblk;
+    const float eupN = more ? hash_chunk(c0 + 2, nxt) : 0.0f;
     // all four tiles' products first, so that the matrix operations overlap
     v4i accs[4];
 #pragma unroll
@@ -685,15 +716,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[Tg >> 1][0], lo, acc, 0, 0, 0);
       accs[Tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[Tg >> 1][1], hi, acc, 0, 0, 0);
     }
+    wave_sync();
+    if (more) stage(c0 + 2, nxt, eupN, alnext);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
       const int bl = c0 + bi;
       const float alpha32 = alpha32s[bi], halpha32 = 0.5f * alpha32s[bi];
-      const float baseA = hasA ? (float)cst[0][bl][gA] : 0.0f;
-      const float ebpA = hasA ? (float)(cst[1][bl][gA] + cst[2][bl][gA]) : 0.0f;
-      const float baseB = hasB ? (float)cst[0][bl][gB] : 0.0f;
-      const float ebpB = hasB ? (float)(cst[1][bl][gB] + cst[2][bl][gB]) : 0.0f;
+      const float baseA = cA[bi].x, ebpA = cA[bi].y, baseB = cB[bi].x, ebpB = cB[bi].y;
       float uA = kNegInf, eA = kNegInf, uB = kNegInf, eB = kNegInf;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
@@ -726,20 +756,22 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
     }
   };
-  // three chunks in flight ahead of the one being computed
+  // three chunks in flight ahead of the one being computed, which has been staged
+  float alA[2], alB[2];
+  stage(0, buf0, hash_chunk(0, buf0), alA);
   for (int c0 = 0; c0 < nblk; c0 += 8) {
-    if (kScanBlocks > 16 && c0 == 8) offset_compute<kScanBlocks>(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, cst, 16);
+    if (kScanBlocks > 16 && c0 == 8) offset_compute(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 16);
     load_chunk(c0 + 6, buf3);
-    process(c0, buf0);
+    process(c0, buf0, buf1, alA, alB);
     if (c0 + 2 >= nblk) break;
     load_chunk(c0 + 8, buf0);
-    process(c0 + 2, buf1);
+    process(c0 + 2, buf1, buf2, alB, alA);
     if (c0 + 4 >= nblk) break;
     load_chunk(c0 + 10, buf1);
-    process(c0 + 4, buf2);
+    process(c0 + 4, buf2, buf3, alA, alB);
     if (c0 + 6 >= nblk) break;
     load_chunk(c0 + 12, buf2);
-    process(c0 + 6, buf3);
+    process(c0 + 6, buf3, buf0, alB, alA);
   }
   wave_sync();
   // per-block maxima of the wave: [query][block] rows of float2
