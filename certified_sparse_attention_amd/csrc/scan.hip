@@ -371,6 +371,7 @@ __device__ inline Bound32 bound32(float base, float ebpad, float alpha, float ha
 
 constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
 constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
+constexpr int kScanBufs = 4;     // streaming scan: chunk buffers (chunks in flight + 1)
 
 // Shared memory of the streaming kernel; its window workgroups reuse it.
 struct StreamSmem {
@@ -591,11 +592,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     uint4 cw[4];
     uint32_t kk[2];
     float ksmax[2];
-    uint32_t kerr[4];   // key-error codes of the lane's key in each of the chunk's four tiles
-    uint32_t vn;
+    uint16_t kerr[4];   // key-error codes of the lane's key in each of the chunk's four tiles
+    uint16_t vn;
   };
-  // Buffer resources over this wave's blocks only: offsets are a per-lane constant plus
-  // a wave-uniform chunk offset, and reads past the wave's blocks or the pool return 0.
+  // Buffer resources over this wave's blocks only.  The chunk offset goes into the
+  // per-lane offset, which the hardware range checks (the scalar offset is not), so the
+  // reads of chunks past the wave's blocks or the pool return 0 and touch no memory.
   const int64_t tokw = min((int64_t)nblk * kBlk, a.npool - blk0 * kBlk);
   const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.codes + ((int64_t)h * a.nb_cap + blk0) * 2048), (short)0, nblk * 2048, kBufDword3);
@@ -608,27 +610,28 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const __amdgpu_buffer_rsrc_t rs_vn = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.vnorm + (int64_t)h * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
   auto load_chunk = [&](int c0, ChunkIn &in) {
-    c0 = __builtin_amdgcn_readfirstlane(c0);   // wave-uniform: offsets stay in SGPRs
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const int oc = c0 * 2048 + lane * 16, ok = c0 * 2 * kD + lane * 4, om = c0 * (int)sizeof(BlockMeta);
+    const int oe = c0 * kBlk * 2 + n16 * 2, ov = c0 * kBlk * 2 + lane * 2;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs_codes, lane * 16, c0 * 2048 + T * 1024, 0);
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs_codes, oc + T * 1024, 0, 0);
       in.cw[T] = make_uint4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
-      in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, lane * 4, (c0 + bi) * 2 * kD, 0);
-      in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, 0, (c0 + bi) * (int)sizeof(BlockMeta), 0));
+      in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, ok + bi * 2 * kD, 0, 0);
+      in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, om + bi * (int)sizeof(BlockMeta), 0, 0));
     }
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
-      in.kerr[T] = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, n16 * 2, (c0 * kBlk + 16 * T) * 2, 0);
-    in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, lane * 2, c0 * kBlk * 2, 0);
+    for (int T = 0; T < 4; ++T) in.kerr[T] = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, oe + 32 * T, 0, 0);
+    in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, ov, 0, 0);
   };
 
   // The offset terms of blocks 0..15 are formed before the stream starts and those of
-  // blocks 16..31 during its first chunks; the loads of both and of the first three
-  // chunks are all in flight before the first wait.
+  // blocks 16..31 during its first chunks; the loads of the first half and of the first
+  // chunks are in flight together before the first wait, those of the second half are
+  // issued once the first chunk is done.
   static_assert(kScanBlocks == 16 || kScanBlocks == 32, "offset terms are formed 16 blocks at a time");
   const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
   const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
@@ -636,11 +639,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   offset_consts(a, h, G, lane, obeta, oqabs);
   OffsetIn off0, off1;
   offset_load(a, h, blk0, nblk, lane, 0, off0);
-  ChunkIn buf0, buf1, buf2, buf3;
-  load_chunk(0, buf0);
-  load_chunk(2, buf1);
-  load_chunk(4, buf2);
-  if (kScanBlocks > 16) offset_load(a, h, blk0, nblk, lane, 16, off1);
+  ChunkIn buf[kScanBufs];
+#pragma unroll
+  for (int k = 0; k + 1 < kScanBufs; ++k) load_chunk(2 * k, buf[k]);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
   offset_compute(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 0);
@@ -756,22 +757,21 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
     }
   };
-  // three chunks in flight ahead of the one being computed, which has been staged
-  float alA[2], alB[2];
-  stage(0, buf0, hash_chunk(0, buf0), alA);
-  for (int c0 = 0; c0 < nblk; c0 += 8) {
-    if (kScanBlocks > 16 && c0 == 8) offset_compute(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 16);
-    load_chunk(c0 + 6, buf3);
-    process(c0, buf0, buf1, alA, alB);
-    if (c0 + 2 >= nblk) break;
-    load_chunk(c0 + 8, buf0);
-    process(c0 + 2, buf1, buf2, alB, alA);
-    if (c0 + 4 >= nblk) break;
-    load_chunk(c0 + 10, buf1);
-    process(c0 + 4, buf2, buf3, alA, alB);
-    if (c0 + 6 >= nblk) break;
-    load_chunk(c0 + 12, buf2);
-    process(c0 + 6, buf3, buf0, alB, alA);
+  // kScanBufs - 1 chunks in flight ahead of the one being computed, which has been staged
+  float alCur[2], alNext[2];
+  stage(0, buf[0], hash_chunk(0, buf[0]), alCur);
+  for (int c0 = 0; c0 < nblk; c0 += 2 * kScanBufs) {
+#pragma unroll
+    for (int k = 0; k < kScanBufs; ++k) {
+      const int c = c0 + 2 * k;
+      if (c >= nblk) break;
+      if (kScanBlocks > 16 && c == 8) offset_compute(off1, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 16);
+      load_chunk(c + 2 * (kScanBufs - 1), buf[(k + kScanBufs - 1) % kScanBufs]);
+      process(c, buf[k], buf[(k + 1) % kScanBufs], alCur, alNext);
+      alCur[0] = alNext[0];
+      alCur[1] = alNext[1];
+      if (kScanBlocks > 16 && c == 0) offset_load(a, h, blk0, nblk, lane, 16, off1);
+    }
   }
   wave_sync();
   // per-block maxima of the wave: [query][block] rows of float2
