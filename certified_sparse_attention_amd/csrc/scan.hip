@@ -311,7 +311,9 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int 
 // way); the split of both channels' weights runs on packed 16-bit integers (|a~| <= 2048).
 // rint is the add of 1.5 2^23: for |p| < 2^22 the sum lies in [2^23, 2^24), where the
 // spacing is 1, so it rounds p to the nearest integer, ties to even, and its low 16 bits
-// hold that integer modulo 2^16 (the constant's own low 16 bits are zero).
+// hold that integer modulo 2^16 (the constant's own low 16 bits are zero).  The product
+// q kscale 2^(11 - x) of two fp16 values and a power of two is exact in fp32, so one
+// fused multiply-add gives the same sum as the product followed by the add.
 typedef short short2v __attribute__((ext_vector_type(2)));
 template <int G>
 __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const float *qv1, uint32_t kk,
@@ -320,9 +322,8 @@ __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const floa
   const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float p0 = qv0[g] * ks0, p1 = qv1[g] * ks1;
-    const short2v w = __builtin_bit_cast(
-        short2v, __builtin_amdgcn_perm(__float_as_uint(p1 + 0x1.8p23f), __float_as_uint(p0 + 0x1.8p23f), 0x05040100u));
+    const float t0 = __builtin_fmaf(qv0[g], ks0, 0x1.8p23f), t1 = __builtin_fmaf(qv1[g], ks1, 0x1.8p23f);
+    const short2v w = __builtin_bit_cast(short2v, __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u));
     const short2v a1 = w >> (short)7;
     const short2v a0 = w & (short)127;
     // bytes: a1 of both channels (row part 0), then a0 of both channels (row part 1)
@@ -377,6 +378,7 @@ constexpr int kScanBufs = 4;     // streaming scan: chunk buffers (chunks in fli
 struct StreamSmem {
   alignas(16) uint8_t Abuf[4][2][2 * 1024];   // per wavefront, one operand per block of a chunk
   alignas(16) float ep[4][64];                 // per wavefront, E^ of the chunk's keys by (n16, tile)
+  alignas(16) float ek[4][64];                 // per wavefront, key-error bounds of the chunk's keys, same order
   float2 cst[4][kScanBlocks][8];                // per block and query: fp32 base, eb + pad
   float2 mx[4][kScanBlocks][8];
 };
@@ -569,6 +571,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   };
   float2(*mx)[8] = sm.st.mx[wv];
   float *ep = sm.st.ep[wv];
+  float *ek = sm.st.ek[wv];
 
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = kTwo && gB < G;
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     uint4 cw[4];
     uint32_t kk[2];
     float ksmax[2];
-    uint16_t kerr[4];   // key-error codes of the lane's key in each of the chunk's four tiles
+    uint16_t kerr;      // key-error code of the chunk's key `lane`
     uint16_t vn;
   };
   // Buffer resources over this wave's blocks only.  The chunk offset goes into the
@@ -612,7 +615,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   auto load_chunk = [&](int c0, ChunkIn &in) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const int oc = c0 * 2048 + lane * 16, ok = c0 * 2 * kD + lane * 4, om = c0 * (int)sizeof(BlockMeta);
-    const int oe = c0 * kBlk * 2 + n16 * 2, ov = c0 * kBlk * 2 + lane * 2;
+    const int ov = c0 * kBlk * 2 + lane * 2;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs_codes, oc + T * 1024, 0, 0);
@@ -623,8 +626,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, ok + bi * 2 * kD, 0, 0);
       in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, om + bi * (int)sizeof(BlockMeta), 0, 0));
     }
-#pragma unroll
-    for (int T = 0; T < 4; ++T) in.kerr[T] = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, oe + 32 * T, 0, 0);
+    in.kerr = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, ov, 0, 0);
     in.vn = __builtin_amdgcn_raw_buffer_load_b16(rs_vn, ov, 0, 0);
   };
 
@@ -668,6 +670,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const int nb2 = min(2, nblk - c0);
     // key 16 T + n goes to ep[4 n + T]: a lane reads its token's four tiles at once
     ep[4 * (lane & 15) + (lane >> 4)] = myEup;
+    ek[4 * (lane & 15) + (lane >> 4)] = h2f(in.kerr);
     float scales[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
@@ -701,6 +704,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       Aop[bi][1] = *reinterpret_cast<const v4i *>(Ab + 1024 + lane * 16);
     }
     const float4 eup4 = *reinterpret_cast<const float4 *>(ep + 4 * n16);
+    const float4 kerr4 = *reinterpret_cast<const float4 *>(ek + 4 * n16);
     wave_sync();
     const bool more = c0 + 2 < nblk;
     const float eupN = more ? hash_chunk(c0 + 2, nxt) : 0.0f;
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         // code sums: every lane group's own ones row for groups of up to four queries
         const int Csum = kTwo ? bperm_i32(48 + n16, acc[2]) : acc[2];
         const float eup = Tg == 0 ? eup4.x : (Tg == 1 ? eup4.y : (Tg == 2 ? eup4.z : eup4.w));
-        const float kerr = h2f((uint16_t)cur.kerr[Tg]);
+        const float kerr = Tg == 0 ? kerr4.x : (Tg == 1 ? kerr4.y : (Tg == 2 ? kerr4.z : kerr4.w));
         const bool valid = tt < nval;
         if (hasA) {
           const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
