@@ -372,7 +372,7 @@ __device__ inline Bound32 bound32(float base, float ebpad, float alpha, float ha
 
 constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
 constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
-constexpr int kScanBufs = 4;     // streaming scan: chunk buffers (chunks in flight + 1)
+constexpr int kScanBufs = 3;     // streaming scan: chunk buffers (chunks in flight + 1)
 
 // Shared memory of the streaming kernel; its window workgroups reuse it.
 struct StreamSmem {
