@@ -588,9 +588,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     qv1[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
   }
 
-  // Software pipeline: the loads of chunks c + 1 .. c + 3 (two blocks each) are in
-  // flight while chunk c is computed.  The loads are unconditional and the loop issues
-  // no global stores or atomics, so the compiler can wait for exactly the older loads.
+  // Software pipeline: the loads of chunks c + 1 .. c + kScanBufs - 1 (two blocks each)
+  // are in flight while chunk c is computed.  The loads are unconditional and the loop
+  // issues no global stores or atomics, so the compiler can wait for the older loads only.
   struct ChunkIn {
     uint4 cw[4];
     uint32_t kk[2];
