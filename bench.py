@@ -110,8 +110,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU form in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the certified decode "
+              "path has no multi-GPU form", file=sys.stderr)
         sys.exit(2)
     import torch
     import certified_sparse_attention_amd as csa
