@@ -13,8 +13,7 @@ Sources, cited by page and section (no other citation style is used here):
 * [A]  "Certified Sparse Attention via Perturbed Retrieval", the authors'
   abstract (GQA-shared 4-bit scan, fresh perturbations per step).
 
-Where the pages leave a step open, the reading taken is stated where it is used
-and listed in the design doc's register of readings.
+Where the pages leave a step open, the reading taken is stated where it is used.
 
 Pinned against something other than itself in ``tests/test_oracle_*.py``:
 dense attention (library softmax), pack (exact rational residual norms), score
