@@ -90,23 +90,13 @@ def kl_lower_root(x, L):
     return np.where(x > 0, lo, 0.0)
 
 
-def level_certificate(*, D_det, N_det, Q_det, k, Vs, Ps, tau, L, Vmax, measure=MEASURE_VALUE):
-    """Certificate at one level from the deterministic and sampled sums.
-
-    D_det, Q_det, Ps scalars; N_det, Vs vectors [128]; k the light-sample count.
-    """
+def _root_inputs(D_det, N_det, k, Vs, Ps, Vmax, measure):
+    """What the level's four KL roots are taken of: the light-sample count k (denominator
+    interval), y (variance proxy) and P / Vmax^2 (lower bound on Q)."""
     k = float(k)
-    D_hat = D_det + tau * k
-    N_hat = N_det + tau * Vs
-    o_hat = N_hat / D_hat
-    mu_hi = float(kl_upper_root(k, L)[0])
-    mu_lo = float(kl_lower_root(k, L)[0])
-    dD = tau * max(k - mu_lo, mu_hi - k)
-    D_hi = D_det + tau * mu_hi
-    out = {"D_hat": D_hat, "N_hat": N_hat, "o_hat": o_hat, "dD": dD, "mu_hi": mu_hi, "mu_lo": mu_lo}
+    pre = {"k": k}
     if measure == MEASURE_DENOM:
-        out["beta"] = dD / (D_hat - dD) if D_hat > dD else math.inf
-        return out
+        return pre
     c = N_det / D_det
     cn = float(np.sqrt(c @ c))
     Rc = Vmax + cn
@@ -114,7 +104,27 @@ def level_certificate(*, D_det, N_det, Q_det, k, Vs, Ps, tau, L, Vmax, measure=M
         y = max((Ps - 2.0 * float(c @ Vs) + k * cn * cn) / (Rc * Rc), 0.0)
     else:
         y = 0.0
-    mu_G = float(kl_upper_root(y, L)[0])
+    pre.update({"c": c, "Rc": Rc, "y": y})
+    if measure == MEASURE_VALUE:
+        pre["yq"] = Ps / (Vmax * Vmax) if Vmax > 0 else 0.0
+    return pre
+
+
+def _certificate_from_roots(*, D_det, N_det, Q_det, Vs, tau, L, Vmax, measure, pre, roots):
+    """The level's bound once its roots are known (the arithmetic of one level)."""
+    k = pre["k"]
+    D_hat = D_det + tau * k
+    N_hat = N_det + tau * Vs
+    o_hat = N_hat / D_hat
+    mu_hi, mu_lo = roots["mu_hi"], roots["mu_lo"]
+    dD = tau * max(k - mu_lo, mu_hi - k)
+    D_hi = D_det + tau * mu_hi
+    out = {"D_hat": D_hat, "N_hat": N_hat, "o_hat": o_hat, "dD": dD, "mu_hi": mu_hi, "mu_lo": mu_lo}
+    if measure == MEASURE_DENOM:
+        out["beta"] = dD / (D_hat - dD) if D_hat > dD else math.inf
+        return out
+    c, Rc, y = pre["c"], pre["Rc"], pre["y"]
+    mu_G = roots["mu_G"]
     sigma2 = tau * tau * Rc * Rc * mu_G
     b = tau * Rc
     zeta = math.sqrt(2.0 * sigma2 * L) + (2.0 / 3.0) * b * L
@@ -126,10 +136,42 @@ def level_certificate(*, D_det, N_det, Q_det, k, Vs, Ps, tau, L, Vmax, measure=M
     if measure == MEASURE_OUTNORM:
         out["beta"] = beta_abs / (on - beta_abs) if on > beta_abs else math.inf
         return out
-    yq = Ps / (Vmax * Vmax) if Vmax > 0 else 0.0
-    mu_Q = float(kl_lower_root(yq, L)[0])
+    mu_Q = roots["mu_Q"]
     Q_lo = Q_det + tau * Vmax * Vmax * mu_Q
     M_lo = max(on - beta_abs, math.sqrt(Q_lo / D_hi))
     out.update({"mu_Q": mu_Q, "Q_lo": Q_lo, "M_lo": M_lo})
     out["beta"] = beta_abs / M_lo if (M_lo > 0 and math.isfinite(beta_abs)) else math.inf
     return out
+
+
+def _roots(pres, L, measure):
+    """The KL roots of several levels at once (the bisections run elementwise, so each
+    level's roots are the same as when it is solved alone)."""
+    k = np.array([p["k"] for p in pres], dtype=np.float64)
+    cols = {"mu_hi": kl_upper_root(k, L), "mu_lo": kl_lower_root(k, L)}
+    if measure != MEASURE_DENOM:
+        cols["mu_G"] = kl_upper_root(np.array([p["y"] for p in pres], dtype=np.float64), L)
+    if measure == MEASURE_VALUE:
+        cols["mu_Q"] = kl_lower_root(np.array([p["yq"] for p in pres], dtype=np.float64), L)
+    return [{name: float(v[i]) for name, v in cols.items()} for i in range(len(pres))]
+
+
+def level_certificate(*, D_det, N_det, Q_det, k, Vs, Ps, tau, L, Vmax, measure=MEASURE_VALUE):
+    """Certificate at one level from the deterministic and sampled sums.
+
+    D_det, Q_det, Ps scalars; N_det, Vs vectors [128]; k the light-sample count.
+    """
+    pre = _root_inputs(D_det, N_det, k, Vs, Ps, Vmax, measure)
+    roots = _roots([pre], L, measure)[0]
+    return _certificate_from_roots(D_det=D_det, N_det=N_det, Q_det=Q_det, Vs=Vs, tau=tau, L=L, Vmax=Vmax,
+                                   measure=measure, pre=pre, roots=roots)
+
+
+def level_certificates(stats, taus, L, Vmax, measure=MEASURE_VALUE):
+    """``level_certificate`` of every level in ``stats`` (dicts with D_det, N_det, Q_det,
+    k, Vs, Ps) at thresholds ``taus``; the roots of all levels are solved together."""
+    pres = [_root_inputs(st["D_det"], st["N_det"], st["k"], st["Vs"], st["Ps"], Vmax, measure) for st in stats]
+    roots = _roots(pres, L, measure) if pres else []
+    return [_certificate_from_roots(D_det=st["D_det"], N_det=st["N_det"], Q_det=st["Q_det"], Vs=st["Vs"],
+                                    tau=float(tau), L=L, Vmax=Vmax, measure=measure, pre=pre, roots=rt)
+            for st, tau, pre, rt in zip(stats, taus, pres, roots)]

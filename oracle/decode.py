@@ -32,7 +32,7 @@ import numpy as np
 
 from .canon import LN2, csum128, first_level, logtau  # noqa: F401
 from .bounds import scan_bounds
-from .certify import MEASURE_VALUE, budget_L, level_certificate
+from .certify import MEASURE_VALUE, budget_L, level_certificates
 from .dense import dense_attention, exact_scores
 from .perturb import perturbations
 
@@ -64,27 +64,23 @@ def _exact_result(q16, K16, V16, n, stop_level):
             "values_read": n, "dense": d}
 
 
-def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64,
-                     seed=0x5EED, step=0, layer=0, measure=MEASURE_VALUE, with_dense=True):
-    """Certified decode for the G queries q16 [G][128] of KV head h.
+def scan_stage(q16, K16, V16, packed, h, n, *, window=64):
+    """Steps 1-3 for the G queries q16 [G][128] of KV head h: everything that does not
+    depend on the perturbations (window scores, bounds, c_lo, C_max and c*).
 
-    K16, V16: fp16 [n_cap][128] of this KV head.  Returns a list (one entry per
-    query) of dicts with o_hat, beta, stop_level, keys_read and a trace.
+    Returns None when n <= window (every key is exact); otherwise a dict with the
+    per-query values in lists indexed by g.
     """
     G = q16.shape[0]
     W = window
     if n <= W:
-        return [_exact_result(q16[g], K16, V16, n, 0) for g in range(G)]
+        return None
     npool = n - W
-    LT = logtau(r, J)
-    TAU = np.exp(LT)
-    L = budget_L(J, delta, measure)
     Vd_all = V16[:n].astype(np.float64)
     vsq_all = csum128(Vd_all * Vd_all)
     Vmax = float(packed["vnorm"][h, :npool].astype(np.float64).max())
     bnd = scan_bounds(q16, packed, h, npool)
-    E = perturbations(seed, step, layer, h, np.arange(npool))
-    results = []
+    per = []
     for g in range(G):
         s_R = exact_scores(q16[g], K16[npool:n])
         c_R = float(s_R.max())
@@ -93,6 +89,28 @@ def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64
         cmax_pos = np.nonzero(UB >= c_lo)[0]
         s_cm = exact_scores(q16[g], K16[cmax_pos])
         c_star = max(c_R, float(s_cm.max())) if cmax_pos.size else c_R
+        w_R = np.exp(s_R - c_star)
+        per.append({"s_R": s_R, "c_R": c_R, "UB": UB, "LB": LB, "c_lo": c_lo, "cmax_pos": cmax_pos,
+                    "c_star": c_star, "D_R": float(w_R.sum()), "N_R": w_R @ Vd_all[npool:n],
+                    "Q_R": float(w_R @ vsq_all[npool:n])})
+    return {"q16": q16, "K16": K16, "V16": V16, "h": h, "n": n, "W": W, "npool": npool,
+            "Vd_all": Vd_all, "vsq_all": vsq_all, "Vmax": Vmax, "per": per}
+
+
+def sample_stage(sc, *, eps, delta, r, J, seed=0x5EED, step=0, layer=0, measure=MEASURE_VALUE,
+                 with_dense=True):
+    """Steps 4-7 for every query of a ``scan_stage`` result, with the perturbations of
+    (seed, step, layer, KV head): buckets, exact rescoring of the candidates, the level
+    sums, the certificate of every level and the stop at the first certified one."""
+    q16, K16, V16, h, n, W, npool = sc["q16"], sc["K16"], sc["V16"], sc["h"], sc["n"], sc["W"], sc["npool"]
+    LT = logtau(r, J)
+    TAU = np.exp(LT)
+    L = budget_L(J, delta, measure)
+    Vd_all, vsq_all, Vmax = sc["Vd_all"], sc["vsq_all"], sc["Vmax"]
+    E = perturbations(seed, step, layer, h, np.arange(npool))
+    results = []
+    for g, pg in enumerate(sc["per"]):
+        c_star, UB = pg["c_star"], pg["UB"]
         p = UB + E
         lub = first_level(p - c_star, LT)
         cand = np.nonzero(lub <= J)[0]
@@ -102,31 +120,25 @@ def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64
         w_c = np.exp(s_c - c_star)
         Vc = Vd_all[cand]
         vsq_c = vsq_all[cand]
-        w_R = np.exp(s_R - c_star)
-        D_R = float(w_R.sum())
-        N_R = w_R @ Vd_all[npool:n]
-        Q_R = float(w_R @ vsq_all[npool:n])
+        stats = [level_sums(j, hl, ll, w_c, Vc, vsq_c, pg["D_R"], pg["N_R"], pg["Q_R"]) for j in range(J + 1)]
+        certs = level_certificates(stats, TAU, L, Vmax, measure)
         levels = []
         stop = None
-        for j in range(J + 1):
-            st = level_sums(j, hl, ll, w_c, Vc, vsq_c, D_R, N_R, Q_R)
-            cert = level_certificate(D_det=st["D_det"], N_det=st["N_det"], Q_det=st["Q_det"],
-                                     k=st["k"], Vs=st["Vs"], Ps=st["Ps"],
-                                     tau=float(TAU[j]), L=L, Vmax=Vmax, measure=measure)
+        for st, cert in zip(stats, certs):
             cert.update(st)
             levels.append(cert)
             if cert["beta"] <= eps:
-                stop = j
+                stop = len(levels) - 1
                 break
-        trace = {"c_R": c_R, "c_lo": c_lo, "c_star": c_star, "cmax_pos": cmax_pos,
+        trace = {"c_R": pg["c_R"], "c_lo": pg["c_lo"], "c_star": c_star, "cmax_pos": pg["cmax_pos"],
                  "lub": lub, "cand": cand, "s_c": s_c, "h": hl, "l": ll, "E": E, "UB": UB,
-                 "LB": LB, "levels": levels, "L": L, "Vmax": Vmax, "D_R": D_R}
+                 "LB": pg["LB"], "levels": levels, "L": L, "Vmax": Vmax, "D_R": pg["D_R"]}
         if stop is None:
             res = _exact_result(q16[g], K16, V16, n, J + 1)
             res["trace"] = trace
             results.append(res)
             continue
-        read_set = np.union1d(cmax_pos, cand[lub[cand] <= stop])
+        read_set = np.union1d(pg["cmax_pos"], cand[lub[cand] <= stop])
         res = {"o_hat": levels[stop]["o_hat"], "beta": float(levels[stop]["beta"]),
                "stop_level": stop, "keys_read": int(W + read_set.size),
                "values_read": int(W + int((ll <= stop).sum())), "trace": trace}
@@ -134,6 +146,20 @@ def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64
             res["dense"] = dense_attention(q16[g], K16, V16, n)
         results.append(res)
     return results
+
+
+def certified_decode(q16, K16, V16, packed, h, n, *, eps, delta, r, J, window=64,
+                     seed=0x5EED, step=0, layer=0, measure=MEASURE_VALUE, with_dense=True):
+    """Certified decode for the G queries q16 [G][128] of KV head h.
+
+    K16, V16: fp16 [n_cap][128] of this KV head.  Returns a list (one entry per
+    query) of dicts with o_hat, beta, stop_level, keys_read and a trace.
+    """
+    sc = scan_stage(q16, K16, V16, packed, h, n, window=window)
+    if sc is None:
+        return [_exact_result(q16[g], K16, V16, n, 0) for g in range(q16.shape[0])]
+    return sample_stage(sc, eps=eps, delta=delta, r=r, J=J, seed=seed, step=step, layer=layer,
+                        measure=measure, with_dense=with_dense)
 
 
 def certified_decode_layer(q16, K16, V16, packed, n, G, **kw):
