@@ -273,6 +273,11 @@ __host__ __device__ inline uint64_t hash_prefix(uint64_t seed, uint64_t step, ui
   h = mix64(h ^ layer);
   return mix64(h ^ kv_head);
 }
+// The steps and constants below follow fdlibm's e_log.c, which carries this notice:
+//   Copyright (C) 1993 by Sun Microsystems, Inc. All rights reserved.
+//   Developed at SunPro, a Sun Microsystems, Inc. business.
+//   Permission to use, copy, modify, and distribute this software is freely granted,
+//   provided that this notice is preserved.
 // ln x for normal positive x, written from the steps of fdlibm's e_log.c (Sun
 // Microsystems, 1993): x = 2^k (1 + f), s = f / (2 + f), an odd polynomial in s with
 // coefficients Lg1..Lg7, ln 2 split into a high and a low part.  Evaluated in fp64

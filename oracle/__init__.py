@@ -20,10 +20,15 @@ dense attention (library softmax), pack (exact rational residual norms), score
 bounds (brute force over every key), hash (published SplitMix64 outputs, KS test),
 inclusion probability, HT unbiasedness and variance, nesting, the small-tau
 limit, the error identity behind beta, the KL roots (library root finder),
-certificate coverage and the empirical failure rate.  Parity unpinned: the
-specific constants of the certificate completion (per-level tail split, the
-centre, the G and Q tails) -- the pages print no numbers for them; they are
-pinned only by their coverage tests and by agreement with the HIP path.
+certificate coverage per tail and per measure at a loose level, each measure's
+beta against the worst case its event allows (brute force), the per-level budget
+against the tails each measure's bound uses (union bound), Pinelis's tail at the
+relaxed root, closed forms when no light key is sampled, and the empirical
+failure rate per measure at delta (Theorem 4) with planted mistakes that fail.
+Parity unpinned against the pages: the specific constants of the certificate
+completion (the per-level tail split, the centre, the G and Q tails) and the
+hash -- the pages print no numbers for them; they are pinned by the rigour checks
+above and by agreement with the HIP path.
 """
 
 from .canon import LN2, RSQRT_D, PADF, csum128, logtau, first_level  # noqa: F401
@@ -31,5 +36,5 @@ from .dense import dense_attention, exact_scores  # noqa: F401
 from .pack import pack_kv_4bit  # noqa: F401
 from .bounds import scan_bounds  # noqa: F401
 from .perturb import splitmix64_mix, hash_prefix, perturbations  # noqa: F401
-from .certify import kl, kl_upper_root, kl_lower_root, level_certificate, tails_per_level  # noqa: F401
-from .decode import certified_decode, certified_decode_layer, level_sums  # noqa: F401
+from .certify import kl, kl_upper_root, kl_lower_root, level_certificate, level_certificates, tails_per_level  # noqa: F401
+from .decode import certified_decode, certified_decode_layer, level_sums, scan_stage, sample_stage  # noqa: F401

@@ -60,6 +60,13 @@ def uniforms(seed: int, step: int, layer: int, kv_head: int, positions) -> np.nd
     return ((h >> np.uint64(11)) + np.uint64(1)).astype(np.float64) * 2.0 ** -53
 
 
+# The steps and constants of log_spec follow fdlibm's e_log.c, which carries this notice:
+#   Copyright (C) 1993 by Sun Microsystems, Inc. All rights reserved.
+#   Developed at SunPro, a Sun Microsystems, Inc. business.
+#   Permission to use, copy, modify, and distribute this software is freely granted,
+#   provided that this notice is preserved.
+
+
 def _f64(bits: int) -> float:
     return float(np.array([bits], dtype=np.uint64).view(np.float64)[0])
 

@@ -4,8 +4,9 @@ What fixes each expected value: the exact dense maximum (brute force), the
 threshold-sampling law Pr[i in S(tau)] = min(1, w_i/tau) (Theoretical Foundation),
 Theorem 1 (unbiasedness, Var D^ = sum_A w(tau - w) <= tau D_A), nesting of the
 samples, the tau -> 0 limit, the algebraic identity behind beta, a library root
-finder for the KL roots, nominal coverage of each tail at a loose level, Theorem 4
-(failure rate <= delta) and Theorem 2 (keys read flat in n).
+finder for the KL roots, nominal coverage of each tail at a loose level and
+Theorem 2 (samples and keys read bounded independently of n).  Theorem 4 and the
+per-measure pins are in test_oracle_measures.py.
 """
 
 import math
@@ -213,61 +214,52 @@ def test_certificate_tails_cover_at_loose_level(small_case):
     assert miss_mu > 0                     # the interval is not vacuous at this level
 
 
-# ---------------------------------------------------------------- P12 Theorem 4
-def _failure_rate(eps, delta, seeds, beta_scale=1.0, monkeypatch=None):
-    w = synth.peaked_head(1024, seed=77, G=4, eps=eps)
-    w.delta = delta
-    packed = oracle.pack_kv_4bit(w.K, w.V, w.n // 32)
-    fails = trials = certified = 0
-    for sd in seeds:
-        for r in _decode(w, packed, seed=sd, eps=eps, delta=delta):
-            trials += 1
-            if r["stop_level"] <= w.J:
-                certified += 1
-                err = float(np.linalg.norm(r["o_hat"] - r["dense"]["o"]))
-                fails += err > eps * r["dense"]["M"]
-    return fails, trials, certified
-
-
-def test_theorem4_failure_rate():
-    fails, trials, certified = _failure_rate(0.05, 0.01, range(100))
-    assert certified > 0.9 * trials
-    assert fails / trials <= 0.01 + 4 * math.sqrt(0.01 * 0.99 / trials)
-
-
-def test_theorem4_detects_a_broken_certificate(monkeypatch):
-    """Planted mistake: a beta 30x too small must push the failure rate over delta."""
-    import oracle.decode as dec
-    real = dec.level_certificate
-
-    def shrunk(**kw):
-        out = real(**kw)
-        out["beta"] = out["beta"] / 30.0
-        return out
-    monkeypatch.setattr(dec, "level_certificate", shrunk)
-    fails, trials, _ = _failure_rate(0.05, 0.01, range(25))
-    assert fails / trials > 0.01 + 4 * math.sqrt(0.01 * 0.99 / trials)
-
-
 # ---------------------------------------------------------------- P13 Theorem 2
-@pytest.mark.slow
-def test_values_read_bounded_independent_of_context_length():
-    """Theorem 2: O(eps^-2 log(1/delta)) values suffice whatever n.
+def _p13_layer(n):
+    """One KV head (4 queries) of the 32768-token layer's recipe at context n: sink of
+    3.5 nats on tokens 0-3 and 1 % power-law heavy hitters along the mean query."""
+    rng = np.random.default_rng(2)
+    _, q, K, V = synth.recipe_layer(rng, 1, 4, n, sink=3.5)
+    return synth.Workload(f"p13.{n}", q, K, V, n, 4, window=64, r=2, J=40, eps=0.05, delta=0.01)
 
-    Theorem 2's m = 2 L eps^-2 is the case where all mass is light; with part of
-    the mass in heavy keys fewer samples are needed, so the count may rise with n
-    toward that bound but never past a fixed multiple of it.
+
+@pytest.mark.slow
+def test_keys_read_flat_in_context_length():
+    """Theorem 2 on the 32768-token layer's generator at n = 16K..128K: the median keys
+    read grows by at most 1.3x while n grows 4x (32K -> 128K), and the values read stay
+    within a fixed multiple of m = 2 L eps^-2."""
+    from oracle.certify import budget_L
+    m = 2.0 * budget_L(40, 0.01, 2) / 0.05 ** 2
+    keys = {}
+    for n in (16384, 32768, 65536, 131072):
+        w = _p13_layer(n)
+        res = _decode(w, with_dense=False)
+        assert all(r["stop_level"] <= w.J for r in res)
+        keys[n] = float(np.median([r["keys_read"] for r in res]))
+        assert max(r["values_read"] - w.window for r in res) <= 3.0 * m
+    assert keys[131072] / keys[32768] <= 1.3, keys
+
+
+@pytest.mark.slow
+def test_light_samples_bounded_independent_of_context_length():
+    """Theorem 2 where all keys are light-ish (no heavy hitters, scores spread by a
+    query of twice the usual norm): the light samples k at the stop level never exceed
+    3 m, m = 2 L eps^-2, at any n, and the keys read stay within a fixed multiple of the
+    values read (the 4-bit candidates around each sampled key).
+
+    On this generator the sample itself still grows with n over 16K..128K, because the
+    light share of the attention mass rises (about 0.45 -> 0.75) and k approaches its
+    n-free ceiling from below; the keys read follow it (about 1.9x from 32K to 128K).
     """
     from oracle.certify import budget_L
     eps = 0.1
     m = 2.0 * budget_L(30, 0.01, 2) / eps ** 2
-    vals, keys = {}, {}
     for n in (16384, 32768, 65536, 131072):
         w = synth.peaked_head(n, seed=9, G=4, heavy=0, eps=eps, q_scale=2.0)
-        res = _decode(w, eps=eps)
-        assert all(r["stop_level"] <= w.J for r in res)
-        vals[n] = max(r["values_read"] - w.window for r in res)
-        keys[n] = float(np.median([r["keys_read"] for r in res]))
-        assert vals[n] <= 3.0 * m, (n, vals[n], m)
-    # keys read grow far slower than n (8x here)
-    assert keys[131072] / keys[16384] <= 4.0, keys
+        res = _decode(w, eps=eps, with_dense=False)
+        for r in res:
+            assert r["stop_level"] <= w.J
+            lv = r["trace"]["levels"][r["stop_level"]]
+            assert lv["k"] <= 3.0 * m, (n, lv["k"], m)
+            assert r["values_read"] - w.window <= 3.0 * m
+            assert r["keys_read"] <= 6.0 * r["values_read"], (n, r["keys_read"], r["values_read"])
