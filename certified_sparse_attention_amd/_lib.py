@@ -36,7 +36,8 @@ class Trace(ctypes.Structure):
                 ("bucket_count", c_void_p), ("lub", c_void_p), ("cmax_count", c_void_p),
                 ("cand_count", c_void_p), ("beta_level", c_void_p), ("dhat_level", c_void_p),
                 ("k_level", c_void_p), ("logtau", c_void_p), ("ev_scan_begin", c_void_p),
-                ("ev_scan_end", c_void_p)]
+                ("ev_scan_end", c_void_p), ("cand_pos", c_void_p), ("cand_hl", c_void_p),
+                ("rescored_count", c_void_p)]
 
 
 SYMBOLS = {

@@ -111,6 +111,7 @@ def allocate_workspace(K: torch.Tensor, G: int, n_max: int, J: int, window: int 
 
 TRACE_FIELDS = ("c_R", "c_lo", "c_star", "bucket_count", "lub", "cmax_count", "cand_count",
                 "beta_level", "dhat_level", "k_level", "logtau")
+TRACE_FIELDS_AFTER_EVENTS = ("cand_pos", "cand_hl", "rescored_count")
 
 
 def _alloc_trace(H_q, J, npool, device):
@@ -127,6 +128,9 @@ def _alloc_trace(H_q, J, npool, device):
         "dhat_level": torch.full((H_q, J + 1), float("nan"), dtype=f64, device=device),
         "k_level": torch.zeros((H_q, J + 1), dtype=i32, device=device),
         "logtau": torch.zeros(J + 1, dtype=f64, device=device),
+        "cand_pos": torch.full((H_q, max(npool, 1)), -1, dtype=i32, device=device),
+        "cand_hl": torch.full((H_q, max(npool, 1)), -1, dtype=i32, device=device),
+        "rescored_count": torch.zeros(H_q, dtype=i32, device=device),
     }
 
 
@@ -168,9 +172,11 @@ def certified_decode_attention(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
             tr = _alloc_trace(H_q, J, n - window, q.device)
         elif isinstance(trace, dict):
             tr = trace
-        vals = [_ptr(tr[f]) if tr is not None else ctypes.c_void_p(0) for f in TRACE_FIELDS]
+        def field(f):
+            return _ptr(tr[f]) if (tr is not None and f in tr) else ctypes.c_void_p(0)
         ev0, ev1 = scan_events if scan_events is not None else (None, None)
-        tr_struct = _lib.Trace(*vals, ctypes.c_void_p(ev0), ctypes.c_void_p(ev1))
+        tr_struct = _lib.Trace(*[field(f) for f in TRACE_FIELDS], ctypes.c_void_p(ev0), ctypes.c_void_p(ev1),
+                               *[field(f) for f in TRACE_FIELDS_AFTER_EVENTS])
     pk = packed.c_struct() if packed is not None else _lib.Packed()
     _lib.check(lib.csa_certified_decode_attention(
         ctypes.byref(sh), ctypes.byref(pr), _ptr(q), _ptr(K), _ptr(V), ctypes.byref(pk), int(n),

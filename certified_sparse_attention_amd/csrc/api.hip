@@ -247,6 +247,25 @@ __global__ __launch_bounds__(256) void trace_kernel(const double *qconst, const 
   if (t == 0) cm[i] = part[0] + part[1] + part[2] + part[3];
 }
 
+// Per-candidate trace, grid (H_q, ceil(npool / 256)): the candidate list and the levels
+// of the entries that were rescored.  Pass 1 rescores the first ccount1 entries (those
+// with l^ub up to the speculative level); a head whose stop level lies past that level
+// went through the second pass or the exact fallback after it, which rescored all.
+__global__ __launch_bounds__(256) void cand_trace_kernel(const int *ccount, const int *ccount1, const int *jspec,
+                                                         const int32_t *stop, const int *candpos, const int *rec_hl,
+                                                         int64_t npool_cap, int64_t npool, int32_t *cand_pos,
+                                                         int32_t *cand_hl, int32_t *rescored) {
+  const int hq = blockIdx.x;
+  const int cnt = ccount[hq];
+  const int nres = (stop[hq] <= jspec[hq]) ? ccount1[hq] : cnt;
+  if (blockIdx.y == 0 && threadIdx.x == 0 && rescored) rescored[hq] = nres;
+  const int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  if (i >= cnt || i >= npool) return;
+  const int64_t src = (int64_t)hq * npool_cap + i, dst = (int64_t)hq * npool + i;
+  if (cand_pos) cand_pos[dst] = candpos[src];
+  if (cand_hl) cand_hl[dst] = (i < nres) ? rec_hl[src] : -1;
+}
+
 // One read of a buffer (16-byte loads; workgroup w streams the w-th contiguous slice) and
 // the XOR of its 32-bit words per workgroup.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *src, int64_t n16, int64_t per,
@@ -468,6 +487,14 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
     auto cp = [&](void *dst, size_t off, size_t bytes) -> hipError_t {
       return dst ? hipMemcpyAsync(dst, at<char>(ws, off), bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
     };
+    if (!all_exact && (trace->cand_pos || trace->cand_hl || trace->rescored_count)) {
+      const unsigned ny = (unsigned)((npool + 255) / 256);
+      hipLaunchKernelGGL(cand_trace_kernel, dim3(Hq, ny), dim3(256), 0, st, at<int>(ws, P.ccount),
+                         at<int>(ws, P.ccount1), at<int>(ws, P.jspec), stop_level, at<int>(ws, P.candpos),
+                         at<int>(ws, P.rec_hl), P.npool_cap, npool, trace->cand_pos, trace->cand_hl,
+                         trace->rescored_count);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "candidate trace");
+    }
     if (!all_exact) {
       if ((e = cp(trace->bucket_count, P.hist, (size_t)Hq * (J1 + 1) * sizeof(int))) != hipSuccess ||
           (e = cp(trace->beta_level, P.betalv, (size_t)Hq * J1 * sizeof(double))) != hipSuccess ||

@@ -20,7 +20,7 @@
  *     and csa_last_error() gives the detail of the calling thread's last failure.
  *     On an argument error nothing is launched.  No C++ exception crosses the ABI.
  *   - Same inputs and parameters give bit-identical outputs (fixed-order
- *     reductions; no floating-point atomics).
+ *     reductions; floating-point atomics only on LDS cells that one thread owns).
  *   - Non-finite K, V or q values are undefined behaviour.
  *   - fp16 arrays are IEEE binary16 bit patterns (uint16_t).
  */
@@ -124,6 +124,18 @@ typedef struct {
  *   ev_scan_begin/end   hipEvent_t that take the start and end times of the 4-bit
  *                       scan kernel's own dispatch (for timing it alone; no marker
  *                       packets are added to the stream).
+ *   cand_pos            int32 [H_q][n_pool]: the candidates (l^ub <= J) in list order,
+ *                       first those with l^ub up to the speculative level, then the
+ *                       rest, each part in position order; entries past cand_count
+ *                       are unspecified.
+ *   cand_hl             int32 [H_q][n_pool]: for the first rescored_count entries of
+ *                       cand_pos, h | (l << 8) with h = first(s - c*) the level from
+ *                       which the key is heavy (always sampled) and l = first((s + E) - c*)
+ *                       its entry level, both in [0, J+1] ([S] Algorithm Components
+ *                       items 1-2: S_j = {l <= j}, B_j = {h <= j}); -1 for the other
+ *                       candidates, which can enter the sample only at levels past the
+ *                       stop level.
+ *   rescored_count      int32 [H_q]: candidates rescored exactly in this call.
  */
 typedef struct {
   double *c_R, *c_lo, *c_star;
@@ -135,6 +147,8 @@ typedef struct {
   int32_t *k_level;
   double *logtau;
   void *ev_scan_begin, *ev_scan_end;
+  int32_t *cand_pos, *cand_hl;
+  int32_t *rescored_count;
 } csa_trace;
 
 /*

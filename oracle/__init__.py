@@ -32,7 +32,7 @@ above and by agreement with the HIP path.
 """
 
 from .canon import LN2, RSQRT_D, PADF, csum128, logtau, first_level  # noqa: F401
-from .dense import dense_attention, exact_scores  # noqa: F401
+from .dense import dense_attention, dense_attention_heads, exact_scores  # noqa: F401
 from .pack import pack_kv_4bit  # noqa: F401
 from .bounds import scan_bounds  # noqa: F401
 from .perturb import splitmix64_mix, hash_prefix, perturbations  # noqa: F401

@@ -32,3 +32,24 @@ def dense_attention(q16: np.ndarray, K16: np.ndarray, V16: np.ndarray, n: int) -
     vsq = (Vd * Vd).sum(axis=1)
     M = float(np.sqrt((w @ vsq) / Dn))
     return {"s": s, "c_star": cstar, "w": w, "D": Dn, "N": N, "o": o, "M": M}
+
+
+def dense_attention_heads(Q16: np.ndarray, K16: np.ndarray, V16: np.ndarray, n: int,
+                          K64: np.ndarray | None = None, V64: np.ndarray | None = None) -> dict:
+    """The same definition for several queries Q16 [G][128] of one KV head at once, with
+    the scores and sums taken by fp64 matrix products (for many decode steps; the
+    summation order differs from ``exact_scores`` by rounding only).
+
+    K64 / V64 may pass the first n rows already in fp64.
+    """
+    Kd = K16[:n].astype(np.float64) if K64 is None else K64[:n]
+    Vd = V16[:n].astype(np.float64) if V64 is None else V64[:n]
+    s = (Kd @ Q16.astype(np.float64).T) * RSQRT_D             # [n][G]
+    cstar = s.max(axis=0)
+    w = np.exp(s - cstar[None, :])
+    Dn = w.sum(axis=0)
+    N = w.T @ Vd                                             # [G][128]
+    o = N / Dn[:, None]
+    vsq = (Vd * Vd).sum(axis=1)
+    M = np.sqrt((w.T @ vsq) / Dn)
+    return {"c_star": cstar, "D": Dn, "N": N, "o": o, "M": M}

@@ -1,9 +1,15 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Bit-exact: packed codes and metadata, score bounds UB/LB, perturbations E, c_lo,
-c*, |C_max|, buckets l^ub (hence candidate sets), candidate counts, stop levels and
-keys read.  Floating point: beta and D^ at every level up to the stop within 1e-4
+c*, |C_max|, buckets l^ub, the candidate set, the heavy and entry levels (h, l) of
+every rescored candidate and hence the sample S_j = {l <= j} and the heavy set
+B_j = {h <= j} at every level up to the stop, candidate counts, stop levels and keys
+read.  Floating point: beta and D^ at every level up to the stop within 1e-4
 relative, |o^_gpu - o^_cpu| <= 1e-3 M.
+
+Shapes: GQA groups of 1 to 7 queries, 1 to 8 KV heads, grids r = 1, 2, 3, deepest
+levels J = 20 to 60, windows of 32, 64 and 128 tokens, contexts that are not
+multiples of 32.
 """
 
 import numpy as np
@@ -54,11 +60,34 @@ def _packed_numpy(p):
     }
 
 
+def _with(w, **kw):
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def _multi_head(n, H_kv, G, seed, q_scale=1.0):
+    rng = np.random.default_rng(seed)
+    _, q, K, V = synth.recipe_layer(rng, H_kv, G, n, sink=2.5, q_scale=q_scale)
+    return synth.Workload(f"layer{H_kv}x{G}", q, K, V, n, G, window=64, r=2, J=40, eps=0.05, delta=0.01)
+
+
 WORKLOADS = {
     "config1": synth.config1,
     "config2": synth.config2,
     "ragged_5000": lambda: synth.peaked_head(5000, seed=31, G=3),
     "ragged_g7": lambda: synth.peaked_head(2100, seed=32, G=7, J=20),
+    "g1": lambda: synth.peaked_head(3001, seed=51, G=1),
+    "g2": lambda: synth.peaked_head(3500, seed=52, G=2),
+    "g5": lambda: synth.peaked_head(4003, seed=53, G=5),
+    "g6": lambda: synth.peaked_head(2650, seed=54, G=6),
+    "r1": lambda: _with(synth.peaked_head(3100, seed=55, G=4, J=25), r=1),
+    "r3": lambda: _with(synth.peaked_head(3100, seed=56, G=4, J=60), r=3),
+    "window32": lambda: synth.peaked_head(3077, seed=57, G=4, window=32),
+    "window128": lambda: synth.peaked_head(3200, seed=58, G=4, window=128),
+    "J60": lambda: synth.peaked_head(2999, seed=59, G=4, J=60, eps=0.02),
+    "kv3_g5": lambda: _multi_head(6000, 3, 5, seed=60),
+    "kv2_g4_flat": lambda: _multi_head(5000, 2, 4, seed=61, q_scale=0.1),
 }
 
 
@@ -114,9 +143,12 @@ def test_scan_bounds_bit_exact(case):
         np.testing.assert_array_equal(E[h], e_ref)
 
 
-def _compare_decode(w, pk_ref, res, tr, **kw):
+def _compare_decode(w, pk_ref, res, tr, ref=None, **kw):
+    """Compare a GPU call (outputs ``res``, trace ``tr``) with the oracle's result ``ref``
+    (computed here from the packed reference when not given)."""
     o_hat, beta, stop, keys = (t.cpu().numpy() for t in res)
-    ref = oracle.certified_decode_layer(w.q, w.K, w.V, pk_ref, w.n, w.G, **kw)
+    if ref is None:
+        ref = oracle.certified_decode_layer(w.q, w.K, w.V, pk_ref, w.n, w.G, **kw)
     trn = {k: v.cpu().numpy() for k, v in tr.items()}
     for hq, r in enumerate(ref):
         M = r["dense"]["M"]
@@ -139,6 +171,7 @@ def _compare_decode(w, pk_ref, res, tr, **kw):
         np.testing.assert_array_equal(trn["bucket_count"][hq],
                                       np.bincount(t["lub"], minlength=kw["J"] + 2))
         assert trn["cand_count"][hq] == t["cand"].size
+        _compare_samples(hq, trn, t, r["stop_level"], kw["J"])
         for j, lv in enumerate(t["levels"]):
             assert trn["k_level"][hq, j] == lv["k"], (hq, j)
             assert abs(trn["dhat_level"][hq, j] - lv["D_hat"]) <= 1e-4 * lv["D_hat"]
@@ -148,6 +181,26 @@ def _compare_decode(w, pk_ref, res, tr, **kw):
             else:
                 assert not np.isfinite(trn["beta_level"][hq, j])
     return ref
+
+
+def _compare_samples(hq, trn, t, stop, J):
+    """The candidate list, the (h, l) of every rescored candidate, and S_j, B_j at every
+    level up to the stop (up to J on the exact fallback), element by element."""
+    cc = int(trn["cand_count"][hq])
+    pos = trn["cand_pos"][hq, :cc]
+    np.testing.assert_array_equal(np.sort(pos), t["cand"])     # the same set, no repeats
+    nres = int(trn["rescored_count"][hq])
+    assert 0 <= nres <= cc
+    hl = trn["cand_hl"][hq, :cc]
+    assert np.all(hl[:nres] >= 0) and np.all(hl[nres:] == -1)
+    rpos = pos[:nres]
+    idx = np.searchsorted(t["cand"], rpos)
+    gh, gl = hl[:nres] & 0xFF, hl[:nres] >> 8
+    np.testing.assert_array_equal(gh, t["h"][idx])
+    np.testing.assert_array_equal(gl, t["l"][idx])
+    for j in range(min(stop, J) + 1):
+        np.testing.assert_array_equal(np.sort(rpos[gl <= j]), t["cand"][t["l"] <= j], err_msg=f"S_{j} of {hq}")
+        np.testing.assert_array_equal(np.sort(rpos[gh <= j]), t["cand"][t["h"] <= j], err_msg=f"B_{j} of {hq}")
 
 
 def _kw(w, **over):
@@ -181,8 +234,6 @@ def test_certified_decode_is_deterministic(case):
 
 @pytest.mark.parametrize("measure", ["denominator", "output_norm"])
 def test_other_measures(case, measure):
-    if case["name"] != "config1":
-        pytest.skip("one workload is enough for the measure switch")
     w = case["w"]
     kw = _kw(w)
     out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,
@@ -287,8 +338,6 @@ def test_stream_read_checksum():
 @pytest.mark.parametrize("budget", [1, 16, 300])
 def test_speculative_budget_does_not_change_results(case, budget):
     """A small candidate budget forces the second pass; results stay oracle-exact."""
-    if case["name"] == "config2" and budget != 16:
-        pytest.skip("one budget is enough for the large workload")
     w = case["w"]
     kw = _kw(w)
     out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,

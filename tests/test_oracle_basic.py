@@ -52,6 +52,19 @@ def test_dense_ragged_n(cfg1):
         np.testing.assert_allclose(d["o"], o_ref, rtol=1e-12, atol=1e-13)
 
 
+def test_dense_heads_matches_library_softmax(cfg1):
+    """The several-queries form of the same definition against torch's fp64 softmax,
+    at full length and at a ragged n."""
+    q = torch.from_numpy(cfg1.q.astype(np.float64))
+    for n in (cfg1.n, 1001):
+        K = torch.from_numpy(cfg1.K[0, :n].astype(np.float64))
+        V = torch.from_numpy(cfg1.V[0, :n].astype(np.float64))
+        a = torch.softmax((q @ K.T) / np.sqrt(128.0), dim=-1)
+        d = oracle.dense_attention_heads(cfg1.q, cfg1.K[0], cfg1.V[0], n)
+        np.testing.assert_allclose(d["o"], (a @ V).numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(d["M"], torch.sqrt(a @ (V * V).sum(dim=1)).numpy(), rtol=1e-12)
+
+
 # ---------------------------------------------------------------- P2 pack
 def test_pack_codes_and_block_metadata(cfg1, cfg1_packed):
     pk = cfg1_packed
