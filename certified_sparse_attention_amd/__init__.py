@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     PackedKV,
     allocate_workspace,
     certified_decode_attention,
+    certified_decode_attention_noalloc,
     dense_decode_attention,
     pack_kv_4bit,
     scan_bounds,

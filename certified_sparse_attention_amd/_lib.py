@@ -48,6 +48,9 @@ SYMBOLS = {
                                                c_void_p, c_void_p, ctypes.POINTER(Packed), c_int64,
                                                c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                                c_void_p, ctypes.POINTER(Trace), c_void_p]),
+    "csa_certified_decode_attention_noalloc": (c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_void_p,
+                                                       c_void_p, c_void_p, ctypes.POINTER(Packed), c_int64,
+                                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "csa_scan_bounds": (c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_void_p, c_void_p,
                                 ctypes.POINTER(Packed), c_int64, c_void_p, c_size_t, c_void_p,
                                 c_void_p, c_void_p, c_void_p]),

@@ -188,6 +188,35 @@ def certified_decode_attention(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
     return o_hat, beta, stop, keys
 
 
+def certified_decode_attention_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, packed: PackedKV,
+                                       n: int, out, *, eps: float, delta: float, r: int, J: int,
+                                       window: int = 64, seed: int = 0x5EED, step: int = 0, layer: int = 0,
+                                       measure="value", cand_budget: int = 0):
+    """The certified step on the library's static scratch (no workspace, nothing allocated
+    here or in the library).  ``out`` = (o_hat fp32 [H_q][128], beta fp64 [H_q], stop_level
+    int32 [H_q], keys_read int64 [H_q]), preallocated by the caller."""
+    _check_fp16("q", q)
+    _check_fp16("K", K)
+    _check_fp16("V", V, K.shape)
+    H_kv = K.shape[0]
+    if q.dim() != 2 or q.shape[1] != 128 or q.shape[0] % H_kv:
+        raise ValueError("q must be [H_kv * G][128]")
+    o_hat, beta, stop, keys = out
+    H_q = q.shape[0]
+    for name, t, dt, shape in (("o_hat", o_hat, torch.float32, (H_q, 128)), ("beta", beta, torch.float64, (H_q,)),
+                               ("stop_level", stop, torch.int32, (H_q,)), ("keys_read", keys, torch.int64, (H_q,))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of shape {shape}")
+    lib = _lib.load()
+    sh = _shape(K, H_q // H_kv)
+    pr = _params(eps, delta, r, J, window, measure, seed, step, layer, cand_budget)
+    pk = packed.c_struct() if packed is not None else _lib.Packed()
+    _lib.check(lib.csa_certified_decode_attention_noalloc(
+        ctypes.byref(sh), ctypes.byref(pr), _ptr(q), _ptr(K), _ptr(V), ctypes.byref(pk), int(n),
+        _ptr(o_hat), _ptr(beta), _ptr(stop), _ptr(keys), _stream()), "csa_certified_decode_attention_noalloc")
+    return o_hat, beta, stop, keys
+
+
 def scan_bounds(q: torch.Tensor, K: torch.Tensor, packed: PackedKV, n: int, *, J: int, r: int = 2,
                 window: int = 64, seed: int = 0x5EED, step: int = 0, layer: int = 0,
                 workspace: torch.Tensor | None = None):

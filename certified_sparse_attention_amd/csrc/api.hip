@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -106,7 +107,8 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.rec_w = take(Hq * npc * sizeof(double));
   P.rec_vsq = take(Hq * npc * sizeof(double));
   P.rec_hl = take(Hq * npc * sizeof(int));
-  P.partial = take(Hq * csa::kNumSeg * J1 * csa::kStatW * sizeof(double));
+  P.nseg_cap = csa::seg_cap_for(npool);
+  P.partial = take(Hq * (size_t)P.nseg_cap * J1 * csa::kStatW * sizeof(double));
   P.betalv = take(Hq * J1 * sizeof(double));
   P.dhatlv = take(Hq * J1 * sizeof(double));
   P.klv = take(Hq * J1 * sizeof(int));
@@ -287,6 +289,52 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *src, int6
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+int check_certified_args(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
+                         const uint16_t *V, const csa_packed *packed, int64_t n, const float *o_hat,
+                         const double *beta, const int32_t *stop_level, const int64_t *keys_read) {
+  int rc = check_shape(shape);
+  if (rc || (rc = check_params(params))) return rc;
+  if (!q || !K || !V || !o_hat || !beta || !stop_level || !keys_read)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "q, K, V and every output must be non-null");
+  if (n < 1 || n > shape->n_cap) return fail(CSA_ERR_INVALID_ARGUMENT, "n must lie in [1, n_cap]");
+  if (n > params->window && (rc = check_packed(packed))) return rc;
+  return CSA_OK;
+}
+
+int certified_run(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
+                  const uint16_t *V, const csa_packed *packed, int64_t n, void *workspace, const csa::Plan &P,
+                  float *o_hat, double *beta, int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
+                  hipStream_t st);
+
+// Scratch of the allocation-free entry point: one static array per GPU (the code object's
+// device globals are instantiated on every device the library runs on), kept until the
+// process ends.  Host code never passes `scratch` itself to a kernel -- in host code the
+// name is a host-side stand-in -- but the device address hipGetSymbolAddress gives for the
+// current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,17 +394,45 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
                                    int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
                                    csa_stream_t stream) {
   g_err[0] = 0;
-  int rc = check_shape(shape);
-  if (rc || (rc = check_params(params))) return rc;
-  if (!q || !K || !V || !o_hat || !beta || !stop_level || !keys_read)
-    return fail(CSA_ERR_INVALID_ARGUMENT, "q, K, V and every output must be non-null");
-  if (n < 1 || n > shape->n_cap) return fail(CSA_ERR_INVALID_ARGUMENT, "n must lie in [1, n_cap]");
-  const bool all_exact = n <= params->window;
-  if (!all_exact && (rc = check_packed(packed))) return rc;
+  int rc = check_certified_args(shape, params, q, K, V, packed, n, o_hat, beta, stop_level, keys_read);
+  if (rc) return rc;
   const csa::Plan P = make_plan(shape, params, n);
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
-  hipStream_t st = (hipStream_t)stream;
+  return certified_run(shape, params, q, K, V, packed, n, workspace, P, o_hat, beta, stop_level, keys_read, trace,
+                       (hipStream_t)stream);
+}
+
+int csa_certified_decode_attention_noalloc(const csa_shape *shape, const csa_params *params, const uint16_t *q,
+                                           const uint16_t *K, const uint16_t *V, const csa_packed *packed,
+                                           int64_t n, float *o_hat, double *beta, int32_t *stop_level,
+                                           int64_t *keys_read, csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_certified_args(shape, params, q, K, V, packed, n, o_hat, beta, stop_level, keys_read);
+  if (rc) return rc;
+  const csa::Plan P = make_plan(shape, params, n);
+  if (P.total > kScratchBytes)
+    return fail(CSA_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; the library's static scratch holds %zu (use "
+                "csa_certified_decode_attention with a workspace)",
+                P.total, kScratchBytes);
+  void *ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return certified_run(shape, params, q, K, V, packed, n, ws, P, o_hat, beta, stop_level, keys_read, nullptr,
+                       (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The certified call on a workspace that holds at least plan P (arguments checked).
+int certified_run(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
+                  const uint16_t *V, const csa_packed *packed, int64_t n, void *workspace, const csa::Plan &P,
+                  float *o_hat, double *beta, int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
+                  hipStream_t st) {
+  int rc = 0;
+  const bool all_exact = n <= params->window;
   void *ev0 = trace ? trace->ev_scan_begin : nullptr;
   void *ev1 = trace ? trace->ev_scan_end : nullptr;
   rc = run_prep_scan(shape, params, q, K, V, packed, n, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
@@ -449,6 +525,7 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   ca.flags = at<int>(ws, P.flags);
   ca.exactp = at<double>(ws, P.exactp);
   ca.exdone = at<int>(ws, P.exdone);
+  ca.nseg_cap = P.nseg_cap;
   ca.cmhist = at<int>(ws, P.cmhist);
   ca.o_hat = o_hat;
   ca.beta = beta;
@@ -511,6 +588,10 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   }
   return CSA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t csa_dense_workspace_bytes(const csa_shape *shape, int64_t n_max) {
   if (check_shape(shape) || n_max < 1) return 0;

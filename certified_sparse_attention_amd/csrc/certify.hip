@@ -40,6 +40,7 @@ struct CertArgs {
   double *rec_w, *rec_vsq;
   const int8_t *lub;
   double *partial, *betalv, *dhatlv;
+  int nseg_cap;                 // segment rows per query head in `partial` (seg_cap_for(npool))
   int *klv, *flags;
   int *exdone;                  // [H_q] chunks of the exact fallback that have finished
   const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list
@@ -62,6 +63,12 @@ constexpr int kStage = 64;        // candidates staged in LDS at a time
 __device__ inline int pass_count(const CertArgs &a, int hq) {
   if (a.pass == 1) return a.ccount1[hq];
   return (a.flags[hq] == 2) ? a.ccount[hq] : -1;
+}
+
+// Most segments a head with at most npool candidates can use (rows of `partial`).
+__host__ __device__ inline int seg_cap_for(int64_t npool) {
+  const int64_t need = (npool + 1023) / 1024;
+  return (npool <= kFusedMax) ? 0 : (int)(need < kNumSeg ? need : kNumSeg);
 }
 
 __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg) {
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
     seg_range(count, seg, i0, i1, nseg);
     zero_acc(s, J1);
     accumulate_mixed(a, s, hq, i0, i1, split);
-    double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
+    double *out = a.partial + ((int64_t)hq * a.nseg_cap + seg) * J1 * kStatW;
     for (int e = threadIdx.x; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
     __syncthreads();
   }
@@ -386,7 +393,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
   } else {
     for (int e = t; e < J1 * kStatW; e += 256) {
       double v = 0.0;
-      for (int sg = 0; sg < nseg; ++sg) v += a.partial[((int64_t)hq * kNumSeg + sg) * J1 * kStatW + e];
+      for (int sg = 0; sg < nseg; ++sg) v += a.partial[((int64_t)hq * a.nseg_cap + sg) * J1 * kStatW + e];
       (&s.acc[0][0])[e] = v;
     }
     __syncthreads();
@@ -629,7 +636,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
         seg_range(count, seg, i0, i1, nseg);
         zero_acc(s, J1);
         accumulate_mixed(a, s, hq, i0, i1, split);
-        double *out = a.partial + ((int64_t)hq * kNumSeg + seg) * J1 * kStatW;
+        double *out = a.partial + ((int64_t)hq * a.nseg_cap + seg) * J1 * kStatW;
         for (int e = t; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
         __syncthreads();
       }

@@ -371,6 +371,7 @@ struct Plan {
   size_t bdone, exdone;  // per-head completion counters (last-workgroup reductions)
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
+  int nseg_cap;        // segment rows per query head in `partial`
   size_t total;
 };
 

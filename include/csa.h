@@ -187,6 +187,24 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
                                    const csa_trace *trace, csa_stream_t stream);
 
 /*
+ * The same certified decode step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments and outputs are those of
+ * csa_certified_decode_attention (no trace).  Scratch space is a static device array of
+ * 64 MiB that the library holds on every GPU it runs on until the process ends; this
+ * call allocates and frees nothing.  Calls whose scratch need (csa_workspace_bytes for
+ * this n) exceeds 64 MiB return CSA_ERR_UNSUPPORTED without launching anything.  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on a GPU (two streams,
+ * two threads) race and give undefined results; order them on one stream.  The per-call
+ * counters in the array are reset by the call itself.
+ */
+int csa_certified_decode_attention_noalloc(const csa_shape *shape, const csa_params *params,
+                                           const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                           const csa_packed *packed, int64_t n, float *o_hat,
+                                           double *beta, int32_t *stop_level, int64_t *keys_read,
+                                           csa_stream_t stream);
+
+/*
  * Diagnostic: the scan's deterministic bounds and perturbations for every pool key.
  *   UB, LB fp64 [H_q][n - window]; E fp64 [H_kv][n - window] (E = -ln u from the
  *   hash of (seed, step, layer, kv_head, position)).  Any output may be NULL.
