@@ -595,7 +595,8 @@ extern "C" {
 
 size_t csa_dense_workspace_bytes(const csa_shape *shape, int64_t n_max) {
   if (check_shape(shape) || n_max < 1) return 0;
-  return align_up((size_t)shape->num_kv_heads * shape->group_size * csa::dense_nsplit(n_max) * 130 * sizeof(float));
+  return align_up((size_t)shape->num_kv_heads * shape->group_size *
+                  csa::dense_nsplit_max(n_max, shape->num_kv_heads) * csa::kDensePart * sizeof(float));
 }
 
 int csa_dense_decode_attention(const csa_shape *shape, const uint16_t *q, const uint16_t *K, const uint16_t *V,
@@ -614,7 +615,8 @@ int csa_dense_decode_attention(const csa_shape *shape, const uint16_t *q, const 
   a.n_cap = shape->n_cap;
   a.n = n;
   a.G = shape->group_size;
-  a.nsplit = csa::dense_nsplit(n);
+  a.nsplit = csa::dense_nsplit(n, shape->num_kv_heads);
+  a.split_len = csa::dense_split_len(n, shape->num_kv_heads);
   a.part = static_cast<float *>(workspace);
   a.o = o;
   hipError_t e = csa::launch_dense(a, shape->num_kv_heads, (hipStream_t)stream);
