@@ -28,7 +28,7 @@ class Packed(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("eps", c_double), ("delta", c_double), ("r", c_int32), ("J", c_int32),
                 ("window", c_int32), ("measure", c_int32), ("seed", c_uint64), ("step", c_uint64),
-                ("layer", c_int32), ("cand_budget", c_int32)]
+                ("layer", c_int32), ("cand_budget", c_int32), ("cand_budget2", c_int32)]
 
 
 class Trace(ctypes.Structure):

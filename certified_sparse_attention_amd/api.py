@@ -72,10 +72,11 @@ def _shape(K: torch.Tensor, G: int) -> _lib.Shape:
     return _lib.Shape(K.shape[0], G, 128, K.shape[1])
 
 
-def _params(eps, delta, r, J, window, measure, seed, step, layer, cand_budget=0) -> _lib.Params:
+def _params(eps, delta, r, J, window, measure, seed, step, layer, cand_budget=0, cand_budget2=0) -> _lib.Params:
     m = MEASURES[measure] if isinstance(measure, str) else int(measure)
     return _lib.Params(float(eps), float(delta), int(r), int(J), int(window), m,
-                       int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), int(layer), int(cand_budget))
+                       int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), int(layer), int(cand_budget),
+                       int(cand_budget2))
 
 
 def pack_kv_4bit(K: torch.Tensor, V: torch.Tensor, packed: PackedKV | None = None,
@@ -138,7 +139,7 @@ def certified_decode_attention(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
                                n: int, *, eps: float, delta: float, r: int, J: int, window: int = 64,
                                seed: int = 0x5EED, step: int = 0, layer: int = 0, measure="value",
                                workspace: torch.Tensor | None = None, trace: bool | dict = False,
-                               scan_events=None, out=None, cand_budget: int = 0):
+                               scan_events=None, out=None, cand_budget: int = 0, cand_budget2: int = 0):
     """One certified decode step of one layer.
 
     q: fp16 [H_q][128]; K, V: fp16 [H_kv][n_cap][128].  Returns (o_hat fp32 [H_q][128],
@@ -155,7 +156,7 @@ def certified_decode_attention(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
     H_q = q.shape[0]
     lib = _lib.load()
     sh = _shape(K, G)
-    pr = _params(eps, delta, r, J, window, measure, seed, step, layer, cand_budget)
+    pr = _params(eps, delta, r, J, window, measure, seed, step, layer, cand_budget, cand_budget2)
     need = int(lib.csa_workspace_bytes(ctypes.byref(sh), ctypes.byref(pr), int(n)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -1,4 +1,6 @@
 // C ABI of the certified decode path (declarations and contracts in include/csa.h).
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -86,6 +88,7 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.vmax = take((size_t)P.H_kv * sizeof(unsigned));
   P.bdone = take(Hq * sizeof(int));
   P.exdone = take(Hq * sizeof(int));
+  P.exdone2 = take(Hq * sizeof(int));
   P.hist = take(Hq * J2 * sizeof(int));
   P.tilecnt = 0;
   P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
@@ -96,6 +99,8 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.ccount = take(Hq * sizeof(int));
   P.ccount1 = take(Hq * sizeof(int));
   P.jspec = take(Hq * sizeof(int));
+  P.ccount2 = take(Hq * sizeof(int));
+  P.jspec2 = take(Hq * sizeof(int));
   P.pbuf = take(Hq * npc * sizeof(double));
   P.ubuf = take(Hq * npc * sizeof(double));
   P.lub = take(Hq * npc);
@@ -113,6 +118,7 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.dhatlv = take(Hq * J1 * sizeof(double));
   P.klv = take(Hq * J1 * sizeof(int));
   P.flags = take(Hq * sizeof(int));
+  P.flags2 = take(Hq * sizeof(int));
   P.exactp = take(Hq * csa::kExactChunks * 130 * sizeof(double));
   P.total = off;
   return P;
@@ -159,6 +165,7 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.flags = at<int>(ws, P.flags);
   pa.bdone = at<int>(ws, P.bdone);
   pa.exdone = at<int>(ws, P.exdone);
+  pa.exdone2 = at<int>(ws, P.exdone2);
   pa.npool_cap = P.npool_cap;
   hipError_t e = csa::launch_prep(pa, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
@@ -250,16 +257,19 @@ __global__ __launch_bounds__(256) void trace_kernel(const double *qconst, const 
 }
 
 // Per-candidate trace, grid (H_q, ceil(npool / 256)): the candidate list and the levels
-// of the entries that were rescored.  Pass 1 rescores the first ccount1 entries (those
-// with l^ub up to the speculative level); a head whose stop level lies past that level
-// went through the second pass or the exact fallback after it, which rescored all.
+// of the entries that were rescored.  Pass p rescores the entries up to the end of its
+// range (levels up to jspec, jspec2, J); a head whose stop level lies past a pass's
+// deepest level went through the next one (the exact fallback only after the last
+// pass, which rescored all).
 __global__ __launch_bounds__(256) void cand_trace_kernel(const int *ccount, const int *ccount1, const int *jspec,
+                                                         const int *ccount2, const int *jspec2,
                                                          const int32_t *stop, const int *candpos, const int *rec_hl,
                                                          int64_t npool_cap, int64_t npool, int32_t *cand_pos,
                                                          int32_t *cand_hl, int32_t *rescored) {
   const int hq = blockIdx.x;
   const int cnt = ccount[hq];
-  const int nres = (stop[hq] <= jspec[hq]) ? ccount1[hq] : cnt;
+  const int st = stop[hq];
+  const int nres = (st <= jspec[hq]) ? ccount1[hq] : ((st <= jspec2[hq]) ? ccount2[hq] : cnt);
   if (blockIdx.y == 0 && threadIdx.x == 0 && rescored) rescored[hq] = nres;
   const int64_t i = (int64_t)blockIdx.y * 256 + threadIdx.x;
   if (i >= cnt || i >= npool) return;
@@ -465,11 +475,14 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
     sa.tilehist = at<int>(ws, P.tilehist);
     sa.ccount1 = at<int>(ws, P.ccount1);
     sa.jspec = at<int>(ws, P.jspec);
+    sa.ccount2 = at<int>(ws, P.ccount2);
+    sa.jspec2 = at<int>(ws, P.jspec2);
     sa.flags = at<int>(ws, P.flags);
     sa.bdone = at<int>(ws, P.bdone);
     sa.tilecm = at<int>(ws, P.tilecm);
     sa.cmhist = at<int>(ws, P.cmhist);
     sa.budget = params->cand_budget > 0 ? params->cand_budget : csa::kDefaultBudget;
+    sa.budget2 = params->cand_budget2 > 0 ? params->cand_budget2 : INT_MAX;   // default: no third range
     sa.pass = 1;
     sa.ccount = at<int>(ws, P.ccount);
     sa.lub = at<int8_t>(ws, P.lub);
@@ -525,6 +538,11 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.flags = at<int>(ws, P.flags);
   ca.exactp = at<double>(ws, P.exactp);
   ca.exdone = at<int>(ws, P.exdone);
+  ca.exdone2 = at<int>(ws, P.exdone2);
+  ca.flags2 = at<int>(ws, P.flags2);
+  ca.ccount2 = at<int>(ws, P.ccount2);
+  ca.jspec2 = at<int>(ws, P.jspec2);
+  ca.H_q = P.H_q;
   ca.nseg_cap = P.nseg_cap;
   ca.cmhist = at<int>(ws, P.cmhist);
   ca.o_hat = o_hat;
@@ -547,7 +565,7 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   }
   // the tail: pass 2 for the heads that need all levels (their remaining candidates are
   // rescored there) and the exact fallback, in one launch that certified heads leave at once
-  if ((e = csa::launch_tail(ca, P.H_q, st)) != hipSuccess) return hip_fail(e, "tail");
+  if ((e = csa::launch_tail(ca, P.H_q, params->cand_budget2 > 0, st)) != hipSuccess) return hip_fail(e, "tail");
 
   if (trace) {
     const int Hq = P.H_q;
@@ -567,7 +585,8 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
     if (!all_exact && (trace->cand_pos || trace->cand_hl || trace->rescored_count)) {
       const unsigned ny = (unsigned)((npool + 255) / 256);
       hipLaunchKernelGGL(cand_trace_kernel, dim3(Hq, ny), dim3(256), 0, st, at<int>(ws, P.ccount),
-                         at<int>(ws, P.ccount1), at<int>(ws, P.jspec), stop_level, at<int>(ws, P.candpos),
+                         at<int>(ws, P.ccount1), at<int>(ws, P.jspec), at<int>(ws, P.ccount2),
+                         at<int>(ws, P.jspec2), stop_level, at<int>(ws, P.candpos),
                          at<int>(ws, P.rec_hl), P.npool_cap, npool, trace->cand_pos, trace->cand_hl,
                          trace->rescored_count);
       if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "candidate trace");

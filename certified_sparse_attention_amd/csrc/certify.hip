@@ -41,10 +41,16 @@ struct CertArgs {
   const int8_t *lub;
   double *partial, *betalv, *dhatlv;
   int nseg_cap;                 // segment rows per query head in `partial` (seg_cap_for(npool))
-  int *klv, *flags;
-  int *exdone;                  // [H_q] chunks of the exact fallback that have finished
-  const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list
-  int pass;                     // 1: levels <= jspec; 2: all levels, heads flagged for extension
+  int *klv;
+  int *flags;                   // [H_q] after pass 1: 0 certified, 1 exact fallback, 2 second pass
+  int *flags2;                  // [H_q] after pass 2 (heads with flags 2): 0, 1, or 3 third pass
+  int *exdone, *exdone2;        // [H_q] finished work items of the second / third-pass launch
+  const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list,
+  const int *ccount2, *jspec2;  // then those with jspec < l^ub <= jspec2, then the rest
+  int H_q;
+  int pass;                     // 1: levels <= jspec; 2: levels <= jspec2; 3: all levels
+  int final_pass;               // the last tail launch (2 when jspec2 = J, else 3): it also
+                                // takes the exact fallback
   int fused_rescore;            // pass 1 rescoring happens in the certificate kernel
   const uint64_t *prefix;       // per KV head hash prefixes
   double *rec_s;
@@ -60,9 +66,20 @@ constexpr int kFusedMax = 2048;   // heads with more candidates use the segmente
 constexpr int kStage = 64;        // candidates staged in LDS at a time
 
 // Candidates this pass accumulates for query head hq (-1: the head is not in this pass).
+// Pass p takes every candidate up to its deepest level: the ones earlier passes rescored
+// from their records, the new ones rescored here.
 __device__ inline int pass_count(const CertArgs &a, int hq) {
   if (a.pass == 1) return a.ccount1[hq];
-  return (a.flags[hq] == 2) ? a.ccount[hq] : -1;
+  if (a.pass == 2) return (a.flags[hq] == 2) ? a.ccount2[hq] : -1;
+  return (a.flags[hq] == 2 && a.flags2[hq] == 3) ? a.ccount[hq] : -1;
+}
+__device__ inline int pass_jmax(const CertArgs &a, int hq) {
+  return (a.pass == 1) ? a.jspec[hq] : ((a.pass == 2) ? a.jspec2[hq] : a.J);
+}
+// The head's state after this pass (read by the next launch; pass 3 is the last).
+__device__ inline void set_status(const CertArgs &a, int hq, int v) {
+  if (a.pass == 1) a.flags[hq] = v;
+  else if (a.pass == 2) a.flags2[hq] = v;
 }
 
 // Most segments a head with at most npool candidates can use (rows of `partial`).
@@ -249,10 +266,10 @@ __device__ void accumulate_mixed(const CertArgs &a, AccSmem &s, int hq, int i0, 
 }
 
 // Which candidates of this pass already have records: the first pass's, when a separate
-// kernel rescored them, and in the second pass the first pass's range.
+// kernel rescored them, and in later passes the earlier passes' ranges.
 __device__ inline int record_split(const CertArgs &a, int hq, int count) {
   if (a.pass == 1) return a.fused_rescore ? 0 : count;
-  return a.ccount1[hq];
+  return (a.pass == 2) ? a.ccount1[hq] : a.ccount2[hq];
 }
 
 constexpr int kSegWorkers = 8;   // workgroups per query head for the segmented accumulation
@@ -360,14 +377,16 @@ struct FinSmem {
 // certificate of every level up to the pass's last level, the stop level and the outputs.
 // Returns true when a level certifies (outputs written); otherwise the head is flagged
 // for the extension pass (2) or for the exact fallback (1).  Uniform across the group.
-__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
+// nparts: partial tables of this pass written by other workgroups (0: accumulate every
+// candidate here; -1: as many as seg_range gives for the count).
+__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts = -1) {
   const int t = threadIdx.x, h = hq / a.G;
   const int lane = t & 63, wv = t >> 6;
   AccSmem &s = f.s;
   const int J1 = a.J + 1;
   // every load that does not depend on the candidate count is issued before it is used
   const int count = pass_count(a, hq);
-  const int jmax = (a.pass == 1) ? a.jspec[hq] : a.J;
+  const int jmax = pass_jmax(a, hq);
   for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
   fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
   for (int j = t; j < a.J + 2; j += 256) {
@@ -387,13 +406,23 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
   if (count < 0) return false;
   int i0, i1, nseg;
   seg_range(count, 0, i0, i1, nseg);
+  if (nparts >= 0) nseg = nparts;
   if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
   } else {
     for (int e = t; e < J1 * kStatW; e += 256) {
       double v = 0.0;
-      for (int sg = 0; sg < nseg; ++sg) v += a.partial[((int64_t)hq * a.nseg_cap + sg) * J1 * kStatW + e];
+      const double *col = a.partial + (int64_t)hq * a.nseg_cap * J1 * kStatW + e;
+      int sg = 0;
+      for (; sg + 8 <= nseg; sg += 8) {
+        double x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = col[(int64_t)(sg + k) * J1 * kStatW];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += x[k];
+      }
+      for (; sg < nseg; ++sg) v += col[(int64_t)sg * J1 * kStatW];
       (&s.acc[0][0])[e] = v;
     }
     __syncthreads();
@@ -500,11 +529,11 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
   __syncthreads();
   const int js = f.jstar;
   if (js > a.J || (js > jmax)) {
-    // no level up to jmax certifies: either the extension pass takes the rest of the
-    // levels, or (jmax = J) the head falls back to exact attention
+    // no level up to jmax certifies: either the next pass takes deeper levels, or
+    // (jmax = J) the head falls back to exact attention
     if (t == 0) {
       const bool extend = (jmax < a.J);
-      a.flags[hq] = extend ? 2 : 1;
+      set_status(a, hq, extend ? a.pass + 1 : 1);
       a.stop[hq] = a.J + 1;
       a.beta[hq] = 0.0;
       a.keys_read[hq] = a.n;
@@ -532,7 +561,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq) {
   if (t < kD)
     a.o_hat[(int64_t)hq * kD + t] = (float)(((f.nr[t] + s.acc[js][t]) + tau * s.acc[js][128 + t]) / D_hat);
   if (t == 0) {
-    a.flags[hq] = 0;
+    set_status(a, hq, 0);
     a.stop[hq] = js;
     a.beta[hq] = f.beta[js];
     a.keys_read[hq] = (int64_t)a.W + f.extra[1] + f.extra[0];
@@ -604,69 +633,158 @@ __device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0,
   __syncthreads();
 }
 
-constexpr int kTailWG = kExactChunks;   // workgroups per query head in the tail
+constexpr int kTailWG = kExactChunks;   // tail workgroups per query head (at least 256 in all)
 
-// Everything after pass 1, for the heads pass 1 did not certify; grid (H_q, kTailWG), 256
-// threads.  Heads flagged for the extension pass: workgroup y accumulates segments y,
-// y + kTailWG, ... of the long candidate lists, and the last workgroup of the head to
-// finish (a counter behind a device-wide fence) runs the extension certificate; if no
-// level certifies, that workgroup computes the exact output over all keys by itself.
-// Heads flagged for the exact fallback by pass 1: workgroup y sums the exact attention
-// over the y-th chunk of the keys and the last one combines the chunks.  Certified
-// heads exit at once.
+// What query head hq does in the tail launch of pass a.pass (2 or 3), and how much: the
+// pass's candidates (kind = the pass), or, in the final launch, the exact fallback
+// (kind 1).  Work units: blocks of 1024 candidates (at most one unit when the certificate
+// workgroup can take them all), or the fallback's chunks.  Built from the states the
+// earlier launches left, which nothing in this launch changes, so every workgroup sees
+// the same plan.
+__device__ inline int tail_units(const CertArgs &a, int hq, int &kind) {
+  const int s1 = a.flags[hq];
+  int i0, i1, nseg;
+  kind = 0;
+  if (a.pass == 2) {
+    if (s1 == 1 && a.final_pass == 2) {
+      kind = 1;
+      return kExactChunks;
+    }
+    if (s1 != 2) return 0;
+    kind = 2;
+    seg_range(a.ccount2[hq], 0, i0, i1, nseg);
+    return max(1, nseg);
+  }
+  const int s2 = (s1 == 2) ? a.flags2[hq] : -1;
+  if (s2 == 3) {
+    kind = 3;
+    seg_range(a.ccount[hq], 0, i0, i1, nseg);
+    return max(1, nseg);
+  }
+  if (s1 == 1 || s2 == 1) {
+    kind = 1;
+    return kExactChunks;
+  }
+  return 0;
+}
+
+// One launch per later pass (grid of at least 256 workgroups, 256 threads).  Every head
+// with work gets its own contiguous group of workgroups, sized by its share of all the
+// work units (at least one, at most its own units), and each workgroup of a group takes
+// one contiguous range of the head's candidates (or of its keys, for the fallback) and
+// writes one partial table; the group's last workgroup to finish (a counter behind a
+// device-wide fence) sums the group's tables and runs the certificate, or combines the
+// fallback's chunks.  A group of one accumulates everything itself.  A certificate of
+// the final pass that finds no level computes the exact output by itself (slow, and
+// rare: the final pass covers every level up to J).  Heads with nothing to do cost one
+// read of their states.
 __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
-  const int hq = blockIdx.x, y = blockIdx.y, t = threadIdx.x;
-  const int fl = a.flags[hq];
-  if (fl == 0) return;
+  const int t = threadIdx.x;
+  const int nwg = (int)gridDim.x, w = (int)blockIdx.x;
   __shared__ union {
     FinSmem f;
     ExactSmem e;
   } u;
+  __shared__ int red[4][2];
+  __shared__ int grp[2][256];     // per head of the chunk: group size, group start
   __shared__ int last;
   AccSmem &s = u.f.s;
-  if (fl == 2) {
-    const int count = a.ccount[hq];
-    int i0, i1, nseg;
-    seg_range(count, 0, i0, i1, nseg);
-    if (nseg > 0) {
-      const int J1 = a.J + 1;
-      fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
-      const int split = record_split(a, hq, count);
-      for (int seg = y; seg < nseg; seg += kTailWG) {
-        seg_range(count, seg, i0, i1, nseg);
-        zero_acc(s, J1);
-        accumulate_mixed(a, s, hq, i0, i1, split);
-        double *out = a.partial + ((int64_t)hq * a.nseg_cap + seg) * J1 * kStatW;
-        for (int e = t; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
-        __syncthreads();
-      }
-    }
-  } else {
-    const int64_t len = (a.n + kTailWG - 1) / kTailWG;
-    const int64_t i0 = y * len, i1 = min<int64_t>(a.n, i0 + len);
-    exact_chunk(a, u.e, hq, i0, i1, a.exactp + ((int64_t)hq * kExactChunks + y) * 130);
+  int *done = (a.pass == 2) ? a.exdone : a.exdone2;
+  // totals over all heads: work units and heads with work
+  int units = 0, busy = 0;
+  for (int hq = t; hq < a.H_q; hq += 256) {
+    int kind;
+    const int n = tail_units(a, hq, kind);
+    units += n;
+    busy += (n > 0);
   }
-  __threadfence();
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    units += __shfl_xor(units, off, 64);
+    busy += __shfl_xor(busy, off, 64);
+  }
+  if ((t & 63) == 0) {
+    red[t >> 6][0] = units;
+    red[t >> 6][1] = busy;
+  }
   __syncthreads();
-  if (t == 0) last = (atomicAdd(a.exdone + hq, 1) == kTailWG - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (fl == 2) {
-    if (certify_head(a, u.f, hq)) return;
+  const int64_t T = (int64_t)red[0][0] + red[1][0] + red[2][0] + red[3][0];
+  const int64_t B = (int64_t)red[0][1] + red[1][1] + red[2][1] + red[3][1];
+  if (T == 0) return;
+  const int64_t spare = max<int64_t>(0, (int64_t)nwg - B);   // nwg >= H_q >= B
+  int64_t start = 0;                                         // first workgroup of this chunk
+  for (int h0 = 0; h0 < a.H_q; h0 += 256) {
     __syncthreads();
-    exact_chunk(a, u.e, hq, 0, a.n, a.exactp + (int64_t)hq * kExactChunks * 130);
-    if (t < kD) a.o_hat[(int64_t)hq * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);
-    return;
-  }
-  if (t < kD) {
-    double N = 0.0, Dn = 0.0;
-    for (int c = 0; c < kTailWG; ++c) {
-      const double *p = a.exactp + ((int64_t)hq * kExactChunks + c) * 130;
-      N += p[t];
-      Dn += p[kD];
+    int kind = 0;
+    const int hq = h0 + t;
+    const int n = (hq < a.H_q) ? tail_units(a, hq, kind) : 0;
+    const int g = (n > 0) ? (int)max<int64_t>(1, min<int64_t>(n, spare * n / T)) : 0;
+    grp[0][t] = g;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {                // inclusive scan of group sizes
+      const int v = (t >= off) ? grp[0][t - off] : 0;
+      __syncthreads();
+      grp[0][t] += v;
+      __syncthreads();
     }
-    a.o_hat[(int64_t)hq * kD + t] = (float)(N / Dn);
+    grp[1][t] = (int)start + grp[0][t] - g;                  // this head's first workgroup
+    __syncthreads();
+    const int64_t chunk_end = start + grp[0][255];
+    if (w >= start && w < chunk_end) {
+      int lo = 0, hi = 255;                                  // the head: first k with end > w
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (start + grp[0][mid] > w) hi = mid; else lo = mid + 1;
+      }
+      const int h = h0 + lo;
+      const int k = w - grp[1][lo];                          // this workgroup's part
+      int k2 = 0;
+      tail_units(a, h, k2);
+      const int gsz = grp[0][lo] - (lo > 0 ? grp[0][lo - 1] : 0);
+      if (k2 == 1) {
+        const int64_t len = (a.n + gsz - 1) / gsz;
+        const int64_t i0 = k * len, i1 = min<int64_t>(a.n, i0 + len);
+        exact_chunk(a, u.e, h, i0, i1, a.exactp + ((int64_t)h * kExactChunks + k) * 130);
+      } else if (gsz > 1) {
+        const int count = pass_count(a, h);
+        const int len = (count + gsz - 1) / gsz;
+        const int i0 = min(count, k * len), i1 = min(count, i0 + len);
+        const int J1 = a.J + 1;
+        fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
+        zero_acc(s, J1);
+        accumulate_mixed(a, s, h, i0, i1, record_split(a, h, count));
+        double *out = a.partial + ((int64_t)h * a.nseg_cap + k) * J1 * kStatW;
+        for (int e = t; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
+      }
+      bool run = true;
+      if (gsz > 1) {
+        __threadfence();
+        __syncthreads();
+        if (t == 0) last = (atomicAdd(done + h, 1) == gsz - 1);
+        __syncthreads();
+        run = last;
+        if (run) __threadfence();
+      }
+      if (run) {
+        if (k2 == 1) {
+          if (t < kD) {
+            double N = 0.0, Dn = 0.0;
+            for (int c = 0; c < gsz; ++c) {
+              const double *p = a.exactp + ((int64_t)h * kExactChunks + c) * 130;
+              N += p[t];
+              Dn += p[kD];
+            }
+            a.o_hat[(int64_t)h * kD + t] = (float)(N / Dn);
+          }
+        } else if (!certify_head(a, u.f, h, gsz > 1 ? gsz : 0) && a.pass == a.final_pass) {
+          __syncthreads();
+          exact_chunk(a, u.e, h, 0, a.n, a.exactp + (int64_t)h * kExactChunks * 130);
+          if (t < kD) a.o_hat[(int64_t)h * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);
+        }
+      }
+      return;                                                // one part per workgroup
+    }
+    start = chunk_end;
   }
 }
 
@@ -677,9 +795,19 @@ hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, bool segmented, hi
   return hipGetLastError();
 }
 
-hipError_t launch_tail(CertArgs a, int H_q, hipStream_t st) {
+// The later passes and the exact fallback, in launches that heads certified earlier leave
+// at once: one launch when the second pass covers every level (the default), two when a
+// second budget splits the remaining levels.
+hipError_t launch_tail(CertArgs a, int H_q, bool three_pass, hipStream_t st) {
+  const unsigned nwg = (unsigned)max(256, min(4096, H_q * kTailWG));
+  a.H_q = H_q;
+  a.final_pass = three_pass ? 3 : 2;
   a.pass = 2;
-  hipLaunchKernelGGL(tail_kernel, dim3(H_q, kTailWG), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(tail_kernel, dim3(nwg), dim3(256), 0, st, a);
+  if (three_pass) {
+    a.pass = 3;
+    hipLaunchKernelGGL(tail_kernel, dim3(nwg), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

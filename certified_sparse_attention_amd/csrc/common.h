@@ -368,7 +368,8 @@ struct Plan {
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
   size_t clo, cstar, vmax, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
       jspec;
-  size_t bdone, exdone;  // per-head completion counters (last-workgroup reductions)
+  size_t bdone, exdone, exdone2;  // per-head completion counters (last-workgroup reductions)
+  size_t ccount2, jspec2, flags2;
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
   int nseg_cap;        // segment rows per query head in `partial`

@@ -47,7 +47,7 @@ struct PrepArgs {
   unsigned long long *clo, *cstar;
   unsigned *vmax;
   int *hist, *ccount, *flags;
-  int *bdone, *exdone;   // per-head completion counters, cleared here
+  int *bdone, *exdone, *exdone2;   // per-head completion counters, cleared here
 };
 
 // One workgroup of 128 threads per query head; thread t owns channel t.
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
     a.flags[hq] = 0;
     a.bdone[hq] = 0;
     a.exdone[hq] = 0;
+    a.exdone2[hq] = 0;
   }
   for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
 }

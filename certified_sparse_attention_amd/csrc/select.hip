@@ -33,12 +33,14 @@ struct SelectArgs {
   int full_lub;           // write l^ub for every pool key (diagnostics)
   int *tilehist;          // [H_q][ntiles][J+2] per-tile cumulative counts of l^ub
   int *tileoff2;          // [H_q][ntiles] offsets of the second range
-  int *ccount1, *jspec;   // [H_q]
+  int *ccount1, *jspec;   // [H_q] end of the first range and its deepest level
+  int *ccount2, *jspec2;  // [H_q] end of the second range and its deepest level
   int *bdone;             // [H_q] tiles whose histogram is written
   int *tilecm;            // [H_q][ntiles][J+2] C_max keys per level and tile
   int *cmhist;            // [H_q][J+2] C_max keys per level
   const int *flags;
   int budget;             // candidates rescored before the first certificate pass
+  int budget2;            // candidates (all ranges so far) before the third pass
   int pass;
 };
 
@@ -143,11 +145,12 @@ __device__ inline void sum_tiles(const int *base, int64_t ntiles, int w, int lan
   *before = pre;
 }
 
-// Stable compaction of both ranges (l^ub <= jspec first, then jspec < l^ub <= J, each in
-// position order): thread = bitmap word.  Every tile's workgroup sums the head's tile
-// histograms itself (they are small and L2-resident), which gives the level histogram,
-// the speculative level jspec (the deepest level whose cumulative candidate count fits
-// the budget) and, from the tiles before it, the tile's offsets without a separate pass.
+// Stable compaction of the three ranges (l^ub <= j1, then j1 < l^ub <= j2, then
+// j2 < l^ub <= J, each in position order): thread = bitmap word.  Every tile's workgroup
+// sums the head's tile histograms itself (they are small and L2-resident), which gives the
+// level histogram, the speculative levels (j1 the deepest level whose cumulative candidate
+// count fits the budget, j2 > j1 the deepest one within the second budget) and, from the
+// tiles before it, the tile's offsets without a separate pass.
 __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
@@ -169,8 +172,11 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   // level 0 alone exceeds the budget, and the first pass then has no candidates
   const unsigned long long fit = __ballot(lane <= J && cum <= a.budget);
   const int js = __popcll(fit) - 1;
+  const unsigned long long fit2 = __ballot(lane <= J && cum <= a.budget2);
+  const int js2 = min(J, max(js + 1, __popcll(fit2) - 1));       // at least one level past j1
   const int tot1v = __shfl(cum, max(js, 0), 64), totJ = __shfl(cum, J, 64);
   const int pre1v = __shfl(pre, max(js, 0), 64), preJ = __shfl(pre, J, 64);
+  const int tot2 = __shfl(cum, js2, 64), pre2 = __shfl(pre, js2, 64);
   const int tot1 = (js >= 0) ? tot1v : 0;
   if (tile == 0) {
     const int below = __shfl_up(cum, 1, 64);
@@ -178,6 +184,8 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     if (lane == 0) {
       a.jspec[hq] = js;
       a.ccount1[hq] = tot1;
+      a.jspec2[hq] = js2;
+      a.ccount2[hq] = tot2;
       a.ccount[hq] = totJ;
     }
     // C_max keys per bucket level
@@ -187,9 +195,10 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       a.cmhist[(int64_t)hq * J2 + lane] = cm;
     }
   }
-  // this tile's offsets: candidates of both ranges in the earlier tiles
+  // this tile's offsets: candidates of each range in the earlier tiles
   const int b1 = (js >= 0) ? pre1v : 0;
-  const int b2 = preJ - b1;
+  const int b2 = pre2 - b1;
+  const int b3 = preJ - pre2;
   const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p0));
   const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
   int *dst = a.candpos + (int64_t)hq * a.npool_cap;
@@ -207,26 +216,29 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     int lv[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) lv[k] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs_lub, 64 * k + lane, 0, 0);
-    int o1 = b1, o2 = tot1 + b2;
+    int o1 = b1, o2 = tot1 + b2, o3 = tot2 + b3;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const uint32_t wk = (uint32_t)__shfl((int)bits, 2 * k + (lane >> 5), 64);
       const bool on = ((wk >> (lane & 31)) & 1u) != 0u;
       const int l = lv[k];
-      const bool in1 = on && l <= js, in2 = on && l > js && l <= J;
-      const unsigned long long m1 = __ballot(in1), m2 = __ballot(in2);
+      const bool in1 = on && l <= js, in2 = on && l > js && l <= js2, in3 = on && l > js2 && l <= J;
+      const unsigned long long m1 = __ballot(in1), m2 = __ballot(in2), m3 = __ballot(in3);
       const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
       const int r2 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m2, 0u));
+      const int r3 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m3 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m3, 0u));
       const int pos = (int)(p_tile + 64 * k + lane);
       if (in1) dst[o1 + r1] = pos;
       if (in2) dst[o2 + r2] = pos;
+      if (in3) dst[o3 + r3] = pos;
       o1 += __popcll(m1);
       o2 += __popcll(m2);
+      o3 += __popcll(m3);
     }
     return;
   }
   // a sparse tile: thread = bitmap word, its candidates in bit order after the earlier words'
-  uint32_t m1 = 0, m2 = 0;
+  uint32_t m1 = 0, m2 = 0, m3 = 0;
   if (bits) {
     const uint32_t wds[8] = {lv0.x, lv0.y, lv0.z, lv0.w, lv1.x, lv1.y, lv1.z, lv1.w};
 #pragma unroll
@@ -234,20 +246,22 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
       if ((bits >> b) & 1u) {
         const int l = (int)(int8_t)((wds[b >> 2] >> (8 * (b & 3))) & 0xFFu);
         if (l <= js) m1 |= 1u << b;
-        else if (l <= J) m2 |= 1u << b;
+        else if (l <= js2) m2 |= 1u << b;
+        else if (l <= J) m3 |= 1u << b;
       }
     }
   }
-  const int n1 = __popc(m1), n2 = __popc(m2);
+  const int n1 = __popc(m1), n2 = __popc(m2), n3 = __popc(m3);
   // exclusive prefix over the 64 lanes
-  int x1 = n1, x2 = n2;
+  int x1 = n1, x2 = n2, x3 = n3;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64);
-    if (lane >= off) { x1 += y1; x2 += y2; }
+    const int y1 = __shfl_up(x1, off, 64), y2 = __shfl_up(x2, off, 64), y3 = __shfl_up(x3, off, 64);
+    if (lane >= off) { x1 += y1; x2 += y2; x3 += y3; }
   }
   int o1 = b1 + x1 - n1;
   int o2 = tot1 + b2 + x2 - n2;
+  int o3 = tot2 + b3 + x3 - n3;
   while (m1) {
     const int b = __ffs(m1) - 1;
     m1 &= m1 - 1u;
@@ -257,6 +271,11 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     const int b = __ffs(m2) - 1;
     m2 &= m2 - 1u;
     dst[o2++] = (int)(p0 + b);
+  }
+  while (m3) {
+    const int b = __ffs(m3) - 1;
+    m3 &= m3 - 1u;
+    dst[o3++] = (int)(p0 + b);
   }
 }
 

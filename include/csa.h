@@ -106,7 +106,12 @@ typedef struct {
   int32_t layer;
   int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 32);
                           heads that certify at no level up to that point get a second pass
-                          over the remaining levels.  Results do not depend on it. */
+                          over deeper levels.  Results do not depend on it. */
+  int32_t cand_budget2; /* 0 (default): the second pass takes every remaining level.  Else
+                           the candidates (all passes so far) the second pass may take; it
+                           takes at least one level more than the first, and heads still
+                           uncertified get a third pass over every remaining level (one more
+                           launch).  Results do not depend on it. */
 } csa_params;
 
 /*

@@ -335,12 +335,12 @@ def test_stream_read_checksum():
             assert got[w] == (np.bitwise_xor.reduce(part) if part.size else 0), (nbytes, wgs, w)
 
 
-@pytest.mark.parametrize("budget", [1, 16, 300])
-def test_speculative_budget_does_not_change_results(case, budget):
-    """A small candidate budget forces the second pass; results stay oracle-exact."""
+@pytest.mark.parametrize("budget,budget2", [(1, 0), (16, 0), (300, 0), (1, 3), (4, 40)])
+def test_speculative_budget_does_not_change_results(case, budget, budget2):
+    """Small candidate budgets force the second and third passes; results stay oracle-exact."""
     w = case["w"]
     kw = _kw(w)
     out = _csa().certified_decode_attention(case["q"], case["K"], case["V"], case["packed"], w.n,
-                                            trace=True, cand_budget=budget, **kw)
+                                            trace=True, cand_budget=budget, cand_budget2=budget2, **kw)
     torch.cuda.synchronize()
     _compare_decode(w, case["pk_ref"], out[:4], out[4], **kw)
