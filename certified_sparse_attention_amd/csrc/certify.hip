@@ -97,7 +97,7 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
 }
 
 struct AccSmem {
-  double acc[kMaxJ + 1][kStatW];        // per-level increments: N[128] V[128] D Q k P
+  alignas(16) double acc[kMaxJ + 1][kStatW];   // per-level increments: N[128] V[128] D Q k P
   double2 ltp[kMaxJ + 2];               // level table in neighbour pairs (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   alignas(16) int hl[kStage];           // read eight at a time
@@ -190,66 +190,102 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
   }
 }
 
-// Exact rescoring of candidates [0, count) of query head hq inside the certificate
-// workgroup (scores and |v|^2 eight lanes per key, one lane per key for E and the
-// levels), then accumulation.  The records are also stored for a second pass.
-__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
-  const double2 *ltp = s.ltp;
+// Exact rescoring of the stage of candidates [c0, c0 + cnt) (cnt <= kStage) of query head
+// hq: scores and |v|^2 eight lanes per key, then one lane per key for E, the levels and
+// the weight; records into the stage (s.hl, s.w, s.vsq, staged V rows s.vs) and into the
+// global records.  The key and value rows are requested before E is formed, so the hash
+// and logarithm (and, with zero_rows, the clearing of the level increments) run while
+// they are in flight.
+__device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int hq, int c0, int cnt,
+                                              const double *q16, double cs, uint64_t prefix, double inv_l1,
+                                              int zero_rows = 0) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
-  const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
-  const double cs = dec_max(a.cstar[hq]);
-  const uint64_t prefix = a.prefix[h];
-  double q16[16];
+  if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
+  __syncthreads();
+  // wavefront wv takes keys 16 wv .. 16 wv + 15, eight lanes per key
+  uint4 kw[2][2], vw[2][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  for (int step = 0; step < 2; ++step) {
+    const int r = 16 * wv + 8 * step + s8;
+    kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
+    if (r < cnt) {
+      const int64_t row = ((int64_t)h * a.n_cap + s.pos[r]) * kD;
+      const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + row) + 2 * k8;
+      const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + row) + 2 * k8;
+      kw[step][0] = ksrc[0];
+      kw[step][1] = ksrc[1];
+      vw[step][0] = vsrc[0];
+      vw[step][1] = vsrc[1];
+    }
+  }
+  double E = 0.0;
+  if (t < cnt) E = perturbation(prefix, s.pos[t]);
+  // the level increments start at zero (rows 0..zero_rows-1), cleared while the rows arrive
+  for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const int r = 16 * wv + 8 * step + s8;
+    double p = 0.0, v = 0.0;
+    if (r < cnt) {
+      p = score_words(q16, kw[step][0], kw[step][1]);
+      // the V row is staged for the accumulation while its |v|^2 is formed
+      uint4 *vdst = reinterpret_cast<uint4 *>(s.vs[r]) + 2 * k8;
+      vdst[0] = vw[step][0];
+      vdst[1] = vw[step][1];
+      v = sumsq_words(vw[step][0], vw[step][1]);
+    }
+    const double sc = r1_combine8(p) * kRsqrtD;
+    const double vs = r1_combine8(v);
+    if (r < cnt && k8 == 0) {
+      s.w[r] = sc;       // the score for now; the weight below
+      s.vsq[r] = vs;
+    }
+  }
+  __syncthreads();
+  if (t < cnt) {
+    const double sc = s.w[t];
+    const int hl = level_of_pairs(sc - cs, s.ltp, a.J, inv_l1);
+    const int ll = level_of_pairs((sc + E) - cs, s.ltp, a.J, inv_l1);
+    const double w = exp(sc - cs);
+    const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
+    s.hl[t] = hl | (ll << 8);
+    s.w[t] = w;
+    s.vsq[t] = vsq;
+    a.rec_s[base + c0 + t] = sc;
+    a.rec_w[base + c0 + t] = w;
+    a.rec_vsq[base + c0 + t] = vsq;
+    a.rec_hl[base + c0 + t] = hl | (ll << 8);
+  }
+  __syncthreads();
+}
+
+// The per-query constants of rescoring: the query chunk of the lane (eight lanes per key,
+// sixteen channels each), c*, the hash prefix and 1 / log tau_1.
+struct RescoreConsts {
+  double q16[16];
+  double cs, inv_l1;
+  uint64_t prefix;
+};
+__device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem &s, int hq, RescoreConsts &c) {
+  const int k8 = threadIdx.x & 7;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c.q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  c.cs = dec_max(a.cstar[hq]);
+  c.prefix = a.prefix[hq / a.G];
+  c.inv_l1 = (a.J >= 1) ? 1.0 / s.ltp[1].y : 0.0;
+}
+
+// Exact rescoring of candidates [i0, i1) of query head hq inside the certificate
+// workgroup, stage by stage, each stage added into the level increments s.acc.
+__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+  RescoreConsts rc;
+  rescore_consts(a, s, hq, rc);
   for (int c0 = i0; c0 < i1; c0 += kStage) {
     const int cnt = min(kStage, i1 - c0);
-    if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
-    __syncthreads();
-    // exact scores and |v|^2: wavefront wv takes keys 16 wv .. 16 wv + 15
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const int r = 16 * wv + 8 * step + s8;
-      double p = 0.0, v = 0.0;
-      if (r < cnt) {
-        const int64_t row = ((int64_t)h * a.n_cap + s.pos[r]) * kD;
-        p = score_chunk(q16, a.K + row, k8);
-        // the V row is staged for the accumulation while its |v|^2 is formed
-        const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + row) + 2 * k8;
-        const uint4 v0 = vsrc[0], v1 = vsrc[1];
-        uint4 *vdst = reinterpret_cast<uint4 *>(s.vs[r]) + 2 * k8;
-        vdst[0] = v0;
-        vdst[1] = v1;
-        v = sumsq_words(v0, v1);
-      }
-      const double sc = r1_combine8(p) * kRsqrtD;
-      const double vs = r1_combine8(v);
-      if (r < cnt && k8 == 0) {
-        s.w[r] = sc;       // the score for now; the weight below
-        s.vsq[r] = vs;
-      }
-    }
-    __syncthreads();
-    if (t < cnt) {
-      const int pos = s.pos[t];
-      const double sc = s.w[t];
-      const double E = perturbation(prefix, pos);
-      const int hl = level_of_pairs(sc - cs, ltp, a.J, inv_l1);
-      const int ll = level_of_pairs((sc + E) - cs, ltp, a.J, inv_l1);
-      const double w = exp(sc - cs);
-      const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
-      s.hl[t] = hl | (ll << 8);
-      s.w[t] = w;
-      s.vsq[t] = vsq;
-      a.rec_s[base + c0 + t] = sc;
-      a.rec_w[base + c0 + t] = w;
-      a.rec_vsq[base + c0 + t] = vsq;
-      a.rec_hl[base + c0 + t] = hl | (ll << 8);
-    }
-    __syncthreads();
-    accumulate_stage(a, s, h, cnt, true);
+    rescore_stage(a, s, hq, c0, cnt, rc.q16, rc.cs, rc.prefix, rc.inv_l1);
+    accumulate_stage(a, s, hq / a.G, cnt, true);
   }
 }
 
@@ -361,7 +397,7 @@ struct FinSmem {
   double tau[kMaxJ + 1];
   int hist[kMaxJ + 2];
   int cmh[kMaxJ + 2];            // C_max keys per bucket level
-  double nr[kD];
+  alignas(16) double nr[kD];
   double vmax;
   double dr, qr;
   double beta[kMaxJ + 1];
@@ -407,7 +443,14 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   int i0, i1, nseg;
   seg_range(count, 0, i0, i1, nseg);
   if (nparts >= 0) nseg = nparts;
-  if (nseg == 0) {
+  // a single stage rescored here: the increments are cleared while its rows arrive
+  if (nseg == 0 && count <= kStage && record_split(a, hq, count) == 0) {
+    __syncthreads();            // the level table s.ltp is filled
+    RescoreConsts rc;
+    rescore_consts(a, s, hq, rc);
+    rescore_stage(a, s, hq, 0, count, rc.q16, rc.cs, rc.prefix, rc.inv_l1, jmax + 1);
+    accumulate_stage(a, s, hq / a.G, count, true);
+  } else if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
   } else {
@@ -467,14 +510,24 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
       const double D_hat = D_det + tau * s.acc[j][258];
       const double iD = 1.0 / D_det, iDh = 1.0 / D_hat;
       double cn2 = 0.0, cV = 0.0, dn2 = 0.0, on2 = 0.0;
-      for (int c = 32 * qt; c < 32 * qt + 32; ++c) {
-        const double nd = f.nr[c] + s.acc[j][c];
-        const double cc = nd * iD;
-        const double o = (nd + tau * s.acc[j][128 + c]) * iDh;
-        cn2 += cc * cc;
-        cV += cc * s.acc[j][128 + c];
-        dn2 += (o - cc) * (o - cc);
-        on2 += o * o;
+      // two channels per 16-byte read, added in channel order
+      const double2 *rN = reinterpret_cast<const double2 *>(&s.acc[j][32 * qt]);
+      const double2 *rV = reinterpret_cast<const double2 *>(&s.acc[j][128 + 32 * qt]);
+      const double2 *rR = reinterpret_cast<const double2 *>(&f.nr[32 * qt]);
+#pragma unroll 4
+      for (int c2 = 0; c2 < 16; ++c2) {
+        const double2 N2 = rN[c2], V2 = rV[c2], R2 = rR[c2];
+        const double Nc[2] = {N2.x, N2.y}, Vc[2] = {V2.x, V2.y}, Rc2[2] = {R2.x, R2.y};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const double nd = Rc2[e] + Nc[e];
+          const double cc = nd * iD;
+          const double o = (nd + tau * Vc[e]) * iDh;
+          cn2 += cc * cc;
+          cV += cc * Vc[e];
+          dn2 += (o - cc) * (o - cc);
+          on2 += o * o;
+        }
       }
       f.dpart[j][qt][0] = cn2;
       f.dpart[j][qt][1] = cV;

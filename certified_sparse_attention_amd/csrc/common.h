@@ -25,9 +25,10 @@ constexpr int kMaxJ = 60;
 constexpr int kMaxG = 7;
 constexpr int kBlocksPerWave = 16;                 // scan: blocks handled by one wavefront
 constexpr int kNumSeg = 64;                        // accumulate: max segments per query
-constexpr int kStatW = 261;                        // per-level stats N[128] V[128] D Q k P, and a
-                                                   // pad column (rows 522 dwords apart: level-
-                                                   // strided LDS reads spread over the banks)
+constexpr int kStatW = 262;                        // per-level stats N[128] V[128] D Q k P, and two
+                                                   // pad columns (rows 16-byte aligned and 524
+                                                   // dwords apart: level-strided LDS reads
+                                                   // spread over the banks)
 
 struct BlockMeta {   // 16 bytes per packed block
   float ksmax;
