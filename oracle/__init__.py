@@ -34,7 +34,7 @@ above and by agreement with the HIP path.
 from .canon import LN2, RSQRT_D, PADF, csum128, logtau, first_level  # noqa: F401
 from .dense import dense_attention, dense_attention_heads, exact_scores  # noqa: F401
 from .pack import pack_kv_4bit  # noqa: F401
-from .bounds import scan_bounds  # noqa: F401
+from .bounds import refine_bounds8, scan_bounds  # noqa: F401
 from .perturb import splitmix64_mix, hash_prefix, perturbations  # noqa: F401
 from .certify import kl, kl_upper_root, kl_lower_root, level_certificate, level_certificates, tails_per_level  # noqa: F401
 from .decode import certified_decode, certified_decode_layer, level_sums, scan_stage, sample_stage  # noqa: F401

@@ -108,3 +108,29 @@ def scan_bounds(q16: np.ndarray, packed: dict, h: int, npool: int) -> dict:
     LB = (shat - slack).reshape(G, 32 * nb)[:, :npool]
     return {"UB": UB, "LB": LB, "I": I.reshape(G, -1)[:, :npool],
             "C": C.reshape(-1)[:npool], "consts": bc}
+
+
+def refine_bounds8(q16: np.ndarray, packed: dict, h: int, positions) -> dict:
+    """8-bit refinement bounds UB8, LB8 [G][len(positions)] of the given keys of KV head h.
+
+    [S] Methodology > Algorithm Components item 4 (8-bit refinement before exact reads).
+    Reading taken (the HIP path follows the same written rules):
+      S8_gi    = R1-sum_t q_gt * (s8_i * k8_it)   (every product exact in fp64)
+      slack8   = (qnp_g * kerr8_i) + 2^-40 * ((128 * s8_i) * qabs_g)
+      UB8 = (S8 + slack8) * RSQRT_D,  LB8 = (S8 - slack8) * RSQRT_D   (fp64, this order).
+    Validity: q.k = q.k~8 + q.(k - k~8); Cauchy-Schwarz bounds the second term by
+    |q| kerr8_i <= qnp kerr8_i; the pad exceeds every fp64 rounding of S8, of the slack
+    and of the exact score, all relative to sum_t |q_t| |k_it| <= qabs * 128 s8_i.
+    """
+    pos = np.asarray(positions, dtype=np.int64)
+    qc = query_constants(q16)
+    qd = q16.astype(np.float64)
+    s8 = packed["s8"][h, pos].astype(np.float64)
+    kt = s8[:, None] * packed["k8"][h, pos].astype(np.float64)          # exact
+    kerr8 = packed["kerr8"][h, pos].astype(np.float64)
+    G = q16.shape[0]
+    S8 = np.empty((G, pos.size), dtype=np.float64)
+    for g in range(G):
+        S8[g] = csum128(qd[g][None, :] * kt) if pos.size else np.empty(0)
+    slack = (qc["qnp"][:, None] * kerr8[None, :]) + PADF * ((128.0 * s8)[None, :] * qc["qabs"][:, None])
+    return {"UB8": (S8 + slack) * RSQRT_D, "LB8": (S8 - slack) * RSQRT_D, "S8": S8}

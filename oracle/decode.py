@@ -11,9 +11,12 @@ Follows the method's steps in the pages' order:
 4. Perturbations E_i (``perturb``), and each pool key's earliest possible level
    l^ub = first((UB + E) - c*) ("bucketed by earliest possible inclusion level",
    [S] item 4).  Reading: buckets are taken relative to the exact c*.
-5. Exact 16-bit reads only for candidates (l^ub <= J): s_i, the heavy level
+5. The 8-bit refinement of every candidate (l^ub <= J): UB8 from the 8-bit copy
+   (``bounds.refine_bounds8``) and the refined level l8 = first((min(UB, UB8) + E) - c*)
+   ([S] item 4: 8-bit refinement, exact reads only for keys that may enter the sample).
+   Exact 16-bit reads only for candidates with l8 <= J: s_i, the heavy level
    h = first(s - c*) and the entry level l = first((s + E) - c*) (so l <= h, and
-   l^ub <= l because UB >= s).
+   l^ub <= l8 <= l because min(UB, UB8) >= s); the others have h = l = J + 1.
 6. Per level j (tau_j = exp(LOGTAU[j])): B_j = {h <= j} (w >= tau, always in),
    A_j = P \\ B_j, S_j = {l <= j}, k = |S_j & A_j|,
    D^ = D_R + D_B + tau k, N^ = N_R + N_B + tau sum_{S&A} v ([S] item 2); the
@@ -24,14 +27,15 @@ Follows the method's steps in the pages' order:
    stop level J + 1, keys read n.  With n <= window every key is in the window:
    o exact, beta = 0, stop level 0, keys read n.
 
-keys_read counts exact 16-bit key reads: window + |C_max union {l^ub <= j*}|
-(reading of "keys read", [S] Summary and Table 1's caption).
+keys_read counts exact 16-bit key reads: window + |C_max union {l8 <= j*}|
+(reading of "keys read", [S] Summary and Table 1's caption); the trace also gives the
+8-bit reads, |{l^ub <= j*}|.
 """
 
 import numpy as np
 
 from .canon import LN2, csum128, first_level, logtau  # noqa: F401
-from .bounds import scan_bounds
+from .bounds import refine_bounds8, scan_bounds
 from .certify import MEASURE_VALUE, budget_L, level_certificates
 from .dense import dense_attention, exact_scores
 from .perturb import perturbations
@@ -94,7 +98,7 @@ def scan_stage(q16, K16, V16, packed, h, n, *, window=64):
                     "c_star": c_star, "D_R": float(w_R.sum()), "N_R": w_R @ Vd_all[npool:n],
                     "Q_R": float(w_R @ vsq_all[npool:n])})
     return {"q16": q16, "K16": K16, "V16": V16, "h": h, "n": n, "W": W, "npool": npool,
-            "Vd_all": Vd_all, "vsq_all": vsq_all, "Vmax": Vmax, "per": per}
+            "Vd_all": Vd_all, "vsq_all": vsq_all, "Vmax": Vmax, "per": per, "packed": packed}
 
 
 def sample_stage(sc, *, eps, delta, r, J, seed=0x5EED, step=0, layer=0, measure=MEASURE_VALUE,
@@ -114,10 +118,17 @@ def sample_stage(sc, *, eps, delta, r, J, seed=0x5EED, step=0, layer=0, measure=
         p = UB + E
         lub = first_level(p - c_star, LT)
         cand = np.nonzero(lub <= J)[0]
-        s_c = exact_scores(q16[g], K16[cand])
-        hl = first_level(s_c - c_star, LT)
-        ll = first_level((s_c + E[cand]) - c_star, LT)
-        w_c = np.exp(s_c - c_star)
+        UB8 = refine_bounds8(q16[g:g + 1], sc["packed"], h, cand)["UB8"][0]
+        l8 = first_level((np.minimum(UB[cand], UB8) + E[cand]) - c_star, LT)
+        ex = l8 <= J                                        # exact 16-bit reads
+        s_c = np.full(cand.size, np.nan)
+        s_c[ex] = exact_scores(q16[g], K16[cand[ex]])
+        hl = np.full(cand.size, J + 1, dtype=np.int32)
+        ll = np.full(cand.size, J + 1, dtype=np.int32)
+        hl[ex] = first_level(s_c[ex] - c_star, LT)
+        ll[ex] = first_level((s_c[ex] + E[cand[ex]]) - c_star, LT)
+        w_c = np.zeros(cand.size)
+        w_c[ex] = np.exp(s_c[ex] - c_star)
         Vc = Vd_all[cand]
         vsq_c = vsq_all[cand]
         stats = [level_sums(j, hl, ll, w_c, Vc, vsq_c, pg["D_R"], pg["N_R"], pg["Q_R"]) for j in range(J + 1)]
@@ -131,14 +142,15 @@ def sample_stage(sc, *, eps, delta, r, J, seed=0x5EED, step=0, layer=0, measure=
                 stop = len(levels) - 1
                 break
         trace = {"c_R": pg["c_R"], "c_lo": pg["c_lo"], "c_star": c_star, "cmax_pos": pg["cmax_pos"],
-                 "lub": lub, "cand": cand, "s_c": s_c, "h": hl, "l": ll, "E": E, "UB": UB,
-                 "LB": pg["LB"], "levels": levels, "L": L, "Vmax": Vmax, "D_R": pg["D_R"]}
+                 "lub": lub, "cand": cand, "UB8": UB8, "l8": l8, "s_c": s_c, "h": hl, "l": ll, "E": E,
+                 "UB": UB, "LB": pg["LB"], "levels": levels, "L": L, "Vmax": Vmax, "D_R": pg["D_R"]}
         if stop is None:
             res = _exact_result(q16[g], K16, V16, n, J + 1)
             res["trace"] = trace
             results.append(res)
             continue
-        read_set = np.union1d(pg["cmax_pos"], cand[lub[cand] <= stop])
+        read_set = np.union1d(pg["cmax_pos"], cand[l8 <= stop])
+        trace["keys_read_8bit"] = int((lub[cand] <= stop).sum())
         res = {"o_hat": levels[stop]["o_hat"], "beta": float(levels[stop]["beta"]),
                "stop_level": stop, "keys_read": int(W + read_set.size),
                "values_read": int(W + int((ll <= stop).sum())), "trace": trace}

@@ -20,6 +20,19 @@ Reading taken (test infrastructure only; the HIP pack follows the same rules):
 
 The integer zero points make the scan's offset term q.kmin an exact integer dot
 product once the query is put on its own power-of-two grid (see ``bounds``).
+
+8-bit refinement copy ([S] Methodology > Algorithm Components item 4: candidates get
+an 8-bit refinement before any exact 16-bit read; the pages give no format).  Reading
+taken: per token, a symmetric 8-bit code of every channel --
+
+* s8_i = fp32 round-to-nearest-even of the fp64 value max_t |k_it| / 127 (0 for a zero
+  key);
+* k8_it = clamp(rint_half_even(k_it / s8_i), -127, 127) in fp64 (0 when s8_i = 0);
+* k~8_it = s8_i * k8_it (exact in fp64);
+* kerr8_i = smallest fp16 h with h^2 >= R1-sum_t (k_it - k~8_it)^2 * (1 + 2^-40).
+
+It is read only for candidates, so it costs no scan bandwidth (134 bytes a candidate
+against 256 for the exact key row).
 """
 
 import numpy as np
@@ -34,7 +47,8 @@ def pack_kv_4bit(K16: np.ndarray, V16: np.ndarray, nblocks: int) -> dict:
 
     K16, V16: fp16 [H_kv][n_cap][128].  Returns logical arrays:
     codes u8 [H_kv][32*nblocks][128]; z int16 and kscale fp16 [H_kv][nblocks][128];
-    kexp int32 [H_kv][nblocks] (kappa = 2^kexp); kerr and vnorm fp16 [H_kv][32*nblocks].
+    kexp int32 [H_kv][nblocks] (kappa = 2^kexp); kerr and vnorm fp16 [H_kv][32*nblocks];
+    the 8-bit copy k8 int8 [H_kv][32*nblocks][128], s8 fp32 and kerr8 fp16 [H_kv][32*nblocks].
     """
     H = K16.shape[0]
     ntok = BLOCK * nblocks
@@ -58,6 +72,14 @@ def pack_kv_4bit(K16: np.ndarray, V16: np.ndarray, nblocks: int) -> dict:
     kerr = fp16_sqrt_up(csum128(res * res) * (1.0 + PADF)).reshape(H, ntok)
     Vd = V16[:, :ntok].astype(np.float64)
     vnorm = fp16_sqrt_up(csum128(Vd * Vd) * (1.0 + PADF))
+    # the 8-bit copy, per token
+    amax = np.abs(Kb).max(axis=3)                             # [H][nb][32], fp16 values
+    s8 = (amax / 127.0).astype(np.float32)
+    s8d = s8.astype(np.float64)
+    k8 = np.clip(np.rint(Kb / np.where(s8d > 0, s8d, 1.0)[..., None]), -127.0, 127.0)
+    k8 = np.where(s8d[..., None] > 0, k8, 0.0)
+    res8 = Kb - s8d[..., None] * k8
+    kerr8 = fp16_sqrt_up(csum128(res8 * res8) * (1.0 + PADF)).reshape(H, ntok)
     return {
         "codes": codes.astype(np.uint8).reshape(H, ntok, 128),
         "z": z.astype(np.int16),
@@ -65,6 +87,9 @@ def pack_kv_4bit(K16: np.ndarray, V16: np.ndarray, nblocks: int) -> dict:
         "kscale": kscale16,
         "kerr": kerr.astype(np.float16),
         "vnorm": vnorm.astype(np.float16),
+        "k8": k8.astype(np.int8).reshape(H, ntok, 128),
+        "s8": s8.reshape(H, ntok),
+        "kerr8": kerr8.astype(np.float16),
         "nblocks": nblocks,
     }
 
