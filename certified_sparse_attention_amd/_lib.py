@@ -22,7 +22,8 @@ class Shape(ctypes.Structure):
 
 class Packed(ctypes.Structure):
     _fields_ = [("codes", c_void_p), ("kscale", c_void_p), ("zq", c_void_p), ("bmeta", c_void_p),
-                ("kerr", c_void_p), ("vnorm", c_void_p)]
+                ("kerr", c_void_p), ("vnorm", c_void_p), ("codes8", c_void_p), ("scale8", c_void_p),
+                ("kerr8", c_void_p)]
 
 
 class Params(ctypes.Structure):
@@ -37,7 +38,7 @@ class Trace(ctypes.Structure):
                 ("cand_count", c_void_p), ("beta_level", c_void_p), ("dhat_level", c_void_p),
                 ("k_level", c_void_p), ("logtau", c_void_p), ("ev_scan_begin", c_void_p),
                 ("ev_scan_end", c_void_p), ("cand_pos", c_void_p), ("cand_hl", c_void_p),
-                ("rescored_count", c_void_p)]
+                ("rescored_count", c_void_p), ("cand_l8", c_void_p)]
 
 
 SYMBOLS = {

@@ -42,6 +42,9 @@ class PackedKV:
     bmeta: torch.Tensor    # uint8 [H_kv][nb][16]
     kerr: torch.Tensor     # fp16 [H_kv][n_cap]
     vnorm: torch.Tensor    # fp16 [H_kv][n_cap]
+    codes8: torch.Tensor   # int8 [H_kv][n_cap][128]  (8-bit refinement copy)
+    scale8: torch.Tensor   # fp32 [H_kv][n_cap]
+    kerr8: torch.Tensor    # fp16 [H_kv][n_cap]
 
     @staticmethod
     def allocate(num_kv_heads: int, n_cap: int, device="cuda") -> "PackedKV":
@@ -53,14 +56,19 @@ class PackedKV:
             bmeta=torch.zeros((num_kv_heads, nb, 16), dtype=torch.uint8, device=device),
             kerr=torch.zeros((num_kv_heads, n_cap), dtype=torch.float16, device=device),
             vnorm=torch.zeros((num_kv_heads, n_cap), dtype=torch.float16, device=device),
+            codes8=torch.zeros((num_kv_heads, n_cap, 128), dtype=torch.int8, device=device),
+            scale8=torch.zeros((num_kv_heads, n_cap), dtype=torch.float32, device=device),
+            kerr8=torch.zeros((num_kv_heads, n_cap), dtype=torch.float16, device=device),
         )
 
     def c_struct(self) -> _lib.Packed:
         return _lib.Packed(*(ctypes.c_void_p(t.data_ptr()) for t in
-                             (self.codes, self.kscale, self.zq, self.bmeta, self.kerr, self.vnorm)))
+                             (self.codes, self.kscale, self.zq, self.bmeta, self.kerr, self.vnorm,
+                              self.codes8, self.scale8, self.kerr8)))
 
     @property
     def bytes_per_token(self) -> float:
+        """Bytes per token of the 4-bit scan's arrays (every key is read once per call)."""
         total = sum(t.numel() * t.element_size() for t in
                     (self.codes, self.kscale, self.zq, self.bmeta, self.kerr, self.vnorm))
         return total / (self.kerr.shape[0] * self.kerr.shape[1])
@@ -112,7 +120,7 @@ def allocate_workspace(K: torch.Tensor, G: int, n_max: int, J: int, window: int 
 
 TRACE_FIELDS = ("c_R", "c_lo", "c_star", "bucket_count", "lub", "cmax_count", "cand_count",
                 "beta_level", "dhat_level", "k_level", "logtau")
-TRACE_FIELDS_AFTER_EVENTS = ("cand_pos", "cand_hl", "rescored_count")
+TRACE_FIELDS_AFTER_EVENTS = ("cand_pos", "cand_hl", "rescored_count", "cand_l8")
 
 
 def _alloc_trace(H_q, J, npool, device):
@@ -132,6 +140,7 @@ def _alloc_trace(H_q, J, npool, device):
         "cand_pos": torch.full((H_q, max(npool, 1)), -1, dtype=i32, device=device),
         "cand_hl": torch.full((H_q, max(npool, 1)), -1, dtype=i32, device=device),
         "rescored_count": torch.zeros(H_q, dtype=i32, device=device),
+        "cand_l8": torch.full((H_q, max(npool, 1)), -1, dtype=i32, device=device),
     }
 
 

@@ -112,6 +112,7 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.rec_w = take(Hq * npc * sizeof(double));
   P.rec_vsq = take(Hq * npc * sizeof(double));
   P.rec_hl = take(Hq * npc * sizeof(int));
+  P.rec_x = take(Hq * npc * sizeof(int));
   P.nseg_cap = csa::seg_cap_for(npool);
   P.partial = take(Hq * (size_t)P.nseg_cap * J1 * csa::kStatW * sizeof(double));
   P.betalv = take(Hq * J1 * sizeof(double));
@@ -128,7 +129,8 @@ template <class T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
 int check_packed(const csa_packed *p) {
-  if (!p || !p->codes || !p->kscale || !p->zq || !p->bmeta || !p->kerr || !p->vnorm)
+  if (!p || !p->codes || !p->kscale || !p->zq || !p->bmeta || !p->kerr || !p->vnorm || !p->codes8 ||
+      !p->scale8 || !p->kerr8)
     return fail(CSA_ERR_INVALID_ARGUMENT, "packed arrays must all be non-null");
   return CSA_OK;
 }
@@ -264,8 +266,9 @@ __global__ __launch_bounds__(256) void trace_kernel(const double *qconst, const 
 __global__ __launch_bounds__(256) void cand_trace_kernel(const int *ccount, const int *ccount1, const int *jspec,
                                                          const int *ccount2, const int *jspec2,
                                                          const int32_t *stop, const int *candpos, const int *rec_hl,
-                                                         int64_t npool_cap, int64_t npool, int32_t *cand_pos,
-                                                         int32_t *cand_hl, int32_t *rescored) {
+                                                         const int *rec_x, int64_t npool_cap, int64_t npool,
+                                                         int32_t *cand_pos, int32_t *cand_hl, int32_t *cand_l8,
+                                                         int32_t *rescored) {
   const int hq = blockIdx.x;
   const int cnt = ccount[hq];
   const int st = stop[hq];
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(256) void cand_trace_kernel(const int *ccount, cons
   const int64_t src = (int64_t)hq * npool_cap + i, dst = (int64_t)hq * npool + i;
   if (cand_pos) cand_pos[dst] = candpos[src];
   if (cand_hl) cand_hl[dst] = (i < nres) ? rec_hl[src] : -1;
+  if (cand_l8) cand_l8[dst] = (i < nres) ? (rec_x[src] & 0xFF) : -1;
 }
 
 // One read of a buffer (16-byte loads; workgroup w streams the w-th contiguous slice) and
@@ -481,16 +485,13 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
     sa.bdone = at<int>(ws, P.bdone);
     sa.tilecm = at<int>(ws, P.tilecm);
     sa.cmhist = at<int>(ws, P.cmhist);
-    sa.budget = params->cand_budget > 0 ? params->cand_budget : csa::kDefaultBudget;
+    // the first pass rescores inside the certificate kernel: at most kFusedMax candidates
+    sa.budget = params->cand_budget > 0 ? std::min(params->cand_budget, csa::kFusedMax) : csa::kDefaultBudget;
     sa.budget2 = params->cand_budget2 > 0 ? params->cand_budget2 : INT_MAX;   // default: no third range
     sa.pass = 1;
     sa.ccount = at<int>(ws, P.ccount);
     sa.lub = at<int8_t>(ws, P.lub);
     sa.candpos = at<int>(ws, P.candpos);
-    sa.rec_s = at<double>(ws, P.rec_s);
-    sa.rec_w = at<double>(ws, P.rec_w);
-    sa.rec_vsq = at<double>(ws, P.rec_vsq);
-    sa.rec_hl = at<int>(ws, P.rec_hl);
     sa.live = at<uint32_t>(ws, P.live);
     sa.nwords = P.npool_cap / 32 + 1;
     sa.full_lub = (trace && trace->lub) ? 1 : 0;
@@ -530,6 +531,10 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.rec_s = at<double>(ws, P.rec_s);
   ca.prefix = at<uint64_t>(ws, P.prefix);
   ca.rec_vsq = at<double>(ws, P.rec_vsq);
+  ca.rec_x = at<int>(ws, P.rec_x);
+  ca.codes8 = packed->codes8;
+  ca.scale8 = packed->scale8;
+  ca.kerr8 = packed->kerr8;
   ca.lub = at<int8_t>(ws, P.lub);
   ca.partial = at<double>(ws, P.partial);
   ca.betalv = at<double>(ws, P.betalv);
@@ -552,17 +557,9 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.all_exact = all_exact ? 1 : 0;
   ca.ccount1 = at<int>(ws, P.ccount1);
   ca.jspec = at<int>(ws, P.jspec);
-  if (all_exact) {
-    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, false, st)) != hipSuccess) return hip_fail(e, "certify");
-  } else {
-    // pass 1: levels up to the speculative level (at most `budget` candidates).  With a
-    // budget within the fused size its rescoring runs inside the certificate kernel;
-    // otherwise a separate rescoring kernel and the segmented accumulation do it.
-    const bool seg1 = sel.budget > csa::kFusedMax;
-    ca.fused_rescore = seg1 ? 0 : 1;
-    if (seg1 && (e = csa::launch_rescore(sel, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "rescore");
-    if ((e = csa::launch_certify_pass(ca, 1, P.H_q, seg1, st)) != hipSuccess) return hip_fail(e, "certify");
-  }
+  // pass 1: levels up to the speculative level (at most `budget` candidates, rescored
+  // inside the certificate kernel); with all_exact, the exact attention of every head
+  if ((e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");
   // the tail: pass 2 for the heads that need all levels (their remaining candidates are
   // rescored there) and the exact fallback, in one launch that certified heads leave at once
   if ((e = csa::launch_tail(ca, P.H_q, params->cand_budget2 > 0, st)) != hipSuccess) return hip_fail(e, "tail");
@@ -582,13 +579,13 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
     auto cp = [&](void *dst, size_t off, size_t bytes) -> hipError_t {
       return dst ? hipMemcpyAsync(dst, at<char>(ws, off), bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
     };
-    if (!all_exact && (trace->cand_pos || trace->cand_hl || trace->rescored_count)) {
+    if (!all_exact && (trace->cand_pos || trace->cand_hl || trace->cand_l8 || trace->rescored_count)) {
       const unsigned ny = (unsigned)((npool + 255) / 256);
       hipLaunchKernelGGL(cand_trace_kernel, dim3(Hq, ny), dim3(256), 0, st, at<int>(ws, P.ccount),
                          at<int>(ws, P.ccount1), at<int>(ws, P.jspec), at<int>(ws, P.ccount2),
                          at<int>(ws, P.jspec2), stop_level, at<int>(ws, P.candpos),
-                         at<int>(ws, P.rec_hl), P.npool_cap, npool, trace->cand_pos, trace->cand_hl,
-                         trace->rescored_count);
+                         at<int>(ws, P.rec_hl), at<int>(ws, P.rec_x), P.npool_cap, npool, trace->cand_pos,
+                         trace->cand_hl, trace->cand_l8, trace->rescored_count);
       if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "candidate trace");
     }
     if (!all_exact) {

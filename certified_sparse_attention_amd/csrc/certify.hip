@@ -49,9 +49,12 @@ struct CertArgs {
   const int *ccount2, *jspec2;  // then those with jspec < l^ub <= jspec2, then the rest
   int H_q;
   int pass;                     // 1: levels <= jspec; 2: levels <= jspec2; 3: all levels
+  const int8_t *codes8;         // the 8-bit refinement copy (csa.h)
+  const float *scale8;
+  const uint16_t *kerr8;
+  int *rec_x;                   // per candidate: l8 | (UB >= c_lo) << 8
   int final_pass;               // the last tail launch (2 when jspec2 = J, else 3): it also
                                 // takes the exact fallback
-  int fused_rescore;            // pass 1 rescoring happens in the certificate kernel
   const uint64_t *prefix;       // per KV head hash prefixes
   double *rec_s;
   double *exactp;
@@ -97,11 +100,12 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
 }
 
 struct AccSmem {
-  alignas(16) double acc[kMaxJ + 1][kStatW];   // per-level increments: N[128] V[128] D Q k P
+  alignas(16) double acc[kMaxJ + 1][kStatW];   // per-level increments: N[128] V[128] D Q k P X
   double2 ltp[kMaxJ + 2];               // level table in neighbour pairs (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   alignas(16) int hl[kStage];           // read eight at a time
   int pos[kStage];
+  int x[kStage];                        // l8 | (UB >= c_lo) << 8
   double w[kStage], vsq[kStage];
 };
 
@@ -169,6 +173,16 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
         }
       }
     }
+    // exact reads outside C_max: thread 130 counts them at their refined level l8
+    if (t == kD + 2) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (e0 + k < cnt) {
+          const int x = s.x[e0 + k], l8 = x & 0xFF;
+          if (l8 <= J && !(x >> 8)) atomicAdd(&s.acc[l8][2 * kD + 4], 1.0);
+        }
+      }
+    }
   }
   __syncthreads();
 }
@@ -184,52 +198,114 @@ __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, 
       s.w[t] = a.rec_w[base + c0 + t];
       s.vsq[t] = a.rec_vsq[base + c0 + t];
       s.pos[t] = a.candpos[base + c0 + t];
+      s.x[t] = a.rec_x[base + c0 + t];
     }
     __syncthreads();
     accumulate_stage(a, s, h, cnt, false);
   }
 }
 
-// Exact rescoring of the stage of candidates [c0, c0 + cnt) (cnt <= kStage) of query head
-// hq: scores and |v|^2 eight lanes per key, then one lane per key for E, the levels and
-// the weight; records into the stage (s.hl, s.w, s.vsq, staged V rows s.vs) and into the
-// global records.  The key and value rows are requested before E is formed, so the hash
-// and logarithm (and, with zero_rows, the clearing of the level increments) run while
-// they are in flight.
+// Rescoring of the stage of candidates [c0, c0 + cnt) (cnt <= kStage) of query head hq.
+// First the 8-bit refinement (eight lanes per key, sixteen channels each):
+//   S8 = R1-sum_t q_t (scale8 k8_t), slack8 = (qnp kerr8) + 2^-40 ((128 scale8) qabs),
+//   UB8 = (S8 + slack8) RSQRT_D, l8 = first((min(UB, UB8) + E) - c*),
+// and the key's C_max bit (UB >= c_lo).  Then, for keys with l8 <= J only, the exact
+// score and |v|^2, and (one lane per key) h, l and the weight; keys with l8 > J can be
+// sampled at no level and get h = l = J + 1.  With kSpec the exact rows are requested
+// together with the 8-bit row (one round trip, for the latency of a short first pass);
+// otherwise only after l8 is known (the bytes of keys the refinement rules out are not
+// read).  Records go into the stage (s.hl, s.x, s.w, s.vsq, staged V rows s.vs) and the
+// global records.  E is hashed, and with zero_rows the level increments are cleared,
+// while the rows are in flight.
+struct RescoreConsts {
+  double q16[16];
+  double cs, inv_l1, qnp, qabs, clo;
+  uint64_t prefix;
+};
+
+template <bool kSpec>
 __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int hq, int c0, int cnt,
-                                              const double *q16, double cs, uint64_t prefix, double inv_l1,
-                                              int zero_rows = 0) {
+                                              const RescoreConsts &rc, int zero_rows = 0) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
   if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
   __syncthreads();
   // wavefront wv takes keys 16 wv .. 16 wv + 15, eight lanes per key
-  uint4 kw[2][2], vw[2][2];
+  uint4 cw8[2], kw[2][2], vw[2][2];
+  float sc8[2];
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
     const int r = 16 * wv + 8 * step + s8;
-    kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
+    cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
+    sc8[step] = 0.0f;
     if (r < cnt) {
-      const int64_t row = ((int64_t)h * a.n_cap + s.pos[r]) * kD;
-      const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + row) + 2 * k8;
-      const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + row) + 2 * k8;
+      const int64_t tok = (int64_t)h * a.n_cap + s.pos[r];
+      cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
+      sc8[step] = a.scale8[tok];
+      if (kSpec) {
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
+        kw[step][0] = ksrc[0];
+        kw[step][1] = ksrc[1];
+        vw[step][0] = vsrc[0];
+        vw[step][1] = vsrc[1];
+      }
+    }
+  }
+  // one lane per key: its perturbation, UB and 8-bit record
+  double E = 0.0, ubt = 0.0, ke8 = 0.0, s8t = 0.0;
+  if (t < cnt) {
+    const int pos = s.pos[t];
+    ubt = a.ubuf[base + pos];
+    ke8 = h2d(a.kerr8[(int64_t)h * a.n_cap + pos]);
+    s8t = (double)a.scale8[(int64_t)h * a.n_cap + pos];
+    E = perturbation(rc.prefix, pos);
+  }
+  for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const int r = 16 * wv + 8 * step + s8;
+    double p = 0.0;
+    if (r < cnt) {
+      const double sc = (double)sc8[step];
+      const uint32_t wd[4] = {cw8[step].x, cw8[step].y, cw8[step].z, cw8[step].w};
+      p = rc.q16[0] * (sc * (double)(int8_t)(wd[0] & 0xFFu));
+#pragma unroll
+      for (int i = 1; i < 16; ++i) p = p + rc.q16[i] * (sc * (double)(int8_t)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu));
+    }
+    const double S8 = r1_combine8(p);
+    if (r < cnt && k8 == 0) s.w[r] = S8;
+  }
+  __syncthreads();
+  if (t < cnt) {
+    const double slack8 = (rc.qnp * ke8) + (kPadF * ((128.0 * s8t) * rc.qabs));
+    const double ub8 = (s.w[t] + slack8) * kRsqrtD;
+    const int l8 = level_of_pairs((fmin(ubt, ub8) + E) - rc.cs, s.ltp, a.J, rc.inv_l1);
+    s.x[t] = l8 | ((ubt >= rc.clo) ? 0x100 : 0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const int r = 16 * wv + 8 * step + s8;
+    const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
+    if (!kSpec && ex) {
+      const int64_t tok = (int64_t)h * a.n_cap + s.pos[r];
+      const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
+      const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
       kw[step][0] = ksrc[0];
       kw[step][1] = ksrc[1];
       vw[step][0] = vsrc[0];
       vw[step][1] = vsrc[1];
     }
   }
-  double E = 0.0;
-  if (t < cnt) E = perturbation(prefix, s.pos[t]);
-  // the level increments start at zero (rows 0..zero_rows-1), cleared while the rows arrive
-  for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
     const int r = 16 * wv + 8 * step + s8;
+    const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
     double p = 0.0, v = 0.0;
-    if (r < cnt) {
-      p = score_words(q16, kw[step][0], kw[step][1]);
+    if (ex) {
+      p = score_words(rc.q16, kw[step][0], kw[step][1]);
       // the V row is staged for the accumulation while its |v|^2 is formed
       uint4 *vdst = reinterpret_cast<uint4 *>(s.vs[r]) + 2 * k8;
       vdst[0] = vw[step][0];
@@ -238,18 +314,23 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     }
     const double sc = r1_combine8(p) * kRsqrtD;
     const double vs = r1_combine8(v);
-    if (r < cnt && k8 == 0) {
+    if (ex && k8 == 0) {
       s.w[r] = sc;       // the score for now; the weight below
       s.vsq[r] = vs;
     }
   }
   __syncthreads();
   if (t < cnt) {
-    const double sc = s.w[t];
-    const int hl = level_of_pairs(sc - cs, s.ltp, a.J, inv_l1);
-    const int ll = level_of_pairs((sc + E) - cs, s.ltp, a.J, inv_l1);
-    const double w = exp(sc - cs);
-    const double vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
+    const int x = s.x[t];
+    int hl = a.J + 1, ll = a.J + 1;
+    double sc = 0.0, w = 0.0, vsq = 0.0;
+    if ((x & 0xFF) <= a.J) {
+      sc = s.w[t];
+      hl = level_of_pairs(sc - rc.cs, s.ltp, a.J, rc.inv_l1);
+      ll = level_of_pairs((sc + E) - rc.cs, s.ltp, a.J, rc.inv_l1);
+      w = exp(sc - rc.cs);
+      vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
+    }
     s.hl[t] = hl | (ll << 8);
     s.w[t] = w;
     s.vsq[t] = vsq;
@@ -257,22 +338,21 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     a.rec_w[base + c0 + t] = w;
     a.rec_vsq[base + c0 + t] = vsq;
     a.rec_hl[base + c0 + t] = hl | (ll << 8);
+    a.rec_x[base + c0 + t] = x;
   }
   __syncthreads();
 }
 
 // The per-query constants of rescoring: the query chunk of the lane (eight lanes per key,
-// sixteen channels each), c*, the hash prefix and 1 / log tau_1.
-struct RescoreConsts {
-  double q16[16];
-  double cs, inv_l1;
-  uint64_t prefix;
-};
+// sixteen channels each), c*, c_lo, |q| pad and sum |q|, the hash prefix, 1 / log tau_1.
 __device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem &s, int hq, RescoreConsts &c) {
   const int k8 = threadIdx.x & 7;
 #pragma unroll
   for (int i = 0; i < 16; ++i) c.q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
   c.cs = dec_max(a.cstar[hq]);
+  c.clo = dec_max(a.clo[hq]);
+  c.qnp = a.qconst[(int64_t)hq * kQc + QC_QNP];
+  c.qabs = a.qconst[(int64_t)hq * kQc + QC_QABS];
   c.prefix = a.prefix[hq / a.G];
   c.inv_l1 = (a.J >= 1) ? 1.0 / s.ltp[1].y : 0.0;
 }
@@ -280,11 +360,12 @@ __device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem 
 // Exact rescoring of candidates [i0, i1) of query head hq inside the certificate
 // workgroup, stage by stage, each stage added into the level increments s.acc.
 __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+  __syncthreads();              // the level table s.ltp is filled
   RescoreConsts rc;
   rescore_consts(a, s, hq, rc);
   for (int c0 = i0; c0 < i1; c0 += kStage) {
     const int cnt = min(kStage, i1 - c0);
-    rescore_stage(a, s, hq, c0, cnt, rc.q16, rc.cs, rc.prefix, rc.inv_l1);
+    rescore_stage<false>(a, s, hq, c0, cnt, rc);
     accumulate_stage(a, s, hq / a.G, cnt, true);
   }
 }
@@ -304,33 +385,8 @@ __device__ void accumulate_mixed(const CertArgs &a, AccSmem &s, int hq, int i0, 
 // Which candidates of this pass already have records: the first pass's, when a separate
 // kernel rescored them, and in later passes the earlier passes' ranges.
 __device__ inline int record_split(const CertArgs &a, int hq, int count) {
-  if (a.pass == 1) return a.fused_rescore ? 0 : count;
+  if (a.pass == 1) return 0;
   return (a.pass == 2) ? a.ccount1[hq] : a.ccount2[hq];
-}
-
-constexpr int kSegWorkers = 8;   // workgroups per query head for the segmented accumulation
-
-// Heads with many candidates: grid (H_q, kSegWorkers); workgroup w accumulates
-// segments w, w + kSegWorkers, ... and writes each segment's increments.
-__global__ __launch_bounds__(256) void accumulate_kernel(CertArgs a) {
-  const int hq = blockIdx.x;
-  const int count = pass_count(a, hq);
-  if (count < 0) return;
-  int i0, i1, nseg;
-  seg_range(count, 0, i0, i1, nseg);
-  if ((int)blockIdx.y >= nseg) return;
-  __shared__ AccSmem s;
-  const int J1 = a.J + 1;
-  fill_level_pairs(s.ltp, a.lt, a.J, threadIdx.x, 256);
-  const int split = record_split(a, hq, count);
-  for (int seg = blockIdx.y; seg < nseg; seg += kSegWorkers) {
-    seg_range(count, seg, i0, i1, nseg);
-    zero_acc(s, J1);
-    accumulate_mixed(a, s, hq, i0, i1, split);
-    double *out = a.partial + ((int64_t)hq * a.nseg_cap + seg) * J1 * kStatW;
-    for (int e = threadIdx.x; e < J1 * kStatW; e += 256) out[e] = (&s.acc[0][0])[e];
-    __syncthreads();
-  }
 }
 
 // Root of kl(x, mu) = mu - x + x ln(x / mu) = L above x: Newton from above on the convex
@@ -448,7 +504,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     __syncthreads();            // the level table s.ltp is filled
     RescoreConsts rc;
     rescore_consts(a, s, hq, rc);
-    rescore_stage(a, s, hq, 0, count, rc.q16, rc.cs, rc.prefix, rc.inv_l1, jmax + 1);
+    rescore_stage<true>(a, s, hq, 0, count, rc, jmax + 1);
     accumulate_stage(a, s, hq / a.G, count, true);
   } else if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
@@ -470,10 +526,10 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     }
     __syncthreads();
   }
-  // prefix over levels, eight rows at a time: thread t takes column t and, for t < 4, the
+  // prefix over levels, eight rows at a time: thread t takes column t and, for t < 5, the
   // scalar column 256 + t as a second chain (the others run it on the pad column)
   {
-    const int c2 = (t < 4) ? 2 * kD + t : kStatW - 1;
+    const int c2 = (t < 5) ? 2 * kD + t : kStatW - 1;
     double run = 0.0, run2 = 0.0;
     int j = 0;
     for (; j + 8 <= jmax + 1; j += 8) {
@@ -593,20 +649,13 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     }
     return false;
   }
-  // keys read: window + |{l^ub <= j*}| + |{i in C_max : l^ub_i > j*}|
+  // keys read exactly: window + |C_max| + the candidates outside C_max whose refined
+  // level l8 is at most j* (column 260 counts them by l8, prefix-summed over levels)
   if (wv == 0) {
-    // C_max keys outside the sample's buckets, and candidates up to the stop level
-    int e = (lane > js && lane <= a.J + 1) ? f.cmh[lane] : 0;
-    int ib = (lane <= js) ? f.hist[lane] : 0;
+    int e = (lane <= a.J + 1) ? f.cmh[lane] : 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      e += __shfl_xor(e, off, 64);
-      ib += __shfl_xor(ib, off, 64);
-    }
-    if (lane == 0) {
-      f.extra[0] = e;
-      f.extra[1] = ib;
-    }
+    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off, 64);
+    if (lane == 0) f.extra[0] = e;
   }
   __syncthreads();
   const double tau = f.tau[js];
@@ -617,7 +666,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     set_status(a, hq, 0);
     a.stop[hq] = js;
     a.beta[hq] = f.beta[js];
-    a.keys_read[hq] = (int64_t)a.W + f.extra[1] + f.extra[0];
+    a.keys_read[hq] = (int64_t)a.W + f.extra[0] + (int64_t)s.acc[js][2 * kD + 4];
   }
   return true;
 }
@@ -841,9 +890,8 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
   }
 }
 
-hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, bool segmented, hipStream_t st) {
+hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, hipStream_t st) {
   a.pass = pass;
-  if (!a.all_exact && segmented) hipLaunchKernelGGL(accumulate_kernel, dim3(H_q, kSegWorkers), dim3(256), 0, st, a);
   hipLaunchKernelGGL(finish_kernel, dim3(H_q), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -25,8 +25,9 @@ constexpr int kMaxJ = 60;
 constexpr int kMaxG = 7;
 constexpr int kBlocksPerWave = 16;                 // scan: blocks handled by one wavefront
 constexpr int kNumSeg = 64;                        // accumulate: max segments per query
-constexpr int kStatW = 262;                        // per-level stats N[128] V[128] D Q k P, and two
-                                                   // pad columns (rows 16-byte aligned and 524
+constexpr int kStatW = 262;                        // per-level stats N[128] V[128] D Q k P X (X:
+                                                   // exact reads outside C_max), and a pad
+                                                   // column (rows 16-byte aligned and 524
                                                    // dwords apart: level-strided LDS reads
                                                    // spread over the banks)
 
@@ -371,7 +372,7 @@ struct Plan {
       jspec;
   size_t bdone, exdone, exdone2;  // per-head completion counters (last-workgroup reductions)
   size_t ccount2, jspec2, flags2;
-  size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl;
+  size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl, rec_x;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
   int nseg_cap;        // segment rows per query head in `partial`
   size_t total;

@@ -1,7 +1,8 @@
-// 4-bit per-block, per-channel key quantization with error-bound metadata
-// ("Certified Sparse Attention via Perturbed Retrieval", summary page,
-// Methodology > Algorithm Components item 4: 4-bit per-block-per-channel keys that
-// give deterministic score bounds).  The rules (zero points on a per-block
+// 4-bit per-block, per-channel key quantization with error-bound metadata, and the
+// per-token 8-bit refinement copy ("Certified Sparse Attention via Perturbed
+// Retrieval", summary page, Methodology > Algorithm Components item 4: 4-bit
+// per-block-per-channel keys that give deterministic score bounds; an 8-bit
+// refinement before exact reads).  The rules (zero points on a per-block
 // power-of-two grid, round-to-nearest scales, round-up norm bounds) are stated in
 // csa.h next to the packed layout.
 //
@@ -17,6 +18,9 @@ struct PackArgs {
   int8_t *zq;
   BlockMeta *bmeta;
   uint16_t *kerr, *vnorm;
+  int8_t *codes8;
+  float *scale8;
+  uint16_t *kerr8;
   int64_t n_cap, nb_cap, block_begin;
 };
 
@@ -33,6 +37,7 @@ __global__ __launch_bounds__(128) void pack_kernel(PackArgs a) {
   __shared__ uint8_t cd[kBlk][kD];
   __shared__ int zi[kD];
   __shared__ double sh_kappa;
+  __shared__ double s8sh[kBlk];
 
   double k[kBlk];
   double mn = 1e300, mx = -1e300;
@@ -111,6 +116,34 @@ __global__ __launch_bounds__(128) void pack_kernel(PackArgs a) {
     a.kerr[(int64_t)h * a.n_cap + tok0 + t] = f16_sqrt_up(s * (1.0 + kPadF));
   }
   __syncthreads();
+  // the 8-bit copy, per token: scale8 = fp32(max_t |k| / 127), codes rint(k / scale8)
+  // clamped to [-127, 127], kerr8 from the residual squares in the R1 order
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) sq[i][t] = fabs(k[i]);
+  __syncthreads();
+  if (t < kBlk) {
+    double m = 0.0;
+    for (int c = 0; c < kD; ++c) m = fmax(m, sq[t][c]);
+    const float sc = (float)(m / 127.0);
+    a.scale8[(int64_t)h * a.n_cap + tok0 + t] = sc;
+    s8sh[t] = (double)sc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBlk; ++i) {
+    const double sc = s8sh[i];
+    const double c8 = (sc > 0.0) ? fmin(fmax(rint(k[i] / sc), -127.0), 127.0) : 0.0;
+    a.codes8[((int64_t)h * a.n_cap + tok0 + i) * kD + t] = (int8_t)c8;
+    const double r = k[i] - sc * c8;
+    sq[i][t] = r * r;
+  }
+  __syncthreads();
+  if (t < kBlk) {
+    const double *row = sq[t];
+    double s = canon_sum([&](int c) { return row[c]; });
+    a.kerr8[(int64_t)h * a.n_cap + tok0 + t] = f16_sqrt_up(s * (1.0 + kPadF));
+  }
+  __syncthreads();
   // vnorm
 #pragma unroll
   for (int i = 0; i < kBlk; ++i) {
@@ -157,6 +190,9 @@ hipError_t launch_pack(const csa_shape &s, const uint16_t *K, const uint16_t *V,
   a.bmeta = reinterpret_cast<BlockMeta *>(p.bmeta);
   a.kerr = p.kerr;
   a.vnorm = p.vnorm;
+  a.codes8 = p.codes8;
+  a.scale8 = p.scale8;
+  a.kerr8 = p.kerr8;
   a.n_cap = s.n_cap;
   a.nb_cap = s.n_cap / kBlk;
   a.block_begin = b0;

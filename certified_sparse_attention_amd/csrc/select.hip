@@ -26,8 +26,6 @@ struct SelectArgs {
   int *hist, *tilecnt, *tileoff, *ccount;
   int8_t *lub;
   int *candpos;
-  double *rec_s, *rec_w, *rec_vsq;
-  int *rec_hl;
   const uint32_t *live;   // [H_q][nwords] keys the scan kept (others have l^ub = J+1, UB < c_lo)
   int64_t nwords;
   int full_lub;           // write l^ub for every pool key (diagnostics)
@@ -279,53 +277,11 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   }
 }
 
-// ---- exact rescore of candidates (one lane per candidate)
-__global__ __launch_bounds__(256) void rescore_kernel(SelectArgs a) {
-  const int hq = blockIdx.x;
-  const int h = hq / a.G;
-  __shared__ double qd[kD];
-  __shared__ double2 ltp[kMaxJ + 2];
-  if (threadIdx.x < kD) qd[threadIdx.x] = (double)a.qf[(int64_t)hq * kD + threadIdx.x];
-  fill_level_pairs(ltp, a.lt, a.J, threadIdx.x, 256);
-  __syncthreads();
-  const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
-  int lo, hi;
-  if (a.pass == 1) {
-    lo = 0;
-    hi = a.ccount1[hq];
-  } else {
-    if (a.flags[hq] != 2) return;
-    lo = a.ccount1[hq];
-    hi = a.ccount[hq];
-  }
-  const double cs = dec_max(a.cstar[hq]);
-  const uint64_t prefix = a.prefix[h];
-  for (int64_t i = lo + (int64_t)blockIdx.y * 256 + threadIdx.x; i < hi; i += (int64_t)gridDim.y * 256) {
-    const int64_t o = (int64_t)hq * a.npool_cap + i;
-    const int pos = a.candpos[o];
-    const double s = exact_score(qd, a.K + ((int64_t)h * a.n_cap + pos) * kD);
-    const double E = perturbation(prefix, pos);
-    const int hl = level_of_pairs(s - cs, ltp, a.J, inv_l1);
-    const int ll = level_of_pairs((s + E) - cs, ltp, a.J, inv_l1);
-    double vsq = 0.0;
-    if (ll <= a.J) vsq = row_sumsq(a.V + ((int64_t)h * a.n_cap + pos) * kD);
-    a.rec_s[o] = s;
-    a.rec_w[o] = exp(s - cs);
-    a.rec_vsq[o] = vsq;
-    a.rec_hl[o] = hl | (ll << 8);
-  }
-}
-
 hipError_t launch_select(const SelectArgs &a, int H_q, hipStream_t st) {
   hipLaunchKernelGGL(bucket_count_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
   hipLaunchKernelGGL(bucket_write_kernel, dim3(H_q, (unsigned)a.ntiles), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_rescore(SelectArgs a, int pass, int H_q, hipStream_t st) {
-  a.pass = pass;
-  hipLaunchKernelGGL(rescore_kernel, dim3(H_q, 64), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
 
 }  // namespace csa

@@ -83,6 +83,13 @@ typedef struct {
  *          int32 kexp; int32 Z1 = sum_t |z_t|; float Kmax = smallest fp32 >=
  *          max_t (|kmin_t| + 15 kscale_t) }.
  *   kerr, vnorm fp16 [H_kv][n_cap].
+ * The 8-bit refinement copy ([S] Algorithm Components item 4: an 8-bit refinement
+ * before exact 16-bit reads), per token i, read only for candidates:
+ *   scale8_i = fp32 round-to-nearest of max_t |k_it| / 127; k8_it = clamp(rint(k_it /
+ *   scale8_i), -127, 127) (0 for a zero key); kerr8_i = smallest fp16 h with h^2 >=
+ *   sum_t (k_it - scale8_i k8_it)^2 (1+2^-40).
+ *   codes8 int8 [H_kv][n_cap][128] (token-major), scale8 fp32 [H_kv][n_cap],
+ *   kerr8 fp16 [H_kv][n_cap]: 134 bytes per token.
  */
 typedef struct {
   uint8_t *codes;
@@ -91,6 +98,9 @@ typedef struct {
   void *bmeta;
   uint16_t *kerr;
   uint16_t *vnorm;
+  int8_t *codes8;
+  float *scale8;
+  uint16_t *kerr8;
 } csa_packed;
 
 /* Parameters of one certified call. */
@@ -104,9 +114,10 @@ typedef struct {
   uint64_t seed;   /* perturbation hash inputs ([S] item 1: 53-bit uniform hash) */
   uint64_t step;   /* decode step: fresh perturbations per step ([A]) */
   int32_t layer;
-  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 32);
-                          heads that certify at no level up to that point get a second pass
-                          over deeper levels.  Results do not depend on it. */
+  int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 32;
+                          values above 2048 act as 2048); heads that certify at no level up
+                          to that point get a second pass over deeper levels.  Results do
+                          not depend on it. */
   int32_t cand_budget2; /* 0 (default): the second pass takes every remaining level.  Else
                            the candidates (all passes so far) the second pass may take; it
                            takes at least one level more than the first, and heads still
@@ -141,6 +152,10 @@ typedef struct {
  *                       candidates, which can enter the sample only at levels past the
  *                       stop level.
  *   rescored_count      int32 [H_q]: candidates rescored exactly in this call.
+ *   cand_l8             int32 [H_q][n_pool]: for the first rescored_count entries of
+ *                       cand_pos, the refined level l8 = first((min(UB, UB8) + E) - c*)
+ *                       in [0, J+1] (the exact key and value are read only when l8 <= J);
+ *                       -1 for the other candidates.
  */
 typedef struct {
   double *c_R, *c_lo, *c_star;
@@ -154,6 +169,7 @@ typedef struct {
   void *ev_scan_begin, *ev_scan_end;
   int32_t *cand_pos, *cand_hl;
   int32_t *rescored_count;
+  int32_t *cand_l8;
 } csa_trace;
 
 /*
@@ -182,7 +198,8 @@ size_t csa_workspace_bytes(const csa_shape *shape, const csa_params *params, int
  *                               certified and o is exact ([S] Results > Certificate
  *                               Validity); 0 when n <= window (every key is exact)
  *   keys_read  int64 [H_q]      exact 16-bit key reads: window + |C_max union
- *                               {l^ub <= j*}| (n on the exact paths)
+ *                               {l8 <= j*}| with l8 the level after the 8-bit
+ *                               refinement (n on the exact paths)
  */
 int csa_certified_decode_attention(const csa_shape *shape, const csa_params *params,
                                    const uint16_t *q, const uint16_t *K, const uint16_t *V,

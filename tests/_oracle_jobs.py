@@ -13,7 +13,7 @@ def _pad(w):
     return w
 
 
-_TRACE_KEEP = ("c_R", "c_lo", "c_star", "cmax_pos", "lub", "cand", "h", "l", "levels")
+_TRACE_KEEP = ("c_R", "c_lo", "c_star", "cmax_pos", "lub", "cand", "h", "l", "l8", "levels")
 _LEVEL_KEEP = ("k", "D_hat", "beta")
 
 

@@ -57,6 +57,9 @@ def _packed_numpy(p):
         "kmax": bm[..., 12:16].copy().view(np.float32)[..., 0],
         "kerr": p.kerr.cpu().numpy(),
         "vnorm": p.vnorm.cpu().numpy(),
+        "codes8": p.codes8.cpu().numpy(),
+        "scale8": p.scale8.cpu().numpy(),
+        "kerr8": p.kerr8.cpu().numpy(),
     }
 
 
@@ -121,6 +124,9 @@ def test_pack_bit_exact(case):
     np.testing.assert_array_equal(got["kexp"], ref["kexp"])
     np.testing.assert_array_equal(got["kerr"].view(np.uint16), ref["kerr"].view(np.uint16))
     np.testing.assert_array_equal(got["vnorm"].view(np.uint16), ref["vnorm"].view(np.uint16))
+    np.testing.assert_array_equal(got["codes8"], ref["k8"])
+    np.testing.assert_array_equal(got["scale8"].view(np.uint32), ref["s8"].view(np.uint32))
+    np.testing.assert_array_equal(got["kerr8"].view(np.uint16), ref["kerr8"].view(np.uint16))
     from oracle.bounds import block_constants
     for h in range(w.H_kv):
         bc = block_constants(w.q[h * w.G:(h + 1) * w.G], ref, h, w.n_cap // 32)
@@ -184,8 +190,9 @@ def _compare_decode(w, pk_ref, res, tr, ref=None, **kw):
 
 
 def _compare_samples(hq, trn, t, stop, J):
-    """The candidate list, the (h, l) of every rescored candidate, and S_j, B_j at every
-    level up to the stop (up to J on the exact fallback), element by element."""
+    """The candidate list, the refined level l8 and the (h, l) of every rescored candidate,
+    and S_j, B_j at every level up to the stop (up to J on the exact fallback), element by
+    element."""
     cc = int(trn["cand_count"][hq])
     pos = trn["cand_pos"][hq, :cc]
     np.testing.assert_array_equal(np.sort(pos), t["cand"])     # the same set, no repeats
@@ -198,6 +205,9 @@ def _compare_samples(hq, trn, t, stop, J):
     gh, gl = hl[:nres] & 0xFF, hl[:nres] >> 8
     np.testing.assert_array_equal(gh, t["h"][idx])
     np.testing.assert_array_equal(gl, t["l"][idx])
+    l8 = trn["cand_l8"][hq, :cc]
+    assert np.all(l8[nres:] == -1)
+    np.testing.assert_array_equal(l8[:nres], t["l8"][idx])
     for j in range(min(stop, J) + 1):
         np.testing.assert_array_equal(np.sort(rpos[gl <= j]), t["cand"][t["l"] <= j], err_msg=f"S_{j} of {hq}")
         np.testing.assert_array_equal(np.sort(rpos[gh <= j]), t["cand"][t["h"] <= j], err_msg=f"B_{j} of {hq}")
