@@ -85,7 +85,9 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
   P.cR = 0;
   P.clo = take(Hq * sizeof(unsigned long long));
   P.cstar = take(Hq * sizeof(unsigned long long));
-  P.vmax = take((size_t)P.H_kv * sizeof(unsigned));
+  P.wstride = std::max<int64_t>(1, ((P.npool_cap + csa::kBlk - 1) / csa::kBlk + csa::kScanBlocks - 1) / csa::kScanBlocks);
+  P.lbpart = take(Hq * (size_t)P.wstride * sizeof(float));
+  P.vpart = take((size_t)P.H_kv * P.wstride * sizeof(unsigned));
   P.bdone = take(Hq * sizeof(int));
   P.exdone = take(Hq * sizeof(int));
   P.exdone2 = take(Hq * sizeof(int));
@@ -161,7 +163,6 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.sR = at<double>(ws, P.sR);
   pa.clo = at<unsigned long long>(ws, P.clo);
   pa.cstar = at<unsigned long long>(ws, P.cstar);
-  pa.vmax = at<unsigned>(ws, P.vmax);
   pa.hist = at<int>(ws, P.hist);
   pa.ccount = at<int>(ws, P.ccount);
   pa.flags = at<int>(ws, P.flags);
@@ -203,7 +204,9 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.pbuf = at<double>(ws, P.pbuf);
   sa.ubuf = at<double>(ws, P.ubuf);
   sa.clo = pa.clo;
-  sa.vmax = pa.vmax;
+  sa.lbpart = at<float>(ws, P.lbpart);
+  sa.vpart = at<unsigned>(ws, P.vpart);
+  sa.wstride = P.wstride;
   sa.lb_out = lb_out;
   sa.e_out = e_out;
   sa.nwords = P.npool_cap / 32 + 1;
@@ -520,7 +523,9 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.win = at<double>(ws, P.win);
   ca.qconst = at<double>(ws, P.qconst);
   ca.cstar = at<unsigned long long>(ws, P.cstar);
-  ca.vmax = at<unsigned>(ws, P.vmax);
+  ca.vpart = at<unsigned>(ws, P.vpart);
+  ca.wstride = P.wstride;
+  ca.wph = npool > 0 ? ((npool + csa::kBlk - 1) / csa::kBlk + csa::kScanBlocks - 1) / csa::kScanBlocks : 0;
   ca.ccount = at<int>(ws, P.ccount);
   ca.candpos = at<int>(ws, P.candpos);
   ca.rec_hl = at<int>(ws, P.rec_hl);

@@ -33,7 +33,8 @@ struct CertArgs {
   const double *win, *qconst;   // window sums relative to c_R; per-query constants (c_R)
   const unsigned long long *cstar, *clo;
   const double *ubuf;
-  const unsigned *vmax;
+  const unsigned *vpart;         // per scan wavefront: largest |v| code of its keys
+  int64_t wph, wstride;          // scan wavefronts per KV head, row stride of vpart
   const int *ccount, *candpos, *hist;
   int *rec_hl;                  // candidate records (written by the fused rescoring)
   const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
@@ -485,7 +486,13 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
     f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
   }
-  if (t == 255) f.vmax = h2d((uint16_t)a.vmax[h]);
+  if (wv == 3) {                 // Vmax: the scan wavefronts' maxima of the head
+    unsigned v = 0u;
+    for (int64_t k = lane; k < a.wph; k += 64) v = max(v, a.vpart[(int64_t)h * a.wstride + k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
+    if (lane == 0) f.vmax = h2d((uint16_t)v);
+  }
   // window sums, rescaled from c_R to c*
   {
     const double cs = dec_max(a.cstar[hq]);

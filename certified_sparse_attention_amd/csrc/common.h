@@ -366,9 +366,10 @@ struct Plan {
   int H_kv, G, H_q, J, W;
   int64_t npool_cap;   // pool capacity per query head
   int64_t ntiles;      // bucket tiles per query head
+  int64_t wstride;     // scan wavefronts per KV head at full pool capacity
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
-  size_t clo, cstar, vmax, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
+  size_t clo, cstar, lbpart, vpart, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
       jspec;
   size_t bdone, exdone, exdone2;  // per-head completion counters (last-workgroup reductions)
   size_t ccount2, jspec2, flags2;

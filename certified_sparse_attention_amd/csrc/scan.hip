@@ -45,7 +45,6 @@ struct PrepArgs {
   uint64_t *prefix;
   double *sR;
   unsigned long long *clo, *cstar;
-  unsigned *vmax;
   int *hist, *ccount, *flags;
   int *bdone, *exdone, *exdone2;   // per-head completion counters, cleared here
 };
@@ -66,7 +65,6 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
   }
   if (g == 0 && t == 0) {
     a.prefix[h] = hash_prefix(a.seed, a.step, (uint64_t)(int64_t)a.layer, (uint64_t)h);
-    a.vmax[h] = 0u;
   }
   const double qv = h2d(a.q[(int64_t)hq * kD + t]);
   a.qf[(int64_t)hq * kD + t] = (float)qv;
@@ -174,7 +172,13 @@ struct ScanArgs {
   double *pbuf, *ubuf;
   uint32_t *live;
   unsigned long long *clo, *cstar;
-  unsigned *vmax;
+  // per streaming wavefront (wph of them per KV head, row stride wstride): a lower bound
+  // of the largest LB of its keys per query, and the largest |v| code of its keys; plain
+  // stores, reduced by the consumers (same-address atomics from every wavefront would
+  // serialize at the end of the scan)
+  float *lbpart;            // [H_q][wstride]
+  unsigned *vpart;          // [H_kv][wstride]
+  int64_t wstride;
   int diag;                 // 1: every key is live and UB/LB/E are written for all keys
   double *lb_out, *e_out;   // diagnostics (may be null)
 };
@@ -787,15 +791,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // c_lo >= every LB: publish the wave's lower bounds of max LB
   lbA = row_max16k(lbA);
   if (kTwo) lbB = row_max16k(lbB);
+  const int64_t wih = gw % wph;   // this wavefront within its head
   if (n16 == 0) {
-    if (hasA && lbA > kNegInf)
-      __hip_atomic_fetch_max(a.clo + hq0 + gA, enc_max((double)lbA), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hasB && lbB > kNegInf)
-      __hip_atomic_fetch_max(a.clo + hq0 + gB, enc_max((double)lbB), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hasA) a.lbpart[(int64_t)(hq0 + gA) * a.wstride + wih] = lbA;
+    if (hasB) a.lbpart[(int64_t)(hq0 + gB) * a.wstride + wih] = lbB;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) vmx = max(vmx, (unsigned)__shfl_xor((int)vmx, off, 64));
-  if (lane == 0) atomicMax(a.vmax + h, vmx);
+  if (lane == 0) a.vpart[(int64_t)h * a.wstride + wih] = vmx;
 }
 
 // Everything one chunk (two blocks) of the refinement reads from the packed cache: its
@@ -866,31 +869,74 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   const int hq0 = h * G;
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = gB < G;
+  // every load of the preamble is issued before the first use: the block maxima, the
+  // queries, the per-query constants (lane g < G), the hash prefix and the scan
+  // wavefronts' LB bounds (the first 128 wavefronts' of every query at once; a longer
+  // pool adds a loop)
   float2 mxA = make_float2(0.0f, 0.0f), mxB = make_float2(0.0f, 0.0f);
   if (n16 < nblk && hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
   if (n16 < nblk && hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
   const double ltJ = a.lt[a.J];
-  for (int g = 0; g < G; ++g) {
-    me.q[g][2 * lane] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane];
-    me.q[g][2 * lane + 1] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
+  float qv[kMaxG][2];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    qv[g][0] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
+    qv[g][1] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
   }
+  unsigned long long clo_enc = 0ull;
+  double pilot = 0.0, qnp = 0.0, qa = 0.0;
+  if (lane < G) {
+    const double *qc = a.qconst + (int64_t)(hq0 + lane) * kQc;
+    clo_enc = __hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pilot = qc[QC_PILOT];
+    qnp = qc[QC_QNP];
+    qa = qc[QC_QA];
+  }
+  const uint64_t prefix0 = a.prefix[h];
+  const int64_t swph = (a.nb_pool + kScanBlocks - 1) / kScanBlocks;
+  float lbs[kMaxG][2];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t k = lane + 64 * i;
+      lbs[g][i] = (g < G && k < swph) ? a.lbpart[(int64_t)(hq0 + g) * a.wstride + k] : -__builtin_huge_valf();
+    }
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    me.q[g][2 * lane] = qv[g][0];
+    me.q[g][2 * lane + 1] = qv[g][1];
+  }
+  // c_lo snapshot per query: c_R (the window's atomic) and the scan wavefronts' bounds
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    float v = fmaxf(lbs[g][0], lbs[g][1]);
+    if (g < G)
+      for (int64_t k = lane + 128; k < swph; k += 64) v = fmaxf(v, a.lbpart[(int64_t)(hq0 + g) * a.wstride + k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    lbs[g][0] = v;
+  }
+  // largest |q_t| over the group (lanes 0..7 hold the queries' values, 0 past G)
+  float qm = (float)qa;
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off, 64));
   if (lane < 8) {
-    double clo = 0.0, thr = 0.0, qnp = 0.0;
+    double clo = 0.0, thr = 0.0;
     if (lane < G) {
-      const double *qc = a.qconst + (int64_t)(hq0 + lane) * kQc;
-      clo = dec_max(__hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      thr = fmax(clo, qc[QC_PILOT]) + ltJ;
-      qnp = qc[QC_QNP];
+      float lb = lbs[0][0];
+#pragma unroll
+      for (int g = 1; g < kMaxG; ++g) lb = (lane == g) ? lbs[g][0] : lb;
+      clo = fmax(dec_max(clo_enc), (double)lb);
+      thr = fmax(clo, pilot) + ltJ;
     }
     me.clo[lane] = clo;
     me.thr[lane] = thr;
-    me.qnp[lane] = qnp;
+    me.qnp[lane] = (lane < G) ? qnp : 0.0;
   }
   if (lane == 0) {
-    float qm = 0.0f;
-    for (int g = 0; g < G; ++g) qm = fmaxf(qm, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
     me.qmax = qm;
-    me.prefix = a.prefix[h];
+    me.prefix = prefix0;
   }
   wave_sync();
 
