@@ -32,6 +32,11 @@ class Params(ctypes.Structure):
                 ("layer", c_int32), ("cand_budget", c_int32), ("cand_budget2", c_int32)]
 
 
+class Item(ctypes.Structure):
+    _fields_ = [("n", c_int64), ("slot", c_int32), ("layer", c_int32), ("eps", c_double),
+                ("seed", c_uint64), ("step", c_uint64)]
+
+
 class Trace(ctypes.Structure):
     _fields_ = [("c_R", c_void_p), ("c_lo", c_void_p), ("c_star", c_void_p),
                 ("bucket_count", c_void_p), ("lub", c_void_p), ("cmax_count", c_void_p),
@@ -52,6 +57,11 @@ SYMBOLS = {
     "csa_certified_decode_attention_noalloc": (c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_void_p,
                                                        c_void_p, c_void_p, ctypes.POINTER(Packed), c_int64,
                                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "csa_workspace_bytes_batch": (c_size_t, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_int32, c_int64]),
+    "csa_certified_decode_attention_batch": (c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_int32,
+                                                     c_int32, ctypes.POINTER(Item), c_void_p, c_void_p, c_void_p,
+                                                     ctypes.POINTER(Packed), c_void_p, c_size_t, c_void_p,
+                                                     c_void_p, c_void_p, c_void_p, c_void_p]),
     "csa_scan_bounds": (c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params), c_void_p, c_void_p,
                                 ctypes.POINTER(Packed), c_int64, c_void_p, c_size_t, c_void_p,
                                 c_void_p, c_void_p, c_void_p]),

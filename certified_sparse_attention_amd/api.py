@@ -227,6 +227,70 @@ def certified_decode_attention_noalloc(q: torch.Tensor, K: torch.Tensor, V: torc
     return o_hat, beta, stop, keys
 
 
+MAX_ITEMS = 64
+
+
+def workspace_bytes_batch(K: torch.Tensor, G: int, num_items: int, n_max: int, J: int, window: int = 64,
+                          r: int = 2) -> int:
+    """Workspace of a batched call (K: the cache, [num_slots][H_kv][n_cap][128])."""
+    lib = _lib.load()
+    sh = _lib.Shape(K.shape[1], G, 128, K.shape[2])
+    pr = _params(0.05, 0.01, r, J, window, "value", 0, 0, 0)
+    return int(lib.csa_workspace_bytes_batch(ctypes.byref(sh), ctypes.byref(pr), int(num_items), int(n_max)))
+
+
+def certified_decode_attention_batch(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, packed: PackedKV,
+                                     items, *, delta: float, r: int, J: int, window: int = 64,
+                                     measure="value", workspace: torch.Tensor | None = None, out=None,
+                                     cand_budget: int = 0, cand_budget2: int = 0):
+    """The certified decode step of several items (requests, or layers) in one call.
+
+    q: fp16 [B][H_q][128]; K, V: fp16 [S][H_kv][n_cap][128] (S cache slots); packed: the
+    packing of K, V viewed as [S * H_kv][n_cap][128].  items: B entries, each a dict with
+    n, slot, eps, seed, step, layer.  Returns (o_hat fp32 [B][H_q][128], beta fp64 [B][H_q],
+    stop_level int32 [B][H_q], keys_read int64 [B][H_q]).
+    """
+    if K.dim() != 4 or K.shape[3] != 128:
+        raise ValueError("K must be [num_slots][H_kv][n_cap][128]")
+    _check_fp16("K", K)
+    _check_fp16("V", V, K.shape)
+    _check_fp16("q", q)
+    S, H_kv, n_cap = K.shape[0], K.shape[1], K.shape[2]
+    B = len(items)
+    if not 1 <= B <= MAX_ITEMS:
+        raise ValueError(f"between 1 and {MAX_ITEMS} items")
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != 128 or q.shape[1] % H_kv:
+        raise ValueError("q must be [num_items][H_kv * G][128]")
+    H_q = q.shape[1]
+    G = H_q // H_kv
+    arr = (_lib.Item * B)()
+    for i, it in enumerate(items):
+        arr[i] = _lib.Item(int(it["n"]), int(it.get("slot", i)), int(it.get("layer", 0)), float(it["eps"]),
+                           int(it.get("seed", 0)) & (2 ** 64 - 1), int(it.get("step", 0)) & (2 ** 64 - 1))
+    n_max = max(int(it["n"]) for it in items)
+    lib = _lib.load()
+    sh = _lib.Shape(H_kv, G, 128, n_cap)
+    pr = _params(1.0, delta, r, J, window, measure, 0, 0, 0, cand_budget, cand_budget2)
+    if workspace is None:
+        nbytes = int(lib.csa_workspace_bytes_batch(ctypes.byref(sh), ctypes.byref(pr), B, n_max))
+        if nbytes == 0:
+            raise ValueError("invalid shape or parameters for the workspace")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    dev = K.device
+    if out is None:
+        out = (torch.empty((B, H_q, 128), dtype=torch.float32, device=dev),
+               torch.empty((B, H_q), dtype=torch.float64, device=dev),
+               torch.empty((B, H_q), dtype=torch.int32, device=dev),
+               torch.empty((B, H_q), dtype=torch.int64, device=dev))
+    o_hat, beta, stop, keys = out
+    pk = packed.c_struct()
+    _lib.check(lib.csa_certified_decode_attention_batch(
+        ctypes.byref(sh), ctypes.byref(pr), int(S), int(B), arr, _ptr(q), _ptr(K), _ptr(V), ctypes.byref(pk),
+        _ptr(workspace), workspace.numel(), _ptr(o_hat), _ptr(beta), _ptr(stop), _ptr(keys), _stream()),
+        "csa_certified_decode_attention_batch")
+    return o_hat, beta, stop, keys
+
+
 def scan_bounds(q: torch.Tensor, K: torch.Tensor, packed: PackedKV, n: int, *, J: int, r: int = 2,
                 window: int = 64, seed: int = 0x5EED, step: int = 0, layer: int = 0,
                 workspace: torch.Tensor | None = None):

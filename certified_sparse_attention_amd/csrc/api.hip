@@ -60,9 +60,35 @@ int check_params(const csa_params *p) {
   return CSA_OK;
 }
 
-csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max) {
+// The items of one call (a single call is one item in cache slot 0).
+struct Call {
+  csa::Batch b;
+  double eps[csa::kMaxItems];
+  uint64_t seed[csa::kMaxItems], step[csa::kMaxItems];
+  int32_t layer[csa::kMaxItems];
+  int64_t n_max;       // the longest item
+  int64_t npool_max;   // its pool (0: every item is its window alone)
+};
+
+Call single_call(const csa_shape *s, const csa_params *p, int64_t n) {
+  Call c{};
+  c.b.nitems = 1;
+  c.b.H_kv = s->num_kv_heads;
+  c.b.n[0] = n;
+  c.b.slot[0] = 0;
+  c.eps[0] = p->eps;
+  c.seed[0] = p->seed;
+  c.step[0] = p->step;
+  c.layer[0] = p->layer;
+  c.n_max = n;
+  c.npool_max = n > p->window ? n - p->window : 0;
+  return c;
+}
+
+// Workspace layout for `nitems` items of up to n_max cached tokens each.
+csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max, int nitems = 1) {
   csa::Plan P;
-  P.H_kv = s->num_kv_heads;
+  P.H_kv = s->num_kv_heads * nitems;
   P.G = s->group_size;
   P.H_q = P.H_kv * P.G;
   P.J = p->J;
@@ -138,22 +164,21 @@ int check_packed(const csa_packed *p) {
 }
 
 // Prep + scan shared by the certified call and the bounds diagnostic.
-int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, const uint16_t *K,
-                  const uint16_t *V, const csa_packed *pk, int64_t n, void *ws, const csa::Plan &P, double *lb_out,
+int run_prep_scan(const csa_shape *s, const csa_params *p, const Call &c, const uint16_t *q, const uint16_t *K,
+                  const uint16_t *V, const csa_packed *pk, void *ws, const csa::Plan &P, double *lb_out,
                   double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st, int diag = 0) {
   csa::PrepArgs pa;
   pa.q = q;
-  pa.K = K;
-  pa.n_cap = s->n_cap;
-  pa.n = n;
-  pa.W = p->window;
+  pa.U = P.H_kv;
+  pa.H_kv = s->num_kv_heads;
   pa.G = P.G;
   pa.J = P.J;
   pa.r = p->r;
-  pa.H_kv = P.H_kv;
-  pa.seed = p->seed;
-  pa.step = p->step;
-  pa.layer = p->layer;
+  for (int i = 0; i < c.b.nitems; ++i) {
+    pa.seed[i] = c.seed[i];
+    pa.step[i] = c.step[i];
+    pa.layer[i] = c.layer[i];
+  }
   pa.qf = at<float>(ws, P.qf);
   pa.qconst = at<double>(ws, P.qconst);
   pa.qA = at<int8_t>(ws, P.qA);
@@ -169,14 +194,13 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   pa.bdone = at<int>(ws, P.bdone);
   pa.exdone = at<int>(ws, P.exdone);
   pa.exdone2 = at<int>(ws, P.exdone2);
-  pa.npool_cap = P.npool_cap;
   hipError_t e = csa::launch_prep(pa, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
-  const int64_t npool = n - p->window;
+  const int64_t npool = c.npool_max;
   csa::ScanArgs sa;
   sa.K = K;
   sa.V = V;
-  sa.n = n;
+  sa.b = c.b;
   sa.W = p->window;
   sa.sR = pa.sR;
   sa.win = at<double>(ws, P.win);
@@ -189,12 +213,11 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const uint16_t *q, co
   sa.vnorm = pk->vnorm;
   sa.n_cap = s->n_cap;
   sa.nb_cap = s->n_cap / csa::kBlk;
-  sa.npool = npool > 0 ? npool : 0;
-  sa.nb_pool = (sa.npool + csa::kBlk - 1) / csa::kBlk;
+  sa.nb_pool = (npool + csa::kBlk - 1) / csa::kBlk;
   sa.nstream = npool > 0 ? csa::scan_stream_wgs(P.H_kv, sa.nb_pool) : 0;
   sa.npool_cap = P.npool_cap;
   sa.G = P.G;
-  sa.H_kv = P.H_kv;
+  sa.U = P.H_kv;
   sa.nbw = (P.npool_cap + csa::kBlk - 1) / csa::kBlk;
   sa.bmax = at<float2>(ws, P.bmax);
   sa.qf = pa.qf;
@@ -318,8 +341,8 @@ int check_certified_args(const csa_shape *shape, const csa_params *params, const
   return CSA_OK;
 }
 
-int certified_run(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
-                  const uint16_t *V, const csa_packed *packed, int64_t n, void *workspace, const csa::Plan &P,
+int certified_run(const csa_shape *shape, const csa_params *params, const Call &c, const uint16_t *q,
+                  const uint16_t *K, const uint16_t *V, const csa_packed *packed, void *workspace, const csa::Plan &P,
                   float *o_hat, double *beta, int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
                   hipStream_t st);
 
@@ -401,8 +424,8 @@ int csa_scan_bounds(const csa_shape *shape, const csa_params *params, const uint
   const csa::Plan P = make_plan(shape, params, n);
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
-  return run_prep_scan(shape, params, q, K, nullptr, packed, n, workspace, P, LB, E, UB, nullptr, nullptr,
-                       (hipStream_t)stream, 1);
+  return run_prep_scan(shape, params, single_call(shape, params, n), q, K, nullptr, packed, workspace, P, LB, E, UB,
+                       nullptr, nullptr, (hipStream_t)stream, 1);
 }
 
 int csa_certified_decode_attention(const csa_shape *shape, const csa_params *params, const uint16_t *q,
@@ -416,7 +439,56 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
   const csa::Plan P = make_plan(shape, params, n);
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
-  return certified_run(shape, params, q, K, V, packed, n, workspace, P, o_hat, beta, stop_level, keys_read, trace,
+  return certified_run(shape, params, single_call(shape, params, n), q, K, V, packed, workspace, P, o_hat, beta,
+                       stop_level, keys_read, trace, (hipStream_t)stream);
+}
+
+size_t csa_workspace_bytes_batch(const csa_shape *shape, const csa_params *params, int32_t num_items,
+                                 int64_t n_max) {
+  if (check_shape(shape) || check_params(params) || n_max < 1 || num_items < 1 || num_items > csa::kMaxItems)
+    return 0;
+  return make_plan(shape, params, n_max, num_items).total;
+}
+
+int csa_certified_decode_attention_batch(const csa_shape *shape, const csa_params *params, int32_t num_slots,
+                                         int32_t num_items, const csa_item *items, const uint16_t *q,
+                                         const uint16_t *K, const uint16_t *V, const csa_packed *packed,
+                                         void *workspace, size_t workspace_bytes, float *o_hat, double *beta,
+                                         int32_t *stop_level, int64_t *keys_read, csa_stream_t stream) {
+  g_err[0] = 0;
+  int rc = check_shape(shape);
+  if (rc || (rc = check_params(params))) return rc;
+  if (num_items < 1 || num_items > csa::kMaxItems)
+    return fail(CSA_ERR_UNSUPPORTED, "num_items must lie in [1, %d]", csa::kMaxItems);
+  if (num_slots < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "num_slots must be >= 1");
+  if ((int64_t)num_slots * shape->num_kv_heads * shape->n_cap >= (int64_t(1) << 40))
+    return fail(CSA_ERR_UNSUPPORTED, "cache too large");
+  if (!items || !q || !K || !V || !o_hat || !beta || !stop_level || !keys_read)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "items, q, K, V and every output must be non-null");
+  Call c{};
+  c.b.nitems = num_items;
+  c.b.H_kv = shape->num_kv_heads;
+  for (int i = 0; i < num_items; ++i) {
+    const csa_item &it = items[i];
+    if (it.n < 1 || it.n > shape->n_cap)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "item %d: n must lie in [1, n_cap]", i);
+    if (it.slot < 0 || it.slot >= num_slots)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "item %d: slot %d outside [0, %d)", i, it.slot, num_slots);
+    if (!(it.eps > 0.0) || !std::isfinite(it.eps)) return fail(CSA_ERR_INVALID_ARGUMENT, "item %d: eps must be > 0", i);
+    c.b.n[i] = it.n;
+    c.b.slot[i] = it.slot;
+    c.eps[i] = it.eps;
+    c.seed[i] = it.seed;
+    c.step[i] = it.step;
+    c.layer[i] = it.layer;
+    c.n_max = std::max(c.n_max, it.n);
+  }
+  c.npool_max = c.n_max > params->window ? c.n_max - params->window : 0;
+  if (c.npool_max > 0 && (rc = check_packed(packed))) return rc;
+  const csa::Plan P = make_plan(shape, params, c.n_max, num_items);
+  if (!workspace || workspace_bytes < P.total)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
+  return certified_run(shape, params, c, q, K, V, packed, workspace, P, o_hat, beta, stop_level, keys_read, nullptr,
                        (hipStream_t)stream);
 }
 
@@ -435,8 +507,8 @@ int csa_certified_decode_attention_noalloc(const csa_shape *shape, const csa_par
                 P.total, kScratchBytes);
   void *ws = nullptr;
   if ((rc = scratch_for_current_device(&ws))) return rc;
-  return certified_run(shape, params, q, K, V, packed, n, ws, P, o_hat, beta, stop_level, keys_read, nullptr,
-                       (hipStream_t)stream);
+  return certified_run(shape, params, single_call(shape, params, n), q, K, V, packed, ws, P, o_hat, beta,
+                       stop_level, keys_read, nullptr, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -444,18 +516,18 @@ int csa_certified_decode_attention_noalloc(const csa_shape *shape, const csa_par
 namespace {
 
 // The certified call on a workspace that holds at least plan P (arguments checked).
-int certified_run(const csa_shape *shape, const csa_params *params, const uint16_t *q, const uint16_t *K,
-                  const uint16_t *V, const csa_packed *packed, int64_t n, void *workspace, const csa::Plan &P,
+int certified_run(const csa_shape *shape, const csa_params *params, const Call &c, const uint16_t *q,
+                  const uint16_t *K, const uint16_t *V, const csa_packed *packed, void *workspace, const csa::Plan &P,
                   float *o_hat, double *beta, int32_t *stop_level, int64_t *keys_read, const csa_trace *trace,
                   hipStream_t st) {
   int rc = 0;
-  const bool all_exact = n <= params->window;
+  const bool all_exact = c.npool_max == 0;   // every item is its window alone
   void *ev0 = trace ? trace->ev_scan_begin : nullptr;
   void *ev1 = trace ? trace->ev_scan_end : nullptr;
-  rc = run_prep_scan(shape, params, q, K, V, packed, n, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
+  rc = run_prep_scan(shape, params, c, q, K, V, packed, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
   if (rc) return rc;
   void *ws = workspace;
-  const int64_t npool = n - params->window;
+  const int64_t npool = c.npool_max;   // (a single call: its pool)
   hipError_t e;
   csa::SelectArgs sel{};
   if (!all_exact) {
@@ -463,7 +535,8 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
     sa.K = K;
     sa.V = V;
     sa.n_cap = shape->n_cap;
-    sa.npool = npool;
+    sa.b = c.b;
+    sa.W = params->window;
     sa.npool_cap = P.npool_cap;
     sa.ntiles = (npool + csa::kBucketTile - 1) / csa::kBucketTile;
     sa.G = P.G;
@@ -504,14 +577,13 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.K = K;
   ca.V = V;
   ca.n_cap = shape->n_cap;
-  ca.n = n;
-  ca.npool = npool > 0 ? npool : 0;
+  ca.b = c.b;
   ca.npool_cap = P.npool_cap;
   ca.G = P.G;
   ca.J = P.J;
   ca.W = params->window;
   ca.measure = params->measure;
-  ca.eps = params->eps;
+  for (int i = 0; i < c.b.nitems; ++i) ca.eps[i] = c.eps[i];
   {
     const int tails = params->measure == CSA_MEASURE_DENOM ? 2 : (params->measure == CSA_MEASURE_OUTNORM ? 5 : 6);
     ca.L = std::log((double)tails * (double)(params->J + 1) / params->delta);
@@ -525,7 +597,6 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.cstar = at<unsigned long long>(ws, P.cstar);
   ca.vpart = at<unsigned>(ws, P.vpart);
   ca.wstride = P.wstride;
-  ca.wph = npool > 0 ? ((npool + csa::kBlk - 1) / csa::kBlk + csa::kScanBlocks - 1) / csa::kScanBlocks : 0;
   ca.ccount = at<int>(ws, P.ccount);
   ca.candpos = at<int>(ws, P.candpos);
   ca.rec_hl = at<int>(ws, P.rec_hl);
@@ -559,7 +630,6 @@ int certified_run(const csa_shape *shape, const csa_params *params, const uint16
   ca.beta = beta;
   ca.stop = stop_level;
   ca.keys_read = keys_read;
-  ca.all_exact = all_exact ? 1 : 0;
   ca.ccount1 = at<int>(ws, P.ccount1);
   ca.jspec = at<int>(ws, P.jspec);
   // pass 1: levels up to the speculative level (at most `budget` candidates, rescored

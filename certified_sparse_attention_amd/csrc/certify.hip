@@ -25,16 +25,18 @@ namespace csa {
 
 struct CertArgs {
   const uint16_t *K, *V;
-  int64_t n_cap, n, npool, npool_cap;
+  int64_t n_cap, npool_cap;
   int G, J, W, measure;
-  double eps, L;
+  double L;
+  Batch b;                       // units: item KV heads (query head hq is in unit hq / G)
+  double eps[kMaxItems];         // per item
   const float *qf;
   const double *lt, *tau, *sR;
   const double *win, *qconst;   // window sums relative to c_R; per-query constants (c_R)
   const unsigned long long *cstar, *clo;
   const double *ubuf;
   const unsigned *vpart;         // per scan wavefront: largest |v| code of its keys
-  int64_t wph, wstride;          // scan wavefronts per KV head, row stride of vpart
+  int64_t wstride;               // row stride of vpart (per unit)
   const int *ccount, *candpos, *hist;
   int *rec_hl;                  // candidate records (written by the fused rescoring)
   const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
@@ -63,8 +65,12 @@ struct CertArgs {
   double *beta;
   int32_t *stop;
   int64_t *keys_read;
-  int all_exact;
 };
+
+// Query head hq: its unit's cached length, cache head and item.
+__device__ inline int64_t head_n(const CertArgs &a, int hq) { return unit_n(a.b, hq / a.G); }
+__device__ inline int64_t head_kv(const CertArgs &a, int hq) { return unit_kv(a.b, hq / a.G); }
+__device__ inline int head_item(const CertArgs &a, int hq) { return (hq / a.G) / a.b.H_kv; }
 
 constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
 constexpr int kStage = 64;        // candidates staged in LDS at a time
@@ -118,7 +124,7 @@ struct AccSmem {
 // candidates' terms in candidate order with LDS atomics that return nothing, so no cell
 // is shared between threads and nothing waits on the sums.
 // V rows are fetched here unless `staged`.
-__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, bool staged) {
+__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int64_t h, int cnt, bool staged) {
   const int t = threadIdx.x, J = a.J;
   if (!staged) {
     // V rows of candidates that enter the sample at some level <= J
@@ -127,7 +133,7 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
       if ((s.hl[r] >> 8) <= J) {
         const int pos = s.pos[r];
         reinterpret_cast<uint4 *>(s.vs[r])[part] =
-            reinterpret_cast<const uint4 *>(a.V + ((int64_t)h * a.n_cap + pos) * kD)[part];
+            reinterpret_cast<const uint4 *>(a.V + (h * a.n_cap + pos) * kD)[part];
       }
     }
     __syncthreads();
@@ -190,7 +196,8 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int h, int cnt, 
 
 // Add candidates [i0, i1) of query head hq from their stored records.
 __device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
-  const int t = threadIdx.x, h = hq / a.G;
+  const int t = threadIdx.x;
+  const int64_t h = head_kv(a, hq);
   const int64_t base = (int64_t)hq * a.npool_cap;
   for (int c0 = i0; c0 < i1; c0 += kStage) {
     const int cnt = min(kStage, i1 - c0);
@@ -227,7 +234,8 @@ struct RescoreConsts {
 template <bool kSpec>
 __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int hq, int c0, int cnt,
                                               const RescoreConsts &rc, int zero_rows = 0) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h = hq / a.G;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t h = head_kv(a, hq);
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
   if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
@@ -241,7 +249,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
     sc8[step] = 0.0f;
     if (r < cnt) {
-      const int64_t tok = (int64_t)h * a.n_cap + s.pos[r];
+      const int64_t tok = h * a.n_cap + s.pos[r];
       cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
       sc8[step] = a.scale8[tok];
       if (kSpec) {
@@ -259,8 +267,8 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   if (t < cnt) {
     const int pos = s.pos[t];
     ubt = a.ubuf[base + pos];
-    ke8 = h2d(a.kerr8[(int64_t)h * a.n_cap + pos]);
-    s8t = (double)a.scale8[(int64_t)h * a.n_cap + pos];
+    ke8 = h2d(a.kerr8[h * a.n_cap + pos]);
+    s8t = (double)a.scale8[h * a.n_cap + pos];
     E = perturbation(rc.prefix, pos);
   }
   for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
@@ -291,7 +299,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     const int r = 16 * wv + 8 * step + s8;
     const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
     if (!kSpec && ex) {
-      const int64_t tok = (int64_t)h * a.n_cap + s.pos[r];
+      const int64_t tok = h * a.n_cap + s.pos[r];
       const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
       const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
       kw[step][0] = ksrc[0];
@@ -367,7 +375,7 @@ __device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0
   for (int c0 = i0; c0 < i1; c0 += kStage) {
     const int cnt = min(kStage, i1 - c0);
     rescore_stage<false>(a, s, hq, c0, cnt, rc);
-    accumulate_stage(a, s, hq / a.G, cnt, true);
+    accumulate_stage(a, s, head_kv(a, hq), cnt, true);
   }
 }
 
@@ -488,7 +496,9 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   }
   if (wv == 3) {                 // Vmax: the scan wavefronts' maxima of the head
     unsigned v = 0u;
-    for (int64_t k = lane; k < a.wph; k += 64) v = max(v, a.vpart[(int64_t)h * a.wstride + k]);
+    const int64_t np = unit_npool(a.b, h, a.W);
+    const int64_t wph = ((np + kBlk - 1) / kBlk + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
+    for (int64_t k = lane; k < wph; k += 64) v = max(v, a.vpart[(int64_t)h * a.wstride + k]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
     if (lane == 0) f.vmax = h2d((uint16_t)v);
@@ -512,7 +522,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
     RescoreConsts rc;
     rescore_consts(a, s, hq, rc);
     rescore_stage<true>(a, s, hq, 0, count, rc, jmax + 1);
-    accumulate_stage(a, s, hq / a.G, count, true);
+    accumulate_stage(a, s, head_kv(a, hq), count, true);
   } else if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
     accumulate_mixed(a, s, hq, 0, count, record_split(a, hq, count));
@@ -639,7 +649,8 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   }
   __syncthreads();
   if (wv == 0) {
-    const unsigned long long ok = __ballot(lane <= jmax && f.beta[lane] <= a.eps);
+    const double eps = a.eps[head_item(a, hq)];
+    const unsigned long long ok = __ballot(lane <= jmax && f.beta[lane] <= eps);
     if (lane == 0) f.jstar = ok ? (__ffsll((long long)ok) - 1) : a.J + 1;
   }
   __syncthreads();
@@ -652,7 +663,7 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
       set_status(a, hq, extend ? a.pass + 1 : 1);
       a.stop[hq] = a.J + 1;
       a.beta[hq] = 0.0;
-      a.keys_read[hq] = a.n;
+      a.keys_read[hq] = head_n(a, hq);
     }
     return false;
   }
@@ -681,12 +692,12 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
 // Pass 1, one workgroup per query head (heads with n <= W go straight to exact attention).
 __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   const int hq = blockIdx.x;
-  if (a.all_exact) {
+  if (unit_npool(a.b, hq / a.G, a.W) == 0) {
     if (threadIdx.x == 0) {
       a.flags[hq] = 1;
       a.stop[hq] = 0;
       a.beta[hq] = 0.0;
-      a.keys_read[hq] = a.n;
+      a.keys_read[hq] = head_n(a, hq);
     }
     return;
   }
@@ -705,7 +716,8 @@ struct ExactSmem {
 // and D (out[kD]), 256 threads.  Keys in batches of 256: one key per thread for its score
 // and weight, then two halves of the batch over the 128 channels.
 __device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0, int64_t i1, double *out) {
-  const int t = threadIdx.x, h = hq / a.G, c = t & (kD - 1), hf = t >> 7;
+  const int t = threadIdx.x, c = t & (kD - 1), hf = t >> 7;
+  const int64_t h = head_kv(a, hq);
   if (t < kD) e.qd[t] = (double)a.qf[(int64_t)hq * kD + t];
   const double cs = dec_max(a.cstar[hq]);
   __syncthreads();
@@ -713,14 +725,14 @@ __device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0,
   for (int64_t b = i0; b < i1; b += 256) {
     const int cnt = (int)min<int64_t>(256, i1 - b);
     if (t < cnt) {
-      const double sc = exact_score(e.qd, a.K + ((int64_t)h * a.n_cap + b + t) * kD);
+      const double sc = exact_score(e.qd, a.K + (h * a.n_cap + b + t) * kD);
       const double w = exp(sc - cs);
       e.w[t] = w;
       accD += w;
     }
     __syncthreads();
     for (int i = 128 * hf; i < min(cnt, 128 * hf + 128); ++i)
-      accN += e.w[i] * h2d(a.V[((int64_t)h * a.n_cap + b + i) * kD + c]);
+      accN += e.w[i] * h2d(a.V[(h * a.n_cap + b + i) * kD + c]);
     __syncthreads();
   }
   // D: wavefront sums, then the four in order; N: the two halves
@@ -851,8 +863,9 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
       tail_units(a, h, k2);
       const int gsz = grp[0][lo] - (lo > 0 ? grp[0][lo - 1] : 0);
       if (k2 == 1) {
-        const int64_t len = (a.n + gsz - 1) / gsz;
-        const int64_t i0 = k * len, i1 = min<int64_t>(a.n, i0 + len);
+        const int64_t nh = head_n(a, h);
+        const int64_t len = (nh + gsz - 1) / gsz;
+        const int64_t i0 = k * len, i1 = min<int64_t>(nh, i0 + len);
         exact_chunk(a, u.e, h, i0, i1, a.exactp + ((int64_t)h * kExactChunks + k) * 130);
       } else if (gsz > 1) {
         const int count = pass_count(a, h);
@@ -887,7 +900,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
           }
         } else if (!certify_head(a, u.f, h, gsz > 1 ? gsz : 0) && a.pass == a.final_pass) {
           __syncthreads();
-          exact_chunk(a, u.e, h, 0, a.n, a.exactp + (int64_t)h * kExactChunks * 130);
+          exact_chunk(a, u.e, h, 0, head_n(a, h), a.exactp + (int64_t)h * kExactChunks * 130);
           if (t < kD) a.o_hat[(int64_t)h * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);
         }
       }
@@ -907,7 +920,8 @@ hipError_t launch_certify_pass(CertArgs a, int pass, int H_q, hipStream_t st) {
 // at once: one launch when the second pass covers every level (the default), two when a
 // second budget splits the remaining levels.
 hipError_t launch_tail(CertArgs a, int H_q, bool three_pass, hipStream_t st) {
-  const unsigned nwg = (unsigned)max(256, min(4096, H_q * kTailWG));
+  // at least one workgroup per query head (every head with work gets its own group)
+  const unsigned nwg = (unsigned)max(max(256, H_q), min(4096, H_q * kTailWG));
   a.H_q = H_q;
   a.final_pass = three_pass ? 3 : 2;
   a.pass = 2;

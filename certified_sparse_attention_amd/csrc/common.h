@@ -23,7 +23,8 @@ constexpr int kD = 128;
 constexpr int kBlk = 32;
 constexpr int kMaxJ = 60;
 constexpr int kMaxG = 7;
-constexpr int kBlocksPerWave = 16;                 // scan: blocks handled by one wavefront
+constexpr int kBlocksPerWave = 16;                 // refinement: blocks per wavefront slot
+constexpr int kScanBlocks = 32;                    // streaming scan: blocks per wavefront
 constexpr int kNumSeg = 64;                        // accumulate: max segments per query
 constexpr int kStatW = 262;                        // per-level stats N[128] V[128] D Q k P X (X:
                                                    // exact reads outside C_max), and a pad
@@ -361,9 +362,30 @@ __device__ inline double wave_max_f64(double v) {
   return v;
 }
 
+// ---------------------------------------------------------------- batch of items
+// One call covers `nitems` items (requests, or layers of one request), each with its own
+// cached length n and its own cache slot; the kernels see nitems * H_kv units, unit u
+// being KV head u % H_kv of item u / H_kv.  Workspace rows are per unit (query head
+// u G + g); cache rows are those of cache head slot H_kv + (u % H_kv).  Passed by value
+// in every kernel's arguments.
+constexpr int kMaxItems = 64;
+struct Batch {
+  int nitems, H_kv;
+  int64_t n[kMaxItems];
+  int32_t slot[kMaxItems];
+};
+__host__ __device__ inline int64_t unit_n(const Batch &b, int u) { return b.n[u / b.H_kv]; }
+__host__ __device__ inline int64_t unit_npool(const Batch &b, int u, int W) {
+  const int64_t n = b.n[u / b.H_kv];
+  return n > W ? n - W : 0;
+}
+__host__ __device__ inline int64_t unit_kv(const Batch &b, int u) {
+  return (int64_t)b.slot[u / b.H_kv] * b.H_kv + u % b.H_kv;
+}
+
 // ---------------------------------------------------------------- workspace plan
 struct Plan {
-  int H_kv, G, H_q, J, W;
+  int H_kv, G, H_q, J, W;   // H_kv, H_q: units and their query heads (all items)
   int64_t npool_cap;   // pool capacity per query head
   int64_t ntiles;      // bucket tiles per query head
   int64_t wstride;     // scan wavefronts per KV head at full pool capacity

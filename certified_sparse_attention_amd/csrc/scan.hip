@@ -33,11 +33,10 @@ __device__ inline void wave_sync() {
 // ------------------------------------------------------------------ prep
 
 struct PrepArgs {
-  const uint16_t *q, *K;
-  int64_t n_cap, n, npool_cap;
-  int W, G, J, r, H_kv;
-  uint64_t seed, step;
-  int layer;
+  const uint16_t *q;        // [units G][128], query head u G + g of unit u
+  int U, H_kv, G, J, r;     // units, KV heads per item
+  uint64_t seed[kMaxItems], step[kMaxItems];   // hash inputs per item
+  int32_t layer[kMaxItems];
   float *qf;
   double *qconst;
   int8_t *qA;
@@ -49,10 +48,10 @@ struct PrepArgs {
   int *bdone, *exdone, *exdone2;   // per-head completion counters, cleared here
 };
 
-// One workgroup of 128 threads per query head; thread t owns channel t.
+// One workgroup of 128 threads per query head (of every unit); thread t owns channel t.
 __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
   const int t = threadIdx.x, lane = t & 63;
-  const int hq = blockIdx.x, h = hq / a.G, g = hq % a.G;
+  const int hq = blockIdx.x, h = hq / a.G, g = hq % a.G;   // h: the unit
   __shared__ double qd[kD];
   __shared__ double part[16];
   __shared__ double red[2];
@@ -64,7 +63,9 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
     a.tau[t] = exp(v);
   }
   if (g == 0 && t == 0) {
-    a.prefix[h] = hash_prefix(a.seed, a.step, (uint64_t)(int64_t)a.layer, (uint64_t)h);
+    // the hash takes the item's seed, step and layer and the head within the layer
+    const int it = h / a.H_kv;
+    a.prefix[h] = hash_prefix(a.seed[it], a.step[it], (uint64_t)(int64_t)a.layer[it], (uint64_t)(h % a.H_kv));
   }
   const double qv = h2d(a.q[(int64_t)hq * kD + t]);
   a.qf[(int64_t)hq * kD + t] = (float)qv;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(prep_kernel, dim3(a.H_kv * a.G), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(prep_kernel, dim3(a.U * a.G), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
@@ -154,8 +155,9 @@ struct ScanArgs {
   const int8_t *zq;
   const BlockMeta *bmeta;
   const uint16_t *kerr, *vnorm;
-  int64_t n_cap, nb_cap, npool, nb_pool, npool_cap, nwords, nbw;
-  int G, H_kv, J;
+  int64_t n_cap, nb_cap, nb_pool, npool_cap, nwords, nbw;   // nb_pool: the longest item's
+  int G, U, J;                                               // units (item KV heads)
+  Batch b;
   const float *qf;
   double *qconst;
   const int8_t *qA;
@@ -163,7 +165,6 @@ struct ScanArgs {
   const double *lt;
   // window work (extra workgroups of the streaming kernel, one per query head)
   const uint16_t *V;
-  int64_t n;
   int W;
   int64_t nstream;          // workgroups of the streaming scan; the rest do window work
   double *sR;               // [H_q][W] window scores
@@ -231,19 +232,19 @@ struct OffsetIn {
   BlockMeta bm;
 };
 
-__device__ inline void offset_load(const ScanArgs &a, int h, int64_t blk0, int nblk, int lane, int col0,
+__device__ inline void offset_load(const ScanArgs &a, int64_t kvh, int64_t blk0, int nblk, int lane, int col0,
                                    OffsetIn &in) {
   const int n16 = lane & 15, grp = lane >> 4;
   in.z1k0 = in.z1k1 = in.z0k0 = in.z0k1 = v4i{0, 0, 0, 0};
   in.bm = BlockMeta{};
   const int col = col0 + n16;
   if (col < nblk) {
-    const int8_t *zb = a.zq + ((int64_t)h * a.nb_cap + blk0 + col) * 256;
+    const int8_t *zb = a.zq + (kvh * a.nb_cap + blk0 + col) * 256;
     in.z1k0 = *reinterpret_cast<const v4i *>(zb + 32 * grp);
     in.z1k1 = *reinterpret_cast<const v4i *>(zb + 32 * grp + 16);
     in.z0k0 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp);
     in.z0k1 = *reinterpret_cast<const v4i *>(zb + 128 + 32 * grp + 16);
-    in.bm = a.bmeta[(int64_t)h * a.nb_cap + blk0 + col];
+    in.bm = a.bmeta[kvh * a.nb_cap + blk0 + col];
   }
 }
 
@@ -291,14 +292,14 @@ __device__ inline void offset_consts(const ScanArgs &a, int h, int G, int lane, 
 }
 
 template <int NB>
-__device__ inline void offset_terms(const ScanArgs &a, int h, int64_t blk0, int nblk, int G, int lane,
+__device__ inline void offset_terms(const ScanArgs &a, int h, int64_t kvh, int64_t blk0, int nblk, int G, int lane,
                                    double (*cst)[NB][8], int col0 = 0) {
   const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
   const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
   double beta[2], qabs[2];
   offset_consts(a, h, G, lane, beta, qabs);
   OffsetIn in;
-  offset_load(a, h, blk0, nblk, lane, col0, in);
+  offset_load(a, kvh, blk0, nblk, lane, col0, in);
   offset_compute(
       in, qa0, qa1, beta, qabs, nblk, G, lane,
       [&](int col, int g, double base, double eb, double pad) {
@@ -376,7 +377,6 @@ __device__ inline Bound32 bound32(float base, float ebpad, float alpha, float ha
 }
 
 constexpr int kPilot = 128;   // pool keys scored exactly up front (a lower bound on c*)
-constexpr int kScanBlocks = 32; // streaming scan: blocks per wavefront
 constexpr int kScanBufs = 3;     // streaming scan: chunk buffers (chunks in flight + 1)
 
 // Shared memory of the streaming kernel; its window workgroups reuse it.
@@ -408,13 +408,14 @@ constexpr int kWinGrp = 3;     // wavefront steps whose rows are read together
 __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int s8 = lane >> 3, k8 = lane & 7;
-  const int h = hq / a.G;
-  const int64_t w0 = (a.n > a.W) ? (a.n - a.W) : 0;
-  const int nw = (int)(a.n - w0);
+  const int h = hq / a.G;                                   // the unit
+  const int64_t kvh = unit_kv(a.b, h), nU = unit_n(a.b, h);  // its cache head and length
+  const int64_t w0 = (nU > a.W) ? (nU - a.W) : 0;
+  const int nw = (int)(nU - w0);
   const int64_t stride = (w0 + kPilot - 1) / kPilot;
   const int npilot = (w0 > 0) ? kPilot : 0;
   const bool vcols = (t < kD) && a.V != nullptr && nw > 0;
-  const uint16_t *vcol = vcols ? a.V + ((int64_t)h * a.n_cap + w0) * kD + t : nullptr;
+  const uint16_t *vcol = vcols ? a.V + (kvh * a.n_cap + w0) * kD + t : nullptr;
   typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
   ushort2v vpre[kWinVPre / 2];   // two rows per register (half-register loads)
   if (vcols) {
@@ -427,8 +428,8 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   double q16[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
-  const uint16_t *Kh = a.K + (int64_t)h * a.n_cap * kD;
-  const uint16_t *Vh = a.V ? a.V + (int64_t)h * a.n_cap * kD : nullptr;
+  const uint16_t *Kh = a.K + kvh * a.n_cap * kD;
+  const uint16_t *Vh = a.V ? a.V + kvh * a.n_cap * kD : nullptr;
   double m = -__builtin_huge_val(), mp = -__builtin_huge_val();
   for (int g0 = 0; g0 < nw + npilot; g0 += 32 * kWinGrp) {
     int64_t pos[kWinGrp];
@@ -563,10 +564,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int64_t wph = (a.nb_pool + kScanBlocks - 1) / kScanBlocks;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wv;
-  if (gw >= (int64_t)a.H_kv * wph) return;
-  const int h = (int)(gw / wph);
+  if (gw >= (int64_t)a.U * wph) return;
+  const int h = (int)(gw / wph);                         // the unit
+  const int64_t kvh = unit_kv(a.b, h);                   // its cache head
+  const int64_t npool = unit_npool(a.b, h, a.W);
   const int64_t blk0 = (gw % wph) * kScanBlocks;
-  const int nblk = (int)min((int64_t)kScanBlocks, a.nb_pool - blk0);
+  if (blk0 * kBlk >= npool) return;                      // past this unit's pool
+  const int nblk = (int)min((int64_t)kScanBlocks, (npool + kBlk - 1) / kBlk - blk0);
   const int n16 = lane & 15, grp = lane >> 4;
   uint8_t *Abuf = sm.st.Abuf[wv][0];
   uint8_t *Abuf1 = sm.st.Abuf[wv][1];
@@ -606,17 +610,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // Buffer resources over this wave's blocks only.  The chunk offset goes into the
   // per-lane offset, which the hardware range checks (the scalar offset is not), so the
   // reads of chunks past the wave's blocks or the pool return 0 and touch no memory.
-  const int64_t tokw = min((int64_t)nblk * kBlk, a.npool - blk0 * kBlk);
+  const int64_t tokw = min((int64_t)nblk * kBlk, npool - blk0 * kBlk);
   const __amdgpu_buffer_rsrc_t rs_codes = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.codes + ((int64_t)h * a.nb_cap + blk0) * 2048), (short)0, nblk * 2048, kBufDword3);
+      (void *)(a.codes + (kvh * a.nb_cap + blk0) * 2048), (short)0, nblk * 2048, kBufDword3);
   const __amdgpu_buffer_rsrc_t rs_ks = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.kscale + ((int64_t)h * a.nb_cap + blk0) * kD), (short)0, nblk * 2 * kD, kBufDword3);
+      (void *)(a.kscale + (kvh * a.nb_cap + blk0) * kD), (short)0, nblk * 2 * kD, kBufDword3);
   const __amdgpu_buffer_rsrc_t rs_bm = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.bmeta + (int64_t)h * a.nb_cap + blk0), (short)0, nblk * (int)sizeof(BlockMeta), kBufDword3);
+      (void *)(a.bmeta + kvh * a.nb_cap + blk0), (short)0, nblk * (int)sizeof(BlockMeta), kBufDword3);
   const __amdgpu_buffer_rsrc_t rs_kerr = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.kerr + (int64_t)h * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
+      (void *)(a.kerr + kvh * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
   const __amdgpu_buffer_rsrc_t rs_vn = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.vnorm + (int64_t)h * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
+      (void *)(a.vnorm + kvh * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
   auto load_chunk = [&](int c0, ChunkIn &in) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const int oc = c0 * 2048 + lane * 16, ok = c0 * 2 * kD + lane * 4, om = c0 * (int)sizeof(BlockMeta);
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   double obeta[2], oqabs[2];
   offset_consts(a, h, G, lane, obeta, oqabs);
   OffsetIn off0, off1;
-  offset_load(a, h, blk0, nblk, lane, 0, off0);
+  offset_load(a, kvh, blk0, nblk, lane, 0, off0);
   ChunkIn buf[kScanBufs];
 #pragma unroll
   for (int k = 0; k + 1 < kScanBufs; ++k) load_chunk(2 * k, buf[k]);
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   auto hash_chunk = [&](const int c0, const ChunkIn &in) {
     const int nb2 = min(2, nblk - c0);
     const int64_t tok0 = (blk0 + c0) * kBlk;
-    const int nval = (int)min((int64_t)(32 * nb2), a.npool - tok0);
+    const int nval = (int)min((int64_t)(32 * nb2), npool - tok0);
     float myEup = 0.0f;
     if (lane < nval) {
       myEup = perturbation_upper32(prefix, tok0 + lane);
@@ -693,7 +697,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // accesses (and the writes before the products) across them.
   auto process = [&](const int c0, const ChunkIn &cur, const ChunkIn &nxt, const float *alpha32s, float *alnext) {
     const int nb2 = min(2, nblk - c0);
-    const int nval = (int)min((int64_t)(32 * nb2), a.npool - (blk0 + c0) * kBlk);
+    const int nval = (int)min((int64_t)(32 * nb2), npool - (blk0 + c0) * kBlk);
     wave_sync();
     float2 cA[2], cB[2];
 #pragma unroll
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       process(c, buf[k], buf[(k + 1) % kScanBufs], alCur, alNext);
       alCur[0] = alNext[0];
       alCur[1] = alNext[1];
-      if (kScanBlocks > 16 && c == 0) offset_load(a, h, blk0, nblk, lane, 16, off1);
+      if (kScanBlocks > 16 && c == 0) offset_load(a, kvh, blk0, nblk, lane, 16, off1);
     }
   }
   wave_sync();
@@ -811,18 +815,19 @@ struct ChunkLoads {
   uint32_t kk[2];
 };
 
-__device__ inline void load_chunk(const ScanArgs &a, int h, int64_t bA, int nb2, int lane, ChunkLoads &L) {
+__device__ inline void load_chunk(const ScanArgs &a, int u, int64_t bA, int nb2, int lane, ChunkLoads &L) {
+  const int64_t h = unit_kv(a.b, u);   // cache head of unit u
   const int64_t mypos = bA * kBlk + lane;
-  L.kerr = (lane < 32 * nb2 && mypos < a.npool) ? (uint32_t)a.kerr[(int64_t)h * a.n_cap + mypos] : 0u;
+  L.kerr = (lane < 32 * nb2 && mypos < unit_npool(a.b, u, a.W)) ? (uint32_t)a.kerr[h * a.n_cap + mypos] : 0u;
 #pragma unroll
   for (int T = 0; T < 4; ++T)
     L.cw[T] = (T < 2 * nb2)
-                  ? reinterpret_cast<const uint4 *>(a.codes + ((int64_t)h * a.nb_cap + bA) * 2048)[T * 64 + lane]
+                  ? reinterpret_cast<const uint4 *>(a.codes + (h * a.nb_cap + bA) * 2048)[T * 64 + lane]
                   : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
-    L.ksmax[bi] = (bi < nb2) ? a.bmeta[(int64_t)h * a.nb_cap + bA + bi].ksmax : 0.0f;
-    L.kk[bi] = (bi < nb2) ? reinterpret_cast<const uint32_t *>(a.kscale + ((int64_t)h * a.nb_cap + bA + bi) * kD)[lane]
+    L.ksmax[bi] = (bi < nb2) ? a.bmeta[h * a.nb_cap + bA + bi].ksmax : 0.0f;
+    L.kk[bi] = (bi < nb2) ? reinterpret_cast<const uint32_t *>(a.kscale + (h * a.nb_cap + bA + bi) * kD)[lane]
                           : 0u;
   }
 }
@@ -843,13 +848,14 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   // local slot s / H_kv of head s % H_kv, so one head's slots fall to different
   // workgroups and a head with many passing blocks shares them with the others' waves
   const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t nslots = (int64_t)a.H_kv * wph;
-  auto slot_head = [&](int w) { return (int)(((int64_t)blockIdx.x * 4 + w) % a.H_kv); };
-  auto slot_blk0 = [&](int w) { return (((int64_t)blockIdx.x * 4 + w) / a.H_kv) * kBlocksPerWave; };
+  const int64_t nslots = (int64_t)a.U * wph;
+  auto slot_head = [&](int w) { return (int)(((int64_t)blockIdx.x * 4 + w) % a.U); };
+  auto slot_blk0 = [&](int w) { return (((int64_t)blockIdx.x * 4 + w) / a.U) * kBlocksPerWave; };
+  auto unit_blocks = [&](int u) { return (unit_npool(a.b, u, a.W) + kBlk - 1) / kBlk; };
   const int64_t gs = (int64_t)blockIdx.x * 4 + wv;
   const int h = slot_head(wv);
   const int64_t blk0 = slot_blk0(wv);
-  const int nblk = (gs < nslots) ? (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, a.nb_pool - blk0)) : 0;
+  const int nblk = (gs < nslots) ? (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, unit_blocks(h) - blk0)) : 0;
   const int G = a.G;
   const int n16 = lane & 15, grp = lane >> 4;
 
@@ -893,7 +899,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     qa = qc[QC_QA];
   }
   const uint64_t prefix0 = a.prefix[h];
-  const int64_t swph = (a.nb_pool + kScanBlocks - 1) / kScanBlocks;
+  const int64_t swph = (unit_blocks(h) + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
   float lbs[kMaxG][2];
 #pragma unroll
   for (int g = 0; g < kMaxG; ++g)
@@ -989,11 +995,11 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     }
   }
   auto job_blk = [&](int j) { return slot_blk0(j >> 3) + 2 * (j & 7); };
-  auto job_nb2 = [&](int j) { return (int)min<int64_t>(2, a.nb_pool - job_blk(j)); };
+  auto job_nb2 = [&](int j) { return (int)min<int64_t>(2, unit_blocks(slot_head(j >> 3)) - job_blk(j)); };
   int cc = jobs ? __ffs((int)jobs) - 1 : -1;
   ChunkLoads cur, nxt;
   if (cc >= 0) load_chunk(a, slot_head(cc >> 3), job_blk(cc), job_nb2(cc), lane, cur);
-  if (chunks) offset_terms(a, h, blk0, nblk, G, lane, cst_all[wv]);
+  if (chunks) offset_terms(a, h, unit_kv(a.b, h), blk0, nblk, G, lane, cst_all[wv]);
   init_operand(Abuf, lane);
   __syncthreads();   // every slot's offset terms and values are in LDS
 
@@ -1002,7 +1008,8 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     const int cn = jobs ? __ffs((int)jobs) - 1 : -1;
     // the job's slot: its head's values
     RefineSlot &S = slot_all[cc >> 3];
-    const int jh = slot_head(cc >> 3), jhq0 = jh * G;
+    const int jh = slot_head(cc >> 3), jhq0 = jh * G;   // the job's unit
+    const int64_t jnpool = unit_npool(a.b, jh, a.W), jkv = unit_kv(a.b, jh);
     float qv0[kMaxG], qv1[kMaxG];
 #pragma unroll
     for (int g = 0; g < kMaxG; ++g) {
@@ -1021,7 +1028,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     const int nb2 = job_nb2(cc);
     const int64_t tok0 = bA * kBlk;
     const int64_t mypos = tok0 + lane;
-    const bool mine = (lane < 32 * nb2) && (mypos < a.npool);
+    const bool mine = (lane < 32 * nb2) && (mypos < jnpool);
     double myEup = 0.0;
     if (mine) myEup = perturbation_upper(prefix, mypos);
     const uint32_t mykerr = cur.kerr;
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         const double kerr = h2d((uint16_t)bperm_i32(tt, (int)mykerr));
         ubA[Tg] = 0.0;
         ubB[Tg] = 0.0;
-        if (pos < a.npool) {
+        if (pos < jnpool) {
           if (hasA) {
             const int I = acc[0] * 128 + acc[1];
             const double shat = (baseA + alpha * (double)I) * kRsqrtD;
@@ -1083,7 +1090,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubA[Tg] = ub;
             lbA = fmax(lbA, lb);
-            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gA) * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gA) * jnpool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrA) + 1.0);
             if (ub >= clo2A - marg) cmA |= 1u << Tg;
             if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
@@ -1095,7 +1102,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             const double ub = shat + slack, lb = shat - slack;
             ubB[Tg] = ub;
             lbB = fmax(lbB, lb);
-            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gB) * a.npool + pos] = lb;
+            if (a.lb_out) a.lb_out[(int64_t)(jhq0 + gB) * jnpool + pos] = lb;
             const double marg = 0x1p-40 * (fabs(ub) + fabs(thrB) + 1.0);
             if (ub >= clo2B - marg) cmB |= 1u << Tg;
             if (a.diag || ub + Eup >= thrB - marg || ub >= clo2B - marg) liveB |= 1u << Tg;
@@ -1142,7 +1149,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
           double q16[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(jhq0 + g2) * kD + 16 * k8 + i];
-          p = score_chunk(q16, a.K + ((int64_t)jh * a.n_cap + pos) * kD, k8);
+          p = score_chunk(q16, a.K + (jkv * a.n_cap + pos) * kD, k8);
         }
         const double sc = r1_combine8(p) * kRsqrtD;
         // c* = max(c_R, these exact scores)
@@ -1157,7 +1164,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     if (__ballot((liveA | liveB) != 0)) {
       if (mine && flag[lane]) {
         myE = perturbation(prefix, mypos);
-        if (a.e_out) a.e_out[(int64_t)jh * a.npool + mypos] = myE;
+        if (a.e_out) a.e_out[(int64_t)jh * jnpool + mypos] = myE;
       }
     }
     wave_sync();
@@ -1220,7 +1227,7 @@ int64_t scan_stream_wgs(int64_t H_kv, int64_t nb_pool) {
 // With events given, they take the kernel's own start and end times from its dispatch (no
 // separate marker packets around it).
 hipError_t launch_scan(const ScanArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
-  const unsigned wgs = (unsigned)(a.nstream + (int64_t)a.H_kv * a.G);
+  const unsigned wgs = (unsigned)(a.nstream + (int64_t)a.U * a.G);
   switch (a.G) {
     case 1: hipExtLaunchKernelGGL(scan_kernel<1>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
     case 2: hipExtLaunchKernelGGL(scan_kernel<2>, dim3(wgs), dim3(256), 0, st, ev0, ev1, 0, a); break;
@@ -1235,7 +1242,7 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t st, hipEvent_t ev0 = nullp
 
 hipError_t launch_refine(const ScanArgs &a, hipStream_t st) {
   const int64_t wph = (a.nb_pool + kBlocksPerWave - 1) / kBlocksPerWave;
-  const unsigned wgs = (unsigned)(((int64_t)a.H_kv * wph + 3) / 4);
+  const unsigned wgs = (unsigned)(((int64_t)a.U * wph + 3) / 4);
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(refine_kernel, dim3(wgs), dim3(256), 0, st, a);
   return hipGetLastError();

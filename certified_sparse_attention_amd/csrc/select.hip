@@ -16,8 +16,9 @@ namespace csa {
 
 struct SelectArgs {
   const uint16_t *K, *V;
-  int64_t n_cap, npool, npool_cap, ntiles;
-  int G, J;
+  int64_t n_cap, npool_cap, ntiles;   // ntiles: the longest item's tiles (row stride)
+  int G, J, W;
+  Batch b;
   const float *qf;
   const double *lt;
   const uint64_t *prefix;
@@ -49,6 +50,8 @@ constexpr int kDenseTile = 512;   // live keys above which a tile's candidates a
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
+  const int64_t npool = unit_npool(a.b, hq / a.G, a.W);
+  if (tile * kBucketTile >= npool) return;   // past this unit's pool
   __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2];
   __shared__ double2 ltp[kMaxJ + 2];
   // this lane's bitmap word (tile word `lane`, read at a clamped position and masked
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const double clo = dec_max(clo_enc);
   const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
   // the word gives the dead count and the bits the lanes read below through shuffles
-  const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p_tile - 32 * lane));
+  const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p_tile - 32 * lane));
   const uint32_t word = rawword & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
   const int dead = valid - __popc(word);
   if (dead) atomicAdd(&hist[a.J + 1], dead);
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     const double *pb = a.pbuf + (int64_t)hq * a.npool_cap + p_tile;
     const double *ubp = a.ubuf + (int64_t)hq * a.npool_cap + p_tile;
     int8_t *lub = a.lub + (int64_t)hq * a.npool_cap + p_tile;
-    const int64_t left = a.npool - p_tile;
+    const int64_t left = npool - p_tile;
     uint32_t on = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
@@ -153,6 +156,9 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
   const int J = a.J, J2 = J + 2;
+  const int64_t npool = unit_npool(a.b, hq / a.G, a.W);
+  const int64_t ntiles = (npool + kBucketTile - 1) / kBucketTile;   // this unit's tiles
+  if (tile > 0 && tile >= ntiles) return;   // (tile 0 writes the head's totals, also of an empty pool)
   const int *th0 = a.tilehist + (int64_t)hq * a.ntiles * J2;
   // this lane's bitmap word (tile word `lane`) and its 32 levels are read together with
   // the histograms (unconditional reads at clamped positions; words past the pool are
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const uint4 lv0 = lw[0], lv1 = lw[1];
   // cumulative level histogram of the head and of the tiles before this one (lane = level)
   int cum = 0, pre = 0;
-  if (lane < J2) sum_tiles(th0, a.ntiles, J2, lane, tile, &cum, &pre);
+  if (lane < J2) sum_tiles(th0, ntiles, J2, lane, tile, &cum, &pre);
   // the levels that fit form a prefix 0..js (cumulative counts only grow); js = -1 when
   // level 0 alone exceeds the budget, and the first pass then has no candidates
   const unsigned long long fit = __ballot(lane <= J && cum <= a.budget);
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
     // C_max keys per bucket level
     if (lane < J2) {
       int cm = 0, unused = 0;
-      sum_tiles(a.tilecm + (int64_t)hq * a.ntiles * J2, a.ntiles, J2, lane, 0, &cm, &unused);
+      sum_tiles(a.tilecm + (int64_t)hq * a.ntiles * J2, ntiles, J2, lane, 0, &cm, &unused);
       a.cmhist[(int64_t)hq * J2 + lane] = cm;
     }
   }
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int b1 = (js >= 0) ? pre1v : 0;
   const int b2 = pre2 - b1;
   const int b3 = preJ - pre2;
-  const int valid = (int)max<int64_t>(0, min<int64_t>(32, a.npool - p0));
+  const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p0));
   const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
   int *dst = a.candpos + (int64_t)hq * a.npool_cap;
   int tile_live = __popc(bits);

@@ -209,6 +209,59 @@ int csa_certified_decode_attention(const csa_shape *shape, const csa_params *par
                                    const csa_trace *trace, csa_stream_t stream);
 
 /*
+ * One item of a batched certified call: a request, or one layer of a request.  Each item
+ * has its own context length, target and fresh perturbations ([S] Results > CPU Speed:
+ * new perturbations at every decode step; the hash inputs of [S] Algorithm Components
+ * item 1 are per item).
+ */
+typedef struct {
+  int64_t n;       /* cached tokens of the item, 1 <= n <= n_cap */
+  int32_t slot;    /* cache slot of the item's K, V and packed arrays, 0 <= slot < num_slots */
+  int32_t layer;   /* hash input */
+  double eps;      /* certificate target of the item, > 0 */
+  uint64_t seed;   /* hash inputs */
+  uint64_t step;
+} csa_item;
+
+#define CSA_MAX_ITEMS 64
+
+/*
+ * Workspace of a batched call of up to num_items items of at most n_max tokens each
+ * (0 on invalid arguments).
+ */
+size_t csa_workspace_bytes_batch(const csa_shape *shape, const csa_params *params, int32_t num_items,
+                                 int64_t n_max);
+
+/*
+ * The certified decode step of num_items items in one set of launches (every kernel of
+ * the path runs once for the whole batch).  The cache holds num_slots slots of
+ * num_kv_heads heads each: item b's KV head h is cache head slot_b * num_kv_heads + h.
+ *   shape    per slot: num_kv_heads, group_size, head_dim 128, n_cap
+ *   params   delta, r, J, window, measure, cand_budget, cand_budget2 shared by all items;
+ *            its eps, seed, step and layer are not used (each item carries its own)
+ *   items    host array of num_items entries, 1 <= num_items <= CSA_MAX_ITEMS
+ *   q        fp16 [num_items][H_q][128]
+ *   K, V     fp16 [num_slots][num_kv_heads][n_cap][128] (device)
+ *   packed   the packing of K, V as num_slots * num_kv_heads heads (csa_pack_kv_4bit with
+ *            num_kv_heads = num_slots * num_kv_heads); each item's blocks up to
+ *            ceil((n - window) / 32) must be packed
+ *   workspace at least csa_workspace_bytes_batch(shape, params, num_items, max n)
+ * Outputs per item and query head, laid out [num_items][H_q] (o_hat [num_items][H_q][128])
+ * with the meaning of csa_certified_decode_attention's.  Each item's outputs are those of
+ * a single call on that item up to the order of floating-point sums (sets, levels, stop
+ * levels and keys_read are the same).  Errors: CSA_ERR_INVALID_ARGUMENT for a bad item
+ * (n, slot, eps) or pointer, CSA_ERR_UNSUPPORTED beyond CSA_MAX_ITEMS, CSA_ERR_WORKSPACE
+ * for a short workspace; nothing is launched then.
+ */
+int csa_certified_decode_attention_batch(const csa_shape *shape, const csa_params *params,
+                                         int32_t num_slots, int32_t num_items, const csa_item *items,
+                                         const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                         const csa_packed *packed, void *workspace,
+                                         size_t workspace_bytes, float *o_hat, double *beta,
+                                         int32_t *stop_level, int64_t *keys_read,
+                                         csa_stream_t stream);
+
+/*
  * The same certified decode step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  Arguments and outputs are those of

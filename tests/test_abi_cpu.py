@@ -121,3 +121,37 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert lib.csa_stream_read(ctypes.c_void_p(0x1004), 1024, 4, fake, None, None, None) == -1   # misaligned
     assert lib.csa_stream_read(fake, 1024, 0, fake, None, None, None) == -1            # no workgroups
     assert lib.csa_stream_read(fake, 1024, 70000, fake, None, None, None) == -1        # too many
+
+
+def test_workspace_bytes_batch_validates(lib):
+    one = lib.csa_workspace_bytes(ctypes.byref(_shape()), ctypes.byref(_params()), 4096)
+    b1 = lib.csa_workspace_bytes_batch(ctypes.byref(_shape()), ctypes.byref(_params()), 1, 4096)
+    b16 = lib.csa_workspace_bytes_batch(ctypes.byref(_shape()), ctypes.byref(_params()), 16, 4096)
+    assert b1 == one and b16 > 8 * one
+    assert lib.csa_workspace_bytes_batch(ctypes.byref(_shape()), ctypes.byref(_params()), 0, 4096) == 0
+    assert lib.csa_workspace_bytes_batch(ctypes.byref(_shape()), ctypes.byref(_params()), 65, 4096) == 0
+    assert lib.csa_workspace_bytes_batch(ctypes.byref(_shape()), ctypes.byref(_params()), 64, 4096) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_items=0), dict(num_items=65), dict(num_slots=0), dict(slot=2), dict(slot=-1), dict(n=0),
+    dict(n=5000), dict(eps=0.0), dict(eps=float("nan")), dict(null_items=True), dict(null_q=True),
+    dict(ws_small=True), dict(J=61),
+])
+def test_batch_call_rejects_bad_arguments(lib, bad):
+    from certified_sparse_attention_amd import _lib
+    sh = _shape(n_cap=4096)
+    pr = _params(**{k: v for k, v in bad.items() if k in ("J",)})
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+    pk = _lib.Packed(*([fake] * 9))
+    nitems = bad.get("num_items", 3)
+    arr = (_lib.Item * max(nitems, 1))()
+    for i in range(max(nitems, 1)):
+        arr[i] = _lib.Item(1000 + i, i % 2, 0, 0.05, 1, 0)
+    arr[0] = _lib.Item(bad.get("n", 1000), bad.get("slot", 0), 0, bad.get("eps", 0.05), 1, 0)
+    rc = lib.csa_certified_decode_attention_batch(
+        ctypes.byref(sh), ctypes.byref(pr), bad.get("num_slots", 2), nitems, None if bad.get("null_items") else arr,
+        None if bad.get("null_q") else fake, fake, fake, ctypes.byref(pk), fake,
+        16 if bad.get("ws_small") else 1 << 40, fake, fake, fake, fake, None)
+    assert rc in (-1, -2, -3), rc
+    assert len(lib.csa_last_error()) > 0
