@@ -70,7 +70,7 @@ struct CertArgs {
 // Query head hq: its unit's cached length, cache head and item.
 __device__ inline int64_t head_n(const CertArgs &a, int hq) { return unit_n(a.b, hq / a.G); }
 __device__ inline int64_t head_kv(const CertArgs &a, int hq) { return unit_kv(a.b, hq / a.G); }
-__device__ inline int head_item(const CertArgs &a, int hq) { return (hq / a.G) / a.b.H_kv; }
+__device__ inline int head_item(const CertArgs &a, int hq) { return unit_item(a.b, hq / a.G); }
 
 constexpr int kFusedMax = 2048;   // heads with more candidates use the segmented accumulation
 constexpr int kStage = 64;        // candidates staged in LDS at a time

@@ -374,12 +374,16 @@ struct Batch {
   int64_t n[kMaxItems];
   int32_t slot[kMaxItems];
 };
-__host__ __device__ inline int64_t unit_n(const Batch &b, int u) { return b.n[u / b.H_kv]; }
+// (a single item reads its entries at fixed offsets: no division and no load that waits
+// for one)
+__host__ __device__ inline int unit_item(const Batch &b, int u) { return b.nitems == 1 ? 0 : u / b.H_kv; }
+__host__ __device__ inline int64_t unit_n(const Batch &b, int u) { return b.nitems == 1 ? b.n[0] : b.n[u / b.H_kv]; }
 __host__ __device__ inline int64_t unit_npool(const Batch &b, int u, int W) {
-  const int64_t n = b.n[u / b.H_kv];
+  const int64_t n = unit_n(b, u);
   return n > W ? n - W : 0;
 }
 __host__ __device__ inline int64_t unit_kv(const Batch &b, int u) {
+  if (b.nitems == 1) return (int64_t)b.slot[0] * b.H_kv + u;
   return (int64_t)b.slot[u / b.H_kv] * b.H_kv + u % b.H_kv;
 }
 

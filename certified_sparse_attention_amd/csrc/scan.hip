@@ -64,7 +64,7 @@ __global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
   }
   if (g == 0 && t == 0) {
     // the hash takes the item's seed, step and layer and the head within the layer
-    const int it = h / a.H_kv;
+    const int it = (a.U == a.H_kv) ? 0 : h / a.H_kv;
     a.prefix[h] = hash_prefix(a.seed[it], a.step[it], (uint64_t)(int64_t)a.layer[it], (uint64_t)(h % a.H_kv));
   }
   const double qv = h2d(a.q[(int64_t)hq * kD + t]);
@@ -879,9 +879,11 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   // queries, the per-query constants (lane g < G), the hash prefix and the scan
   // wavefronts' LB bounds (the first 128 wavefronts' of every query at once; a longer
   // pool adds a loop)
+  // (block maxima at clamped positions, used below only for the slot's own blocks)
+  const int64_t bcol = min<int64_t>(blk0 + n16, a.nbw - 1);
   float2 mxA = make_float2(0.0f, 0.0f), mxB = make_float2(0.0f, 0.0f);
-  if (n16 < nblk && hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + blk0 + n16];
-  if (n16 < nblk && hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + blk0 + n16];
+  if (hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + bcol];
+  if (hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + bcol];
   const double ltJ = a.lt[a.J];
   float qv[kMaxG][2];
 #pragma unroll
@@ -905,9 +907,14 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   for (int g = 0; g < kMaxG; ++g)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int64_t k = lane + 64 * i;
-      lbs[g][i] = (g < G && k < swph) ? a.lbpart[(int64_t)(hq0 + g) * a.wstride + k] : -__builtin_huge_valf();
+      const int64_t k = lane + 64 * i;   // (read within the row; entries past swph are masked below)
+      lbs[g][i] = (g < G && k < a.wstride) ? a.lbpart[(int64_t)(hq0 + g) * a.wstride + k] : -__builtin_huge_valf();
     }
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i >= swph) lbs[g][i] = -__builtin_huge_valf();
 #pragma unroll
   for (int g = 0; g < kMaxG; ++g) {
     me.q[g][2 * lane] = qv[g][0];

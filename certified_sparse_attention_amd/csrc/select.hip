@@ -50,8 +50,9 @@ constexpr int kDenseTile = 512;   // live keys above which a tile's candidates a
 __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const int hq = blockIdx.x, lane = threadIdx.x;
   const int64_t tile = blockIdx.y;
+  // (tiles past this unit's pool find no valid keys: their rows are written as zeros and
+  // never read)
   const int64_t npool = unit_npool(a.b, hq / a.G, a.W);
-  if (tile * kBucketTile >= npool) return;   // past this unit's pool
   __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2];
   __shared__ double2 ltp[kMaxJ + 2];
   // this lane's bitmap word (tile word `lane`, read at a clamped position and masked
