@@ -8,11 +8,12 @@ The timed loop rotates over the 32 layers of a Llama-3.1-8B-shaped decode step
 that no layer's data is still in the 256 MB Infinity Cache when it is read again.
 
 Beside the headline line the same JSON object carries, per workload (the 128K layer,
-the 32K layer, the 16-request ragged batch, the appending GQA-7 layer over 256
-steps): the median and p10/p90 over 100 timed iterations of the certified call, of
-its 4-bit scan kernel and of the library's dense decode; keys read and stop levels;
-and the CPU legs (the oracle on one core and on a process per KV head, a CPU fp64
-dense attention, and the appending layer's failure rate against the oracle's exact
+all 32 layers of the step in one batched call, the 32K layer, the 16-request ragged
+batch as one batched call and as 16 single calls, the appending GQA-7 layer over 256
+steps): the median and p10/p90 over timed iterations of the certified call, of its
+4-bit scan kernel and of the library's dense decode; keys read and stop levels; and the
+CPU legs (the oracle on one core and on a process per KV head, a CPU fp64 dense
+attention, and the appending layer's failure rate against the oracle's exact
 attention).
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
@@ -231,21 +232,25 @@ def leg_32k(csa, torch, timer, dev, iters, warm):
 
 def leg_ragged(csa, torch, timer, dev, iters, warm):
     """The 16-request ragged batch (n from 16K to 128K, eps per request, odd requests
-    near-flat): a step is one certified call per request, issued back to back."""
+    near-flat), its caches in one [16][H_kv][131072][128] tensor (request b = slot b): a
+    step as one batched call, and as 16 single calls issued back to back."""
     import synth
     with ThreadPoolExecutor(max_workers=8) as ex:
         ws_ = list(ex.map(synth.config4_request, range(16)))
-    items = []
-    order = sorted(range(16), key=lambda b: -ws_[b].n)         # the longest first lends its workspaces
+    B = 16
+    K_all = torch.zeros((B, H_KV, N_CTX, D), dtype=torch.float16, device=dev)
+    V_all = torch.zeros_like(K_all)
+    packed_all = csa.PackedKV.allocate(B * H_KV, N_CTX, dev)
     by_b = {}
+    order = sorted(range(B), key=lambda b: -ws_[b].n)         # the longest first lends its workspaces
     for b in order:
         w = ws_[b]
-        cap = -(-w.n_cap // 32) * 32
-        if cap != w.n_cap:
-            pad = ((0, 0), (0, cap - w.n_cap), (0, 0))
-            w.K, w.V = np.pad(w.K, pad), np.pad(w.V, pad)
-        by_b[b] = prepare_item(csa, torch, w, dev, share=by_b[order[0]] if by_b else None)
-    items = [by_b[b] for b in range(16)]
+        K_all[b, :, :w.n_cap].copy_(torch.from_numpy(w.K))
+        V_all[b, :, :w.n_cap].copy_(torch.from_numpy(w.V))
+        pk = csa.pack_kv_4bit(K_all[b], V_all[b], packed_all.slot(B, b))
+        by_b[b] = prepare_item(csa, torch, w, dev, K_all[b], V_all[b], pk,
+                               share=by_b[order[0]] if by_b else None)
+    items = [by_b[b] for b in range(B)]
     torch.cuda.synchronize()
     per_req = certified_leg(csa, torch, timer, items, 16 * max(1, iters // 16) * 1, warm)
 
@@ -261,18 +266,81 @@ def leg_ragged(csa, torch, timer, dev, iters, warm):
     bt = timer.calls(batch, iters)
     dbt = timer.calls(dbatch, iters)
     flat = [bool(w.extra["flat"]) for w in ws_]
-    stops = [items[b]["out"][2].cpu().numpy() for b in range(16)]
-    keys = [items[b]["out"][3].cpu().numpy() for b in range(16)]
+    stops = [items[b]["out"][2].cpu().numpy() for b in range(B)]
+    keys = [items[b]["out"][3].cpu().numpy() for b in range(B)]
+    # the same step as one batched call
+    qb = torch.stack([it["q"] for it in items])
+    bitems = [dict(n=w.n, slot=b, eps=w.eps, seed=w.seed, step=0, layer=w.layer) for b, w in enumerate(ws_)]
+    nbytes = csa.workspace_bytes_batch(K_all, GQA, B, N_CTX, 48, WINDOW)
+    bws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    bout = (torch.empty((B, H_KV * GQA, D), dtype=torch.float32, device=dev),
+            torch.empty((B, H_KV * GQA), dtype=torch.float64, device=dev),
+            torch.empty((B, H_KV * GQA), dtype=torch.int32, device=dev),
+            torch.empty((B, H_KV * GQA), dtype=torch.int64, device=dev))
+
+    def one_call(i, _):
+        for it in bitems:
+            it["step"] = i
+        csa.certified_decode_attention_batch(qb, K_all, V_all, packed_all, bitems, delta=0.01, r=2, J=48,
+                                             window=WINDOW, workspace=bws, out=bout)
+    for i in range(warm):
+        one_call(i, None)
+    torch.cuda.synchronize()
+    ot = timer.calls(one_call, iters)
+    bstops = bout[2].cpu().numpy()
     return {"workload": "16 requests x (8 KV heads x GQA 4), n ~ U{16384..131072}, eps in {0.02, 0.05, 0.1}, "
                         "odd requests near-flat (query x 0.1), delta=0.01, r=2, J=48",
-            "batch_ms": pct(bt), "batch_steps_per_s": 1e3 / float(np.median(bt)), "dense_batch_ms": pct(dbt),
+            "batched_call_ms": pct(ot), "batched_call_steps_per_s": 1e3 / float(np.median(ot)),
+            "single_calls_ms": pct(bt), "single_calls_steps_per_s": 1e3 / float(np.median(bt)),
+            "dense_batch_ms": pct(dbt),
             "n": [int(w.n) for w in ws_], "eps": [float(w.eps) for w in ws_],
             "keys_read_median": {"peaked": float(np.median(np.concatenate([k for k, f in zip(keys, flat) if not f]))),
                                  "near_flat": float(np.median(np.concatenate([k for k, f in zip(keys, flat) if f])))},
             "stop_level_median": {"peaked": float(np.median(np.concatenate([s for s, f in zip(stops, flat) if not f]))),
                                   "near_flat": float(np.median(np.concatenate([s for s, f in zip(stops, flat) if f])))},
             "fallback_heads": int(sum(int((s > 48).sum()) for s in stops)),
+            "batched_fallback_heads": int((bstops > 48).sum()),
             "per_request_call_ms": per_req["call_ms"], "per_request_scan_kernel_ms": per_req["scan_kernel_ms"]}
+
+
+def leg_full_step_batched(csa, torch, dev, layers, K_all, V_all, packed_all, w0, iters, warm):
+    """All L layers' attention calls of one decode step in one batched call (item l = layer
+    l, cache slot l, fresh perturbations per layer and step).  In a model the layers run
+    one after the other; the batched call is the form for independent work (requests of a
+    batch, or a layer's calls gathered by a scheduler)."""
+    L = len(layers)
+    q = torch.stack([ly["q"] for ly in layers])
+    items = [dict(n=N_CTX, slot=l, eps=w0.eps, seed=w0.seed, step=0, layer=ly["layer"]) for l, ly in enumerate(layers)]
+    nbytes = csa.workspace_bytes_batch(K_all, GQA, L, N_CTX, w0.J, WINDOW)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    H_q = H_KV * GQA
+    out = (torch.empty((L, H_q, D), dtype=torch.float32, device=dev), torch.empty((L, H_q), dtype=torch.float64, device=dev),
+           torch.empty((L, H_q), dtype=torch.int32, device=dev), torch.empty((L, H_q), dtype=torch.int64, device=dev))
+
+    def call(i, _=None):
+        for it in items:
+            it["step"] = i
+        csa.certified_decode_attention_batch(q, K_all, V_all, packed_all, items, delta=w0.delta, r=w0.r, J=w0.J,
+                                             window=WINDOW, workspace=ws, out=out)
+    for i in range(warm):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        evs[i][0].record()
+        call(warm + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    stops = out[2].cpu().numpy()
+    keys = out[3].cpu().numpy()
+    med = float(np.median(ms))
+    return {"workload": f"{L} layers x ({H_KV} KV heads x GQA {GQA}), n={N_CTX}, one batched call per step",
+            "call_ms": pct(ms), "full_steps_per_s": 1e3 / med, "layer_calls_per_s": L * 1e3 / med,
+            "scan_gbs_whole_call": SCAN_BYTES_PER_TOKEN * (N_CTX - WINDOW) * H_KV * L / (med * 1e-3) / 1e9,
+            "workspace_bytes": nbytes,
+            "keys_read_median": float(np.median(keys)), "stop_level_median": float(np.median(stops)),
+            "fallback_heads": int((stops > w0.J).sum())}
 
 
 def leg_appending(csa, torch, dev, steps=256):
@@ -422,13 +490,20 @@ def main():
     t_gen = time.perf_counter()
     layers = []
     w0 = None
+    # the step's caches in one tensor [L][H_kv][n][128] (layer l = cache slot l), packed as
+    # L * H_kv heads; single calls take a layer's views
+    K_all = torch.empty((L, H_KV, N_CTX, D), dtype=torch.float16, device=dev)
+    V_all = torch.empty_like(K_all)
+    packed_all = csa.PackedKV.allocate(L * H_KV, N_CTX, dev)
     for w in gen_layers(L):
         if w0 is None:
             w0 = w
-        K = torch.from_numpy(w.K).to(dev)
-        V = torch.from_numpy(w.V).to(dev)
+        l = w.layer
+        K_all[l].copy_(torch.from_numpy(w.K))
+        V_all[l].copy_(torch.from_numpy(w.V))
+        K, V = K_all[l], V_all[l]
         q = torch.from_numpy(w.q).to(dev)
-        packed = csa.pack_kv_4bit(K, V)
+        packed = csa.pack_kv_4bit(K, V, packed_all.slot(L, l))
         layers.append({"q": q, "K": K, "V": V, "packed": packed, "layer": w.layer})
         if w is not w0:
             del w
@@ -561,6 +636,10 @@ def main():
     }
     appending = None
     if not args.headline_only:
+        log("full step of all layers in one batched call")
+        result["full_step_batched"] = leg_full_step_batched(csa, torch, dev, layers, K_all, V_all, packed_all, w0,
+                                                            max(10, iters // 5), 3)
+        torch.cuda.empty_cache()
         for name, fn in (("config_32k_layer", lambda: leg_32k(csa, torch, timer, dev, iters, args.warmup)),
                          ("config_ragged_batch", lambda: leg_ragged(csa, torch, timer, dev, iters, args.warmup))):
             log(f"{name} leg")

@@ -66,6 +66,13 @@ class PackedKV:
                              (self.codes, self.kscale, self.zq, self.bmeta, self.kerr, self.vnorm,
                               self.codes8, self.scale8, self.kerr8)))
 
+    def slot(self, num_slots: int, s: int) -> "PackedKV":
+        """Views of cache slot s of a packing over num_slots slots of equal head count."""
+        H = self.kerr.shape[0] // num_slots
+        return PackedKV(*(t[s * H:(s + 1) * H] for t in
+                          (self.codes, self.kscale, self.zq, self.bmeta, self.kerr, self.vnorm,
+                           self.codes8, self.scale8, self.kerr8)))
+
     @property
     def bytes_per_token(self) -> float:
         """Bytes per token of the 4-bit scan's arrays (every key is read once per call)."""

@@ -87,9 +87,7 @@ def _check_against_single(res, dev, q, items, G, J):
     S, H_kv, n_cap, _ = Kd.shape
     for b, it in enumerate(items):
         s = it["slot"]
-        sub = csa.PackedKV(*(getattr(packed, f).view(S, H_kv, *getattr(packed, f).shape[1:])[s]
-                             for f in ("codes", "kscale", "zq", "bmeta", "kerr", "vnorm", "codes8", "scale8",
-                                       "kerr8")))
+        sub = packed.slot(S, s)
         one = csa.certified_decode_attention(_to(q[b]), Kd[s], Vd[s], sub, it["n"], eps=it["eps"], delta=0.01, r=2,
                                              J=J, window=64, seed=it["seed"], step=it["step"], layer=it["layer"])
         torch.cuda.synchronize()

@@ -3,8 +3,8 @@
 * the 128K Llama-shaped layer the bench times (8 KV heads x GQA 4), layers 0 and 31,
   every query head;
 * all 16 requests of the ragged batch (n from 16K to 128K, per-request epsilon, odd
-  requests near-flat), every query head; the oracle side of each request runs in CPU
-  worker processes while the GPU side runs;
+  requests near-flat), every query head, as 16 single calls and as one batched call; the
+  oracle side of each request runs in CPU worker processes while the GPU side runs;
 * the appending Qwen-shaped layer (4 KV heads x GQA 7, n = 131072 + t) with fresh
   perturbations each step, packing each block as an append completes it: parity at
   steps 0, 1, 33 and 255, and over all 256 steps the rate of certified heads whose
@@ -25,7 +25,7 @@ import torch
 
 import oracle
 import synth
-from test_gpu_parity import _compare_decode, _kw, _to, pad_cache
+from test_gpu_parity import DEV, _compare_decode, _kw, _to, pad_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,35 @@ def test_ragged_request(b, ragged_refs):
     ref = ragged_refs[b].result()
     _compare_decode(w, None, out[:4], out[4], ref=ref, **kw)
     assert len(ref) == w.H_q
+
+
+def test_ragged_batch_in_one_call(ragged_refs):
+    """All 16 requests in one batched call (each its own cache slot, n, eps and seed),
+    every request's heads against the oracle."""
+    csa = _csa()
+    ws = [pad_cache(synth.config4_request(b)) for b in range(16)]
+    n_cap = max(w.n_cap for w in ws)
+    K = torch.zeros((16, 8, n_cap, 128), dtype=torch.float16, device=DEV)
+    V = torch.zeros_like(K)
+    for b, w in enumerate(ws):
+        K[b, :, :w.n_cap] = _to(w.K)
+        V[b, :, :w.n_cap] = _to(w.V)
+    q = _to(np.stack([w.q for w in ws]))
+    packed = csa.pack_kv_4bit(K.view(16 * 8, n_cap, 128), V.view(16 * 8, n_cap, 128))
+    items = [dict(n=w.n, slot=b, eps=w.eps, seed=w.seed, step=w.step, layer=w.layer) for b, w in enumerate(ws)]
+    _say(f"ragged batch: n = {[w.n for w in ws]}")
+    out = csa.certified_decode_attention_batch(q, K, V, packed, items, delta=0.01, r=2, J=48, window=64)
+    torch.cuda.synchronize()
+    o_hat, beta, stop, keys = (t.cpu().numpy() for t in out)
+    for b, w in enumerate(ws):
+        ref = ragged_refs[b].result()
+        for hq, r in enumerate(ref):
+            assert int(stop[b, hq]) == r["stop_level"], (b, hq)
+            assert int(keys[b, hq]) == r["keys_read"], (b, hq)
+            assert np.linalg.norm(o_hat[b, hq].astype(np.float64) - r["o_hat"]) <= 1e-3 * r["dense"]["M"], (b, hq)
+            if r["stop_level"] <= 48:
+                assert abs(beta[b, hq] - r["beta"]) <= 1e-4 * abs(r["beta"]), (b, hq)
+    del K, V, packed
 
 
 # ---------------------------------------------------------------- the appending layer
