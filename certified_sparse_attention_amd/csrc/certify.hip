@@ -5,8 +5,9 @@
 //   Methodology > Algorithm Components item 2: D^ = D_R + D_B + tau k,
 //     N^ = N_R + N_B + tau sum_{S & A} v (heavy keys B with w >= tau are always in
 //     the sample, light keys A enter with probability w / tau);
-//   item 3: on the grid tau_j, a Chernoff interval for the Poisson-binomial sample
-//     count, a Hilbert-space Bernstein bound on Z_c = sum_A (tau X - w)(v - c),
+//   item 3: on the grid tau_j, a Chernoff interval for the number of light samples
+//     (independent Bernoulli draws), a Bernstein-type bound for Hilbert-space vectors
+//     on Z_c = sum_A (tau X - w)(v - c),
 //     beta = (zeta + |o^ - c| dD) / (D^ - dD), stop at the first certified level;
 //   Theorem 4: validity per head and per measure over all levels (union bound:
 //     each level spends delta/(J+1), split over its one-sided tails);

@@ -2,9 +2,9 @@
 //
 // "Certified Sparse Attention via Perturbed Retrieval": summary page, Methodology >
 // Algorithm Components items 1 (window / pool split, Exp(1) perturbations from a
-// 53-bit hash) and 4 (4-bit keys give deterministic score bounds; candidates are
-// bucketed by their earliest possible inclusion level); authors' abstract (the scan
-// is shared across a GQA group and reads every key once).
+// 53-bit hash) and 4 (4-bit keys bound every score with certainty; candidates are
+// grouped by the first level at which they could be sampled); authors' abstract (the
+// scan is shared across a GQA group and reads every key once).
 //
 // Bound per pool key i and query g (all integers exact; fp64 in this order):
 //   shat  = (base_gb + alpha_b I_gi) * RSQRT_D

@@ -2,8 +2,8 @@
 //
 // "Certified Sparse Attention via Perturbed Retrieval", summary page, Methodology >
 // Algorithm Components item 4: the exact maximum is computed over a small part of
-// the pool; candidates are bucketed by their earliest possible inclusion level and
-// only keys that may enter the sample get exact 16-bit reads.  Item 1: the sample
+// the pool; candidates are grouped by the first level at which they could be sampled,
+// and 16-bit keys are read only for candidates.  Item 1: the sample
 // at threshold tau is {i in P : s_i - c* + E_i >= log tau}.
 //
 //   c_lo  = max(c_R, max_P LB);  C_max = {i in P : UB_i >= c_lo}

@@ -111,7 +111,7 @@ typedef struct {
   int32_t J;       /* deepest level, 0..60 */
   int32_t window;  /* recent tokens always read exactly ([S] item 1; 64 on the pages), 32..1024 */
   int32_t measure; /* enum csa_measure */
-  uint64_t seed;   /* perturbation hash inputs ([S] item 1: 53-bit uniform hash) */
+  uint64_t seed;   /* perturbation hash inputs ([S] item 1: u from 53 bits of a hash) */
   uint64_t step;   /* decode step: fresh perturbations per step ([A]) */
   int32_t layer;
   int32_t cand_budget; /* candidates rescored before the first certificate pass (0: 32;

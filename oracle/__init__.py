@@ -23,8 +23,11 @@ limit, the error identity behind beta, the KL roots (library root finder),
 certificate coverage per tail and per measure at a loose level, each measure's
 beta against the worst case its event allows (brute force), the per-level budget
 against the tails each measure's bound uses (union bound), Pinelis's tail at the
-relaxed root, closed forms when no light key is sampled, and the empirical
-failure rate per measure at delta (Theorem 4) with planted mistakes that fail.
+relaxed root, closed forms when no light key is sampled, the empirical
+failure rate per measure at delta (Theorem 4) with planted mistakes that fail, and
+the 8-bit tier (code rounding and the residual norm by exact rationals, bound
+validity and the absence of false negatives by brute force over every key, the
+relations between the sample, the exact reads and the 8-bit reads).
 Parity unpinned against the pages: the specific constants of the certificate
 completion (the per-level tail split, the centre, the G and Q tails) and the
 hash -- the pages print no numbers for them; they are pinned by the rigour checks

@@ -1,8 +1,9 @@
 """Per-level certificates (test infrastructure only).
 
 [S] Methodology > Algorithm Components item 3 fixes the shape: on the grid
-tau_j = 2^(-j/r) with a per-level failure budget, a Chernoff interval for the
-Poisson-binomial sample count (denominator), a Hilbert-space Bernstein bound on
+tau_j = 2^(-j/r) with a per-level failure budget, a Chernoff interval for the number
+of light samples, a sum of independent Bernoulli draws (denominator), a Bernstein-type
+concentration bound for vectors in a Hilbert space on
 Z_c = sum_{i in A} (tau X_i - w_i)(v_i - c) (numerator), the output bound
 beta = (zeta + |o^ - c| dD) / (D^ - dD), and a stop at the first certified level.
 [S] Theorem 4: validity per head and per error measure, uniformly over levels.

@@ -9,11 +9,11 @@ Follows the method's steps in the pages' order:
 3. Exact maximum over a small set: c_lo = max(c_R, max_P LB); C_max = {UB >= c_lo};
    c* = max(c_R, max over C_max of s) ([S] item 4, "exact maximum").
 4. Perturbations E_i (``perturb``), and each pool key's earliest possible level
-   l^ub = first((UB + E) - c*) ("bucketed by earliest possible inclusion level",
-   [S] item 4).  Reading: buckets are taken relative to the exact c*.
+   l^ub = first((UB + E) - c*) ([S] item 4: candidates are grouped by the first level
+   at which they could be sampled).  Reading: buckets are taken relative to the exact c*.
 5. The 8-bit refinement of every candidate (l^ub <= J): UB8 from the 8-bit copy
    (``bounds.refine_bounds8``) and the refined level l8 = first((min(UB, UB8) + E) - c*)
-   ([S] item 4: 8-bit refinement, exact reads only for keys that may enter the sample).
+   ([S] item 4: an 8-bit tier narrows the candidates before any 16-bit key is read).
    Exact 16-bit reads only for candidates with l8 <= J: s_i, the heavy level
    h = first(s - c*) and the entry level l = first((s + E) - c*) (so l <= h, and
    l^ub <= l8 <= l because min(UB, UB8) >= s); the others have h = l = J + 1.

@@ -1,7 +1,8 @@
 """4-bit per-block, per-channel key quantization with error-bound metadata.
 
-[S] Methodology > Algorithm Components item 4 fixes only "4-bit per-block-per-
-channel quantization (as in KIVI)" used to give deterministic score upper bounds.
+[S] Methodology > Algorithm Components item 4 fixes only that keys are quantized to 4
+bits per block and per channel, in the manner of the KIVI key quantizer, and that the
+quantized keys give score bounds that hold with certainty.
 Reading taken (test infrastructure only; the HIP pack follows the same rules):
 
 * blocks of 32 consecutive tokens, aligned at multiples of 32; only complete

@@ -1,7 +1,7 @@
-"""Exp(1) perturbations from a 53-bit uniform hash (test infrastructure only).
+"""Exp(1) perturbations from hashed uniforms (test infrastructure only).
 
-[S] Methodology > Algorithm Components item 1: each pool key gets E_i = -ln u_i with
-u_i from a 53-bit uniform hash; [A] and [S] Results > CPU Speed: fresh
+[S] Methodology > Algorithm Components item 1: each pool key gets E_i = -ln u_i, the
+uniform u_i taken from 53 bits of a hash; [A] and [S] Results > CPU Speed: fresh
 perturbations at every decoding step.  The hash itself is not given.  Reading
 taken: a chain of the SplitMix64 generator's output function (Steele, Lea and
 Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014, with the

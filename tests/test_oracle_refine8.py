@@ -1,6 +1,6 @@
 """Pins of the 8-bit refinement tier (summary page "Certified Sparse Attention via
-Perturbed Retrieval", Methodology > Algorithm Components item 4: 8-bit refinement, and
-exact 16-bit reads only for keys that may enter the sample).
+Perturbed Retrieval", Methodology > Algorithm Components item 4: an 8-bit tier narrows
+the candidates before any exact 16-bit key is read).
 
 What fixes each expected value: exact rational arithmetic (the residual norm bound),
 the rounding property of the codes, brute-force exact scores of every pool key (bound
