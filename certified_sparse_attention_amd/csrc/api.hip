@@ -163,48 +163,31 @@ int check_packed(const csa_packed *p) {
   return CSA_OK;
 }
 
-// Prep + scan shared by the certified call and the bounds diagnostic.
-int run_prep_scan(const csa_shape *s, const csa_params *p, const Call &c, const uint16_t *q, const uint16_t *K,
+// The scan (whose window workgroups also store the per-call constants) and the
+// refinement, shared by the certified call and the bounds diagnostic.
+int run_scan(const csa_shape *s, const csa_params *p, const Call &c, const uint16_t *q, const uint16_t *K,
                   const uint16_t *V, const csa_packed *pk, void *ws, const csa::Plan &P, double *lb_out,
                   double *e_out, double *ub_diag, void *ev0, void *ev1, hipStream_t st, int diag = 0) {
-  csa::PrepArgs pa;
-  pa.q = q;
-  pa.U = P.H_kv;
-  pa.H_kv = s->num_kv_heads;
-  pa.G = P.G;
-  pa.J = P.J;
-  pa.r = p->r;
-  for (int i = 0; i < c.b.nitems; ++i) {
-    pa.seed[i] = c.seed[i];
-    pa.step[i] = c.step[i];
-    pa.layer[i] = c.layer[i];
-  }
-  pa.qf = at<float>(ws, P.qf);
-  pa.qconst = at<double>(ws, P.qconst);
-  pa.qA = at<int8_t>(ws, P.qA);
-  pa.lt = at<double>(ws, P.lt);
-  pa.tau = at<double>(ws, P.tau);
-  pa.prefix = at<uint64_t>(ws, P.prefix);
-  pa.sR = at<double>(ws, P.sR);
-  pa.clo = at<unsigned long long>(ws, P.clo);
-  pa.cstar = at<unsigned long long>(ws, P.cstar);
-  pa.hist = at<int>(ws, P.hist);
-  pa.ccount = at<int>(ws, P.ccount);
-  pa.flags = at<int>(ws, P.flags);
-  pa.bdone = at<int>(ws, P.bdone);
-  pa.exdone = at<int>(ws, P.exdone);
-  pa.exdone2 = at<int>(ws, P.exdone2);
-  hipError_t e = csa::launch_prep(pa, st);
-  if (e != hipSuccess) return hip_fail(e, "prep");
   const int64_t npool = c.npool_max;
   csa::ScanArgs sa;
   sa.K = K;
   sa.V = V;
   sa.b = c.b;
   sa.W = p->window;
-  sa.sR = pa.sR;
+  sa.q = q;
+  sa.r = p->r;
+  for (int i = 0; i < c.b.nitems; ++i) {
+    sa.seed[i] = c.seed[i];
+    sa.step[i] = c.step[i];
+    sa.layer[i] = c.layer[i];
+  }
+  sa.sR = at<double>(ws, P.sR);
   sa.win = at<double>(ws, P.win);
-  sa.cstar = pa.cstar;
+  sa.cstar = at<unsigned long long>(ws, P.cstar);
+  sa.tau = at<double>(ws, P.tau);
+  sa.ccount = at<int>(ws, P.ccount);
+  sa.exdone = at<int>(ws, P.exdone);
+  sa.exdone2 = at<int>(ws, P.exdone2);
   sa.codes = pk->codes;
   sa.kscale = pk->kscale;
   sa.zq = pk->zq;
@@ -220,13 +203,13 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const Call &c, const 
   sa.U = P.H_kv;
   sa.nbw = (P.npool_cap + csa::kBlk - 1) / csa::kBlk;
   sa.bmax = at<float2>(ws, P.bmax);
-  sa.qf = pa.qf;
-  sa.qconst = pa.qconst;
-  sa.qA = pa.qA;
-  sa.prefix = pa.prefix;
+  sa.qf = at<float>(ws, P.qf);
+  sa.qconst = at<double>(ws, P.qconst);
+  sa.qA = at<int8_t>(ws, P.qA);
+  sa.prefix = at<uint64_t>(ws, P.prefix);
   sa.pbuf = at<double>(ws, P.pbuf);
   sa.ubuf = at<double>(ws, P.ubuf);
-  sa.clo = pa.clo;
+  sa.clo = at<unsigned long long>(ws, P.clo);
   sa.lbpart = at<float>(ws, P.lbpart);
   sa.vpart = at<unsigned>(ws, P.vpart);
   sa.wstride = P.wstride;
@@ -234,10 +217,10 @@ int run_prep_scan(const csa_shape *s, const csa_params *p, const Call &c, const 
   sa.e_out = e_out;
   sa.nwords = P.npool_cap / 32 + 1;
   sa.J = P.J;
-  sa.lt = pa.lt;
+  sa.lt = at<double>(ws, P.lt);
   sa.live = at<uint32_t>(ws, P.live);
   sa.diag = diag;
-  e = csa::launch_scan(sa, st, (hipEvent_t)ev0, (hipEvent_t)ev1);
+  hipError_t e = csa::launch_scan(sa, st, (hipEvent_t)ev0, (hipEvent_t)ev1);
   if (e != hipSuccess) return hip_fail(e, "scan");
   if (npool <= 0) return CSA_OK;
   e = csa::launch_refine(sa, st);
@@ -424,7 +407,7 @@ int csa_scan_bounds(const csa_shape *shape, const csa_params *params, const uint
   const csa::Plan P = make_plan(shape, params, n);
   if (!workspace || workspace_bytes < P.total)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed", P.total);
-  return run_prep_scan(shape, params, single_call(shape, params, n), q, K, nullptr, packed, workspace, P, LB, E, UB,
+  return run_scan(shape, params, single_call(shape, params, n), q, K, nullptr, packed, workspace, P, LB, E, UB,
                        nullptr, nullptr, (hipStream_t)stream, 1);
 }
 
@@ -524,7 +507,7 @@ int certified_run(const csa_shape *shape, const csa_params *params, const Call &
   const bool all_exact = c.npool_max == 0;   // every item is its window alone
   void *ev0 = trace ? trace->ev_scan_begin : nullptr;
   void *ev1 = trace ? trace->ev_scan_end : nullptr;
-  rc = run_prep_scan(shape, params, c, q, K, V, packed, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
+  rc = run_scan(shape, params, c, q, K, V, packed, workspace, P, nullptr, nullptr, nullptr, ev0, ev1, st);
   if (rc) return rc;
   void *ws = workspace;
   const int64_t npool = c.npool_max;   // (a single call: its pool)

@@ -30,111 +30,6 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ------------------------------------------------------------------ prep
-
-struct PrepArgs {
-  const uint16_t *q;        // [units G][128], query head u G + g of unit u
-  int U, H_kv, G, J, r;     // units, KV heads per item
-  uint64_t seed[kMaxItems], step[kMaxItems];   // hash inputs per item
-  int32_t layer[kMaxItems];
-  float *qf;
-  double *qconst;
-  int8_t *qA;
-  double *lt, *tau;
-  uint64_t *prefix;
-  double *sR;
-  unsigned long long *clo, *cstar;
-  int *hist, *ccount, *flags;
-  int *bdone, *exdone, *exdone2;   // per-head completion counters, cleared here
-};
-
-// One workgroup of 128 threads per query head (of every unit); thread t owns channel t.
-__global__ __launch_bounds__(128) void prep_kernel(PrepArgs a) {
-  const int t = threadIdx.x, lane = t & 63;
-  const int hq = blockIdx.x, h = hq / a.G, g = hq % a.G;   // h: the unit
-  __shared__ double qd[kD];
-  __shared__ double part[16];
-  __shared__ double red[2];
-  __shared__ double smax[2];
-
-  if (hq == 0 && t <= a.J) {
-    double v = (-(double)t * kLn2) / (double)a.r;
-    a.lt[t] = v;
-    a.tau[t] = exp(v);
-  }
-  if (g == 0 && t == 0) {
-    // the hash takes the item's seed, step and layer and the head within the layer
-    const int it = (a.U == a.H_kv) ? 0 : h / a.H_kv;
-    a.prefix[h] = hash_prefix(a.seed[it], a.step[it], (uint64_t)(int64_t)a.layer[it], (uint64_t)(h % a.H_kv));
-  }
-  const double qv = h2d(a.q[(int64_t)hq * kD + t]);
-  a.qf[(int64_t)hq * kD + t] = (float)qv;
-  qd[t] = qv;
-  __syncthreads();
-  // R1 sums: threads 0..7 own the partial sums of q^2, threads 8..15 those of |q|
-  if (t < 16) {
-    const int p = t & 7;
-    double acc = (t < 8) ? qd[16 * p] * qd[16 * p] : fabs(qd[16 * p]);
-    for (int c = 1; c < 16; ++c) acc = acc + ((t < 8) ? qd[16 * p + c] * qd[16 * p + c] : fabs(qd[16 * p + c]));
-    part[t] = acc;
-  }
-  double qa = fabs(qv);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) qa = fmax(qa, __shfl_xor(qa, off, 64));
-  if (lane == 0) smax[t >> 6] = qa;
-  __syncthreads();
-  qa = fmax(smax[0], smax[1]);
-  double beta = 0.0;
-  if (qa > 0.0) {
-    int e;
-    (void)frexp(qa, &e);
-    beta = ldexp(1.0, e - 11);
-  }
-  if (t == 0) {
-    const double ss = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-    const double sa = ((part[8] + part[9]) + (part[10] + part[11])) + ((part[12] + part[13]) + (part[14] + part[15]));
-    const float qn = f32_sqrt_up(ss * (1.0 + kPadF));
-    double *qc = a.qconst + (int64_t)hq * kQc;
-    qc[QC_BETA] = beta;
-    qc[QC_QNP] = (double)qn * (1.0 + kPadF);
-    qc[QC_QABS] = sa;
-    qc[QC_QA] = qa;
-    qc[QC_QN] = (double)qn;
-  }
-  // operand rows of the offset-term MFMA: this query's two rows; query slot 0 clears
-  // the rows of the unused slots
-  {
-    const int qi = (beta > 0.0) ? (int)rint(qv / beta) : 0;   // exact scaling
-    const int q1 = (qi + 64) >> 7;
-    const int q0 = qi - 128 * q1;
-    const int kg = t >> 5, kh = (t >> 4) & 1, b = t & 15;
-    int8_t *A = a.qA + (int64_t)h * 2048;
-    A[kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b] = (int8_t)q1;
-    A[kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b] = (int8_t)q0;
-    if (g == 0)
-      for (int gs = a.G; gs < 8; ++gs) {
-        A[kh * 1024 + (op_row(gs, 0) + 16 * kg) * 16 + b] = 0;
-        A[kh * 1024 + (op_row(gs, 1) + 16 * kg) * 16 + b] = 0;
-      }
-  }
-  // c_lo and c* start empty: the window work and the scan raise them
-  if (t == 0) {
-    a.clo[hq] = enc_max(-__builtin_huge_val());
-    a.cstar[hq] = enc_max(-__builtin_huge_val());
-    a.ccount[hq] = 0;
-    a.flags[hq] = 0;
-    a.bdone[hq] = 0;
-    a.exdone[hq] = 0;
-    a.exdone2[hq] = 0;
-  }
-  for (int j = t; j < a.J + 2; j += kD) a.hist[(int64_t)hq * (a.J + 2) + j] = 0;
-}
-
-hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(prep_kernel, dim3(a.U * a.G), dim3(128), 0, st, a);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ scan
 //
 // The scan is two kernels.
@@ -156,13 +51,19 @@ struct ScanArgs {
   const BlockMeta *bmeta;
   const uint16_t *kerr, *vnorm;
   int64_t n_cap, nb_cap, nb_pool, npool_cap, nwords, nbw;   // nb_pool: the longest item's
-  int G, U, J;                                               // units (item KV heads)
+  int G, U, J, r;                                            // units (item KV heads)
   Batch b;
-  const float *qf;
+  const uint16_t *q;        // fp16 [units G][128]
+  uint64_t seed[kMaxItems], step[kMaxItems];   // hash inputs per item
+  int32_t layer[kMaxItems];
+  // per-call constants, written by the window workgroups for the later kernels (the
+  // streaming wavefronts derive their own from q)
+  float *qf;
   double *qconst;
-  const int8_t *qA;
-  const uint64_t *prefix;
-  const double *lt;
+  int8_t *qA;
+  uint64_t *prefix;
+  double *lt, *tau;
+  int *ccount, *exdone, *exdone2;   // per-head counters, cleared by the window workgroups
   // window work (extra workgroups of the streaming kernel, one per query head)
   const uint16_t *V;
   int W;
@@ -220,6 +121,121 @@ __device__ inline void init_operand(uint8_t *Abuf, int lane, bool every_group = 
     A4[lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
     A4[64 + lane] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
   }
+  wave_sync();
+}
+
+
+// ------------------------------------------------------------------ query constants
+// Per query (R1 sums: the 128 channels in 8 chunks of 16 summed in channel order, then
+// the fixed tree ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)); all fp64):
+//   qa    = max_t |q_t|;  beta = 2^(e - 11) for qa = f 2^e, f in [1/2, 1) (0 for q = 0)
+//   qabs  = R1-sum |q_t|;  qn = the fp32 square root of R1-sum q_t^2 (1 + 2^-40),
+//   rounded up;  qnp = qn (1 + 2^-40)
+//   the integer grid of the offset term: qi_t = rint(q_t / beta) = 128 q1_t + q0_t with
+//   q1 = floor((qi + 64) / 128), q0 = qi - 128 q1, in operand rows op_row(g, 0 / 1).
+struct QueryConsts {
+  double qa, beta, qabs, qn, qnp;
+  float ib;   // 1 / beta (a power of two, exact in fp32; 0 when beta = 0)
+};
+
+__device__ inline QueryConsts query_consts_from(double ss, double sa, double qa) {
+  QueryConsts c;
+  c.qa = qa;
+  c.beta = 0.0;
+  c.ib = 0.0f;
+  if (qa > 0.0) {
+    int e;
+    (void)frexp(qa, &e);
+    c.beta = ldexp(1.0, e - 11);
+    c.ib = ldexpf(1.0f, 11 - e);
+  }
+  c.qabs = sa;
+  const float qn = f32_sqrt_up(ss * (1.0 + kPadF));
+  c.qn = (double)qn;
+  c.qnp = (double)qn * (1.0 + kPadF);
+  return c;
+}
+
+// One wavefront's constants of its G queries: lane l holds channels 2l, 2l + 1 of every
+// query (qv0, qv1).  Lanes 8g .. 8g + 7 sum query g's chunks through `st` (128 G floats
+// of LDS) and lane 8g computes its constants; the lane then takes those of its two query
+// slots gA = l / 16 and gB = gA + 4 (qnp, qabs, beta), the largest |q| of the group, and
+// its slice of the offset term's A operand (qa0, qa1: lane L = row + 16 kg holds the
+// bytes of channels 32 kg + 16 kh + b, b = 0..15, of row `row`, kh = 0 / 1).
+template <int G>
+__device__ inline void wave_query_consts(const float *qv0, const float *qv1, int lane, float *st, float &qmax,
+                                         float &qnpA, float &qnpB, double *obeta, double *oqabs, v4i &qa0,
+                                         v4i &qa1) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st[g * kD + 2 * lane] = qv0[g];
+    st[g * kD + 2 * lane + 1] = qv1[g];
+  }
+  wave_sync();
+  const int gq = lane >> 3, k = lane & 7;
+  double ss = 0.0, sa = 0.0, mx = 0.0;
+  if (gq < G) {
+    const float *c = st + gq * kD + 16 * k;
+    double x = (double)c[0];
+    ss = x * x;
+    sa = fabs(x);
+    mx = fabs(x);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      x = (double)c[i];
+      ss = ss + x * x;
+      sa = sa + fabs(x);
+      mx = fmax(mx, fabs(x));
+    }
+  }
+  // the tree over a query's 8 chunks (lane k = 0 of its group ends with the sums)
+#pragma unroll
+  for (int off = 1; off <= 4; off <<= 1) {
+    ss = ss + __shfl_xor(ss, off, 64);
+    sa = sa + __shfl_xor(sa, off, 64);
+    mx = fmax(mx, __shfl_xor(mx, off, 64));
+  }
+  // lane 8g: query g's constants, then every lane takes what it needs
+  const QueryConsts mine = query_consts_from(ss, sa, mx);
+  const int gA = lane >> 4, gB = gA + 4;
+  const double npA = __shfl(mine.qnp, 8 * gA, 64), npB = __shfl(mine.qnp, 8 * min(gB, 7), 64);
+  obeta[0] = (gA < G) ? __shfl(mine.beta, 8 * gA, 64) : 0.0;
+  oqabs[0] = (gA < G) ? __shfl(mine.qabs, 8 * gA, 64) : 0.0;
+  const double bB = __shfl(mine.beta, 8 * min(gB, 7), 64), aB = __shfl(mine.qabs, 8 * min(gB, 7), 64);
+  obeta[1] = (gB < G) ? bB : 0.0;
+  oqabs[1] = (gB < G) ? aB : 0.0;
+  qnpA = (gA < G) ? (float)npA : 0.0f;
+  qnpB = (gB < G) ? (float)npB : 0.0f;
+  float m = (gq < G) ? (float)mine.qa : 0.0f;   // (the group's largest |q| is in all its lanes)
+#pragma unroll
+  for (int off = 8; off <= 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  qmax = m;
+  wave_sync();   // the chunk sums are read: the staging area takes the operand next
+  // the operand: each lane quantizes its two channels of every query (beta is a power of
+  // two, so q / beta is exact in fp32 and rint matches the fp64 definition) and writes
+  // the byte pairs into the rows of its channel group; rows of unused query slots are 0
+  uint8_t *A = reinterpret_cast<uint8_t *>(st);
+  const int c0 = 2 * lane, kg = c0 >> 5, kh = (c0 >> 4) & 1, b = c0 & 15;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t hi = 0u, lo = 0u;   // the two channels' bytes of the high and low row
+    if (g < G) {
+      const float ib = __shfl(mine.ib, 8 * g, 64);   // 0 for a zero query: its rows stay 0
+      const float qs[2] = {qv0[g < G ? g : 0], qv1[g < G ? g : 0]};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int qi = (int)rintf(qs[e] * ib);
+        const int q1 = (qi + 64) >> 7;
+        hi |= (uint32_t)(q1 & 0xFF) << (8 * e);
+        lo |= (uint32_t)((qi - 128 * q1) & 0xFF) << (8 * e);
+      }
+    }
+    *reinterpret_cast<uint16_t *>(A + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b) = (uint16_t)hi;
+    *reinterpret_cast<uint16_t *>(A + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b) = (uint16_t)lo;
+  }
+  wave_sync();
+  qa0 = *reinterpret_cast<const v4i *>(A + lane * 16);
+  qa1 = *reinterpret_cast<const v4i *>(A + 1024 + lane * 16);
   wave_sync();
 }
 
@@ -390,6 +406,9 @@ struct StreamSmem {
 struct WindowSmem {
   double sw[kMaxWin], vsq[kMaxWin];
   double red[2][4];
+  double qd[kD];       // the query (fp64)
+  double part[16];     // its R1 chunk sums of q^2 and |q|
+  double smax[2];
 };
 union ScanSmem {
   StreamSmem st;
@@ -408,8 +427,75 @@ constexpr int kWinGrp = 3;     // wavefront steps whose rows are read together
 __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int s8 = lane >> 3, k8 = lane & 7;
-  const int h = hq / a.G;                                   // the unit
+  const int h = hq / a.G, g = hq % a.G;                     // the unit and the query in it
   const int64_t kvh = unit_kv(a.b, h), nU = unit_n(a.b, h);  // its cache head and length
+  // the call's constants of this query, stored for the later kernels (thread t < 128
+  // owns channel t): level table (first query head), hash prefix (first query of a
+  // unit), qf, the query constants, its rows of the offset term's A operand; and the
+  // per-head counters cleared
+  {
+    if (hq == 0 && t <= a.J) {
+      const double v = (-(double)t * kLn2) / (double)a.r;
+      a.lt[t] = v;
+      a.tau[t] = exp(v);
+    }
+    if (g == 0 && t == 0) {
+      const int it = (a.U == a.b.H_kv) ? 0 : h / a.b.H_kv;
+      a.prefix[h] = hash_prefix(a.seed[it], a.step[it], (uint64_t)(int64_t)a.layer[it], (uint64_t)(h % a.b.H_kv));
+    }
+    if (t == 0) {
+      a.ccount[hq] = 0;
+      a.exdone[hq] = 0;
+      a.exdone2[hq] = 0;
+    }
+    const double qv = (t < kD) ? h2d(a.q[(int64_t)hq * kD + t]) : 0.0;
+    if (t < kD) {
+      a.qf[(int64_t)hq * kD + t] = (float)qv;
+      sm.qd[t] = qv;
+    }
+    __syncthreads();
+    // R1 chunk sums: threads 0..7 those of q^2, threads 8..15 those of |q|
+    if (t < 16) {
+      const int p = t & 7;
+      double acc = (t < 8) ? sm.qd[16 * p] * sm.qd[16 * p] : fabs(sm.qd[16 * p]);
+      for (int c = 1; c < 16; ++c)
+        acc = acc + ((t < 8) ? sm.qd[16 * p + c] * sm.qd[16 * p + c] : fabs(sm.qd[16 * p + c]));
+      sm.part[t] = acc;
+    }
+    double qa = fabs(qv);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) qa = fmax(qa, __shfl_xor(qa, off, 64));
+    if (lane == 0 && wv < 2) sm.smax[wv] = qa;
+    __syncthreads();
+    qa = fmax(sm.smax[0], sm.smax[1]);
+    const double ss = ((sm.part[0] + sm.part[1]) + (sm.part[2] + sm.part[3])) +
+                      ((sm.part[4] + sm.part[5]) + (sm.part[6] + sm.part[7]));
+    const double sa = ((sm.part[8] + sm.part[9]) + (sm.part[10] + sm.part[11])) +
+                      ((sm.part[12] + sm.part[13]) + (sm.part[14] + sm.part[15]));
+    const QueryConsts c = query_consts_from(ss, sa, qa);
+    if (t == 0) {
+      double *qc = a.qconst + (int64_t)hq * kQc;
+      qc[QC_BETA] = c.beta;
+      qc[QC_QNP] = c.qnp;
+      qc[QC_QABS] = c.qabs;
+      qc[QC_QA] = c.qa;
+      qc[QC_QN] = c.qn;
+    }
+    if (t < kD) {
+      const int qi = (c.beta > 0.0) ? (int)rint(qv / c.beta) : 0;   // exact scaling
+      const int q1 = (qi + 64) >> 7;
+      const int q0 = qi - 128 * q1;
+      const int kg = t >> 5, kh = (t >> 4) & 1, b = t & 15;
+      int8_t *A = a.qA + (int64_t)h * 2048;
+      A[kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b] = (int8_t)q1;
+      A[kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b] = (int8_t)q0;
+      if (g == 0)   // the rows of unused query slots
+        for (int gs = a.G; gs < 8; ++gs) {
+          A[kh * 1024 + (op_row(gs, 0) + 16 * kg) * 16 + b] = 0;
+          A[kh * 1024 + (op_row(gs, 1) + 16 * kg) * 16 + b] = 0;
+        }
+    }
+  }
   const int64_t w0 = (nU > a.W) ? (nU - a.W) : 0;
   const int nw = (int)(nU - w0);
   const int64_t stride = (w0 + kPilot - 1) / kPilot;
@@ -427,7 +513,7 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   }
   double q16[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
+  for (int i = 0; i < 16; ++i) q16[i] = sm.qd[16 * k8 + i];
   const uint16_t *Kh = a.K + kvh * a.n_cap * kD;
   const uint16_t *Vh = a.V ? a.V + kvh * a.n_cap * kD : nullptr;
   double m = -__builtin_huge_val(), mp = -__builtin_huge_val();
@@ -512,8 +598,9 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
     double *qc = a.qconst + (int64_t)hq * kQc;
     qc[QC_CR] = cr;
     qc[QC_PILOT] = pilot;
-    __hip_atomic_fetch_max(a.clo + hq, enc_max(cr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_max(a.cstar + hq, enc_max(cr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // c_lo and c* start at c_R (nothing else writes them during the scan)
+    a.clo[hq] = enc_max(cr);
+    a.cstar[hq] = enc_max(cr);
   }
 }
 
@@ -585,16 +672,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = kTwo && gB < G;
   const int hq0 = h * G;
-  const float qnpA = hasA ? (float)a.qconst[(int64_t)(hq0 + gA) * kQc + QC_QNP] : 0.0f;
-  const float qnpB = hasB ? (float)a.qconst[(int64_t)(hq0 + gB) * kQc + QC_QNP] : 0.0f;
-  float qmax = 0.0f;
-#pragma unroll
-  for (int g = 0; g < G; ++g) qmax = fmaxf(qmax, (float)a.qconst[(int64_t)(hq0 + g) * kQc + QC_QA]);
+  // the group's queries (fp16 -> fp32, exact): the lane's two channels of each
   float qv0[G], qv1[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    qv0[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane];
-    qv1[g] = a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1];
+    const uint32_t w2 = reinterpret_cast<const uint32_t *>(a.q + (int64_t)(hq0 + g) * kD)[lane];
+    qv0[g] = h2f((uint16_t)(w2 & 0xFFFFu));
+    qv1[g] = h2f((uint16_t)(w2 >> 16));
   }
 
   // Software pipeline: the loads of chunks c + 1 .. c + kScanBufs - 1 (two blocks each)
@@ -644,20 +728,24 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // chunks are in flight together before the first wait, those of the second half are
   // issued once the first chunk is done.
   static_assert(kScanBlocks == 16 || kScanBlocks == 32, "offset terms are formed 16 blocks at a time");
-  const v4i qa0 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + lane * 16);
-  const v4i qa1 = *reinterpret_cast<const v4i *>(a.qA + (int64_t)h * 2048 + 1024 + lane * 16);
-  double obeta[2], oqabs[2];
-  offset_consts(a, h, G, lane, obeta, oqabs);
   OffsetIn off0, off1;
   offset_load(a, kvh, blk0, nblk, lane, 0, off0);
   ChunkIn buf[kScanBufs];
 #pragma unroll
   for (int k = 0; k + 1 < kScanBufs; ++k) load_chunk(2 * k, buf[k]);
+  // the query constants, while the first loads are in flight (staged in the first
+  // operand buffer, which is set up afterwards)
+  v4i qa0, qa1;
+  float qnpA, qnpB, qmax;
+  double obeta[2], oqabs[2];
+  wave_query_consts<G>(qv0, qv1, lane, reinterpret_cast<float *>(Abuf), qmax, qnpA, qnpB, obeta, oqabs, qa0, qa1);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
   offset_compute(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 0);
 
-  const uint64_t prefix = a.prefix[h];
+  const int item = (a.U == a.b.H_kv) ? 0 : h / a.b.H_kv;
+  const uint64_t prefix =
+      hash_prefix(a.seed[item], a.step[item], (uint64_t)(int64_t)a.layer[item], (uint64_t)(h % a.b.H_kv));
   float lbA = -__builtin_huge_valf(), lbB = -__builtin_huge_valf();
   unsigned vmx = 0u;
   constexpr float kNegInf = -__builtin_huge_valf();
