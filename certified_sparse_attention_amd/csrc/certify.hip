@@ -232,25 +232,47 @@ struct RescoreConsts {
   uint64_t prefix;
 };
 
+// Candidate positions of the first stage, read before the candidate count is known: the
+// rows of the lane's two steps (32 step + 8 wv + lane / 8) and thread t's key.  Entries
+// past the count are read at clamped indices inside the row and never used.
+struct StagePre {
+  int pos_r[2];
+  int pos_t;
+};
+__device__ __forceinline__ void stage_positions(const CertArgs &a, int hq, StagePre &p) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int *cp = a.candpos + (int64_t)hq * a.npool_cap;
+  const int last = (int)a.npool_cap - 1;
+#pragma unroll
+  for (int step = 0; step < 2; ++step) p.pos_r[step] = cp[min(32 * step + 8 * wv + (lane >> 3), last)];
+  p.pos_t = cp[min(t, last)];
+}
+
 template <bool kSpec>
 __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int hq, int c0, int cnt,
-                                              const RescoreConsts &rc, int zero_rows = 0) {
+                                              const RescoreConsts &rc, int zero_rows = 0,
+                                              bool use_pre = false, StagePre pre = StagePre{}) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t h = head_kv(a, hq);
   const int s8 = lane >> 3, k8 = lane & 7;
   const int64_t base = (int64_t)hq * a.npool_cap;
-  if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
-  __syncthreads();
-  // wavefront wv takes keys 16 wv .. 16 wv + 15, eight lanes per key
+  if (use_pre) {   // (c0 = 0) the positions were read with the counts
+    if (t < cnt) s.pos[t] = pre.pos_t;
+  } else {
+    if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
+    __syncthreads();
+  }
+  // step k takes keys 32 k .. 32 k + 31, wavefront wv eight of them (eight lanes per key), so a
+  // stage of at most 32 keys is one step of every wavefront
   uint4 cw8[2], kw[2][2], vw[2][2];
   float sc8[2];
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
-    const int r = 16 * wv + 8 * step + s8;
+    const int r = 32 * step + 8 * wv + s8;
     cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
     sc8[step] = 0.0f;
     if (r < cnt) {
-      const int64_t tok = h * a.n_cap + s.pos[r];
+      const int64_t tok = h * a.n_cap + (use_pre ? pre.pos_r[step] : s.pos[r]);
       cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
       sc8[step] = a.scale8[tok];
       if (kSpec) {
@@ -266,7 +288,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   // one lane per key: its perturbation, UB and 8-bit record
   double E = 0.0, ubt = 0.0, ke8 = 0.0, s8t = 0.0;
   if (t < cnt) {
-    const int pos = s.pos[t];
+    const int pos = use_pre ? pre.pos_t : s.pos[t];
     ubt = a.ubuf[base + pos];
     ke8 = h2d(a.kerr8[h * a.n_cap + pos]);
     s8t = (double)a.scale8[h * a.n_cap + pos];
@@ -275,7 +297,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
-    const int r = 16 * wv + 8 * step + s8;
+    const int r = 32 * step + 8 * wv + s8;
     double p = 0.0;
     if (r < cnt) {
       const double sc = (double)sc8[step];
@@ -297,7 +319,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   __syncthreads();
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
-    const int r = 16 * wv + 8 * step + s8;
+    const int r = 32 * step + 8 * wv + s8;
     const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
     if (!kSpec && ex) {
       const int64_t tok = h * a.n_cap + s.pos[r];
@@ -311,7 +333,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   }
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
-    const int r = 16 * wv + 8 * step + s8;
+    const int r = 32 * step + 8 * wv + s8;
     const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
     double p = 0.0, v = 0.0;
     if (ex) {
@@ -355,7 +377,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
 
 // The per-query constants of rescoring: the query chunk of the lane (eight lanes per key,
 // sixteen channels each), c*, c_lo, |q| pad and sum |q|, the hash prefix, 1 / log tau_1.
-__device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem &s, int hq, RescoreConsts &c) {
+__device__ __forceinline__ void rescore_consts_load(const CertArgs &a, int hq, RescoreConsts &c) {
   const int k8 = threadIdx.x & 7;
 #pragma unroll
   for (int i = 0; i < 16; ++i) c.q16[i] = (double)a.qf[(int64_t)hq * kD + 16 * k8 + i];
@@ -364,6 +386,10 @@ __device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem 
   c.qnp = a.qconst[(int64_t)hq * kQc + QC_QNP];
   c.qabs = a.qconst[(int64_t)hq * kQc + QC_QABS];
   c.prefix = a.prefix[hq / a.G];
+}
+// (s.ltp must be filled and the workgroup past a barrier since)
+__device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem &s, int hq, RescoreConsts &c) {
+  rescore_consts_load(a, hq, c);
   c.inv_l1 = (a.J >= 1) ? 1.0 / s.ltp[1].y : 0.0;
 }
 
@@ -481,6 +507,9 @@ struct FinSmem {
 // for the extension pass (2) or for the exact fallback (1).  Uniform across the group.
 // nparts: partial tables of this pass written by other workgroups (0: accumulate every
 // candidate here; -1: as many as seg_range gives for the count).
+// kFirst: the pass-1 kernel (a.pass == 1), whose single stage has its positions and
+// constants read with the counts.
+template <bool kFirst>
 __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts = -1) {
   const int t = threadIdx.x, h = hq / a.G;
   const int lane = t & 63, wv = t >> 6;
@@ -489,6 +518,15 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   // every load that does not depend on the candidate count is issued before it is used
   const int count = pass_count(a, hq);
   const int jmax = pass_jmax(a, hq);
+  // pass 1 takes its candidates (at most `budget`) in one stage when they fit: their
+  // positions and the rescoring constants are read together with the counts
+  const bool spec = kFirst && (nparts < 0);
+  StagePre pre{};
+  RescoreConsts rc;
+  if (spec) {
+    stage_positions(a, hq, pre);
+    rescore_consts_load(a, hq, rc);
+  }
   for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
   fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
   for (int j = t; j < a.J + 2; j += 256) {
@@ -520,9 +558,9 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   // a single stage rescored here: the increments are cleared while its rows arrive
   if (nseg == 0 && count <= kStage && record_split(a, hq, count) == 0) {
     __syncthreads();            // the level table s.ltp is filled
-    RescoreConsts rc;
-    rescore_consts(a, s, hq, rc);
-    rescore_stage<true>(a, s, hq, 0, count, rc, jmax + 1);
+    if (spec) rc.inv_l1 = (a.J >= 1) ? 1.0 / s.ltp[1].y : 0.0;
+    else rescore_consts(a, s, hq, rc);
+    rescore_stage<true>(a, s, hq, 0, count, rc, jmax + 1, spec, pre);
     accumulate_stage(a, s, head_kv(a, hq), count, true);
   } else if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
@@ -703,7 +741,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     return;
   }
   __shared__ FinSmem f;
-  certify_head(a, f, hq);
+  certify_head<true>(a, f, hq);
 }
 
 struct ExactSmem {
@@ -899,7 +937,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
             }
             a.o_hat[(int64_t)h * kD + t] = (float)(N / Dn);
           }
-        } else if (!certify_head(a, u.f, h, gsz > 1 ? gsz : 0) && a.pass == a.final_pass) {
+        } else if (!certify_head<false>(a, u.f, h, gsz > 1 ? gsz : 0) && a.pass == a.final_pass) {
           __syncthreads();
           exact_chunk(a, u.e, h, 0, head_n(a, h), a.exactp + (int64_t)h * kExactChunks * 130);
           if (t < kD) a.o_hat[(int64_t)h * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);

@@ -12,6 +12,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/csa.h"
 
 namespace csa {

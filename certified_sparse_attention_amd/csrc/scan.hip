@@ -369,6 +369,19 @@ __device__ inline void block_grid(float qmax, float ksmax, double &alpha, float 
   }
 }
 
+// The same grid step in fp32 (a power of two, so equal to the fp32 rounding of the fp64 one).
+__device__ inline void block_grid32(float qmax, float ksmax, float &alpha, float &scale) {
+  const float m = qmax * ksmax;
+  alpha = 0.0f;
+  scale = 0.0f;
+  if (m > 0.0f) {
+    int x;
+    (void)frexpf(m, &x);
+    alpha = ldexpf(1.0f, x - 11);
+    scale = ldexpf(1.0f, 11 - x);
+  }
+}
+
 // fp32 bounds of one (query, key): ub >= UB, lb <= LB, ube >= UB + E^.  The fp64
 // bound rounds at most ~10 times with unit 2^-53 and this fp32 evaluation at most
 // ~12 times with unit 2^-24, each relative to M = (|base| + |alpha I|) R + slack, so a
@@ -770,11 +783,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     ek[4 * (lane & 15) + (lane >> 4)] = h2f(in.kerr);
     float scales[2];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      double alpha;
-      block_grid(qmax, in.ksmax[bi], alpha, scales[bi]);
-      al[bi] = (float)alpha;
-    }
+    for (int bi = 0; bi < 2; ++bi) block_grid32(qmax, in.ksmax[bi], al[bi], scales[bi]);
     build_operand<G>(Abuf, qv0, qv1, in.kk[0], scales[0], lane);
     if (nb2 > 1) build_operand<G>(Abuf1, qv0, qv1, in.kk[1], scales[1], lane);
   };
@@ -820,6 +829,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     }
     wave_sync();
     if (more) stage(c0 + 2, nxt, eupN, alnext);
+    // (chunks with all 64 keys in the pool, all but the last of a wavefront or pool, take
+    // the copy without the per-key masks)
+    auto bounds = [&](auto kFull) __attribute__((always_inline)) {
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       if (bi >= nb2) break;
@@ -836,7 +848,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         const int Csum = kTwo ? bperm_i32(48 + n16, acc[2]) : acc[2];
         const float eup = Tg == 0 ? eup4.x : (Tg == 1 ? eup4.y : (Tg == 2 ? eup4.z : eup4.w));
         const float kerr = Tg == 0 ? kerr4.x : (Tg == 1 ? kerr4.y : (Tg == 2 ? kerr4.z : kerr4.w));
-        const bool valid = tt < nval;
+        const bool valid = decltype(kFull)::value || tt < nval;
         if (hasA) {
           const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
           uA = T ? fmaxf(uA, valid ? r.ub : kNegInf) : (valid ? r.ub : kNegInf);
@@ -857,6 +869,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         if (hasB) mx[bl][gB] = make_float2(uB, eB);
       }
     }
+    };
+    if (nval == 64) bounds(std::true_type{});
+    else bounds(std::false_type{});
   };
   // kScanBufs - 1 chunks in flight ahead of the one being computed, which has been staged
   float alCur[2], alNext[2];
