@@ -643,13 +643,21 @@ __device__ inline void row_max16x2(float &u, float &v) {
           "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
           : "+v"(u), "+v"(v));
 }
-__device__ inline float row_max16k(float v) {
-  int k = fkey(v);
+__device__ inline int row_max16key(int k) {
   k = max(k, __builtin_amdgcn_update_dpp(k, k, 0xB1, 0xF, 0xF, false));    // quad_perm 1032
   k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x4E, 0xF, 0xF, false));    // quad_perm 2301
   k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x141, 0xF, 0xF, false));   // row_half_mirror
   k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x140, 0xF, 0xF, false));   // row_mirror
-  return fkey_inv(k);
+  return k;
+}
+__device__ inline float row_max16k(float v) { return fkey_inv(row_max16key(fkey(v))); }
+// Maximum over the 64 lanes (every lane active), the same in every lane: the rows' maxima
+// by DPP, then the four rows' from scalar reads.
+__device__ inline float wave_max_f32(float v) {
+  const int k = row_max16key(fkey(v));
+  const int r0 = __builtin_amdgcn_readlane(k, 0), r1 = __builtin_amdgcn_readlane(k, 16);
+  const int r2 = __builtin_amdgcn_readlane(k, 32), r3 = __builtin_amdgcn_readlane(k, 48);
+  return fkey_inv(max(max(r0, r1), max(r2, r3)));
 }
 
 template <int G>
@@ -1026,12 +1034,10 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   // c_lo snapshot per query: c_R (the window's atomic) and the scan wavefronts' bounds
 #pragma unroll
   for (int g = 0; g < kMaxG; ++g) {
+    if (g >= G) break;   // (G is the same for every lane)
     float v = fmaxf(lbs[g][0], lbs[g][1]);
-    if (g < G)
-      for (int64_t k = lane + 128; k < swph; k += 64) v = fmaxf(v, a.lbpart[(int64_t)(hq0 + g) * a.wstride + k]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    lbs[g][0] = v;
+    for (int64_t k = lane + 128; k < swph; k += 64) v = fmaxf(v, a.lbpart[(int64_t)(hq0 + g) * a.wstride + k]);
+    lbs[g][0] = wave_max_f32(v);
   }
   // largest |q_t| over the group (lanes 0..7 hold the queries' values, 0 past G)
   float qm = (float)qa;
