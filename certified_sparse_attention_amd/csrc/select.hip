@@ -168,6 +168,10 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int64_t p0 = wi * 32;
   const int64_t p_tile = tile * 2048;
   const uint32_t word = a.live[(int64_t)hq * a.nwords + min(wi, a.nwords - 1)];
+  const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p0));
+  const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
+  // a tile without live keys has no candidate to place (tile 0 still writes the totals)
+  if (tile > 0 && __ballot(bits != 0u) == 0ull) return;
   const uint4 *lw = reinterpret_cast<const uint4 *>(a.lub + (int64_t)hq * a.npool_cap + min(p0, a.npool_cap - 32));
   const uint4 lv0 = lw[0], lv1 = lw[1];
   // cumulative level histogram of the head and of the tiles before this one (lane = level)
@@ -204,8 +208,6 @@ __global__ __launch_bounds__(64) void bucket_write_kernel(SelectArgs a) {
   const int b1 = (js >= 0) ? pre1v : 0;
   const int b2 = pre2 - b1;
   const int b3 = preJ - pre2;
-  const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p0));
-  const uint32_t bits = word & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
   int *dst = a.candpos + (int64_t)hq * a.npool_cap;
   int tile_live = __popc(bits);
 #pragma unroll
