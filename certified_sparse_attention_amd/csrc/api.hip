@@ -114,13 +114,10 @@ csa::Plan make_plan(const csa_shape *s, const csa_params *p, int64_t n_max, int 
   P.wstride = std::max<int64_t>(1, ((P.npool_cap + csa::kBlk - 1) / csa::kBlk + csa::kScanBlocks - 1) / csa::kScanBlocks);
   P.lbpart = take(Hq * (size_t)P.wstride * sizeof(float));
   P.vpart = take((size_t)P.H_kv * P.wstride * sizeof(unsigned));
-  P.bdone = take(Hq * sizeof(int));
   P.exdone = take(Hq * sizeof(int));
   P.exdone2 = take(Hq * sizeof(int));
   P.hist = take(Hq * J2 * sizeof(int));
-  P.tilecnt = 0;
-  P.tileoff = take(Hq * (size_t)P.ntiles * sizeof(int));
-  P.tileoff2 = take(Hq * (size_t)P.ntiles * sizeof(int));
+  P.tilelist = take(Hq * (size_t)P.ntiles * csa::kTileList * sizeof(int));
   P.tilehist = take(Hq * (size_t)P.ntiles * J2 * sizeof(int));
   P.tilecm = take(Hq * (size_t)P.ntiles * J2 * sizeof(int));
   P.cmhist = take(Hq * J2 * sizeof(int));
@@ -513,44 +510,26 @@ int certified_run(const csa_shape *shape, const csa_params *params, const Call &
   const int64_t npool = c.npool_max;   // (a single call: its pool)
   hipError_t e;
   csa::SelectArgs sel{};
+  // the first pass rescores inside the certificate kernel: at most kFusedMax candidates
+  const int budget = params->cand_budget > 0 ? std::min(params->cand_budget, csa::kFusedMax) : csa::kDefaultBudget;
+  const int budget2 = params->cand_budget2 > 0 ? params->cand_budget2 : INT_MAX;   // default: no third range
   if (!all_exact) {
     csa::SelectArgs &sa = sel;
-    sa.K = K;
-    sa.V = V;
-    sa.n_cap = shape->n_cap;
     sa.b = c.b;
     sa.W = params->window;
     sa.npool_cap = P.npool_cap;
     sa.ntiles = (npool + csa::kBucketTile - 1) / csa::kBucketTile;
     sa.G = P.G;
     sa.J = P.J;
-    sa.qf = at<float>(ws, P.qf);
     sa.lt = at<double>(ws, P.lt);
-    sa.prefix = at<uint64_t>(ws, P.prefix);
     sa.pbuf = at<double>(ws, P.pbuf);
     sa.ubuf = at<double>(ws, P.ubuf);
     sa.clo = at<unsigned long long>(ws, P.clo);
     sa.cstar = at<unsigned long long>(ws, P.cstar);
-    sa.hist = at<int>(ws, P.hist);
-    sa.tilecnt = nullptr;
-    sa.tileoff = at<int>(ws, P.tileoff);
-    sa.tileoff2 = at<int>(ws, P.tileoff2);
     sa.tilehist = at<int>(ws, P.tilehist);
-    sa.ccount1 = at<int>(ws, P.ccount1);
-    sa.jspec = at<int>(ws, P.jspec);
-    sa.ccount2 = at<int>(ws, P.ccount2);
-    sa.jspec2 = at<int>(ws, P.jspec2);
-    sa.flags = at<int>(ws, P.flags);
-    sa.bdone = at<int>(ws, P.bdone);
     sa.tilecm = at<int>(ws, P.tilecm);
-    sa.cmhist = at<int>(ws, P.cmhist);
-    // the first pass rescores inside the certificate kernel: at most kFusedMax candidates
-    sa.budget = params->cand_budget > 0 ? std::min(params->cand_budget, csa::kFusedMax) : csa::kDefaultBudget;
-    sa.budget2 = params->cand_budget2 > 0 ? params->cand_budget2 : INT_MAX;   // default: no third range
-    sa.pass = 1;
-    sa.ccount = at<int>(ws, P.ccount);
+    sa.tilelist = at<int>(ws, P.tilelist);
     sa.lub = at<int8_t>(ws, P.lub);
-    sa.candpos = at<int>(ws, P.candpos);
     sa.live = at<uint32_t>(ws, P.live);
     sa.nwords = P.npool_cap / 32 + 1;
     sa.full_lub = (trace && trace->lub) ? 1 : 0;
@@ -615,6 +594,17 @@ int certified_run(const csa_shape *shape, const csa_params *params, const Call &
   ca.keys_read = keys_read;
   ca.ccount1 = at<int>(ws, P.ccount1);
   ca.jspec = at<int>(ws, P.jspec);
+  if (!all_exact) {   // pass 1 places the candidates from the bucket counts
+    ca.tilehist = sel.tilehist;
+    ca.tilecm = sel.tilecm;
+    ca.tilelist = sel.tilelist;
+    ca.ntiles = sel.ntiles;
+    ca.live = sel.live;
+    ca.nwords = sel.nwords;
+    ca.budget = budget;
+    ca.budget2 = budget2;
+    ca.full_list = trace ? 1 : 0;
+  }
   // pass 1: levels up to the speculative level (at most `budget` candidates, rescored
   // inside the certificate kernel); with all_exact, the exact attention of every head
   if ((e = csa::launch_certify_pass(ca, 1, P.H_q, st)) != hipSuccess) return hip_fail(e, "certify");

@@ -38,19 +38,27 @@ struct CertArgs {
   const double *ubuf;
   const unsigned *vpart;         // per scan wavefront: largest |v| code of its keys
   int64_t wstride;               // row stride of vpart (per unit)
-  const int *ccount, *candpos, *hist;
+  int *ccount, *candpos, *hist;  // (pass 1 writes the totals and the candidate list)
   int *rec_hl;                  // candidate records (written by the fused rescoring)
-  const int *cmhist;            // [H_q][J+2] C_max keys per bucket level
+  int *cmhist;                  // [H_q][J+2] C_max keys per bucket level
   double *rec_w, *rec_vsq;
-  const int8_t *lub;
+  const int8_t *lub;            // [H_q][npool_cap] l^ub of live keys (bucket count)
+  const int *tilehist;          // [H_q][ntiles][J+2] per-tile cumulative level counts
+  const int *tilecm;            // [H_q][ntiles][J+2] per-tile C_max keys per level
+  const int *tilelist;          // [H_q][ntiles][kTileList] per-tile live keys in level order
+  int64_t ntiles;               // row stride of the tile tables
+  const uint32_t *live;         // [H_q][nwords] live keys (refinement)
+  int64_t nwords;
+  int budget, budget2;          // candidates of the first pass; of the first two (INT_MAX: all)
+  int full_list;                // place every range even when pass 1 certifies (diagnostics)
   double *partial, *betalv, *dhatlv;
   int nseg_cap;                 // segment rows per query head in `partial` (seg_cap_for(npool))
   int *klv;
   int *flags;                   // [H_q] after pass 1: 0 certified, 1 exact fallback, 2 second pass
   int *flags2;                  // [H_q] after pass 2 (heads with flags 2): 0, 1, or 3 third pass
   int *exdone, *exdone2;        // [H_q] finished work items of the second / third-pass launch
-  const int *ccount1, *jspec;   // candidates with l^ub <= jspec come first in the list,
-  const int *ccount2, *jspec2;  // then those with jspec < l^ub <= jspec2, then the rest
+  int *ccount1, *jspec;         // candidates with l^ub <= jspec come first in the list,
+  int *ccount2, *jspec2;        // then those with jspec < l^ub <= jspec2, then the rest
   int H_q;
   int pass;                     // 1: levels <= jspec; 2: levels <= jspec2; 3: all levels
   const int8_t *codes8;         // the 8-bit refinement copy (csa.h)
@@ -107,8 +115,21 @@ __device__ inline void seg_range(int count, int seg, int &i0, int &i1, int &nseg
   i1 = min(count, i0 + len);
 }
 
+// Scratch of pass 1's candidate placement (it runs before and after the level sums).
+struct PlaceScratch {
+  int tiles[256];   // tiles of the current chunk with candidates in the range
+  int toff[256];    // the list index of each one's first candidate
+  int ws[2][4];
+  int slot[256];    // first range: the tile-list entry of each candidate
+  int key[256];     // first range: the candidates' positions
+  int sum[4][64], cms[4][64];   // per-wavefront level totals
+  int th[64][64];               // the tiles' cumulative level counts (heads of at most 64 tiles)
+};
 struct AccSmem {
-  alignas(16) double acc[kMaxJ + 1][kStatW];   // per-level increments: N[128] V[128] D Q k P X
+  union {
+    alignas(16) double acc[kMaxJ + 1][kStatW];   // per-level increments: N[128] V[128] D Q k P X
+    PlaceScratch pl;
+  };
   double2 ltp[kMaxJ + 2];               // level table in neighbour pairs (for rescoring)
   uint16_t vs[kStage][kD];              // staged V rows
   alignas(16) int hl[kStage];           // read eight at a time
@@ -232,20 +253,18 @@ struct RescoreConsts {
   uint64_t prefix;
 };
 
-// Candidate positions of the first stage, read before the candidate count is known: the
-// rows of the lane's two steps (32 step + 8 wv + lane / 8) and thread t's key.  Entries
-// past the count are read at clamped indices inside the row and never used.
+// Candidate positions of the first stage (placed in LDS by pass 1): the rows of the lane's
+// two steps (32 step + 8 wv + lane / 8) and thread t's key.  Entries past the count are
+// read but never used.
 struct StagePre {
   int pos_r[2];
   int pos_t;
 };
-__device__ __forceinline__ void stage_positions(const CertArgs &a, int hq, StagePre &p) {
+__device__ __forceinline__ void stage_positions(const int *pos, StagePre &p) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int *cp = a.candpos + (int64_t)hq * a.npool_cap;
-  const int last = (int)a.npool_cap - 1;
 #pragma unroll
-  for (int step = 0; step < 2; ++step) p.pos_r[step] = cp[min(32 * step + 8 * wv + (lane >> 3), last)];
-  p.pos_t = cp[min(t, last)];
+  for (int step = 0; step < 2; ++step) p.pos_r[step] = pos[32 * step + 8 * wv + (lane >> 3)];
+  p.pos_t = pos[min(t, kStage - 1)];
 }
 
 template <bool kSpec>
@@ -500,6 +519,59 @@ struct FinSmem {
   long long extra[4];
 };
 
+// The certificate's inputs that depend on nothing of the pass: thresholds and level
+// table, V_max from the scan's wavefront maxima, the window sums rescaled from c_R to c*,
+// and (after pass 1, which has them from its own sums) the C_max counts per level.  They
+// are read into registers first (head_issue) and written to LDS later (head_commit), so
+// the loads travel together with whatever the caller issues in between.
+struct HeadPre {
+  double tau, ltx, lty;   // thread t: tau_t and the level-table pair of level t
+  double win;             // thread t < kD + 2: window sum t (relative to c_R)
+  double cr;
+  unsigned long long cs;  // c* (encoded)
+  unsigned vp;            // wavefront 3: its lanes' V_max bits
+  int cmh;                // thread t <= J + 1: C_max keys at level t (not in pass 1)
+};
+template <bool kFirst>
+__device__ __forceinline__ void head_issue(const CertArgs &a, int hq, HeadPre &p) {
+  const int t = threadIdx.x, h = hq / a.G;
+  const int lane = t & 63, wv = t >> 6, J = a.J;
+  p.tau = (t <= J) ? a.tau[t] : 0.0;
+  p.ltx = (t >= 1 && t <= J + 1) ? a.lt[t - 1] : __builtin_huge_val();
+  p.lty = (t <= J) ? a.lt[t] : -__builtin_huge_val();
+  p.win = (t < kD + 2) ? a.win[(int64_t)hq * kWinW + t] : 0.0;
+  p.cr = a.qconst[(int64_t)hq * kQc + QC_CR];
+  p.cs = a.cstar[hq];
+  p.cmh = (!kFirst && t <= J + 1) ? a.cmhist[(int64_t)hq * (J + 2) + t] : 0;
+  p.vp = 0u;
+  if (wv == 3) {
+    const int64_t np = unit_npool(a.b, h, a.W);
+    const int64_t wph = ((np + kBlk - 1) / kBlk + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
+    const unsigned *vp = a.vpart + (int64_t)h * a.wstride;
+    const unsigned v0 = (lane < wph) ? vp[lane] : 0u, v1 = (lane + 64 < wph) ? vp[lane + 64] : 0u;
+    unsigned v = max(v0, v1);
+    for (int64_t k = lane + 128; k < wph; k += 64) v = max(v, vp[k]);
+    p.vp = v;
+  }
+}
+template <bool kFirst>
+__device__ __forceinline__ void head_commit(const CertArgs &a, FinSmem &f, const HeadPre &p) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, J = a.J;
+  if (t <= J) f.tau[t] = p.tau;
+  if (t <= J + 1) f.s.ltp[t] = make_double2(p.ltx, p.lty);
+  if (!kFirst && t <= J + 1) f.cmh[t] = p.cmh;
+  if (wv == 3) {
+    unsigned v = p.vp;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
+    if (lane == 0) f.vmax = h2d((uint16_t)v);
+  }
+  const double sc = exp(p.cr - dec_max(p.cs));
+  if (t < kD) f.nr[t] = p.win * sc;
+  if (t == kD) f.dr = p.win * sc;
+  if (t == kD + 1) f.qr = p.win * sc;
+}
+
 // The certificate of query head hq in pass a.pass, by one workgroup of 256 threads: level
 // sums (directly, or from the segments' increments), window sums, prefix over levels, the
 // certificate of every level up to the pass's last level, the stop level and the outputs.
@@ -507,49 +579,33 @@ struct FinSmem {
 // for the extension pass (2) or for the exact fallback (1).  Uniform across the group.
 // nparts: partial tables of this pass written by other workgroups (0: accumulate every
 // candidate here; -1: as many as seg_range gives for the count).
-// kFirst: the pass-1 kernel (a.pass == 1), whose single stage has its positions and
-// constants read with the counts.
+// kFirst: pass 1 in the certificate kernel, after its placement step, which left the
+// candidate count (pcount) and deepest level (pjmax) of the pass, the head_issue inputs in
+// LDS, the rescoring constants (*rc0) and, when the candidates fit one stage, their
+// positions in s.pos.
 template <bool kFirst>
-__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts = -1) {
+__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts, int pcount,
+                             int pjmax, const RescoreConsts *rc0) {
   const int t = threadIdx.x, h = hq / a.G;
   const int lane = t & 63, wv = t >> 6;
   AccSmem &s = f.s;
   const int J1 = a.J + 1;
   // every load that does not depend on the candidate count is issued before it is used
-  const int count = pass_count(a, hq);
-  const int jmax = pass_jmax(a, hq);
+  const int count = kFirst ? pcount : pass_count(a, hq);
+  const int jmax = kFirst ? pjmax : pass_jmax(a, hq);
   // pass 1 takes its candidates (at most `budget`) in one stage when they fit: their
-  // positions and the rescoring constants are read together with the counts
+  // positions are in LDS, the rescoring constants are read now
   const bool spec = kFirst && (nparts < 0);
   StagePre pre{};
   RescoreConsts rc;
   if (spec) {
-    stage_positions(a, hq, pre);
-    rescore_consts_load(a, hq, rc);
+    stage_positions(s.pos, pre);
+    rc = *rc0;
   }
-  for (int j = t; j < J1; j += 256) f.tau[j] = a.tau[j];
-  fill_level_pairs(s.ltp, a.lt, a.J, t, 256);
-  for (int j = t; j < a.J + 2; j += 256) {
-    f.hist[j] = a.hist[(int64_t)hq * (a.J + 2) + j];
-    f.cmh[j] = a.cmhist[(int64_t)hq * (a.J + 2) + j];
-  }
-  if (wv == 3) {                 // Vmax: the scan wavefronts' maxima of the head
-    unsigned v = 0u;
-    const int64_t np = unit_npool(a.b, h, a.W);
-    const int64_t wph = ((np + kBlk - 1) / kBlk + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
-    for (int64_t k = lane; k < wph; k += 64) v = max(v, a.vpart[(int64_t)h * a.wstride + k]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
-    if (lane == 0) f.vmax = h2d((uint16_t)v);
-  }
-  // window sums, rescaled from c_R to c*
-  {
-    const double cs = dec_max(a.cstar[hq]);
-    const double sc = exp(a.qconst[(int64_t)hq * kQc + QC_CR] - cs);
-    const double *wr = a.win + (int64_t)hq * kWinW;
-    if (t < kD) f.nr[t] = wr[t] * sc;
-    if (t == kD) f.dr = wr[kD] * sc;
-    if (t == kD + 1) f.qr = wr[kD + 1] * sc;
+  if (!kFirst) {
+    HeadPre hp;
+    head_issue<false>(a, hq, hp);
+    head_commit<false>(a, f, hp);
   }
   if (count < 0) return false;
   int i0, i1, nseg;
@@ -728,11 +784,158 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts =
   return true;
 }
 
-// Pass 1, one workgroup per query head (heads with n <= W go straight to exact attention).
+// Exclusive prefix of v[0..N) over the workgroup's 256 threads in thread order; tot[] gets
+// the sums.  All threads take part; two barriers.
+template <int N>
+__device__ __forceinline__ void wg_excl_scan(int *v, int (*ws)[4], int *tot) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int x[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) x[k] = v[k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int y = __shfl_up(x[k], off, 64);
+      if (lane >= off) x[k] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) ws[k][wv] = x[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = ws[k][w];
+      all += c;
+      before += (w < wv) ? c : 0;
+    }
+    tot[k] = all;
+    v[k] = before + x[k] - v[k];
+  }
+  __syncthreads();
+}
+
+// Pass 1's placement of the candidates with lo < l^ub <= hi (levels from the bucket
+// count; lo = -1 for the first range) in position order, at list indices base, base + 1,
+// ...: the tiles' counts come from their cumulative histograms, so each tile's first index
+// is a prefix over tiles, and a wavefront places one tile at a time (lane = bitmap word;
+// the levels of its live keys from the l^ub bytes).  Indices below nstage also go into the
+// stage's positions s.pos.  Ends with the workgroup in step.
+__device__ void place_range(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int lo, int hi, int base,
+                            int nstage) {
+  AccSmem &s = f.s;
+  PlaceScratch &ps = s.pl;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, J2 = a.J + 2;
+  const int64_t row = (int64_t)hq * a.npool_cap;
+  const int64_t ntiles = (npool + kBucketTile - 1) / kBucketTile;   // this head's tiles
+  const int *th = a.tilehist + (int64_t)hq * a.ntiles * J2;
+  int run = base;
+  for (int64_t k0 = 0; k0 < ntiles; k0 += 256) {
+    const int64_t k = k0 + t;
+    int c = 0;
+    if (k < ntiles) {
+      const int *r = th + k * J2;
+      c = r[hi] - (lo >= 0 ? r[lo] : 0);
+    }
+    int v[2] = {c, c > 0 ? 1 : 0}, tot[2];
+    wg_excl_scan<2>(v, ps.ws, tot);
+    if (c > 0) {
+      ps.tiles[v[1]] = (int)k;
+      ps.toff[v[1]] = run + v[0];
+    }
+    __syncthreads();
+    for (int i = wv; i < tot[1]; i += 4) {
+      const int64_t tk = ps.tiles[i];
+      const int64_t wi = tk * 64 + lane, p0 = wi * 32;
+      const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p0));
+      uint32_t bits = 0u, m = 0u;
+      if (valid > 0) bits = a.live[(int64_t)hq * a.nwords + wi] & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
+      if (bits) {
+        const uint4 *lp = reinterpret_cast<const uint4 *>(a.lub + row + p0);
+        const uint4 l0 = lp[0], l1 = lp[1];
+        const uint32_t x[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+        for (int b = 0; b < 32; ++b) {
+          const int l = (int)(int8_t)((x[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+          if (((bits >> b) & 1u) && l > lo && l <= hi) m |= 1u << b;
+        }
+      }
+      const int n = __popc(m);
+      int xs = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(xs, off, 64);
+        if (lane >= off) xs += y;
+      }
+      int o = ps.toff[i] + xs - n;
+      while (m) {
+        const int b = __ffs((int)m) - 1;
+        m &= m - 1u;
+        const int pos = (int)(p0 + b);
+        a.candpos[row + o] = pos;
+        if (o < nstage) s.pos[o] = pos;
+        ++o;
+      }
+    }
+    run += tot[0];
+    __syncthreads();
+  }
+}
+
+// Pass 1's first range (l^ub <= js, tot1 candidates) from the tiles' level-ordered lists:
+// tile k holds the range's keys in its first tilehist[k][js] list entries, so each
+// candidate is one read; the list is then put in position order by ranking in LDS.
+// Returns false, having written nothing, when the range has more candidates than threads
+// or a tile holds more of them than its list; uniform across the workgroup.
+__device__ bool place_first_lists(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int js, int tot1,
+                                  int nstage) {
+  AccSmem &s = f.s;
+  PlaceScratch &ps = s.pl;
+  const int t = threadIdx.x, J2 = a.J + 2;
+  if (tot1 > 256) return false;
+  const int64_t ntiles = (npool + kBucketTile - 1) / kBucketTile;
+  const int *th = a.tilehist + (int64_t)hq * a.ntiles * J2;
+  int run = 0;
+  for (int64_t k0 = 0; k0 < ntiles; k0 += 256) {
+    const int64_t k = k0 + t;
+    const int c = (k < ntiles) ? th[k * J2 + js] : 0;
+    int v[2] = {c, c > kTileList ? 1 : 0}, tot[2];
+    wg_excl_scan<2>(v, ps.ws, tot);
+    if (tot[1] > 0) return false;
+    for (int e = 0; e < c; ++e) ps.slot[run + v[0] + e] = (int)(k * kTileList + e);
+    run += tot[0];
+  }
+  __syncthreads();
+  int pos = 0;
+  if (t < tot1) {
+    pos = a.tilelist[(int64_t)hq * a.ntiles * kTileList + ps.slot[t]];
+    ps.key[t] = pos;
+  }
+  __syncthreads();
+  if (t < tot1) {   // positions are distinct: the ranks are a permutation
+    int r = 0;
+    for (int i = 0; i < tot1; ++i) r += (ps.key[i] < pos) ? 1 : 0;
+    a.candpos[(int64_t)hq * a.npool_cap + r] = pos;
+    if (r < nstage) s.pos[r] = pos;
+  }
+  return true;
+}
+
+// Pass 1, one workgroup per query head (heads with n <= W go straight to exact attention):
+// the head's level totals and speculative levels from the tile histograms, the first range
+// of the candidate list, the certificate of the levels up to the speculative level, and,
+// for heads that need a later pass (or with every range requested), the other ranges.
 __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   const int hq = blockIdx.x;
-  if (unit_npool(a.b, hq / a.G, a.W) == 0) {
-    if (threadIdx.x == 0) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t npool = unit_npool(a.b, hq / a.G, a.W);
+  if (npool == 0) {
+    if (t == 0) {
       a.flags[hq] = 1;
       a.stop[hq] = 0;
       a.beta[hq] = 0.0;
@@ -741,7 +944,132 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     return;
   }
   __shared__ FinSmem f;
-  certify_head<true>(a, f, hq);
+  PlaceScratch &ps = f.s.pl;
+  const int J = a.J, J2 = J + 2;
+  const int64_t ntiles = (npool + kBucketTile - 1) / kBucketTile;
+  const bool small = ntiles <= 64;   // the tile rows are kept in LDS
+  // the first eight entries of every tile's level-ordered list, read before it is known
+  // how many of them the first range takes (thread t: tile t >> 2, entries (t & 3) + 4 i)
+  const int sk = t >> 2, se = t & 3;
+  int sp[2] = {0, 0};
+  if (small && sk < ntiles) {
+    const int *lp = a.tilelist + ((int64_t)hq * a.ntiles + sk) * kTileList + se;
+    sp[0] = lp[0];
+    sp[1] = lp[4];
+  }
+  // the certificate's inputs and the rescoring constants travel with the tile sums
+  HeadPre hp;
+  head_issue<true>(a, hq, hp);
+  RescoreConsts rc;
+  rescore_consts_load(a, hq, rc);
+  // level totals over the tiles (lane = level; wavefront wv sums tiles wv, wv + 4, ...):
+  // candidates at levels <= j, C_max keys per level
+  {
+    int cum = 0, cm = 0;
+    if (lane < J2) {
+      const int *th = a.tilehist + (int64_t)hq * a.ntiles * J2 + lane;
+      const int *tc = a.tilecm + (int64_t)hq * a.ntiles * J2 + lane;
+      for (int64_t k0 = wv; k0 < ntiles; k0 += 64) {
+        int u[16], w[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int64_t kk = k0 + 4 * k;
+          u[k] = (kk < ntiles) ? th[kk * J2] : 0;
+          w[k] = (kk < ntiles) ? tc[kk * J2] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          cum += u[k];
+          cm += w[k];
+          if (small && k0 + 4 * k < ntiles) ps.th[k0 + 4 * k][lane] = u[k];
+        }
+      }
+    }
+    ps.sum[wv][lane] = cum;
+    ps.cms[wv][lane] = cm;
+  }
+  head_commit<true>(a, f, hp);
+  __syncthreads();
+  const int cum = ps.sum[0][lane] + ps.sum[1][lane] + ps.sum[2][lane] + ps.sum[3][lane];
+  // the levels that fit form a prefix 0..js (cumulative counts only grow); js = -1 when
+  // level 0 alone exceeds the budget, and the first pass then has no candidates
+  const unsigned long long fit = __ballot(lane <= J && cum <= a.budget);
+  const int js = (int)__popcll(fit) - 1;   // (the count is unsigned)
+  const unsigned long long fit2 = __ballot(lane <= J && cum <= a.budget2);
+  const int js2 = min(J, max(js + 1, (int)__popcll(fit2) - 1));   // at least one level past js
+  const int tot1v = __shfl(cum, max(js, 0), 64), tot2 = __shfl(cum, js2, 64);
+  const int tot1 = (js >= 0) ? tot1v : 0;
+  if (wv == 0) {
+    const int cm = ps.cms[0][lane] + ps.cms[1][lane] + ps.cms[2][lane] + ps.cms[3][lane];
+    const int below = __shfl_up(cum, 1, 64), totJ = __shfl(cum, J, 64);
+    const int64_t hr = (int64_t)hq * J2;
+    if (lane < J2) {
+      a.hist[hr + lane] = cum - (lane > 0 ? below : 0);
+      a.cmhist[hr + lane] = cm;
+      f.cmh[lane] = cm;
+    }
+    if (lane == 0) {
+      a.jspec[hq] = js;
+      a.ccount1[hq] = tot1;
+      a.jspec2[hq] = js2;
+      a.ccount2[hq] = tot2;
+      a.ccount[hq] = totJ;
+    }
+  }
+  const int nstage = (tot1 <= kStage) ? tot1 : 0;
+  bool placed = js < 0;
+  if (!placed && small) {
+    // the first range's count per tile (lane = tile; every wavefront computes all of them)
+    // and the tiles' first list indices; when no tile has more than eight, the entries
+    // read above are the whole range, and a candidate's index is its tile's first index
+    // plus its rank by position among the tile's entries
+    const int c = (lane < ntiles) ? ps.th[lane][js] : 0;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (__ballot(c > 8) == 0ull) {
+      const int ck = __shfl(c, sk, 64), first = __shfl(incl - c, sk, 64);
+      const int lb = lane & ~3;   // the tile's entries: lanes lb .. lb + 3, both registers
+      int r0 = 0, r1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q0 = __shfl(sp[0], lb + j, 64), q1 = __shfl(sp[1], lb + j, 64);
+        if (j < ck) {
+          r0 += (q0 < sp[0]) ? 1 : 0;
+          r1 += (q0 < sp[1]) ? 1 : 0;
+        }
+        if (j + 4 < ck) {
+          r0 += (q1 < sp[0]) ? 1 : 0;
+          r1 += (q1 < sp[1]) ? 1 : 0;
+        }
+      }
+      const int64_t row = (int64_t)hq * a.npool_cap;
+      if (se < ck) {
+        a.candpos[row + first + r0] = sp[0];
+        if (first + r0 < nstage) f.s.pos[first + r0] = sp[0];
+      }
+      if (se + 4 < ck) {
+        a.candpos[row + first + r1] = sp[1];
+        if (first + r1 < nstage) f.s.pos[first + r1] = sp[1];
+      }
+      placed = true;
+    }
+  }
+  if (!placed && !place_first_lists(a, f, hq, npool, js, tot1, nstage))
+    place_range(a, f, hq, npool, -1, js, 0, nstage);
+  // (more than one stage: the rescoring reads the list back from memory)
+  if (tot1 > kStage) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tot1 > kStage) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const bool ok = certify_head<true>(a, f, hq, -1, tot1, js, &rc);
+  if ((!ok && js < J) || a.full_list) {
+    __syncthreads();
+    place_range(a, f, hq, npool, js, js2, tot1, 0);
+    if (js2 < J) place_range(a, f, hq, npool, js2, J, tot2, 0);
+  }
 }
 
 struct ExactSmem {
@@ -937,7 +1265,7 @@ __global__ __launch_bounds__(256) void tail_kernel(CertArgs a) {
             }
             a.o_hat[(int64_t)h * kD + t] = (float)(N / Dn);
           }
-        } else if (!certify_head<false>(a, u.f, h, gsz > 1 ? gsz : 0) && a.pass == a.final_pass) {
+        } else if (!certify_head<false>(a, u.f, h, gsz > 1 ? gsz : 0, -1, 0, nullptr) && a.pass == a.final_pass) {
           __syncthreads();
           exact_chunk(a, u.e, h, 0, head_n(a, h), a.exactp + (int64_t)h * kExactChunks * 130);
           if (t < kD) a.o_hat[(int64_t)h * kD + t] = (float)(u.e.half[t] / u.e.dsum[0]);

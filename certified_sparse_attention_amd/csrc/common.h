@@ -397,9 +397,8 @@ struct Plan {
   int64_t wstride;     // scan wavefronts per KV head at full pool capacity
   // offsets in bytes
   size_t qf, qconst, qA, lt, tau, prefix, sR, cR;     // per-call constants
-  size_t clo, cstar, lbpart, vpart, hist, tilecnt, tileoff, tileoff2, tilehist, tilecm, cmhist, ccount, ccount1,
-      jspec;
-  size_t bdone, exdone, exdone2;  // per-head completion counters (last-workgroup reductions)
+  size_t clo, cstar, lbpart, vpart, hist, tilelist, tilehist, tilecm, cmhist, ccount, ccount1, jspec;
+  size_t exdone, exdone2;  // per-head completion counters (last-workgroup reductions)
   size_t ccount2, jspec2, flags2;
   size_t pbuf, ubuf, lub, live, bmax, win, candpos, rec_s, rec_w, rec_vsq, rec_hl, rec_x;
   size_t partial, betalv, dhatlv, klv, flags, exactp;
@@ -411,6 +410,7 @@ struct Plan {
 enum { QC_BETA = 0, QC_QNP, QC_QABS, QC_CR, QC_QA, QC_QN, QC_PILOT, kQc = 8 };
 
 constexpr int kBucketTile = 2048;   // positions per bucket tile (64 bitmap words)
+constexpr int kTileList = 64;       // positions per tile listed in level order (the tile's lowest levels)
 constexpr int kDefaultBudget = 32;   // candidates rescored before the first certificate pass
 constexpr int kExactChunks = 8;                    // tail: workgroups (exact chunks) per query head
 constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 for gfx9-family raw loads

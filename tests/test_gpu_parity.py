@@ -213,6 +213,25 @@ def _compare_samples(hq, trn, t, stop, J):
         np.testing.assert_array_equal(np.sort(rpos[gh <= j]), t["cand"][t["h"] <= j], err_msg=f"B_{j} of {hq}")
 
 
+def _check_list_order(trn, H_q, J, budget=0, budget2=0):
+    """The candidate list is the first range (l^ub <= j1), then the second (j1 < l^ub <= j2),
+    then the third (j2 < l^ub <= J), each in position order, where j1 is the deepest level
+    whose cumulative bucket count fits the first budget (32 unless given, at most 2048) and
+    j2 > j1 the deepest one within the second (no limit unless given)."""
+    b1 = min(budget, 2048) if budget > 0 else 32
+    b2 = budget2 if budget2 > 0 else np.iinfo(np.int64).max
+    for hq in range(H_q):
+        cum = np.cumsum(trn["bucket_count"][hq][:J + 1])
+        j1 = int(np.sum(cum <= b1)) - 1
+        j2 = min(J, max(j1 + 1, int(np.sum(cum <= b2)) - 1))
+        npool = trn["lub"].shape[1]
+        lub = trn["lub"][hq, :npool].astype(np.int64)
+        at = np.arange(npool)
+        want = np.concatenate([at[lub <= j1], at[(lub > j1) & (lub <= j2)], at[(lub > j2) & (lub <= J)]])
+        cc = int(trn["cand_count"][hq])
+        np.testing.assert_array_equal(trn["cand_pos"][hq, :cc], want, err_msg=f"candidate list of {hq}")
+
+
 def _kw(w, **over):
     kw = dict(eps=w.eps, delta=w.delta, r=w.r, J=w.J, window=w.window, seed=w.seed, step=w.step,
               layer=w.layer)
@@ -227,6 +246,8 @@ def test_certified_decode_parity(case):
                                             trace=True, **kw)
     torch.cuda.synchronize()
     _compare_decode(w, case["pk_ref"], out[:4], out[4], **kw)
+    trn = {k: v.cpu().numpy() for k, v in out[4].items()}
+    _check_list_order(trn, w.H_q, w.J)
     lt = out[4]["logtau"].cpu().numpy()
     np.testing.assert_array_equal(lt, oracle.logtau(w.r, w.J))
 
@@ -330,6 +351,39 @@ def test_level_zero_over_the_budget():
     assert max(level0) > 2048, level0
 
 
+@pytest.mark.parametrize("cluster,budget,crowd", [(40, 64, 8), (120, 200, 64)])
+def test_clustered_first_range(cluster, budget, crowd):
+    """A run of strong keys inside one bucket tile puts more of the first range in that tile
+    than the entries the certificate kernel reads ahead per tile (40 keys), or than a
+    tile's level-ordered list holds (120 keys): the list, its order and every result stay
+    oracle-exact."""
+    rng = np.random.default_rng(91)
+    q32, q, K, V = synth.recipe_layer(rng, 1, 4, 12288, heavy_frac=0.0)
+    qbar = q.astype(np.float64).mean(axis=0)
+    dirv = np.sqrt(128.0) * qbar / float(qbar @ qbar)
+    K = K.astype(np.float32)
+    K[0, 3000:3000 + cluster] += (10.0 * dirv).astype(np.float32)
+    K = K.astype(np.float16)
+    w = pad_cache(synth.Workload("cluster12k", q, K, V, 12288, 4, window=64, r=2, J=30, eps=0.1, delta=0.01))
+    pk_ref = oracle.pack_kv_4bit(w.K, w.V, w.n_cap // 32)
+    qg, Kg, Vg = _to(w.q), _to(w.K), _to(w.V)
+    packed = _csa().pack_kv_4bit(Kg, Vg)
+    kw = _kw(w)
+    out = _csa().certified_decode_attention(qg, Kg, Vg, packed, w.n, trace=True, cand_budget=budget, **kw)
+    torch.cuda.synchronize()
+    _compare_decode(w, pk_ref, out[:4], out[4], **kw)
+    trn = {k: v.cpu().numpy() for k, v in out[4].items()}
+    _check_list_order(trn, w.H_q, w.J, budget)
+    # the first range does crowd one tile
+    most = 0
+    for hq in range(w.H_q):
+        cum = np.cumsum(trn["bucket_count"][hq][:w.J + 1])
+        tot1 = int(cum[int(np.sum(cum <= budget)) - 1]) if cum[0] <= budget else 0
+        if tot1:
+            most = max(most, int(np.bincount(trn["cand_pos"][hq, :tot1] // 2048).max()))
+    assert most > crowd, most
+
+
 def test_stream_read_checksum():
     """The read helper visits every 32-bit word once: per-workgroup XORs match the host's."""
     rng = np.random.default_rng(5)
@@ -354,3 +408,4 @@ def test_speculative_budget_does_not_change_results(case, budget, budget2):
                                             trace=True, cand_budget=budget, cand_budget2=budget2, **kw)
     torch.cuda.synchronize()
     _compare_decode(w, case["pk_ref"], out[:4], out[4], **kw)
+    _check_list_order({k: v.cpu().numpy() for k, v in out[4].items()}, w.H_q, w.J, budget, budget2)
