@@ -445,9 +445,11 @@ __device__ inline int record_split(const CertArgs &a, int hq, int count) {
 }
 
 // Root of kl(x, mu) = mu - x + x ln(x / mu) = L above x: Newton from above on the convex
-// increasing branch, stopped when a step no longer decreases mu or moves it by at most
-// 2^-44 of itself (every iterate stays above the root, so the bound stays valid).  The
-// step is mu - f mu / (mu - x) with f = (mu - x) + x (ln x - ln mu) - L.
+// increasing branch (every iterate stays above the root, so the bound is valid wherever
+// it stops).  It stops when a step no longer decreases mu, or after a step that moved mu
+// by at most 2^-26 of itself: Newton's relative error after such a step is about
+// x / (2 (mu - x)) times its square, far below the 1e-4 the certificate is compared to.
+// The step is mu - f mu / (mu - x) with f = (mu - x) + x (ln x - ln mu) - L.
 __device__ inline double kl_upper(double x, double L) {
   if (!(x > 0.0)) return L;
   const double lx = log(x);
@@ -456,7 +458,7 @@ __device__ inline double kl_upper(double x, double L) {
     const double f = (mu - x) + x * (lx - log(mu)) - L;
     const double nx = mu - f * mu / (mu - x);
     if (!(nx < mu)) break;
-    const bool small = mu - nx <= 0x1p-44 * mu;   // converged: the iterate stays above the root
+    const bool small = mu - nx <= 0x1p-26 * mu;   // converged: the iterate stays above the root
     mu = nx;
     if (small) break;
   }
@@ -472,7 +474,7 @@ __device__ inline double kl_lower(double x, double L) {
     const double f = (mu - x) + x * (lx - log(mu)) - L;
     const double nx = mu - f * mu / (mu - x);
     if (!(nx > mu) || !(nx < x)) break;
-    const bool small = nx - mu <= 0x1p-44 * mu;   // converged: the iterate stays below the root
+    const bool small = nx - mu <= 0x1p-26 * mu;   // converged: the iterate stays below the root
     mu = nx;
     if (small) break;
   }
@@ -887,6 +889,12 @@ __device__ void place_range(const CertArgs &a, FinSmem &f, int hq, int64_t npool
   }
 }
 
+// Lane L of the caller's quad of lanes (a DPP quad broadcast).
+template <int L>
+__device__ __forceinline__ int quad_lane(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x55 * L, 0xF, 0xF, false);
+}
+
 // Pass 1's first range (l^ub <= js, tot1 candidates) from the tiles' level-ordered lists:
 // tile k holds the range's keys in its first tilehist[k][js] list entries, so each
 // candidate is one read; the list is then put in position order by ranking in LDS.
@@ -997,11 +1005,12 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   const int js = (int)__popcll(fit) - 1;   // (the count is unsigned)
   const unsigned long long fit2 = __ballot(lane <= J && cum <= a.budget2);
   const int js2 = min(J, max(js + 1, (int)__popcll(fit2) - 1));   // at least one level past js
-  const int tot1v = __shfl(cum, max(js, 0), 64), tot2 = __shfl(cum, js2, 64);
+  // (js, js2 and J are the same in every lane: lane reads, not shuffles)
+  const int tot1v = __builtin_amdgcn_readlane(cum, max(js, 0)), tot2 = __builtin_amdgcn_readlane(cum, js2);
   const int tot1 = (js >= 0) ? tot1v : 0;
   if (wv == 0) {
     const int cm = ps.cms[0][lane] + ps.cms[1][lane] + ps.cms[2][lane] + ps.cms[3][lane];
-    const int below = __shfl_up(cum, 1, 64), totJ = __shfl(cum, J, 64);
+    const int below = __shfl_up(cum, 1, 64), totJ = __builtin_amdgcn_readlane(cum, J);
     const int64_t hr = (int64_t)hq * J2;
     if (lane < J2) {
       a.hist[hr + lane] = cum - (lane > 0 ? below : 0);
@@ -1032,11 +1041,13 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     }
     if (__ballot(c > 8) == 0ull) {
       const int ck = __shfl(c, sk, 64), first = __shfl(incl - c, sk, 64);
-      const int lb = lane & ~3;   // the tile's entries: lanes lb .. lb + 3, both registers
+      // the tile's entries are in the lane's quad (lanes 4 (lane / 4) + j), both registers
+      const int e0[4] = {quad_lane<0>(sp[0]), quad_lane<1>(sp[0]), quad_lane<2>(sp[0]), quad_lane<3>(sp[0])};
+      const int e1[4] = {quad_lane<0>(sp[1]), quad_lane<1>(sp[1]), quad_lane<2>(sp[1]), quad_lane<3>(sp[1])};
       int r0 = 0, r1 = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int q0 = __shfl(sp[0], lb + j, 64), q1 = __shfl(sp[1], lb + j, 64);
+        const int q0 = e0[j], q1 = e1[j];
         if (j < ck) {
           r0 += (q0 < sp[0]) ? 1 : 0;
           r1 += (q0 < sp[1]) ? 1 : 0;
