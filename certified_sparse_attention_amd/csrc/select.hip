@@ -59,11 +59,11 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   const double cs = dec_max(cs_enc);
   const double clo = dec_max(clo_enc);
   const double inv_l1 = (a.J >= 1) ? 1.0 / ltp[1].y : 0.0;
-  // the word gives the dead count and the bits the lanes read below through shuffles
+  // the word's bits are read by the lanes below through shuffles; the keys that are not
+  // live count at level J + 1 only through the tile's total (no per-lane atomics)
   const int valid = (int)max<int64_t>(0, min<int64_t>(32, npool - p_tile - 32 * lane));
   const uint32_t word = rawword & ((valid == 32) ? 0xFFFFFFFFu : ((1u << valid) - 1u));
-  const int dead = valid - __popc(word);
-  if (dead) atomicAdd(&hist[a.J + 1], dead);
+  const int tile_keys = (int)max<int64_t>(0, min<int64_t>(kBucketTile, npool - p_tile));
   // positions p_tile + 64 k + lane, k = 0..31: lane reads bit (lane & 31) of tile word
   // 2k + (lane >> 5), so every load and store of a round covers 64 consecutive keys
   const bool any = __ballot(word != 0u) != 0ull;
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  // inclusive prefix over levels (lane = level)
+  // inclusive prefix over levels of the live keys (lane = level); at J + 1 the count is
+  // every pool key of the tile
   if (lane < a.J + 2) {
     int c = hist[lane];
 #pragma unroll
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
       const int y = __shfl_up(c, off, 64);
       if (lane >= off) c += y;
     }
-    a.tilehist[((int64_t)hq * a.ntiles + tile) * (a.J + 2) + lane] = c;
+    a.tilehist[((int64_t)hq * a.ntiles + tile) * (a.J + 2) + lane] = (lane == a.J + 1) ? tile_keys : c;
     a.tilecm[((int64_t)hq * a.ntiles + tile) * (a.J + 2) + lane] = cmh[lane];
     slot[lane] = c - hist[lane];   // first list index of the level
   }
