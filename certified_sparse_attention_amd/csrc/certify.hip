@@ -531,7 +531,7 @@ struct HeadPre {
   double win;             // thread t < kD + 2: window sum t (relative to c_R)
   double cr;
   unsigned long long cs;  // c* (encoded)
-  unsigned vp;            // wavefront 3: its lanes' V_max bits
+  unsigned vp0, vp1;      // wavefront 3: its lanes' V_max bits (two entries each)
   int cmh;                // thread t <= J + 1: C_max keys at level t (not in pass 1)
 };
 template <bool kFirst>
@@ -545,15 +545,21 @@ __device__ __forceinline__ void head_issue(const CertArgs &a, int hq, HeadPre &p
   p.cr = a.qconst[(int64_t)hq * kQc + QC_CR];
   p.cs = a.cstar[hq];
   p.cmh = (!kFirst && t <= J + 1) ? a.cmhist[(int64_t)hq * (J + 2) + t] : 0;
-  p.vp = 0u;
+  p.vp0 = p.vp1 = 0u;
   if (wv == 3) {
+    // (entries past the unit's wavefronts are read within the row and not used; the two
+    // loads are only combined at head_commit, so nothing waits for them here)
     const int64_t np = unit_npool(a.b, h, a.W);
     const int64_t wph = ((np + kBlk - 1) / kBlk + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
     const unsigned *vp = a.vpart + (int64_t)h * a.wstride;
-    const unsigned v0 = (lane < wph) ? vp[lane] : 0u, v1 = (lane + 64 < wph) ? vp[lane + 64] : 0u;
-    unsigned v = max(v0, v1);
-    for (int64_t k = lane + 128; k < wph; k += 64) v = max(v, vp[k]);
-    p.vp = v;
+    const unsigned v0 = vp[min<int64_t>(lane, a.wstride - 1)], v1 = vp[min<int64_t>(lane + 64, a.wstride - 1)];
+    p.vp0 = (lane < wph) ? v0 : 0u;
+    p.vp1 = (lane + 64 < wph) ? v1 : 0u;
+    if (wph > 128) {
+      unsigned v = 0u;
+      for (int64_t k = lane + 128; k < wph; k += 64) v = max(v, vp[k]);
+      p.vp0 = max(p.vp0, v);
+    }
   }
 }
 template <bool kFirst>
@@ -563,7 +569,7 @@ __device__ __forceinline__ void head_commit(const CertArgs &a, FinSmem &f, const
   if (t <= J + 1) f.s.ltp[t] = make_double2(p.ltx, p.lty);
   if (!kFirst && t <= J + 1) f.cmh[t] = p.cmh;
   if (wv == 3) {
-    unsigned v = p.vp;
+    unsigned v = max(p.vp0, p.vp1);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
     if (lane == 0) f.vmax = h2d((uint16_t)v);

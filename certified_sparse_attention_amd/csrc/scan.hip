@@ -954,7 +954,7 @@ struct RefineSlot {
 
 __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   // wave slots of kBlocksPerWave blocks, interleaved over the KV heads: global slot s is
   // local slot s / H_kv of head s % H_kv, so one head's slots fall to different
   // workgroups and a head with many passing blocks shares them with the others' waves
@@ -966,7 +966,6 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   const int64_t gs = (int64_t)blockIdx.x * 4 + wv;
   const int h = slot_head(wv);
   const int64_t blk0 = slot_blk0(wv);
-  const int nblk = (gs < nslots) ? (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, unit_blocks(h) - blk0)) : 0;
   const int G = a.G;
   const int n16 = lane & 15, grp = lane >> 4;
 
@@ -991,10 +990,11 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
   // wavefronts' LB bounds (the first 128 wavefronts' of every query at once; a longer
   // pool adds a loop)
   // (block maxima at clamped positions, used below only for the slot's own blocks)
+  // (read unconditionally at clamped rows, so that no load waits at a branch's end; the
+  // rows of query slots past G are not used)
   const int64_t bcol = min<int64_t>(blk0 + n16, a.nbw - 1);
-  float2 mxA = make_float2(0.0f, 0.0f), mxB = make_float2(0.0f, 0.0f);
-  if (hasA) mxA = a.bmax[(int64_t)(hq0 + gA) * a.nbw + bcol];
-  if (hasB) mxB = a.bmax[(int64_t)(hq0 + gB) * a.nbw + bcol];
+  const float2 mxA = a.bmax[(int64_t)(hq0 + min(gA, G - 1)) * a.nbw + bcol];
+  const float2 mxB = a.bmax[(int64_t)(hq0 + min(gB, G - 1)) * a.nbw + bcol];
   const double ltJ = a.lt[a.J];
   float qv[kMaxG][2];
 #pragma unroll
@@ -1002,15 +1002,13 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     qv[g][0] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane] : 0.0f;
     qv[g][1] = (g < G) ? a.qf[(int64_t)(hq0 + g) * kD + 2 * lane + 1] : 0.0f;
   }
-  unsigned long long clo_enc = 0ull;
-  double pilot = 0.0, qnp = 0.0, qa = 0.0;
-  if (lane < G) {
-    const double *qc = a.qconst + (int64_t)(hq0 + lane) * kQc;
-    clo_enc = __hip_atomic_load(a.clo + hq0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pilot = qc[QC_PILOT];
-    qnp = qc[QC_QNP];
-    qa = qc[QC_QA];
-  }
+  // (lane g < G takes query g; the other lanes read query G - 1's and drop the values)
+  const int gq = min(lane, G - 1);
+  const double *qc = a.qconst + (int64_t)(hq0 + gq) * kQc;
+  const unsigned long long clo_r = __hip_atomic_load(a.clo + hq0 + gq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const double pilot_r = qc[QC_PILOT], qnp_r = qc[QC_QNP], qa_r = qc[QC_QA];
+  const unsigned long long clo_enc = (lane < G) ? clo_r : 0ull;
+  const double pilot = (lane < G) ? pilot_r : 0.0, qnp = (lane < G) ? qnp_r : 0.0, qa = (lane < G) ? qa_r : 0.0;
   const uint64_t prefix0 = a.prefix[h];
   const int64_t swph = (unit_blocks(h) + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
   float lbs[kMaxG][2];
@@ -1039,6 +1037,8 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     for (int64_t k = lane + 128; k < swph; k += 64) v = fmaxf(v, a.lbpart[(int64_t)(hq0 + g) * a.wstride + k]);
     lbs[g][0] = wave_max_f32(v);
   }
+  // the slot's blocks (counted once the loads above are under way)
+  const int nblk = (gs < nslots) ? (int)max<int64_t>(0, min<int64_t>(kBlocksPerWave, unit_blocks(h) - blk0)) : 0;
   // largest |q_t| over the group (lanes 0..7 hold the queries' values, 0 past G)
   float qm = (float)qa;
 #pragma unroll
