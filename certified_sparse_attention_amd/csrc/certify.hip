@@ -146,7 +146,7 @@ struct AccSmem {
 // candidates' terms in candidate order with LDS atomics that return nothing, so no cell
 // is shared between threads and nothing waits on the sums.
 // V rows are fetched here unless `staged`.
-__device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int64_t h, int cnt, bool staged) {
+__device__ __forceinline__ void accumulate_stage(const CertArgs &a, AccSmem &s, int64_t h, int cnt, bool staged) {
   const int t = threadIdx.x, J = a.J;
   if (!staged) {
     // V rows of candidates that enter the sample at some level <= J
@@ -217,7 +217,7 @@ __device__ void accumulate_stage(const CertArgs &a, AccSmem &s, int64_t h, int c
 }
 
 // Add candidates [i0, i1) of query head hq from their stored records.
-__device__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+__device__ __forceinline__ void accumulate_range(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
   const int t = threadIdx.x;
   const int64_t h = head_kv(a, hq);
   const int64_t base = (int64_t)hq * a.npool_cap;
@@ -267,7 +267,7 @@ __device__ __forceinline__ void stage_positions(const int *pos, StagePre &p) {
   p.pos_t = pos[min(t, kStage - 1)];
 }
 
-template <bool kSpec>
+template <bool kSpec, int kSteps = 2>
 __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int hq, int c0, int cnt,
                                               const RescoreConsts &rc, int zero_rows = 0,
                                               bool use_pre = false, StagePre pre = StagePre{}) {
@@ -282,37 +282,40 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     __syncthreads();
   }
   // step k takes keys 32 k .. 32 k + 31, wavefront wv eight of them (eight lanes per key), so a
-  // stage of at most 32 keys is one step of every wavefront
+  // stage of at most 32 keys is one step of every wavefront (kSteps = 1: cnt <= 32).  Every
+  // load is issued before any is used (slots past cnt read position 0 and drop the values),
+  // and the lane's perturbation is formed while they travel.
   uint4 cw8[2], kw[2][2], vw[2][2];
   float sc8[2];
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
+    if (step >= kSteps) {
+      cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
+      sc8[step] = 0.0f;
+      continue;
+    }
     const int r = 32 * step + 8 * wv + s8;
-    cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
-    sc8[step] = 0.0f;
-    if (r < cnt) {
-      const int64_t tok = h * a.n_cap + (use_pre ? pre.pos_r[step] : s.pos[r]);
-      cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
-      sc8[step] = a.scale8[tok];
-      if (kSpec) {
-        const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
-        const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
-        kw[step][0] = ksrc[0];
-        kw[step][1] = ksrc[1];
-        vw[step][0] = vsrc[0];
-        vw[step][1] = vsrc[1];
-      }
+    const int pr = (r < cnt) ? (use_pre ? pre.pos_r[step] : s.pos[r]) : 0;
+    const int64_t tok = h * a.n_cap + pr;
+    cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
+    sc8[step] = a.scale8[tok];
+    kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
+    if (kSpec) {
+      const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
+      const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
+      kw[step][0] = ksrc[0];
+      kw[step][1] = ksrc[1];
+      vw[step][0] = vsrc[0];
+      vw[step][1] = vsrc[1];
     }
   }
   // one lane per key: its perturbation, UB and 8-bit record
-  double E = 0.0, ubt = 0.0, ke8 = 0.0, s8t = 0.0;
-  if (t < cnt) {
-    const int pos = use_pre ? pre.pos_t : s.pos[t];
-    ubt = a.ubuf[base + pos];
-    ke8 = h2d(a.kerr8[h * a.n_cap + pos]);
-    s8t = (double)a.scale8[h * a.n_cap + pos];
-    E = perturbation(rc.prefix, pos);
-  }
+  const int post = (t < cnt) ? (use_pre ? pre.pos_t : s.pos[t]) : 0;
+  const double ubt = a.ubuf[base + post];
+  const uint16_t ke8_raw = a.kerr8[h * a.n_cap + post];
+  const float s8t_raw = a.scale8[h * a.n_cap + post];
+  double E = 0.0;
+  if (t < cnt) E = perturbation(rc.prefix, post);
   for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
@@ -330,6 +333,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
   }
   __syncthreads();
   if (t < cnt) {
+    const double ke8 = h2d(ke8_raw), s8t = (double)s8t_raw;
     const double slack8 = (rc.qnp * ke8) + (kPadF * ((128.0 * s8t) * rc.qabs));
     const double ub8 = (s.w[t] + slack8) * kRsqrtD;
     const int l8 = level_of_pairs((fmin(ubt, ub8) + E) - rc.cs, s.ltp, a.J, rc.inv_l1);
@@ -414,7 +418,7 @@ __device__ __forceinline__ void rescore_consts(const CertArgs &a, const AccSmem 
 
 // Exact rescoring of candidates [i0, i1) of query head hq inside the certificate
 // workgroup, stage by stage, each stage added into the level increments s.acc.
-__device__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
+__device__ __forceinline__ void rescore_accumulate(const CertArgs &a, AccSmem &s, int hq, int i0, int i1) {
   __syncthreads();              // the level table s.ltp is filled
   RescoreConsts rc;
   rescore_consts(a, s, hq, rc);
@@ -432,7 +436,7 @@ __device__ inline void zero_acc(AccSmem &s, int J1) {
 
 // Candidates [i0, i1): those below `split` from their stored records, the rest rescored
 // here (records stored), in index order.
-__device__ void accumulate_mixed(const CertArgs &a, AccSmem &s, int hq, int i0, int i1, int split) {
+__device__ __forceinline__ void accumulate_mixed(const CertArgs &a, AccSmem &s, int hq, int i0, int i1, int split) {
   if (i0 < split) accumulate_range(a, s, hq, i0, min(i1, split));
   if (i1 > split) rescore_accumulate(a, s, hq, max(i0, split), i1);
 }
@@ -592,7 +596,7 @@ __device__ __forceinline__ void head_commit(const CertArgs &a, FinSmem &f, const
 // LDS, the rescoring constants (*rc0) and, when the candidates fit one stage, their
 // positions in s.pos.
 template <bool kFirst>
-__device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts, int pcount,
+__device__ __forceinline__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts, int pcount,
                              int pjmax, const RescoreConsts *rc0) {
   const int t = threadIdx.x, h = hq / a.G;
   const int lane = t & 63, wv = t >> 6;
@@ -624,7 +628,8 @@ __device__ bool certify_head(const CertArgs &a, FinSmem &f, int hq, int nparts, 
     __syncthreads();            // the level table s.ltp is filled
     if (spec) rc.inv_l1 = (a.J >= 1) ? 1.0 / s.ltp[1].y : 0.0;
     else rescore_consts(a, s, hq, rc);
-    rescore_stage<true>(a, s, hq, 0, count, rc, jmax + 1, spec, pre);
+    if (count <= 32) rescore_stage<true, 1>(a, s, hq, 0, count, rc, jmax + 1, spec, pre);
+    else rescore_stage<true, 2>(a, s, hq, 0, count, rc, jmax + 1, spec, pre);
     accumulate_stage(a, s, head_kv(a, hq), count, true);
   } else if (nseg == 0) {
     zero_acc(s, jmax + 1);      // rows above jmax may receive increments but are never read
@@ -834,7 +839,7 @@ __device__ __forceinline__ void wg_excl_scan(int *v, int (*ws)[4], int *tot) {
 // is a prefix over tiles, and a wavefront places one tile at a time (lane = bitmap word;
 // the levels of its live keys from the l^ub bytes).  Indices below nstage also go into the
 // stage's positions s.pos.  Ends with the workgroup in step.
-__device__ void place_range(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int lo, int hi, int base,
+__device__ __forceinline__ void place_range(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int lo, int hi, int base,
                             int nstage) {
   AccSmem &s = f.s;
   PlaceScratch &ps = s.pl;
@@ -906,7 +911,7 @@ __device__ __forceinline__ int quad_lane(int x) {
 // candidate is one read; the list is then put in position order by ranking in LDS.
 // Returns false, having written nothing, when the range has more candidates than threads
 // or a tile holds more of them than its list; uniform across the workgroup.
-__device__ bool place_first_lists(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int js, int tot1,
+__device__ __forceinline__ bool place_first_lists(const CertArgs &a, FinSmem &f, int hq, int64_t npool, int js, int tot1,
                                   int nstage) {
   AccSmem &s = f.s;
   PlaceScratch &ps = s.pl;
@@ -1099,7 +1104,7 @@ struct ExactSmem {
 // Exact attention sums over keys [i0, i1) of query head hq relative to c*: N[c] (out[c])
 // and D (out[kD]), 256 threads.  Keys in batches of 256: one key per thread for its score
 // and weight, then two halves of the batch over the 128 channels.
-__device__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0, int64_t i1, double *out) {
+__device__ __forceinline__ void exact_chunk(const CertArgs &a, ExactSmem &e, int hq, int64_t i0, int64_t i1, double *out) {
   const int t = threadIdx.x, c = t & (kD - 1), hf = t >> 7;
   const int64_t h = head_kv(a, hq);
   if (t < kD) e.qd[t] = (double)a.qf[(int64_t)hq * kD + t];
