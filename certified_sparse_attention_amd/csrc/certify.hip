@@ -535,7 +535,8 @@ struct HeadPre {
   double win;             // thread t < kD + 2: window sum t (relative to c_R)
   double cr;
   unsigned long long cs;  // c* (encoded)
-  unsigned vp0, vp1;      // wavefront 3: its lanes' V_max bits (two entries each)
+  unsigned vp0, vp1, vp2;  // wavefront 3: its lanes' V_max bits (entries lane, lane + 64, the rest)
+  int vpn;                 // wavefront 3: how many of the first 128 entries exist
   int cmh;                // thread t <= J + 1: C_max keys at level t (not in pass 1)
 };
 template <bool kFirst>
@@ -549,20 +550,21 @@ __device__ __forceinline__ void head_issue(const CertArgs &a, int hq, HeadPre &p
   p.cr = a.qconst[(int64_t)hq * kQc + QC_CR];
   p.cs = a.cstar[hq];
   p.cmh = (!kFirst && t <= J + 1) ? a.cmhist[(int64_t)hq * (J + 2) + t] : 0;
-  p.vp0 = p.vp1 = 0u;
+  p.vp0 = p.vp1 = p.vp2 = 0u;
+  p.vpn = 0;
   if (wv == 3) {
     // (entries past the unit's wavefronts are read within the row and not used; the two
     // loads are only combined at head_commit, so nothing waits for them here)
     const int64_t np = unit_npool(a.b, h, a.W);
     const int64_t wph = ((np + kBlk - 1) / kBlk + kScanBlocks - 1) / kScanBlocks;   // the unit's scan wavefronts
     const unsigned *vp = a.vpart + (int64_t)h * a.wstride;
-    const unsigned v0 = vp[min<int64_t>(lane, a.wstride - 1)], v1 = vp[min<int64_t>(lane + 64, a.wstride - 1)];
-    p.vp0 = (lane < wph) ? v0 : 0u;
-    p.vp1 = (lane + 64 < wph) ? v1 : 0u;
-    if (wph > 128) {
+    p.vp0 = vp[min<int64_t>(lane, a.wstride - 1)];
+    p.vp1 = vp[min<int64_t>(lane + 64, a.wstride - 1)];
+    p.vpn = (int)min<int64_t>(wph, 128);
+    if (wph > 128) {   // (a separate value: no wait for the two loads above at this branch)
       unsigned v = 0u;
       for (int64_t k = lane + 128; k < wph; k += 64) v = max(v, vp[k]);
-      p.vp0 = max(p.vp0, v);
+      p.vp2 = v;
     }
   }
 }
@@ -573,7 +575,7 @@ __device__ __forceinline__ void head_commit(const CertArgs &a, FinSmem &f, const
   if (t <= J + 1) f.s.ltp[t] = make_double2(p.ltx, p.lty);
   if (!kFirst && t <= J + 1) f.cmh[t] = p.cmh;
   if (wv == 3) {
-    unsigned v = max(p.vp0, p.vp1);
+    unsigned v = max(max(lane < p.vpn ? p.vp0 : 0u, lane + 64 < p.vpn ? p.vp1 : 0u), p.vp2);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
     if (lane == 0) f.vmax = h2d((uint16_t)v);
@@ -984,11 +986,13 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   // level totals over the tiles (lane = level; wavefront wv sums tiles wv, wv + 4, ...):
   // candidates at levels <= j, C_max keys per level
   {
+    // (at most 64 tiles: one straight block of loads, no loop whose header would wait for
+    // every load issued before it)
     int cum = 0, cm = 0;
     if (lane < J2) {
       const int *th = a.tilehist + (int64_t)hq * a.ntiles * J2 + lane;
       const int *tc = a.tilecm + (int64_t)hq * a.ntiles * J2 + lane;
-      for (int64_t k0 = wv; k0 < ntiles; k0 += 64) {
+      auto sum16 = [&](int64_t k0, bool keep) __attribute__((always_inline)) {
         int u[16], w[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -1000,8 +1004,13 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
         for (int k = 0; k < 16; ++k) {
           cum += u[k];
           cm += w[k];
-          if (small && k0 + 4 * k < ntiles) ps.th[k0 + 4 * k][lane] = u[k];
+          if (keep && k0 + 4 * k < ntiles) ps.th[k0 + 4 * k][lane] = u[k];
         }
+      };
+      if (small) {
+        sum16(wv, true);
+      } else {
+        for (int64_t k0 = wv; k0 < ntiles; k0 += 64) sum16(k0, false);
       }
     }
     ps.sum[wv][lane] = cum;
