@@ -703,8 +703,10 @@ int csa_stream_read(const void *buf, int64_t bytes, int workgroups, uint32_t *si
 int csa_event_create(void **event) {
   if (!event) return fail(CSA_ERR_INVALID_ARGUMENT, "event is null");
   hipEvent_t ev;
-  hipError_t e = hipEventCreate(&ev);
-  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  // timing only: no system-scope fence when the event is recorded, so recording it does not
+  // write back and invalidate the caches under the kernels that follow
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   *event = ev;
   return CSA_OK;
 }

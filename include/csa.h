@@ -315,7 +315,9 @@ const char *csa_last_error(void);
 int csa_stream_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *ev_begin,
                     void *ev_end, void *stream);
 
-/* Event helpers for timing on the caller's stream (host side; events are hipEvent_t). */
+/* Event helpers for timing on the caller's stream (host side; events are hipEvent_t).  The
+ * events are for timing only: they are created without the system-scope fence at record
+ * time (hipEventDisableSystemFence), so synchronize the device before reading a time. */
 int csa_event_create(void **event);
 int csa_event_destroy(void *event);
 int csa_event_elapsed_ms(void *begin, void *end, float *ms);
