@@ -972,9 +972,10 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
   // the first eight entries of every tile's level-ordered list, read before it is known
   // how many of them the first range takes (thread t: tile t >> 2, entries (t & 3) + 4 i)
   const int sk = t >> 2, se = t & 3;
+  // (tiles past the head's read its last tile's entries, which no candidate takes)
   int sp[2] = {0, 0};
-  if (small && sk < ntiles) {
-    const int *lp = a.tilelist + ((int64_t)hq * a.ntiles + sk) * kTileList + se;
+  if (small) {
+    const int *lp = a.tilelist + ((int64_t)hq * a.ntiles + min<int64_t>(sk, ntiles - 1)) * kTileList + se;
     sp[0] = lp[0];
     sp[1] = lp[4];
   }
@@ -992,19 +993,23 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     if (lane < J2) {
       const int *th = a.tilehist + (int64_t)hq * a.ntiles * J2 + lane;
       const int *tc = a.tilecm + (int64_t)hq * a.ntiles * J2 + lane;
+      // (rows past the head's tiles are read at its last tile and counted as 0: loads and
+      // LDS writes without branches; ps.th rows past ntiles are not read)
       auto sum16 = [&](int64_t k0, bool keep) __attribute__((always_inline)) {
         int u[16], w[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const int64_t kk = k0 + 4 * k;
-          u[k] = (kk < ntiles) ? th[kk * J2] : 0;
-          w[k] = (kk < ntiles) ? tc[kk * J2] : 0;
+          const int64_t kk = min<int64_t>(k0 + 4 * k, ntiles - 1);
+          u[k] = th[kk * J2];
+          w[k] = tc[kk * J2];
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
+          const bool in = k0 + 4 * k < ntiles;
+          u[k] = in ? u[k] : 0;
           cum += u[k];
-          cm += w[k];
-          if (keep && k0 + 4 * k < ntiles) ps.th[k0 + 4 * k][lane] = u[k];
+          cm += in ? w[k] : 0;
+          if (keep) ps.th[k0 + 4 * k][lane] = u[k];
         }
       };
       if (small) {
