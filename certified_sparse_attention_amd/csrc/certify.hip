@@ -256,6 +256,23 @@ struct RescoreConsts {
 // Candidate positions of the first stage (placed in LDS by pass 1): the rows of the lane's
 // two steps (32 step + 8 wv + lane / 8) and thread t's key.  Entries past the count are
 // read but never used.
+// One DPP move of a double (both halves; lanes without a source get 0).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+// The same sum as r1_combine8, ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) over the
+// eight lanes of an item, but only in the item's first lane (lane 8 i): two quad
+// exchanges and a shift by four lanes within the row, no LDS round trips.
+__device__ __forceinline__ double r1_combine8_first(double p) {
+  p = p + dpp_f64<0xB1>(p);    // quad_perm(1, 0, 3, 2): lane ^ 1
+  p = p + dpp_f64<0x4E>(p);    // quad_perm(2, 3, 0, 1): lane ^ 2
+  return p + dpp_f64<0x104>(p);   // row_shl:4: lane + 4 (the item's second half)
+}
+
 struct StagePre {
   int pos_r[2];
   int pos_t;
@@ -328,7 +345,7 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
 #pragma unroll
       for (int i = 1; i < 16; ++i) p = p + rc.q16[i] * (sc * (double)(int8_t)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu));
     }
-    const double S8 = r1_combine8(p);
+    const double S8 = r1_combine8_first(p);
     if (r < cnt && k8 == 0) s.w[r] = S8;
   }
   __syncthreads();
@@ -367,8 +384,8 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
       vdst[1] = vw[step][1];
       v = sumsq_words(vw[step][0], vw[step][1]);
     }
-    const double sc = r1_combine8(p) * kRsqrtD;
-    const double vs = r1_combine8(v);
+    const double sc = r1_combine8_first(p) * kRsqrtD;
+    const double vs = r1_combine8_first(v);
     if (ex && k8 == 0) {
       s.w[r] = sc;       // the score for now; the weight below
       s.vsq[r] = vs;
@@ -902,6 +919,18 @@ __device__ __forceinline__ void place_range(const CertArgs &a, FinSmem &f, int h
   }
 }
 
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves (shifts within rows of
+// 16, then the row broadcasts of lanes 15 and 31), no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Lane L of the caller's quad of lanes (a DPP quad broadcast).
 template <int L>
 __device__ __forceinline__ int quad_lane(int x) {
@@ -1058,12 +1087,7 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
     // read above are the whole range, and a candidate's index is its tile's first index
     // plus its rank by position among the tile's entries
     const int c = (lane < ntiles) ? ps.th[lane][js] : 0;
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_incl_scan(c);
     if (__ballot(c > 8) == 0ull) {
       const int ck = __shfl(c, sk, 64), first = __shfl(incl - c, sk, 64);
       // the tile's entries are in the lane's quad (lanes 4 (lane / 4) + j), both registers
@@ -1082,14 +1106,17 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
           r1 += (q1 < sp[1]) ? 1 : 0;
         }
       }
+      // (the indices lie in [0, tot1) by construction; the bound keeps every store in the
+      // head's row regardless)
       const int64_t row = (int64_t)hq * a.npool_cap;
-      if (se < ck) {
-        a.candpos[row + first + r0] = sp[0];
-        if (first + r0 < nstage) f.s.pos[first + r0] = sp[0];
+      const int o0 = first + r0, o1 = first + r1;
+      if (se < ck && o0 < tot1) {
+        a.candpos[row + o0] = sp[0];
+        if (o0 < nstage) f.s.pos[o0] = sp[0];
       }
-      if (se + 4 < ck) {
-        a.candpos[row + first + r1] = sp[1];
-        if (first + r1 < nstage) f.s.pos[first + r1] = sp[1];
+      if (se + 4 < ck && o1 < tot1) {
+        a.candpos[row + o1] = sp[1];
+        if (o1 < nstage) f.s.pos[o1] = sp[1];
       }
       placed = true;
     }
