@@ -256,6 +256,18 @@ struct RescoreConsts {
 // Candidate positions of the first stage (placed in LDS by pass 1): the rows of the lane's
 // two steps (32 step + 8 wv + lane / 8) and thread t's key.  Entries past the count are
 // read but never used.
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves (shifts within rows of
+// 16, then the row broadcasts of lanes 15 and 31), no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // One DPP move of a double (both halves; lanes without a source get 0).
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double x) {
@@ -591,6 +603,10 @@ __device__ __forceinline__ void head_commit(const CertArgs &a, FinSmem &f, const
   if (t <= J) f.tau[t] = p.tau;
   if (t <= J + 1) f.s.ltp[t] = make_double2(p.ltx, p.lty);
   if (!kFirst && t <= J + 1) f.cmh[t] = p.cmh;
+  if (!kFirst && wv == 0) {   // |C_max| (pass 1 takes it from its own sums)
+    const int tot = __builtin_amdgcn_readlane(wave_incl_scan(lane <= J + 1 ? p.cmh : 0), 63);
+    if (lane == 0) f.extra[0] = tot;
+  }
   if (wv == 3) {
     unsigned v = max(max(lane < p.vpn ? p.vp0 : 0u, lane + 64 < p.vpn ? p.vp1 : 0u), p.vp2);
 #pragma unroll
@@ -794,15 +810,9 @@ __device__ __forceinline__ bool certify_head(const CertArgs &a, FinSmem &f, int 
     }
     return false;
   }
-  // keys read exactly: window + |C_max| + the candidates outside C_max whose refined
-  // level l8 is at most j* (column 260 counts them by l8, prefix-summed over levels)
-  if (wv == 0) {
-    int e = (lane <= a.J + 1) ? f.cmh[lane] : 0;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off, 64);
-    if (lane == 0) f.extra[0] = e;
-  }
-  __syncthreads();
+  // keys read exactly: window + |C_max| (f.extra[0], written by thread 0 before) + the
+  // candidates outside C_max whose refined level l8 is at most j* (column 260 counts them
+  // by l8, prefix-summed over levels)
   const double tau = f.tau[js];
   const double D_hat = (f.dr + s.acc[js][256]) + tau * s.acc[js][258];
   if (t < kD)
@@ -917,18 +927,6 @@ __device__ __forceinline__ void place_range(const CertArgs &a, FinSmem &f, int h
     run += tot[0];
     __syncthreads();
   }
-}
-
-// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves (shifts within rows of
-// 16, then the row broadcasts of lanes 15 and 31), no LDS round trips.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
-  return x;
 }
 
 // Lane L of the caller's quad of lanes (a DPP quad broadcast).
@@ -1071,6 +1069,8 @@ __global__ __launch_bounds__(256) void finish_kernel(CertArgs a) {
       a.cmhist[hr + lane] = cm;
       f.cmh[lane] = cm;
     }
+    const int cm_all = __builtin_amdgcn_readlane(wave_incl_scan(lane < J2 ? cm : 0), 63);
+    if (lane == 0) f.extra[0] = cm_all;   // |C_max|
     if (lane == 0) {
       a.jspec[hq] = js;
       a.ccount1[hq] = tot1;
