@@ -175,6 +175,35 @@ __device__ inline double r1_combine8(double p) {
   p = p + __shfl_xor(p, 4, 64);
   return p;
 }
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves (shifts within rows of
+// 16, then the row broadcasts of lanes 15 and 31), no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// One DPP move of a double (both halves; lanes without a source get 0).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+// The same sum as r1_combine8, ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) over the
+// eight lanes of an item, but only in the item's first lane (lane 8 i): two quad
+// exchanges and a shift by four lanes within the row, no LDS round trips.
+__device__ __forceinline__ double r1_combine8_first(double p) {
+  p = p + dpp_f64<0xB1>(p);    // quad_perm(1, 0, 3, 2): lane ^ 1
+  p = p + dpp_f64<0x4E>(p);    // quad_perm(2, 3, 0, 1): lane ^ 2
+  return p + dpp_f64<0x104>(p);   // row_shl:4: lane + 4 (the item's second half)
+}
+
 // q . k over sixteen fp16 values held in two 16-byte words (q given as doubles), in
 // index order.
 __device__ inline double score_words(const double *q16, uint4 a, uint4 b) {

@@ -1231,6 +1231,18 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     // stores share the load counter, so loads issued before this job's stores would be
     // waited for together with them)
     if (cn >= 0) load_chunk(a, slot_head(cn >> 3), job_blk(cn), job_nb2(cn), lane, nxt);
+    // exact perturbations of the chunk's live tokens (lane = token): formed while the first
+    // C_max candidates' rows are on their way, or here if the chunk has none
+    wave_sync();
+    const bool needE = __ballot((liveA | liveB) != 0) != 0ull;
+    const bool myLive = mine && flag[lane] != 0;
+    double myE = 0.0;
+    auto exact_E = [&]() __attribute__((always_inline)) {
+      if (needE && myLive) {
+        myE = perturbation(prefix, mypos);
+        if (a.e_out) a.e_out[(int64_t)jh * jnpool + mypos] = myE;
+      }
+    };
     // exact scores of C_max candidates: c* = max(c_R, max over them), since a key with
     // UB < c_lo scores below c_lo <= c*.  Every candidate of the chunk (both slots, all
     // tiles) is listed in LDS first, then they are scored eight lanes per key.
@@ -1260,28 +1272,24 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
           g2 = v >> 8;
           pos = tok0 + (v & 0xFF);
         }
-        double p = 0.0;
-        if (pos >= 0) {
-          double q16[16];
+        // the query chunk from the slot's LDS copy and the key chunk (position 0 for the
+        // lanes past the list, dropped) are requested before anything waits for them
+        const int64_t kpos = (pos >= 0) ? pos : 0;
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + (jkv * a.n_cap + kpos) * kD) + 2 * k8;
+        const uint4 kw0 = ksrc[0], kw1 = ksrc[1];
+        if (e0 == 0) exact_E();
+        double q16[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) q16[i] = (double)a.qf[(int64_t)(jhq0 + g2) * kD + 16 * k8 + i];
-          p = score_chunk(q16, a.K + (jkv * a.n_cap + pos) * kD, k8);
-        }
-        const double sc = r1_combine8(p) * kRsqrtD;
+        for (int i = 0; i < 16; ++i) q16[i] = (double)S.q[g2][16 * k8 + i];
+        const double p = (pos >= 0) ? score_words(q16, kw0, kw1) : 0.0;
+        const double sc = r1_combine8_first(p) * kRsqrtD;
         // c* = max(c_R, these exact scores)
         if (pos >= 0 && k8 == 0)
           __hip_atomic_fetch_max(a.cstar + jhq0 + g2, enc_max(sc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       wave_sync();
-    }
-    // exact perturbations for the chunk's live tokens (lane = token)
-    wave_sync();
-    double myE = 0.0;
-    if (__ballot((liveA | liveB) != 0)) {
-      if (mine && flag[lane]) {
-        myE = perturbation(prefix, mypos);
-        if (a.e_out) a.e_out[(int64_t)jh * jnpool + mypos] = myE;
-      }
+    } else {
+      exact_E();
     }
     wave_sync();
 #pragma unroll
