@@ -202,15 +202,11 @@ __device__ __forceinline__ void accumulate_stage(const CertArgs &a, AccSmem &s, 
         }
       }
     }
-    // exact reads outside C_max: thread 130 counts them at their refined level l8
-    if (t == kD + 2) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (e0 + k < cnt) {
-          const int x = s.x[e0 + k], l8 = x & 0xFF;
-          if (l8 <= J && !(x >> 8)) atomicAdd(&s.acc[l8][2 * kD + 4], 1.0);
-        }
-      }
+    // exact reads outside C_max: threads 130 + k count candidate e0 + k at its refined level
+    // l8 (whole numbers: the order of the additions does not matter)
+    if (t >= kD + 2 && t < kD + 10 && e0 + (t - kD - 2) < cnt) {
+      const int x = s.x[e0 + (t - kD - 2)], l8 = x & 0xFF;
+      if (l8 <= J && !(x >> 8)) atomicAdd(&s.acc[l8][2 * kD + 4], 1.0);
     }
   }
   __syncthreads();
