@@ -277,24 +277,26 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
     if (t < cnt) s.pos[t] = a.candpos[base + c0 + t];
     __syncthreads();
   }
-  // step k takes keys 32 k .. 32 k + 31, wavefront wv eight of them (eight lanes per key), so a
+  // Step k takes keys 32 k .. 32 k + 31, wavefront wv eight of them (eight lanes per key), so a
   // stage of at most 32 keys is one step of every wavefront (kSteps = 1: cnt <= 32).  Every
-  // load is issued before any is used (slots past cnt read position 0 and drop the values),
-  // and the lane's perturbation is formed while they travel.
+  // load of every step is issued before any is used (slots past cnt read position 0 and
+  // drop the values).  The eight lanes of a key then form its scalars (perturbation, 8-bit
+  // bound and level, exact levels and weight) alike from sums that reach all eight, so no
+  // barrier separates the 8-bit bound, the exact score and the records.
   uint4 cw8[2], kw[2][2], vw[2][2];
   float sc8[2];
+  double ubt[2];
+  uint16_t ke8r[2];
+  int pr[2];
 #pragma unroll
-  for (int step = 0; step < 2; ++step) {
-    if (step >= kSteps) {
-      cw8[step] = kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
-      sc8[step] = 0.0f;
-      continue;
-    }
+  for (int step = 0; step < kSteps; ++step) {
     const int r = 32 * step + 8 * wv + s8;
-    const int pr = (r < cnt) ? (use_pre ? pre.pos_r[step] : s.pos[r]) : 0;
-    const int64_t tok = h * a.n_cap + pr;
+    pr[step] = (r < cnt) ? (use_pre ? pre.pos_r[step] : s.pos[r]) : 0;
+    const int64_t tok = h * a.n_cap + pr[step];
     cw8[step] = reinterpret_cast<const uint4 *>(a.codes8 + tok * kD)[k8];
     sc8[step] = a.scale8[tok];
+    ubt[step] = a.ubuf[base + pr[step]];
+    ke8r[step] = a.kerr8[tok];
     kw[step][0] = kw[step][1] = vw[step][0] = vw[step][1] = make_uint4(0, 0, 0, 0);
     if (kSpec) {
       const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
@@ -305,43 +307,38 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
       vw[step][1] = vsrc[1];
     }
   }
-  // one lane per key: its perturbation, UB and 8-bit record
-  const int post = (t < cnt) ? (use_pre ? pre.pos_t : s.pos[t]) : 0;
-  const double ubt = a.ubuf[base + post];
-  const uint16_t ke8_raw = a.kerr8[h * a.n_cap + post];
-  const float s8t_raw = a.scale8[h * a.n_cap + post];
-  double E = 0.0;
-  if (t < cnt) E = perturbation(rc.prefix, post);
+  double E[2];
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int r = 32 * step + 8 * wv + s8;
+    E[step] = (r < cnt) ? perturbation(rc.prefix, pr[step]) : 0.0;
+  }
   for (int e = t; e < zero_rows * kStatW; e += 256) (&s.acc[0][0])[e] = 0.0;
 #pragma unroll
-  for (int step = 0; step < 2; ++step) {
+  for (int step = 0; step < kSteps; ++step) {
     const int r = 32 * step + 8 * wv + s8;
+    const bool act = r < cnt;
+    // the 8-bit bound and its level l8
     double p = 0.0;
-    if (r < cnt) {
-      const double sc = (double)sc8[step];
+    const double sc = (double)sc8[step];
+    if (act) {
       const uint32_t wd[4] = {cw8[step].x, cw8[step].y, cw8[step].z, cw8[step].w};
       p = rc.q16[0] * (sc * (double)(int8_t)(wd[0] & 0xFFu));
 #pragma unroll
       for (int i = 1; i < 16; ++i) p = p + rc.q16[i] * (sc * (double)(int8_t)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu));
     }
-    const double S8 = r1_combine8_first(p);
-    if (r < cnt && k8 == 0) s.w[r] = S8;
-  }
-  __syncthreads();
-  if (t < cnt) {
-    const double ke8 = h2d(ke8_raw), s8t = (double)s8t_raw;
-    const double slack8 = (rc.qnp * ke8) + (kPadF * ((128.0 * s8t) * rc.qabs));
-    const double ub8 = (s.w[t] + slack8) * kRsqrtD;
-    const int l8 = level_of_pairs((fmin(ubt, ub8) + E) - rc.cs, s.ltp, a.J, rc.inv_l1);
-    s.x[t] = l8 | ((ubt >= rc.clo) ? 0x100 : 0);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int step = 0; step < 2; ++step) {
-    const int r = 32 * step + 8 * wv + s8;
-    const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
+    const double S8 = r1_combine8_all(p);
+    int l8 = a.J + 1, x = 0;
+    if (act) {
+      const double slack8 = (rc.qnp * h2d(ke8r[step])) + (kPadF * ((128.0 * sc) * rc.qabs));
+      const double ub8 = (S8 + slack8) * kRsqrtD;
+      l8 = level_of_pairs((fmin(ubt[step], ub8) + E[step]) - rc.cs, s.ltp, a.J, rc.inv_l1);
+      x = l8 | ((ubt[step] >= rc.clo) ? 0x100 : 0);
+    }
+    // the exact score and |v|^2 of the keys with l8 <= J (rows read now unless speculative)
+    const bool ex = act && l8 <= a.J;
     if (!kSpec && ex) {
-      const int64_t tok = h * a.n_cap + s.pos[r];
+      const int64_t tok = h * a.n_cap + pr[step];
       const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.K + tok * kD) + 2 * k8;
       const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.V + tok * kD) + 2 * k8;
       kw[step][0] = ksrc[0];
@@ -349,47 +346,38 @@ __device__ __forceinline__ void rescore_stage(const CertArgs &a, AccSmem &s, int
       vw[step][0] = vsrc[0];
       vw[step][1] = vsrc[1];
     }
-  }
-#pragma unroll
-  for (int step = 0; step < 2; ++step) {
-    const int r = 32 * step + 8 * wv + s8;
-    const bool ex = r < cnt && (s.x[r] & 0xFF) <= a.J;
-    double p = 0.0, v = 0.0;
+    double ps = 0.0, pv = 0.0;
     if (ex) {
-      p = score_words(rc.q16, kw[step][0], kw[step][1]);
+      ps = score_words(rc.q16, kw[step][0], kw[step][1]);
       // the V row is staged for the accumulation while its |v|^2 is formed
       uint4 *vdst = reinterpret_cast<uint4 *>(s.vs[r]) + 2 * k8;
       vdst[0] = vw[step][0];
       vdst[1] = vw[step][1];
-      v = sumsq_words(vw[step][0], vw[step][1]);
+      pv = sumsq_words(vw[step][0], vw[step][1]);
     }
-    const double sc = r1_combine8_first(p) * kRsqrtD;
-    const double vs = r1_combine8_first(v);
-    if (ex && k8 == 0) {
-      s.w[r] = sc;       // the score for now; the weight below
-      s.vsq[r] = vs;
+    const double scx = r1_combine8_all(ps) * kRsqrtD;
+    const double vs = r1_combine8_all(pv);
+    // the key's levels, weight and records (its first lane writes them)
+    if (act && k8 == 0) {
+      int hl = a.J + 1, ll = a.J + 1;
+      double sco = 0.0, w = 0.0, vsq = 0.0;
+      if (ex) {
+        sco = scx;
+        hl = level_of_pairs(scx - rc.cs, s.ltp, a.J, rc.inv_l1);
+        ll = level_of_pairs((scx + E[step]) - rc.cs, s.ltp, a.J, rc.inv_l1);
+        w = exp(scx - rc.cs);
+        vsq = (ll <= a.J) ? vs : 0.0;
+      }
+      s.hl[r] = hl | (ll << 8);
+      s.w[r] = w;
+      s.vsq[r] = vsq;
+      s.x[r] = x;
+      a.rec_s[base + c0 + r] = sco;
+      a.rec_w[base + c0 + r] = w;
+      a.rec_vsq[base + c0 + r] = vsq;
+      a.rec_hl[base + c0 + r] = hl | (ll << 8);
+      a.rec_x[base + c0 + r] = x;
     }
-  }
-  __syncthreads();
-  if (t < cnt) {
-    const int x = s.x[t];
-    int hl = a.J + 1, ll = a.J + 1;
-    double sc = 0.0, w = 0.0, vsq = 0.0;
-    if ((x & 0xFF) <= a.J) {
-      sc = s.w[t];
-      hl = level_of_pairs(sc - rc.cs, s.ltp, a.J, rc.inv_l1);
-      ll = level_of_pairs((sc + E) - rc.cs, s.ltp, a.J, rc.inv_l1);
-      w = exp(sc - rc.cs);
-      vsq = (ll <= a.J) ? s.vsq[t] : 0.0;
-    }
-    s.hl[t] = hl | (ll << 8);
-    s.w[t] = w;
-    s.vsq[t] = vsq;
-    a.rec_s[base + c0 + t] = sc;
-    a.rec_w[base + c0 + t] = w;
-    a.rec_vsq[base + c0 + t] = vsq;
-    a.rec_hl[base + c0 + t] = hl | (ll << 8);
-    a.rec_x[base + c0 + t] = x;
   }
   __syncthreads();
 }

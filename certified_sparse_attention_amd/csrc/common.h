@@ -204,6 +204,15 @@ __device__ __forceinline__ double r1_combine8_first(double p) {
   return p + dpp_f64<0x104>(p);   // row_shl:4: lane + 4 (the item's second half)
 }
 
+// The same sum as r1_combine8 in all eight lanes of the item (identical bits: the last
+// addition is A + B in the first half and B + A in the second), by DPP moves: two quad
+// exchanges, then the other half of the item by a shift of four lanes either way.
+__device__ __forceinline__ double r1_combine8_all(double p) {
+  p = p + dpp_f64<0xB1>(p);    // lane ^ 1
+  p = p + dpp_f64<0x4E>(p);    // lane ^ 2
+  const double up = dpp_f64<0x104>(p), dn = dpp_f64<0x114>(p);   // row_shl:4, row_shr:4
+  return p + (((threadIdx.x & 4) != 0) ? dn : up);
+}
 // q . k over sixteen fp16 values held in two 16-byte words (q given as doubles), in
 // index order.
 __device__ inline double score_words(const double *q16, uint4 a, uint4 b) {
