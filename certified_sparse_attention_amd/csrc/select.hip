@@ -44,6 +44,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
   // never read)
   const int64_t npool = unit_npool(a.b, hq / a.G, a.W);
   __shared__ int hist[kMaxJ + 2], cmh[kMaxJ + 2], slot[kMaxJ + 2];
+  __shared__ __attribute__((aligned(16))) uint32_t wt[2][32];   // the tile's words, even ones first
   __shared__ double2 ltp[kMaxJ + 2];
   // this lane's bitmap word (tile word `lane`, read at a clamped position and masked
   // below), c* and c_lo are read together with the level table
@@ -74,10 +75,16 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(SelectArgs a) {
     const double *ubp = a.ubuf + (int64_t)hq * a.npool_cap + p_tile;
     int8_t *lub = a.lub + (int64_t)hq * a.npool_cap + p_tile;
     const int64_t left = npool - p_tile;
+    // (the words go through LDS, even ones first: a lane's 32 words are then 8 vector reads)
+    wt[lane & 1][lane >> 1] = word;
+    __builtin_amdgcn_wave_barrier();
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(wt[lane >> 5]);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const uint32_t wk = (uint32_t)__shfl((int)word, 2 * k + (lane >> 5), 64);
-      on |= ((wk >> (lane & 31)) & 1u) << k;
+    for (int k4 = 0; k4 < 8; ++k4) {
+      const uint4 w4 = wrow[k4];
+      const uint32_t wk[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) on |= ((wk[i] >> (lane & 31)) & 1u) << (4 * k4 + i);
     }
     // all loads of the lane's live keys first, then the levels
     double pv[32], uv[32];
