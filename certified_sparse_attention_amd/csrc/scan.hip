@@ -156,61 +156,122 @@ __device__ inline QueryConsts query_consts_from(double ss, double sa, double qa)
   return c;
 }
 
-// One wavefront's constants of its G queries: lane l holds channels 2l, 2l + 1 of every
-// query (qv0, qv1).  Lanes 8g .. 8g + 7 sum query g's chunks through `st` (128 G floats
-// of LDS) and lane 8g computes its constants; the lane then takes those of its two query
-// slots gA = l / 16 and gB = gA + 4 (qnp, qabs, beta), the largest |q| of the group, and
-// its slice of the offset term's A operand (qa0, qa1: lane L = row + 16 kg holds the
-// bytes of channels 32 kg + 16 kh + b, b = 0..15, of row `row`, kh = 0 / 1).
+// Maximum over the 16 lanes of a row with integer DPP maxima on order-preserving keys.
+__device__ inline int fkey(float v) {
+  const int b = __float_as_int(v);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ inline float fkey_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+// Maxima over the 16 lanes of each row of two values at once: four DPP steps (swap
+// neighbours, swap pairs, mirror half-rows, mirror rows), each a max with the moved
+// value.  Every source lane lies in the row, so the masks are full and no lane keeps an
+// old value; every lane must be active.  The nops give the two wait states a DPP read
+// needs after a VALU write of its operand.
+__device__ inline void row_max16x2(float &u, float &v) {
+  __asm__("s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "s_nop 1\n\t"
+          "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
+          : "+v"(u), "+v"(v));
+}
+__device__ inline int row_max16key(int k) {
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0xB1, 0xF, 0xF, false));    // quad_perm 1032
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x4E, 0xF, 0xF, false));    // quad_perm 2301
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x140, 0xF, 0xF, false));   // row_mirror
+  return k;
+}
+__device__ inline float row_max16k(float v) { return fkey_inv(row_max16key(fkey(v))); }
+// Maximum over the 64 lanes (every lane active), the same in every lane: the rows' maxima
+// by DPP, then the four rows' from scalar reads.
+__device__ inline float wave_max_f32(float v) {
+  const int k = row_max16key(fkey(v));
+  const int r0 = __builtin_amdgcn_readlane(k, 0), r1 = __builtin_amdgcn_readlane(k, 16);
+  const int r2 = __builtin_amdgcn_readlane(k, 32), r3 = __builtin_amdgcn_readlane(k, 48);
+  return fkey_inv(max(max(r0, r1), max(r2, r3)));
+}
+// Sum over the 16 lanes of each row, the same in all of them (every lane active): pairs,
+// quads, half-rows, rows, each step adding the value of a lane in the other part.
+__device__ inline float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Lane l's value of v, as a wave-uniform value (the bits move, not a converted value).
+__device__ inline float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// One wavefront's constants of its G queries, for the streaming bounds only (lane l holds
+// channels 2l, 2l + 1 of every query in qv0, qv1).  They need not equal the exact
+// constants that the window workgroups store for the later kernels, only bound them:
+//   - max |q| is exact in fp32, so beta, 1 / beta and the integer grid q~ are the exact
+//     ones, and so are the offset terms base and eb;
+//   - the sum of squares is taken in fp32 over the wave (squares of fp16 values are exact
+//     in fp32; at most 7 roundings on any path, so the true sum S is at most
+//     s (1 + 2^-21)), and qnp32 = sqrt(s (1 + 2^-10)) (1 + 2^-10) in fp32 exceeds
+//     sqrt(S) (1 + 2^-11) with a square root within one ulp, above the exact qnp, which is
+//     below sqrt(S) (1 + 2^-22);
+//   - 128 max |q| stands in for sum |q| in the pad 2^-40 qabs Kmax.
+// A larger qnp or pad only raises every upper bound and lowers every lower bound.  The
+// lane then takes the values of its two query slots gA = l / 16 and gB = gA + 4 (qnp,
+// qabs, beta), the largest |q| of the group, and its slice of the offset term's A
+// operand (qa0, qa1: lane L = row + 16 kg holds the bytes of channels 32 kg + 16 kh + b,
+// b = 0..15, of row `row`, kh = 0 / 1), built in `st` (2 KB of LDS).
 template <int G>
 __device__ inline void wave_query_consts(const float *qv0, const float *qv1, int lane, float *st, float &qmax,
                                          float &qnpA, float &qnpB, double *obeta, double *oqabs, v4i &qa0,
                                          v4i &qa1) {
+  float qa[G], ss[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    st[g * kD + 2 * lane] = qv0[g];
-    st[g * kD + 2 * lane + 1] = qv1[g];
+    qa[g] = row_max16k(fmaxf(fabsf(qv0[g]), fabsf(qv1[g])));
+    ss[g] = row_sum16(qv0[g] * qv0[g] + qv1[g] * qv1[g]);
   }
-  wave_sync();
-  const int gq = lane >> 3, k = lane & 7;
-  double ss = 0.0, sa = 0.0, mx = 0.0;
-  if (gq < G) {
-    const float *c = st + gq * kD + 16 * k;
-    double x = (double)c[0];
-    ss = x * x;
-    sa = fabs(x);
-    mx = fabs(x);
+  const int gA = lane >> 4, gB = gA + 4;
+  float ib[G];
+  qmax = 0.0f;
+  qnpA = qnpB = 0.0f;
+  obeta[0] = obeta[1] = oqabs[0] = oqabs[1] = 0.0;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      x = (double)c[i];
-      ss = ss + x * x;
-      sa = sa + fabs(x);
-      mx = fmax(mx, fabs(x));
+  for (int g = 0; g < G; ++g) {
+    const float m = fmaxf(fmaxf(readlane_f32(qa[g], 0), readlane_f32(qa[g], 16)),
+                          fmaxf(readlane_f32(qa[g], 32), readlane_f32(qa[g], 48)));
+    const float s = (readlane_f32(ss[g], 0) + readlane_f32(ss[g], 16)) +
+                    (readlane_f32(ss[g], 32) + readlane_f32(ss[g], 48));
+    qmax = fmaxf(qmax, m);
+    double beta = 0.0;
+    ib[g] = 0.0f;   // 0 for a zero query: its rows stay 0
+    if (m > 0.0f) {
+      int e;
+      (void)frexpf(m, &e);
+      beta = ldexp(1.0, e - 11);
+      ib[g] = ldexpf(1.0f, 11 - e);
+    }
+    const float qnp = __builtin_sqrtf(s * 0x1.004p0f) * 0x1.004p0f;
+    const double qabs = 128.0 * (double)m;
+    if (g == gA) {
+      qnpA = qnp;
+      obeta[0] = beta;
+      oqabs[0] = qabs;
+    }
+    if (g == gB) {
+      qnpB = qnp;
+      obeta[1] = beta;
+      oqabs[1] = qabs;
     }
   }
-  // the tree over a query's 8 chunks (lane k = 0 of its group ends with the sums)
-#pragma unroll
-  for (int off = 1; off <= 4; off <<= 1) {
-    ss = ss + __shfl_xor(ss, off, 64);
-    sa = sa + __shfl_xor(sa, off, 64);
-    mx = fmax(mx, __shfl_xor(mx, off, 64));
-  }
-  // lane 8g: query g's constants, then every lane takes what it needs
-  const QueryConsts mine = query_consts_from(ss, sa, mx);
-  const int gA = lane >> 4, gB = gA + 4;
-  const double npA = __shfl(mine.qnp, 8 * gA, 64), npB = __shfl(mine.qnp, 8 * min(gB, 7), 64);
-  obeta[0] = (gA < G) ? __shfl(mine.beta, 8 * gA, 64) : 0.0;
-  oqabs[0] = (gA < G) ? __shfl(mine.qabs, 8 * gA, 64) : 0.0;
-  const double bB = __shfl(mine.beta, 8 * min(gB, 7), 64), aB = __shfl(mine.qabs, 8 * min(gB, 7), 64);
-  obeta[1] = (gB < G) ? bB : 0.0;
-  oqabs[1] = (gB < G) ? aB : 0.0;
-  qnpA = (gA < G) ? (float)npA : 0.0f;
-  qnpB = (gB < G) ? (float)npB : 0.0f;
-  float m = (gq < G) ? (float)mine.qa : 0.0f;   // (the group's largest |q| is in all its lanes)
-#pragma unroll
-  for (int off = 8; off <= 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  qmax = m;
-  wave_sync();   // the chunk sums are read: the staging area takes the operand next
   // the operand: each lane quantizes its two channels of every query (beta is a power of
   // two, so q / beta is exact in fp32 and rint matches the fp64 definition) and writes
   // the byte pairs into the rows of its channel group; rows of unused query slots are 0
@@ -220,11 +281,10 @@ __device__ inline void wave_query_consts(const float *qv0, const float *qv1, int
   for (int g = 0; g < 8; ++g) {
     uint32_t hi = 0u, lo = 0u;   // the two channels' bytes of the high and low row
     if (g < G) {
-      const float ib = __shfl(mine.ib, 8 * g, 64);   // 0 for a zero query: its rows stay 0
       const float qs[2] = {qv0[g < G ? g : 0], qv1[g < G ? g : 0]};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int qi = (int)rintf(qs[e] * ib);
+        const int qi = (int)rintf(qs[e] * ib[g < G ? g : 0]);
         const int q1 = (qi + 64) >> 7;
         hi |= (uint32_t)(q1 & 0xFF) << (8 * e);
         lo |= (uint32_t)((qi - 128 * q1) & 0xFF) << (8 * e);
@@ -617,48 +677,6 @@ __device__ void window_work(const ScanArgs &a, int hq, WindowSmem &sm) {
   }
 }
 
-// Maximum over the 16 lanes of a row with integer DPP maxima on order-preserving keys.
-__device__ inline int fkey(float v) {
-  const int b = __float_as_int(v);
-  return b ^ ((b >> 31) & 0x7FFFFFFF);
-}
-__device__ inline float fkey_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
-// Maxima over the 16 lanes of each row of two values at once: four DPP steps (swap
-// neighbours, swap pairs, mirror half-rows, mirror rows), each a max with the moved
-// value.  Every source lane lies in the row, so the masks are full and no lane keeps an
-// old value; every lane must be active.  The nops give the two wait states a DPP read
-// needs after a VALU write of its operand.
-__device__ inline void row_max16x2(float &u, float &v) {
-  __asm__("s_nop 1\n\t"
-          "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-          "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-          "s_nop 1\n\t"
-          "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-          "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-          "s_nop 1\n\t"
-          "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-          "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-          "s_nop 1\n\t"
-          "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
-          "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
-          : "+v"(u), "+v"(v));
-}
-__device__ inline int row_max16key(int k) {
-  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0xB1, 0xF, 0xF, false));    // quad_perm 1032
-  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x4E, 0xF, 0xF, false));    // quad_perm 2301
-  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x141, 0xF, 0xF, false));   // row_half_mirror
-  k = max(k, __builtin_amdgcn_update_dpp(k, k, 0x140, 0xF, 0xF, false));   // row_mirror
-  return k;
-}
-__device__ inline float row_max16k(float v) { return fkey_inv(row_max16key(fkey(v))); }
-// Maximum over the 64 lanes (every lane active), the same in every lane: the rows' maxima
-// by DPP, then the four rows' from scalar reads.
-__device__ inline float wave_max_f32(float v) {
-  const int k = row_max16key(fkey(v));
-  const int r0 = __builtin_amdgcn_readlane(k, 0), r1 = __builtin_amdgcn_readlane(k, 16);
-  const int r2 = __builtin_amdgcn_readlane(k, 32), r3 = __builtin_amdgcn_readlane(k, 48);
-  return fkey_inv(max(max(r0, r1), max(r2, r3)));
-}
 
 template <int G>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
@@ -780,7 +798,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     float myEup = 0.0f;
     if (lane < nval) {
       myEup = perturbation_upper32(prefix, tok0 + lane);
-      vmx = max(vmx, in.vn);
+      vmx = max(vmx, (unsigned)in.vn);
     }
     return myEup;
   };
