@@ -126,6 +126,8 @@ __device__ inline void init_operand(uint8_t *Abuf, int lane, bool every_group = 
 
 
 // ------------------------------------------------------------------ query constants
+// The exact constants, which the window workgroups compute and store for the later
+// kernels (the streaming wavefronts use fp32 bounds of them, below).
 // Per query (R1 sums: the 128 channels in 8 chunks of 16 summed in channel order, then
 // the fixed tree ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)); all fp64):
 //   qa    = max_t |q_t|;  beta = 2^(e - 11) for qa = f 2^e, f in [1/2, 1) (0 for q = 0)

@@ -4,7 +4,8 @@
 upper bounds u_i >= s_i for all scores, and the scan that computes them is integer
 dot-product work; [A]: the scan is shared across a GQA group and reads every key.
 The pages do not give the bound's formula.  Reading taken (test infrastructure
-only; the HIP scan follows the same written rules):
+only; the HIP scan's exact pass follows the same written rules, and its streaming pass
+uses fp32 values that can only widen these bounds):
 
 Per call, query g (fp16 q_g):
   Q1. qa_g = max_t |q_gt|; beta_g = 2^(e-11) with qa_g = f 2^e, f in [0.5, 1)
