@@ -12,8 +12,9 @@
 //   UB = shat + slack, LB = shat - slack, p = UB + E_i
 // with I_gi = sum_t a~_gbt c_it and C_i = sum_t c_it from one i8 MFMA chain, and
 // base_gb = beta_g kappa_b sum_t q~_gt z_bt from a second one.  The integer weights
-// a~ = rint(q kscale 2^(11-x)) lie in [-2048, 2048]; each is split a~ = 128 a1 + a0
-// (a1 in [-16, 16], a0 in [-64, 63]) into two int8 rows of the MFMA's A operand.
+// a~ = rint(q kscale 2^(11-x)) lie in [-2048, 2048]; each is split into two int8 rows of
+// the MFMA's A operand, a~ = 256 a1 + a0 (a1 in [-8, 8], a0 in [-128, 127]) in the
+// streaming scan and a~ = 128 a1 + a0 (a1 in [-16, 16], a0 in [0, 127]) in the refinement.
 //
 // MFMA operand rows (16): query g's high part at row 4(g%4) + 2(g/4), its low part
 // one row below; row 14 is all ones (gives C_i); row 15 is zero.  So G <= 7.
@@ -215,86 +216,84 @@ __device__ inline float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// One wavefront's constants of its G queries, for the streaming bounds only (lane l holds
-// channels 2l, 2l + 1 of every query in qv0, qv1).  They need not equal the exact
-// constants that the window workgroups store for the later kernels, only bound them:
+// Lanes of the streaming scan: lane l takes the query slots gA = l / 16 and gB = gA + 4
+// (groups of five to seven queries), each with channels 8 o .. 8 o + 7, o = l % 16, so
+// the 16 lanes of a slot are one DPP row.  op_octet gives the byte offset of those eight
+// channels in operand row `row` (lane L = row + 16 kg holds the bytes of channels
+// 32 kg + 16 kh + b, b = 0..15, in half kh of the operand).
+__device__ inline int op_octet(int row, int o) {
+  return ((o >> 1) & 1) * 1024 + (row + 16 * (o >> 2)) * 16 + 8 * (o & 1);
+}
+
+// One wavefront's constants of its G queries, for the streaming bounds only (q8A, q8B:
+// the lane's eight channels of slots gA and gB, zero for slots past G).  They need not
+// equal the exact constants that the window workgroups store for the later kernels, only
+// bound them:
 //   - max |q| is exact in fp32, so beta, 1 / beta and the integer grid q~ are the exact
 //     ones, and so are the offset terms base and eb;
-//   - the sum of squares is taken in fp32 over the wave (squares of fp16 values are exact
-//     in fp32; at most 7 roundings on any path, so the true sum S is at most
-//     s (1 + 2^-21)), and qnp32 = sqrt(s (1 + 2^-10)) (1 + 2^-10) in fp32 exceeds
-//     sqrt(S) (1 + 2^-11) with a square root within one ulp, above the exact qnp, which is
-//     below sqrt(S) (1 + 2^-22);
+//   - the sum of squares is taken in fp32 (squares of fp16 values are exact in fp32; at
+//     most 11 roundings on any path, so the true sum S is at most s (1 + 2^-20)), and
+//     qnp32 = sqrt(s (1 + 2^-10)) (1 + 2^-10) in fp32 exceeds sqrt(S) (1 + 2^-11) with a
+//     square root within one ulp, above the exact qnp, which is below sqrt(S) (1 + 2^-22);
 //   - 128 max |q| stands in for sum |q| in the pad 2^-40 qabs Kmax.
 // A larger qnp or pad only raises every upper bound and lowers every lower bound.  The
-// lane then takes the values of its two query slots gA = l / 16 and gB = gA + 4 (qnp,
-// qabs, beta), the largest |q| of the group, and its slice of the offset term's A
-// operand (qa0, qa1: lane L = row + 16 kg holds the bytes of channels 32 kg + 16 kh + b,
-// b = 0..15, of row `row`, kh = 0 / 1), built in `st` (2 KB of LDS).
+// lane gets the values of its slots (qnp, qabs, beta), the largest |q| of the group, and
+// its slice of the offset term's A operand (qa0, qa1), built in A (2 KB of LDS): rows
+// op_row(g, 0 / 1) hold q~ = 128 q1 + q0 with q1 = floor((q~ + 64) / 128).
 template <int G>
-__device__ inline void wave_query_consts(const float *qv0, const float *qv1, int lane, float *st, float &qmax,
-                                         float &qnpA, float &qnpB, double *obeta, double *oqabs, v4i &qa0,
-                                         v4i &qa1) {
-  float qa[G], ss[G];
+__device__ inline void wave_query_consts8(const float *q8A, const float *q8B, int lane, uint8_t *A, float &qmax,
+                                          float &qnpA, float &qnpB, double *obeta, double *oqabs, v4i &qa0,
+                                          v4i &qa1) {
+  constexpr bool kTwo = G > 4;
+  const int gA = lane >> 4, gB = gA + 4, o = lane & 15;
+  float mA = 0.0f, sA = 0.0f, mB = 0.0f, sB = 0.0f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    qa[g] = row_max16k(fmaxf(fabsf(qv0[g]), fabsf(qv1[g])));
-    ss[g] = row_sum16(qv0[g] * qv0[g] + qv1[g] * qv1[g]);
-  }
-  const int gA = lane >> 4, gB = gA + 4;
-  float ib[G];
-  qmax = 0.0f;
-  qnpA = qnpB = 0.0f;
-  obeta[0] = obeta[1] = oqabs[0] = oqabs[1] = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = fmaxf(fmaxf(readlane_f32(qa[g], 0), readlane_f32(qa[g], 16)),
-                          fmaxf(readlane_f32(qa[g], 32), readlane_f32(qa[g], 48)));
-    const float s = (readlane_f32(ss[g], 0) + readlane_f32(ss[g], 16)) +
-                    (readlane_f32(ss[g], 32) + readlane_f32(ss[g], 48));
-    qmax = fmaxf(qmax, m);
-    double beta = 0.0;
-    ib[g] = 0.0f;   // 0 for a zero query: its rows stay 0
-    if (m > 0.0f) {
-      int e;
-      (void)frexpf(m, &e);
-      beta = ldexp(1.0, e - 11);
-      ib[g] = ldexpf(1.0f, 11 - e);
-    }
-    const float qnp = __builtin_sqrtf(s * 0x1.004p0f) * 0x1.004p0f;
-    const double qabs = 128.0 * (double)m;
-    if (g == gA) {
-      qnpA = qnp;
-      obeta[0] = beta;
-      oqabs[0] = qabs;
-    }
-    if (g == gB) {
-      qnpB = qnp;
-      obeta[1] = beta;
-      oqabs[1] = qabs;
+  for (int i = 0; i < 8; ++i) {
+    mA = fmaxf(mA, fabsf(q8A[i]));
+    sA += q8A[i] * q8A[i];
+    if (kTwo) {
+      mB = fmaxf(mB, fabsf(q8B[i]));
+      sB += q8B[i] * q8B[i];
     }
   }
-  // the operand: each lane quantizes its two channels of every query (beta is a power of
-  // two, so q / beta is exact in fp32 and rint matches the fp64 definition) and writes
-  // the byte pairs into the rows of its channel group; rows of unused query slots are 0
-  uint8_t *A = reinterpret_cast<uint8_t *>(st);
-  const int c0 = 2 * lane, kg = c0 >> 5, kh = (c0 >> 4) & 1, b = c0 & 15;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    uint32_t hi = 0u, lo = 0u;   // the two channels' bytes of the high and low row
-    if (g < G) {
-      const float qs[2] = {qv0[g < G ? g : 0], qv1[g < G ? g : 0]};
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int qi = (int)rintf(qs[e] * ib[g < G ? g : 0]);
-        const int q1 = (qi + 64) >> 7;
-        hi |= (uint32_t)(q1 & 0xFF) << (8 * e);
-        lo |= (uint32_t)((qi - 128 * q1) & 0xFF) << (8 * e);
+  mA = row_max16k(mA);
+  sA = row_sum16(sA);
+  qmax = fmaxf(fmaxf(readlane_f32(mA, 0), readlane_f32(mA, 16)), fmaxf(readlane_f32(mA, 32), readlane_f32(mA, 48)));
+  if (kTwo) {
+    mB = row_max16k(mB);
+    sB = row_sum16(sB);
+    qmax = fmaxf(qmax, fmaxf(fmaxf(readlane_f32(mB, 0), readlane_f32(mB, 16)),
+                             fmaxf(readlane_f32(mB, 32), readlane_f32(mB, 48))));
+  }
+  // the slot's constants and its rows of the offset operand (zero rows for empty slots)
+  auto slot = [&](const float *q8, float m, float ss, bool valid, int g, double &beta, double &qabs, float &qnp) {
+    beta = 0.0;
+    qabs = 0.0;
+    qnp = 0.0f;
+    float ib = 0.0f;   // 0 for a zero query: its rows stay 0
+    if (valid) {
+      if (m > 0.0f) {
+        int e;
+        (void)frexpf(m, &e);
+        beta = ldexp(1.0, e - 11);
+        ib = ldexpf(1.0f, 11 - e);
       }
+      qnp = __builtin_sqrtf(ss * 0x1.004p0f) * 0x1.004p0f;
+      qabs = 128.0 * (double)m;
     }
-    *reinterpret_cast<uint16_t *>(A + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + b) = (uint16_t)hi;
-    *reinterpret_cast<uint16_t *>(A + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + b) = (uint16_t)lo;
-  }
+    uint32_t hi[2] = {0u, 0u}, lo[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int qi = (int)rintf(q8[i] * ib);
+      const int q1 = (qi + 64) >> 7;
+      hi[i >> 2] |= (uint32_t)(q1 & 0xFF) << (8 * (i & 3));
+      lo[i >> 2] |= (uint32_t)((qi - 128 * q1) & 0xFF) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2 *>(A + op_octet(op_row(g, 0), o)) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2 *>(A + op_octet(op_row(g, 1), o)) = make_uint2(lo[0], lo[1]);
+  };
+  slot(q8A, mA, sA, gA < G, gA, obeta[0], oqabs[0], qnpA);
+  slot(q8B, mB, sB, kTwo && gB < G, gB, obeta[1], oqabs[1], qnpB);
   wave_sync();
   qa0 = *reinterpret_cast<const v4i *>(A + lane * 16);
   qa1 = *reinterpret_cast<const v4i *>(A + 1024 + lane * 16);
@@ -416,6 +415,45 @@ __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const floa
     *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = (uint16_t)pk;
     *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = (uint16_t)(pk >> 16);
   }
+}
+
+// The group's integer weights of one block in the streaming scan (lanes as for
+// wave_query_consts8; kk: the eight channels' fp16 scales).  Here a~ = 256 a1 + a0 with
+// a1 = floor((a~ + 128) / 256) in [-8, 8] and a0 in [-128, 127], both signed bytes, so
+// that each row part of the lane's eight channels is one 8-byte store.  The rint is the
+// add of 1.5 2^23 + 128 (128 is even, so ties go as for 1.5 2^23 alone); the sum's bits
+// are 0x4B400000 + v with v = a~ + 128, whose byte 1 is floor(v / 256) = a1 (the 0x4000
+// above it has a zero low byte) and whose byte 0 is v mod 256 = a0 + 128, a0 once its top
+// bit is flipped.  (q 2^(11 - x)) kscale is exact in fp32, as for build_operand.
+template <int G>
+__device__ inline void build_operand8(uint8_t *Abuf, const float *q8A, const float *q8B, uint4 kk, float scale,
+                                      int lane) {
+  constexpr bool kTwo = G > 4;
+  const int gA = lane >> 4, gB = gA + 4, o = lane & 15;
+  const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+  float ks[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ks[2 * j] = h2f((uint16_t)(kw[j] & 0xFFFFu));
+    ks[2 * j + 1] = h2f((uint16_t)(kw[j] >> 16));
+  }
+  auto one = [&](const float *q8, int g) {
+    constexpr float kMagic = 0x1.8p23f + 128.0f;
+    uint32_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = __float_as_uint(__builtin_fmaf(q8[i] * scale, ks[i], kMagic));
+    uint32_t pr[4];   // channels 2j, 2j + 1: a1, a1, a0 + 128, a0 + 128
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x04000501u);
+    const uint32_t hi0 = __builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u);
+    const uint32_t hi1 = __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u);
+    const uint32_t lo0 = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u) ^ 0x80808080u;
+    const uint32_t lo1 = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u) ^ 0x80808080u;
+    *reinterpret_cast<uint2 *>(Abuf + op_octet(op_row(g, 0), o)) = make_uint2(hi0, hi1);
+    *reinterpret_cast<uint2 *>(Abuf + op_octet(op_row(g, 1), o)) = make_uint2(lo0, lo1);
+  };
+  if (gA < G) one(q8A, gA);
+  if (kTwo && gB < G) one(q8B, gB);
 }
 
 // Weight grid of one block: alpha = 2^(x - 11) with m = max_t |q_t| kscale_t = f 2^x.
@@ -713,13 +751,21 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int gA = grp, gB = grp + 4;
   const bool hasA = gA < G, hasB = kTwo && gB < G;
   const int hq0 = h * G;
-  // the group's queries (fp16 -> fp32, exact): the lane's two channels of each
-  float qv0[G], qv1[G];
+  // the group's queries (fp16 -> fp32, exact): the lane's eight channels of slots gA and
+  // gB (read at clamped rows, zero for slots past G)
+  float q8A[8], q8B[8];
+  {
+    const int o = lane & 15;
+    const uint4 wa = *reinterpret_cast<const uint4 *>(a.q + (int64_t)(hq0 + min(gA, G - 1)) * kD + 8 * o);
+    const uint4 wb = *reinterpret_cast<const uint4 *>(a.q + (int64_t)(hq0 + min(gB, G - 1)) * kD + 8 * o);
+    const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, ub[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint32_t w2 = reinterpret_cast<const uint32_t *>(a.q + (int64_t)(hq0 + g) * kD)[lane];
-    qv0[g] = h2f((uint16_t)(w2 & 0xFFFFu));
-    qv1[g] = h2f((uint16_t)(w2 >> 16));
+    for (int j = 0; j < 4; ++j) {
+      q8A[2 * j] = hasA ? h2f((uint16_t)(ua[j] & 0xFFFFu)) : 0.0f;
+      q8A[2 * j + 1] = hasA ? h2f((uint16_t)(ua[j] >> 16)) : 0.0f;
+      q8B[2 * j] = hasB ? h2f((uint16_t)(ub[j] & 0xFFFFu)) : 0.0f;
+      q8B[2 * j + 1] = hasB ? h2f((uint16_t)(ub[j] >> 16)) : 0.0f;
+    }
   }
 
   // Software pipeline: the loads of chunks c + 1 .. c + kScanBufs - 1 (two blocks each)
@@ -727,7 +773,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // issues no global stores or atomics, so the compiler can wait for the older loads only.
   struct ChunkIn {
     uint4 cw[4];
-    uint32_t kk[2];
+    uint4 kk[2];        // the lane's eight channels' scales of both blocks
     float ksmax[2];
     uint16_t kerr;      // key-error code of the chunk's key `lane`
     uint16_t vn;
@@ -748,7 +794,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       (void *)(a.vnorm + kvh * a.n_cap + blk0 * kBlk), (short)0, (int)tokw * 2, kBufDword3);
   auto load_chunk = [&](int c0, ChunkIn &in) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    const int oc = c0 * 2048 + lane * 16, ok = c0 * 2 * kD + lane * 4, om = c0 * (int)sizeof(BlockMeta);
+    const int oc = c0 * 2048 + lane * 16, ok = c0 * 2 * kD + (lane & 15) * 16, om = c0 * (int)sizeof(BlockMeta);
     const int ov = c0 * kBlk * 2 + lane * 2;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -757,7 +803,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
-      in.kk[bi] = __builtin_amdgcn_raw_buffer_load_b32(rs_ks, ok + bi * 2 * kD, 0, 0);
+      const v4u k4 = __builtin_amdgcn_raw_buffer_load_b128(rs_ks, ok + bi * 2 * kD, 0, 0);
+      in.kk[bi] = make_uint4(k4.x, k4.y, k4.z, k4.w);
       in.ksmax[bi] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bm, om + bi * (int)sizeof(BlockMeta), 0, 0));
     }
     in.kerr = __builtin_amdgcn_raw_buffer_load_b16(rs_kerr, ov, 0, 0);
@@ -779,7 +826,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   v4i qa0, qa1;
   float qnpA, qnpB, qmax;
   double obeta[2], oqabs[2];
-  wave_query_consts<G>(qv0, qv1, lane, reinterpret_cast<float *>(Abuf), qmax, qnpA, qnpB, obeta, oqabs, qa0, qa1);
+  wave_query_consts8<G>(q8A, q8B, lane, Abuf, qmax, qnpA, qnpB, obeta, oqabs, qa0, qa1);
   init_operand(Abuf, lane, !kTwo);
   init_operand(Abuf1, lane, !kTwo);
   offset_compute(off0, qa0, qa1, obeta, oqabs, nblk, G, lane, keep_offsets, 0);
@@ -812,8 +859,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     float scales[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) block_grid32(qmax, in.ksmax[bi], al[bi], scales[bi]);
-    build_operand<G>(Abuf, qv0, qv1, in.kk[0], scales[0], lane);
-    if (nb2 > 1) build_operand<G>(Abuf1, qv0, qv1, in.kk[1], scales[1], lane);
+    build_operand8<G>(Abuf, q8A, q8B, in.kk[0], scales[0], lane);
+    if (nb2 > 1) build_operand8<G>(Abuf1, q8A, q8B, in.kk[1], scales[1], lane);
   };
   // process(c0, cur, nxt): bounds of the chunk staged before, with the next chunk hashed
   // while the operand reads are in flight and staged while the products run.  The
@@ -878,13 +925,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         const float kerr = Tg == 0 ? kerr4.x : (Tg == 1 ? kerr4.y : (Tg == 2 ? kerr4.z : kerr4.w));
         const bool valid = decltype(kFull)::value || tt < nval;
         if (hasA) {
-          const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 128 + acc[1], Csum, kerr, eup);
+          const Bound32 r = bound32(baseA, ebpA, alpha32, halpha32, qnpA, acc[0] * 256 + acc[1], Csum, kerr, eup);
           uA = T ? fmaxf(uA, valid ? r.ub : kNegInf) : (valid ? r.ub : kNegInf);
           eA = T ? fmaxf(eA, valid ? r.ube : kNegInf) : (valid ? r.ube : kNegInf);
           lbA = fmaxf(lbA, valid ? r.lb : kNegInf);
         }
         if (hasB) {
-          const Bound32 r = bound32(baseB, ebpB, alpha32, halpha32, qnpB, acc[2] * 128 + acc[3], Csum, kerr, eup);
+          const Bound32 r = bound32(baseB, ebpB, alpha32, halpha32, qnpB, acc[2] * 256 + acc[3], Csum, kerr, eup);
           uB = T ? fmaxf(uB, valid ? r.ub : kNegInf) : (valid ? r.ub : kNegInf);
           eB = T ? fmaxf(eB, valid ? r.ube : kNegInf) : (valid ? r.ube : kNegInf);
           lbB = fmaxf(lbB, valid ? r.lb : kNegInf);
