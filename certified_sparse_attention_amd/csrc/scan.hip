@@ -418,15 +418,18 @@ __device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const floa
 }
 
 // The group's integer weights of one block in the streaming scan (lanes as for
-// wave_query_consts8; kk: the eight channels' fp16 scales).  Here a~ = 256 a1 + a0 with
-// a1 = floor((a~ + 128) / 256) in [-8, 8] and a0 in [-128, 127], both signed bytes, so
-// that each row part of the lane's eight channels is one 8-byte store.  The rint is the
-// add of 1.5 2^23 + 128 (128 is even, so ties go as for 1.5 2^23 alone); the sum's bits
-// are 0x4B400000 + v with v = a~ + 128, whose byte 1 is floor(v / 256) = a1 (the 0x4000
-// above it has a zero low byte) and whose byte 0 is v mod 256 = a0 + 128, a0 once its top
-// bit is flipped.  (q 2^(11 - x)) kscale is exact in fp32, as for build_operand.
+// wave_query_consts8; kk: the eight channels' fp16 scales; alpha = 2^(x - 11), the
+// block's grid step, or 0).  Here a~ = 256 a1 + a0 with a1 = floor((a~ + 128) / 256) in
+// [-8, 8] and a0 in [-128, 127], both signed bytes, so that each row part of the lane's
+// eight channels is one 8-byte store.  The rint is one fused multiply-add of q kscale
+// (exact inside the FMA) and (1.5 2^23 + 128) alpha: the sum's spacing is alpha, so it
+// rounds q kscale / alpha to the nearest integer, ties to even (128 is even), and its
+// mantissa bits are 0x400000 + v with v = a~ + 128.  Byte 1 of them is floor(v / 256) =
+// a1 (the 0x4000 above it has a zero low byte) and byte 0 is v mod 256 = a0 + 128, a0
+// once its top bit is flipped.  With alpha = 0 (a zero query group or zero scales) every
+// product is 0 and the constant is taken unscaled, so that every weight is 0.
 template <int G>
-__device__ inline void build_operand8(uint8_t *Abuf, const float *q8A, const float *q8B, uint4 kk, float scale,
+__device__ inline void build_operand8(uint8_t *Abuf, const float *q8A, const float *q8B, uint4 kk, float alpha,
                                       int lane) {
   constexpr bool kTwo = G > 4;
   const int gA = lane >> 4, gB = gA + 4, o = lane & 15;
@@ -437,11 +440,12 @@ __device__ inline void build_operand8(uint8_t *Abuf, const float *q8A, const flo
     ks[2 * j] = h2f((uint16_t)(kw[j] & 0xFFFFu));
     ks[2 * j + 1] = h2f((uint16_t)(kw[j] >> 16));
   }
+  constexpr float kMagic = 0x1.8p23f + 128.0f;
+  const float magic = (alpha > 0.0f) ? kMagic * alpha : kMagic;
   auto one = [&](const float *q8, int g) {
-    constexpr float kMagic = 0x1.8p23f + 128.0f;
     uint32_t t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = __float_as_uint(__builtin_fmaf(q8[i] * scale, ks[i], kMagic));
+    for (int i = 0; i < 8; ++i) t[i] = __float_as_uint(__builtin_fmaf(q8[i], ks[i], magic));
     uint32_t pr[4];   // channels 2j, 2j + 1: a1, a1, a0 + 128, a0 + 128
 #pragma unroll
     for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_perm(t[2 * j + 1], t[2 * j], 0x04000501u);
@@ -859,8 +863,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     float scales[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) block_grid32(qmax, in.ksmax[bi], al[bi], scales[bi]);
-    build_operand8<G>(Abuf, q8A, q8B, in.kk[0], scales[0], lane);
-    if (nb2 > 1) build_operand8<G>(Abuf1, q8A, q8B, in.kk[1], scales[1], lane);
+    build_operand8<G>(Abuf, q8A, q8B, in.kk[0], al[0], lane);
+    if (nb2 > 1) build_operand8<G>(Abuf1, q8A, q8B, in.kk[1], al[1], lane);
   };
   // process(c0, cur, nxt): bounds of the chunk staged before, with the next chunk hashed
   // while the operand reads are in flight and staged while the products run.  The
