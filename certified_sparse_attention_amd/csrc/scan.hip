@@ -13,8 +13,7 @@
 // with I_gi = sum_t a~_gbt c_it and C_i = sum_t c_it from one i8 MFMA chain, and
 // base_gb = beta_g kappa_b sum_t q~_gt z_bt from a second one.  The integer weights
 // a~ = rint(q kscale 2^(11-x)) lie in [-2048, 2048]; each is split into two int8 rows of
-// the MFMA's A operand, a~ = 256 a1 + a0 (a1 in [-8, 8], a0 in [-128, 127]) in the
-// streaming scan and a~ = 128 a1 + a0 (a1 in [-16, 16], a0 in [0, 127]) in the refinement.
+// the MFMA's A operand, a~ = 256 a1 + a0 (a1 in [-8, 8], a0 in [-128, 127]).
 //
 // MFMA operand rows (16): query g's high part at row 4(g%4) + 2(g/4), its low part
 // one row below; row 14 is all ones (gives C_i); row 15 is zero.  So G <= 7.
@@ -387,37 +386,7 @@ __device__ inline void offset_terms(const ScanArgs &a, int h, int64_t kvh, int64
       col0);
 }
 
-// The query group's integer weights of one block, written into the A operand rows.
-// Lane l owns channels 2l, 2l + 1; a~ = rint((q kscale) 2^(11 - x)) = 128 a1 + a0 with
-// a1 = floor(a~ / 128) in [-16, 16] and a0 in [0, 127], both signed bytes.  The
-// power-of-two scale is applied to kscale first (exact, and the product rounds the same
-// way); the split of both channels' weights runs on packed 16-bit integers (|a~| <= 2048).
-// rint is the add of 1.5 2^23: for |p| < 2^22 the sum lies in [2^23, 2^24), where the
-// spacing is 1, so it rounds p to the nearest integer, ties to even, and its low 16 bits
-// hold that integer modulo 2^16 (the constant's own low 16 bits are zero).  The product
-// q kscale 2^(11 - x) of two fp16 values and a power of two is exact in fp32, so one
-// fused multiply-add gives the same sum as the product followed by the add.
-typedef short short2v __attribute__((ext_vector_type(2)));
-template <int G>
-__device__ inline void build_operand(uint8_t *Abuf, const float *qv0, const float *qv1, uint32_t kk,
-                                     float scale, int lane) {
-  const float ks0 = h2f((uint16_t)(kk & 0xFFFFu)) * scale, ks1 = h2f((uint16_t)(kk >> 16)) * scale;
-  const int kg = lane >> 4, kh = (lane >> 3) & 1, bb = 2 * (lane & 7);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float t0 = __builtin_fmaf(qv0[g], ks0, 0x1.8p23f), t1 = __builtin_fmaf(qv1[g], ks1, 0x1.8p23f);
-    const short2v w = __builtin_bit_cast(short2v, __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u));
-    const short2v a1 = w >> (short)7;
-    const short2v a0 = w & (short)127;
-    // bytes: a1 of both channels (row part 0), then a0 of both channels (row part 1)
-    const uint32_t pk = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
-                                              0x06040200u);
-    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 0) + 16 * kg) * 16 + bb) = (uint16_t)pk;
-    *reinterpret_cast<uint16_t *>(Abuf + kh * 1024 + (op_row(g, 1) + 16 * kg) * 16 + bb) = (uint16_t)(pk >> 16);
-  }
-}
-
-// The group's integer weights of one block in the streaming scan (lanes as for
+// The group's integer weights of one block (lanes as for
 // wave_query_consts8; kk: the eight channels' fp16 scales; alpha = 2^(x - 11), the
 // block's grid step, or 0).  Here a~ = 256 a1 + a0 with a1 = floor((a~ + 128) / 256) in
 // [-8, 8] and a0 in [-128, 127], both signed bytes, so that each row part of the lane's
@@ -989,12 +958,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 // Everything one chunk (two blocks) of the refinement reads from the packed cache: its
 // codes (four tiles), the key-error code of the lane's key and both blocks' scale maximum
-// and channel scales of the lane's two channels.
+// and channel scales of the lane's eight channels (8 (lane % 16) ..).
 struct ChunkLoads {
   uint4 cw[4];
   uint32_t kerr;
   float ksmax[2];
-  uint32_t kk[2];
+  uint4 kk[2];
 };
 
 __device__ inline void load_chunk(const ScanArgs &a, int u, int64_t bA, int nb2, int lane, ChunkLoads &L) {
@@ -1009,8 +978,8 @@ __device__ inline void load_chunk(const ScanArgs &a, int u, int64_t bA, int nb2,
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
     L.ksmax[bi] = (bi < nb2) ? a.bmeta[h * a.nb_cap + bA + bi].ksmax : 0.0f;
-    L.kk[bi] = (bi < nb2) ? reinterpret_cast<const uint32_t *>(a.kscale + (h * a.nb_cap + bA + bi) * kD)[lane]
-                          : 0u;
+    L.kk[bi] = (bi < nb2) ? reinterpret_cast<const uint4 *>(a.kscale + (h * a.nb_cap + bA + bi) * kD)[lane & 15]
+                          : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -1197,11 +1166,12 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
     RefineSlot &S = slot_all[cc >> 3];
     const int jh = slot_head(cc >> 3), jhq0 = jh * G;   // the job's unit
     const int64_t jnpool = unit_npool(a.b, jh, a.W), jkv = unit_kv(a.b, jh);
-    float qv0[kMaxG], qv1[kMaxG];
+    // the lane's eight channels of its query slots (as in the streaming scan)
+    float q8A[8], q8B[8];
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) {
-      qv0[g] = (g < G) ? S.q[g][2 * lane] : 0.0f;
-      qv1[g] = (g < G) ? S.q[g][2 * lane + 1] : 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      q8A[i] = hasA ? S.q[gA][8 * (lane & 15) + i] : 0.0f;
+      q8B[i] = hasB ? S.q[hasB ? gB : 0][8 * (lane & 15) + i] : 0.0f;
     }
     const float qmax = S.qmax;
     const uint64_t prefix = S.prefix;
@@ -1233,15 +1203,16 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
       float scale;
       block_grid(qmax, cur.ksmax[bi], alpha, scale);
       const double halpha = alpha / 2.0;
-      const uint32_t kk = cur.kk[bi];
+      const uint4 kk = cur.kk[bi];
+      const float alpha32 = (float)alpha;   // a power of two (or 0): exact
       switch (G) {
-        case 1: build_operand<1>(Abuf, qv0, qv1, kk, scale, lane); break;
-        case 2: build_operand<2>(Abuf, qv0, qv1, kk, scale, lane); break;
-        case 3: build_operand<3>(Abuf, qv0, qv1, kk, scale, lane); break;
-        case 4: build_operand<4>(Abuf, qv0, qv1, kk, scale, lane); break;
-        case 5: build_operand<5>(Abuf, qv0, qv1, kk, scale, lane); break;
-        case 6: build_operand<6>(Abuf, qv0, qv1, kk, scale, lane); break;
-        default: build_operand<7>(Abuf, qv0, qv1, kk, scale, lane); break;
+        case 1: build_operand8<1>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        case 2: build_operand8<2>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        case 3: build_operand8<3>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        case 4: build_operand8<4>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        case 5: build_operand8<5>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        case 6: build_operand8<6>(Abuf, q8A, q8B, kk, alpha32, lane); break;
+        default: build_operand8<7>(Abuf, q8A, q8B, kk, alpha32, lane); break;
       }
       wave_sync();
       const v4i A0 = *reinterpret_cast<const v4i *>(Abuf + lane * 16);
@@ -1271,7 +1242,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
         ubB[Tg] = 0.0;
         if (pos < jnpool) {
           if (hasA) {
-            const int I = acc[0] * 128 + acc[1];
+            const int I = acc[0] * 256 + acc[1];
             const double shat = (baseA + alpha * (double)I) * kRsqrtD;
             const double slack = (((halpha * (double)Csum + qnpA * kerr) + ebA) + padA) * kRsqrtD;
             const double ub = shat + slack, lb = shat - slack;
@@ -1283,7 +1254,7 @@ __global__ __launch_bounds__(256) void refine_kernel(ScanArgs a) {
             if (a.diag || ub + Eup >= thrA - marg || ub >= clo2A - marg) liveA |= 1u << Tg;
           }
           if (hasB) {
-            const int I = acc[2] * 128 + acc[3];
+            const int I = acc[2] * 256 + acc[3];
             const double shat = (baseB + alpha * (double)I) * kRsqrtD;
             const double slack = (((halpha * (double)Csum + qnpB * kerr) + ebB) + padB) * kRsqrtD;
             const double ub = shat + slack, lb = shat - slack;
